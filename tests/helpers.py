@@ -1,0 +1,52 @@
+"""Test helpers: assemble oracle problems from the seeded generators.
+
+Only tests import this module.  Quantised weights for the oracle come from the
+oracle's own quantiser; nothing here touches the GPU library.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synthetic as S
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    """||a - b||_F / ||b||_F in float64 (0 when both are 0)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b.ravel())
+    na = np.linalg.norm((a - b).ravel())
+    if nb == 0.0:
+        return 0.0 if na == 0.0 else float("inf")
+    return float(na / nb)
+
+
+def bf(bits) -> np.ndarray:
+    return oracle.bf16_to_float(bits).astype(np.float64)
+
+
+def quantize_weights(w_gate_up_bits: np.ndarray, w_down_bits: np.ndarray, fmt_w: int = oracle.E4M3):
+    """Pre-quantise weights along the backward contraction axis:
+    W_down [E,I,H] along H, W_gate_up [E,H,2,I] along I (both: the last axis)."""
+    E, H, _, I = w_gate_up_bits.shape
+    gu_c, gu_s = oracle.quantize(w_gate_up_bits.reshape(E * H * 2, I), 1, fmt_w)
+    d_c, d_s = oracle.quantize(w_down_bits.reshape(E * I, H), 1, fmt_w)
+    return (gu_c.reshape(E, H, 2, I), gu_s.reshape(E, H, 2, I // 32),
+            d_c.reshape(E, I, H), d_s.reshape(E, I, H // 32))
+
+
+def moe_problem(cfg: S.MoeConfig, nthreads: int = 0, N=None):
+    """(oracle.MoeProblem, extras) for a workload config, built on the host."""
+    topk, aff = S.routing(cfg)
+    if N is None:
+        N = oracle.num_blocks(cfg.T, cfg.K, cfg.E, cfg.B)
+    tpid, b2e = oracle.build_blocks(topk, cfg.E, cfg.B, N)
+    t = S.moe_tensors(cfg, N, "cpu")
+    bits = {k: (None if v is None else S.bf16_bits(v)) for k, v in t.items()}
+    gu_c, gu_s, d_c, d_s = quantize_weights(bits["w_gate_up"], bits["w_down"])
+    p = oracle.MoeProblem(T=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, N=N, B=cfg.B, hidden=bits["hidden"],
+                          aff=aff, wgu_codes=gu_c, wgu_scales=gu_s, wd_codes=d_c, wd_scales=d_s,
+                          tpid=tpid, b2e=b2e, dy=bits["dy"], ckpt=bits["ckpt"], b2=bits["b2"],
+                          affinity_on=cfg.affinity_on, has_bias=int(cfg.has_bias), nthreads=nthreads)
+    return p, dict(topk=topk, bits=bits)
