@@ -1,0 +1,210 @@
+/*
+ * mxfp8_moe.h -- C ABI of the MI355X (gfx950) MXFP8 MoE-backward library
+ * (libmxfp8_moe.so).
+ *
+ * What it computes is defined by three pages:
+ *   [P1] AWS Neuron NKI library, "Blockwise MM Backward MXFP8 Kernel API
+ *        Reference": gradients of a blockwise Mixture-of-Experts SwiGLU layer
+ *        from BF16 activations, MXFP8 weights and block routing indices.
+ *   [P2] AWS Neuron NKI library, "Matmul MXFP8 Backward Kernel API
+ *        Reference": dX and dW of a linear layer Y = X W^T with MXFP8
+ *        quantised operands.
+ *   [P3] sonic-moe, functional/backward.py: the fused gated-activation
+ *        backward epilogue and the bias / affinity reductions.
+ *
+ * Conventions for every entry point
+ *  - Pointers named in a signature are DEVICE pointers unless marked "host".
+ *    bf16 tensors are passed as uint16_t bit patterns; all tensors are dense,
+ *    row-major and must be 16-byte aligned.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates or frees device memory and keeps no state between calls.
+ *  - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t, NULL
+ *    for the default stream) and the call returns without synchronising.  A
+ *    device fault surfaces at the caller's next synchronisation.
+ *  - Arguments are validated before anything is enqueued.  On a validation
+ *    failure the call returns a non-zero mxfp8_status, records a message that
+ *    mxfp8_last_error() returns on the calling thread, and leaves every output
+ *    untouched.  No C++ exception crosses this interface.
+ *  - Outputs are fully overwritten (never accumulated into).
+ *
+ * MXFP8 (P1: "32-element quantization group"): a group of 32 consecutive
+ * elements along the quantised axis shares one E8M0 scale byte S (value
+ * 2^(S-127)); each element is an 8-bit OCP E4M3 or E5M2 code.  The scale is
+ * X = floor(log2(amax)) - emax (emax 8 for E4M3, 15 for E5M2), clamped to
+ * [-127,127], with X = -127 for an all-zero group; codes round v*2^-X to
+ * nearest-even and saturate at the format maximum.
+ */
+#ifndef MXFP8_MOE_H
+#define MXFP8_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MXFP8_E4M3 = 0, MXFP8_E5M2 = 1 } mxfp8_fmt;
+
+typedef enum {
+  MXFP8_OK = 0,
+  MXFP8_ERR_INVALID_ARG = 1, /* bad shape, null pointer, misalignment, bad enum   */
+  MXFP8_ERR_UNSUPPORTED = 2, /* a valid combination this library does not run    */
+  MXFP8_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query */
+  MXFP8_ERR_HIP = 4          /* the HIP runtime refused a launch                 */
+} mxfp8_status;
+
+/* Host.  Message of the last failing call on this thread ("" if none). */
+const char* mxfp8_last_error(void);
+
+/* Host.  Library version string. */
+const char* mxfp8_version(void);
+
+/* ---------------------------------------------------------------------------
+ * mxfp8_quantize -- P1's 32-element MXFP8 group quantisation of a BF16 tensor.
+ *   x      [rows, cols] bf16.
+ *   axis 1: groups of 32 along cols;  scales [rows, cols/32]  (cols % 32 == 0).
+ *   axis 0: groups of 32 along rows;  scales [rows/32, cols]  (rows % 32 == 0).
+ *   fmt    MXFP8_E4M3 or MXFP8_E5M2.
+ *   codes  [rows, cols] u8, in x's layout;  scales: E8M0 bytes as above.
+ * Errors: INVALID_ARG for a null pointer, a bad axis/fmt, a non-multiple of 32
+ * along the quantised axis or rows*cols == 0 with non-null pointers is fine
+ * (nothing is enqueued).
+ * ------------------------------------------------------------------------- */
+int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis, int fmt,
+                   uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * matmul_mxfp8_bwd -- P2: the backward of Y = X W^T with X [M,K], W [N,K]:
+ *   input_grad  dX = dY W    [M,K]  (contraction over N)
+ *   weight_grad dW = dY^T X  [N,K]  (contraction over M)
+ * Each operand is quantised in groups of 32 along the contraction axis of the
+ * product it feeds (dY twice: along N for dX, along M for dW), products are
+ * accumulated in fp32 and the outputs are bf16 (P2: output_dtype bf16).
+ *   output_grad [M,N], weights [N,K], input_activation [M,K]: bf16.
+ *   fmt_*: element format per operand (P2's default float8_e5m2; the common
+ *          training choice is E5M2 for dY, E4M3 for W and X).
+ *   M % 32 == 0, N % 32 == 0, K % 32 == 0.
+ *   workspace: >= matmul_mxfp8_bwd_workspace_size(M,N,K) bytes of device
+ *   memory, 256-byte aligned; it holds the quantised operands (P2:
+ *   "spill quantized blocks to HBM for reuse"):
+ *     [0]  dY codes along N  [M,N]  + scales [M,N/32]
+ *     [1]  W^T codes along N [K,N]  + scales [K,N/32]
+ *     [2]  dY^T codes along M [N,M] + scales [N,M/32]
+ *     [3]  X^T codes along M [K,M]  + scales [K,M/32]
+ *   each region starting on a 256-byte boundary, in this order, codes first.
+ * ------------------------------------------------------------------------- */
+size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
+int matmul_mxfp8_bwd(const uint16_t* output_grad, const uint16_t* weights,
+                     const uint16_t* input_activation, int64_t M, int64_t N, int64_t K,
+                     int fmt_output_grad, int fmt_weights, int fmt_input,
+                     uint16_t* input_grad, uint16_t* weight_grad,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Routing blocks (P1 parameters token_position_to_id [N*B], block_to_expert
+ * [N,1] and the "Dimensions" paragraph).  P1 leaves their construction to
+ * the caller; this helper builds them from top-k expert ids:
+ *   expert e owns ceil(n_e/B) consecutive blocks, experts in ascending id,
+ *   tokens in ascending id within an expert; empty slots hold -1; blocks past
+ *   the last used one hold -1 everywhere and map to expert E-1.
+ * moe_num_blocks (host) returns P1's N = (T*TopK - (E-1))/B + E - 1 with the
+ * division rounded up -- the worst case over all routings -- or -1 when
+ * T*K < E or a size is not positive.
+ *   topk_ids [T,K] int32, distinct per row, each in [0,E) (ids outside [0,E)
+ *   are ignored).  N >= moe_num_blocks(T,K,E,B) (checked).
+ *   workspace >= moe_build_blocks_workspace_size(E) bytes.
+ * ------------------------------------------------------------------------- */
+int64_t moe_num_blocks(int64_t T, int64_t K, int64_t E, int64_t block_size);
+size_t moe_build_blocks_workspace_size(int64_t E);
+int moe_build_blocks(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
+                     int64_t block_size, int64_t N, int32_t* token_position_to_id,
+                     int32_t* block_to_expert, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_bwd_mxfp8 -- P1's blockwise_mm_bwd_mxfp8: all gradients of a blockwise
+ * MoE SwiGLU layer.  Forward, per routed (token t, expert e) with affinity a:
+ *   g = x_t Wgu[e][:,0,:] (+b1),  u = x_t Wgu[e][:,1,:] (+b1),  inter = silu(g)*u
+ *   affinity on H (0): y_t += a * (inter Wd[e] + b2[e])
+ *   affinity on I (1): y_t += (a * inter) Wd[e]            (no bias)
+ * Backward (P1 phases; P3's epilogue):
+ *   Phase 1  dS = dY_t Wd[e]^T (quantised along H), fused epilogue:
+ *            d(a) = sum_i dS*inter + <dY_t, b2[e]>,  dInter = a*dS,
+ *            dGate = dInter*up*silu'(g),  dUp = dInter*silu(g)
+ *   Phase 3  dX_t += [dGate,dUp] Wgu[e]^T    (quantised along I)
+ *   Phase 2  dWgu[e] = sum over the expert's slots of x^T [dGate,dUp]
+ *   Phase 4  dWd[e]  = sum of inter^T (a*dY)   (on H)  or  (a*inter)^T dY (on I)
+ *   bias     db1[e] = sum [dGate,dUp],  db2[e] = sum a*dY
+ * Phases 2 and 4 quantise along the token axis in groups of 32 consecutive
+ * slots of one block.  Rounding points: gate_act, inter, a*inter, a*dY, dGate
+ * and dUp are bf16 (the precision of the checkpoints P1 accepts); dS, dInter,
+ * d(a) and every accumulator are fp32; outputs are bf16.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int64_t T, H, I, E, N, block_size;   /* I is P1's I_TP; block_size in {128,256,512,1024};
+                                          H % 32 == 0, I % 32 == 0, N >= moe_num_blocks  */
+  const uint16_t* hidden_states;                  /* [T,H] bf16                          */
+  const float*    expert_affinities_masked;       /* [T*E] fp32, index t*E+e             */
+  const uint8_t*  gate_up_codes;                  /* [E,H,2,I] codes, fmt_weight         */
+  const uint8_t*  gate_up_scales;                 /* [E,H,2,I/32]: groups along I        */
+  const uint8_t*  down_codes;                     /* [E,I,H] codes, fmt_weight           */
+  const uint8_t*  down_scales;                    /* [E,I,H/32]: groups along H          */
+  const int32_t*  token_position_to_id;           /* [N*B]; outside [0,T) = padding slot */
+  const int32_t*  block_to_expert;                /* [N], each in [0,E)                  */
+  const uint16_t* output_hidden_states_grad;      /* [T,H] bf16                          */
+  const uint16_t* gate_up_proj_act_checkpoint_T;  /* [N,2,I,B] bf16, required:
+                                                     [b,0,i,p] = gate_pre, [b,1,i,p] = up;
+                                                     padding slots' values are ignored  */
+  const uint16_t* down_proj_bias;                 /* [E,H] bf16, required iff has_bias   */
+  int affinity_on;      /* 0 = affinity on H (output), 1 = on I (intermediate)          */
+  int has_bias;         /* 1: add <dY,b2> to d(a) and write both bias gradients         */
+  int fmt_weight;       /* element format of the pre-quantised weights (E4M3)           */
+  int fmt_act;          /* activations X, inter, a*inter in Phases 2/4 (E4M3)          */
+  int fmt_grad;         /* dY, a*dY, dGate/dUp (E5M2)                                   */
+  uint16_t* hidden_states_grad;                   /* [T,H] bf16; unrouted tokens -> 0   */
+  uint16_t* expert_affinities_masked_grad;        /* [T*E] bf16; unrouted pairs -> 0    */
+  uint16_t* gate_up_proj_weight_grad;             /* [E,H,2,I] bf16; empty experts -> 0 */
+  uint16_t* down_proj_weight_grad;                /* [E,I,H] bf16                        */
+  uint16_t* gate_and_up_proj_bias_grad;           /* [E,2,I] bf16 (has_bias)             */
+  uint16_t* down_proj_bias_grad;                  /* [E,H] bf16 (has_bias)               */
+} moe_bwd_mxfp8_args;
+
+/* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised
+ * operands can be read back from them after a call:
+ *   dy_codes/dy_scales        [T,H] / [T,H/32]        dY along H (Phase 1)
+ *   x_tok_codes/scales        [H,P] / [H,P/32]        X along slots (Phase 2), P = N*B
+ *   gy_tok_codes/scales       [H,P] / [H,P/32]        a*dY (on H) or dY (on I), Phase 4
+ *   inter_tok_codes/scales    [I,P] / [I,P/32]        inter (on H) or a*inter (on I)
+ *   dgu_row_codes/scales      [P,2I] / [P,2I/32]      [dGate|dUp] along I (Phase 3)
+ *   dgu_tok_codes/scales      [2I,P] / [2I,P/32]      [dGate;dUp] along slots (Phase 2)
+ *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
+ *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
+ *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending.
+ * Pad slots hold code 0.  Rows of a region are contiguous; no padding between rows. */
+typedef struct {
+  size_t dy_codes, dy_scales, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
+      inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
+      dgu_tok_scales, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      expert_block_list, total;
+} moe_bwd_mxfp8_workspace_layout;
+
+/* Host.  Fills *layout for the shapes in *args (pointers are not read).
+ * Returns MXFP8_OK or INVALID_ARG. */
+int moe_bwd_mxfp8_workspace_query(const moe_bwd_mxfp8_args* args,
+                                  moe_bwd_mxfp8_workspace_layout* layout);
+/* Host.  Workspace size in bytes (0 on invalid shapes). */
+size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
+
+/* Enqueues the whole backward.  Errors: INVALID_ARG (shapes, null required
+ * pointers, alignment, formats), UNSUPPORTED (block_size outside the set,
+ * affinity on I together with a bias), WORKSPACE (too small).  Device-side
+ * preconditions (not checked): block_to_expert entries in [0,E) (blocks with
+ * other values are skipped); each (t,e) pair appears in at most one slot. */
+int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP8_MOE_H */

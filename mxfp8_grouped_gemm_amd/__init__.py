@@ -1,0 +1,259 @@
+"""Python binding of libmxfp8_moe.so (include/mxfp8_moe.h).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the library's gfx950 kernels.
+There is no fallback -- if the shared library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+E4M3 = 0
+E5M2 = 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp8_moe.so")
+
+_lib = None
+_p = C.c_void_p
+_i64 = C.c_int64
+
+
+class MxError(RuntimeError):
+    """A library call returned a non-zero mxfp8_status."""
+
+    def __init__(self, name, status, msg):
+        super().__init__(f"{name} failed (status {status}): {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with mxfp8_grouped_gemm_amd/build.py "
+                               "(or __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+class MoeBwdArgs(C.Structure):
+    _fields_ = [("T", _i64), ("H", _i64), ("I", _i64), ("E", _i64), ("N", _i64), ("block_size", _i64),
+                ("hidden_states", _p), ("expert_affinities_masked", _p), ("gate_up_codes", _p),
+                ("gate_up_scales", _p), ("down_codes", _p), ("down_scales", _p),
+                ("token_position_to_id", _p), ("block_to_expert", _p), ("output_hidden_states_grad", _p),
+                ("gate_up_proj_act_checkpoint_T", _p), ("down_proj_bias", _p),
+                ("affinity_on", C.c_int), ("has_bias", C.c_int), ("fmt_weight", C.c_int),
+                ("fmt_act", C.c_int), ("fmt_grad", C.c_int),
+                ("hidden_states_grad", _p), ("expert_affinities_masked_grad", _p),
+                ("gate_up_proj_weight_grad", _p), ("down_proj_weight_grad", _p),
+                ("gate_and_up_proj_bias_grad", _p), ("down_proj_bias_grad", _p)]
+
+
+LAYOUT_FIELDS = ("dy_codes", "dy_scales", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
+                 "inter_tok_codes", "inter_tok_scales", "dgu_row_codes", "dgu_row_scales", "dgu_tok_codes",
+                 "dgu_tok_scales", "dx_acc", "daff_slot", "db1_acc", "db2_acc", "expert_block_offsets",
+                 "expert_block_list", "total")
+
+
+class MoeWorkspaceLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in LAYOUT_FIELDS]
+
+
+def _declare(L):
+    L.mxfp8_last_error.restype = C.c_char_p
+    L.mxfp8_version.restype = C.c_char_p
+    L.mxfp8_quantize.restype = C.c_int
+    L.mxfp8_quantize.argtypes = [_p, _i64, _i64, C.c_int, C.c_int, _p, _p, _p]
+    L.moe_num_blocks.restype = _i64
+    L.moe_num_blocks.argtypes = [_i64, _i64, _i64, _i64]
+    for name, res, args in (
+        ("matmul_mxfp8_bwd_workspace_size", C.c_size_t, [_i64, _i64, _i64]),
+        ("matmul_mxfp8_bwd", C.c_int, [_p, _p, _p, _i64, _i64, _i64, C.c_int, C.c_int, C.c_int, _p, _p,
+                                       _p, C.c_size_t, _p]),
+        ("moe_build_blocks_workspace_size", C.c_size_t, [_i64]),
+        ("moe_build_blocks", C.c_int, [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, C.c_size_t, _p]),
+        ("moe_bwd_mxfp8_workspace_query", C.c_int, [C.POINTER(MoeBwdArgs), C.POINTER(MoeWorkspaceLayout)]),
+        ("moe_bwd_mxfp8_workspace_size", C.c_size_t, [C.POINTER(MoeBwdArgs)]),
+        ("moe_bwd_mxfp8", C.c_int, [C.POINTER(MoeBwdArgs), _p, C.c_size_t, _p]),
+    ):
+        if hasattr(L, name):
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+
+
+def version() -> str:
+    return lib().mxfp8_version().decode()
+
+
+def last_error() -> str:
+    return lib().mxfp8_last_error().decode()
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise MxError(name, rc, last_error())
+
+
+def _stream(t: torch.Tensor):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name):
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+# ----------------------------------------------------------------------------- quantiser
+def mxfp8_quantize(x: torch.Tensor, axis: int = 1, fmt: int = E4M3):
+    """x [rows, cols] bf16 -> (codes uint8 [rows, cols], scales uint8 E8M0).
+
+    axis 1: groups of 32 along cols, scales [rows, cols/32];
+    axis 0: groups of 32 along rows, scales [rows/32, cols]."""
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    sshape = (rows, cols // 32) if axis == 1 else (rows // 32, cols)
+    scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp8_quantize(_dev(x, torch.bfloat16, "x"), rows, cols, axis, fmt, codes.data_ptr(),
+                                scales.data_ptr(), _stream(x)), "mxfp8_quantize")
+    return codes, scales
+
+
+# ----------------------------------------------------------------------------- dense backward
+def matmul_mxfp8_bwd(output_grad: torch.Tensor, weights: torch.Tensor, input_activation: torch.Tensor,
+                     fmt_output_grad: int = E5M2, fmt_weights: int = E4M3, fmt_input: int = E4M3,
+                     workspace: Optional[torch.Tensor] = None, out=None):
+    """dX = dY W [M,K] and dW = dY^T X [N,K] for Y = X W^T (bf16 in, bf16 out)."""
+    M, N = output_grad.shape
+    K = weights.shape[1]
+    L = lib()
+    ws_bytes = L.matmul_mxfp8_bwd_workspace_size(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=output_grad.device)
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.bfloat16, device=output_grad.device),
+               torch.empty((N, K), dtype=torch.bfloat16, device=output_grad.device))
+    dx, dw = out
+    _check(L.matmul_mxfp8_bwd(_dev(output_grad, torch.bfloat16, "output_grad"),
+                              _dev(weights, torch.bfloat16, "weights"),
+                              _dev(input_activation, torch.bfloat16, "input_activation"), M, N, K,
+                              fmt_output_grad, fmt_weights, fmt_input, _dev(dx, torch.bfloat16, "dx"),
+                              _dev(dw, torch.bfloat16, "dw"), workspace.data_ptr(), workspace.numel(),
+                              _stream(output_grad)), "matmul_mxfp8_bwd")
+    return dx, dw
+
+
+def matmul_workspace_regions(M: int, N: int, K: int):
+    """Byte offsets of the dense workspace regions, as documented in the header."""
+    def up(v):
+        return (v + 255) // 256 * 256
+    sizes = [(M * N, M * N // 32), (K * N, K * N // 32), (N * M, N * M // 32), (K * M, K * M // 32)]
+    off, out = 0, []
+    for c, s in sizes:
+        co = off
+        off = up(off + c)
+        so = off
+        off = up(off + s)
+        out.append((co, so))
+    return out
+
+
+# ----------------------------------------------------------------------------- routing
+def moe_num_blocks(T: int, K: int, E: int, block_size: int) -> int:
+    return int(lib().moe_num_blocks(T, K, E, block_size))
+
+
+def moe_build_blocks(topk_ids: torch.Tensor, E: int, block_size: int, N: Optional[int] = None):
+    """topk_ids [T,K] int32 -> (token_position_to_id [N*B] int32, block_to_expert [N] int32)."""
+    T, K = topk_ids.shape
+    if N is None:
+        N = moe_num_blocks(T, K, E, block_size)
+    L = lib()
+    ws = torch.empty(L.moe_build_blocks_workspace_size(E), dtype=torch.uint8, device=topk_ids.device)
+    tpid = torch.empty(N * block_size, dtype=torch.int32, device=topk_ids.device)
+    b2e = torch.empty(N, dtype=torch.int32, device=topk_ids.device)
+    _check(L.moe_build_blocks(_dev(topk_ids, torch.int32, "topk_ids"), T, K, E, block_size, N,
+                              tpid.data_ptr(), b2e.data_ptr(), ws.data_ptr(), ws.numel(), _stream(topk_ids)),
+           "moe_build_blocks")
+    return tpid, b2e
+
+
+# ----------------------------------------------------------------------------- MoE backward
+class MoeBwd:
+    """One MoE backward problem bound to device tensors (P1's argument list).
+
+    Allocates the outputs and the workspace once; ``run()`` enqueues the whole
+    backward on the current stream."""
+
+    def __init__(self, hidden_states, expert_affinities_masked, gate_up_codes, gate_up_scales, down_codes,
+                 down_scales, token_position_to_id, block_to_expert, output_hidden_states_grad, block_size,
+                 gate_up_proj_act_checkpoint_T, down_proj_bias=None, affinity_on=0, fmt_weight=E4M3,
+                 fmt_act=E4M3, fmt_grad=E5M2, workspace=None):
+        T, H = hidden_states.shape
+        E, _, _, I = gate_up_codes.shape
+        N = block_to_expert.numel()
+        dev = hidden_states.device
+        self.keep = [hidden_states, expert_affinities_masked, gate_up_codes, gate_up_scales, down_codes,
+                     down_scales, token_position_to_id, block_to_expert, output_hidden_states_grad,
+                     gate_up_proj_act_checkpoint_T, down_proj_bias]
+        has_bias = down_proj_bias is not None
+        self.out = dict(
+            dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+            daff=torch.empty(T * E, dtype=torch.bfloat16, device=dev),
+            dwgu=torch.empty((E, H, 2, I), dtype=torch.bfloat16, device=dev),
+            dwd=torch.empty((E, I, H), dtype=torch.bfloat16, device=dev),
+            db1=torch.empty((E, 2, I), dtype=torch.bfloat16, device=dev) if has_bias else None,
+            db2=torch.empty((E, H), dtype=torch.bfloat16, device=dev) if has_bias else None)
+        o = self.out
+        self.args = MoeBwdArgs(
+            T, H, I, E, N, block_size,
+            _dev(hidden_states, torch.bfloat16, "hidden_states"),
+            _dev(expert_affinities_masked, torch.float32, "expert_affinities_masked"),
+            _dev(gate_up_codes, torch.uint8, "gate_up_codes"), _dev(gate_up_scales, torch.uint8, "gate_up_scales"),
+            _dev(down_codes, torch.uint8, "down_codes"), _dev(down_scales, torch.uint8, "down_scales"),
+            _dev(token_position_to_id, torch.int32, "token_position_to_id"),
+            _dev(block_to_expert, torch.int32, "block_to_expert"),
+            _dev(output_hidden_states_grad, torch.bfloat16, "output_hidden_states_grad"),
+            _dev(gate_up_proj_act_checkpoint_T, torch.bfloat16, "gate_up_proj_act_checkpoint_T"),
+            _dev(down_proj_bias, torch.bfloat16, "down_proj_bias"),
+            affinity_on, int(has_bias), fmt_weight, fmt_act, fmt_grad,
+            o["dx"].data_ptr(), o["daff"].data_ptr(), o["dwgu"].data_ptr(), o["dwd"].data_ptr(),
+            o["db1"].data_ptr() if has_bias else None, o["db2"].data_ptr() if has_bias else None)
+        L = lib()
+        lay = MoeWorkspaceLayout()
+        _check(L.moe_bwd_mxfp8_workspace_query(C.byref(self.args), C.byref(lay)), "moe_bwd_mxfp8_workspace_query")
+        self.layout = {n: getattr(lay, n) for n in LAYOUT_FIELDS}
+        if workspace is None:
+            workspace = torch.empty(self.layout["total"], dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self.device = dev
+
+    def run(self):
+        _check(lib().moe_bwd_mxfp8(C.byref(self.args), self.workspace.data_ptr(), self.workspace.numel(),
+                                   C.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)),
+               "moe_bwd_mxfp8")
+        return self.out
+
+    def region(self, name: str, nbytes: int) -> torch.Tensor:
+        """A uint8 view of one workspace region (for reading quantised operands back)."""
+        off = self.layout[name]
+        return self.workspace[off:off + nbytes]
+
+
+def moe_bwd_mxfp8(*args, **kw):
+    """Functional form: builds a MoeBwd and runs it once; returns the gradient dict."""
+    return MoeBwd(*args, **kw).run()

@@ -1,0 +1,111 @@
+// mx_device.hpp -- device helpers for the gfx950 MXFP8 kernels: bf16 <-> fp32,
+// the E8M0 scale rule and the OCP E4M3 / E5M2 encoders.
+//
+// MX groups (P1, "Blockwise MM Backward MXFP8 Kernel API Reference": MXFP8 with
+// 32-element quantization groups): one E8M0 byte X+127 per group with
+// X = floor(log2 amax) - emax (emax 8 for E4M3, 15 for E5M2), clamped to
+// [-127,127]; element codes round v * 2^-X to nearest-even and saturate at the
+// format's largest finite value.  The encoder below works on the fp32 bit
+// pattern with integer arithmetic only, so it is exact for every input and
+// independent of the FP environment (denormal flushing, rounding mode).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int kE4M3 = 0;
+constexpr int kE5M2 = 1;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// |x| as the integer bit pattern (for max-reductions on non-negative floats:
+// ordering of non-negative IEEE patterns is the ordering of their values).
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+__device__ __forceinline__ uint32_t abs_bits_bf16(uint16_t b) { return (uint32_t(b) & 0x7fffu) << 16; }
+
+// E8M0 scale exponent X for a group whose largest magnitude has fp32 bits
+// `amax_bits`: floor(log2 amax) is the biased exponent field minus 127 for
+// normal numbers; zeros and subnormals (field 0) fall below -127 - emax and
+// clamp to -127, which is the all-zero rule as well.
+template <int FMT>
+__device__ __forceinline__ int scale_exp(uint32_t amax_bits) {
+  constexpr int emax = FMT == kE4M3 ? 8 : 15;
+  int X = int(amax_bits >> 23) - 127 - emax;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// Round-to-nearest-even right shift of a positive significand.
+__device__ __forceinline__ uint32_t rne_shr(uint32_t x, int s) {
+  if (s <= 0) return x;
+  if (s >= 32) return 0;
+  const uint32_t r = x >> s;
+  const uint32_t rem = x & ((1u << s) - 1u);
+  const uint32_t half = 1u << (s - 1);
+  return r + ((rem > half) || (rem == half && (r & 1u)) ? 1u : 0u);
+}
+
+// Code of v * 2^-X in format FMT (v given as fp32 bits; finite).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode(uint32_t vbits, int X) {
+  constexpr int mbits = FMT == kE4M3 ? 3 : 2;
+  constexpr int bias = FMT == kE4M3 ? 7 : 15;
+  constexpr int emin = 1 - bias;                       // exponent of the smallest normal
+  constexpr int emax = FMT == kE4M3 ? 8 : 15;          // exponent of the largest binade
+  constexpr uint32_t qmax = FMT == kE4M3 ? 14u : 7u;   // largest significand in that binade
+  constexpr uint32_t maxcode = FMT == kE4M3 ? 0x7Eu : 0x7Bu;
+  const uint32_t sign = (vbits >> 24) & 0x80u;
+  const uint32_t ef = (vbits >> 23) & 0xffu;
+  uint32_t sig = vbits & 0x7fffffu;
+  int e;                                               // v = sig * 2^(e-23), sig in [2^23, 2^24)
+  if (ef == 0) {
+    if (sig == 0) return sign;
+    const int lz = __clz(sig) - 8;                     // normalise an fp32 subnormal
+    sig <<= lz;
+    e = -126 - lz;
+  } else {
+    sig |= 0x800000u;
+    e = int(ef) - 127;
+  }
+  int ey = e - X;                                      // exponent of y = v * 2^-X
+  if (ey > emax) return sign | maxcode;
+  if (ey >= emin) {
+    uint32_t q = rne_shr(sig, 23 - mbits);             // in [2^mbits, 2^(mbits+1)]
+    if (q == (2u << mbits)) { q = 1u << mbits; ++ey; }
+    if (ey > emax || (ey == emax && q > qmax)) return sign | maxcode;
+    return sign | (uint32_t(ey + bias) << mbits) | (q - (1u << mbits));
+  }
+  // subnormal target: multiples of 2^(emin - mbits)
+  const int s = 23 - mbits + emin - ey;                // > 23 - mbits
+  return sign | rne_shr(sig, s);
+}
+
+// Runtime-format dispatch.
+__device__ __forceinline__ int scale_exp_rt(int fmt, uint32_t amax_bits) {
+  return fmt == kE4M3 ? scale_exp<kE4M3>(amax_bits) : scale_exp<kE5M2>(amax_bits);
+}
+__device__ __forceinline__ uint32_t encode_rt(int fmt, uint32_t vbits, int X) {
+  return fmt == kE4M3 ? encode<kE4M3>(vbits, X) : encode<kE5M2>(vbits, X);
+}
+
+// ---- wavefront (64-lane) reductions ------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_xor(uint32_t v, int width) {
+  for (int o = 1; o < width; o <<= 1) v = max(v, uint32_t(__shfl_xor(int(v), o, 64)));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int width) {
+  for (int o = 1; o < width; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace mx

@@ -1,0 +1,217 @@
+// quantize.hip -- MXFP8 quantisers for gfx950 (HBM-bound; no MFMA).
+//
+// Three kernels share the encoder of mx_device.hpp:
+//   quant_rows : groups of 32 along the contiguous axis (codes in place).
+//   quant_cols : groups of 32 along the strided axis (codes in place).
+//   quant_tok  : groups of 32 along the strided axis, written transposed so the
+//                quantised axis becomes contiguous (the K-contiguous operand a
+//                scaled MFMA reads), with optional row gather by index, optional
+//                per-row fp32 scale (bf16(fp32(a * v))), used for the dense
+//                backward's dY^T / W^T / X^T and the MoE token-axis operands.
+// Group size, scale rule and rounding: P1 ("Blockwise MM Backward MXFP8 Kernel
+// API Reference": 32-element MXFP8 quantization groups).
+#include "kernels.hpp"
+#include "mx_device.hpp"
+
+namespace mx {
+
+// ---------------------------------------------------------------------------
+// quant_rows: 4 lanes per group, 8 bf16 (16 B) per lane.  A wave covers 16
+// groups = 1 KiB of input per load instruction, fully coalesced.
+template <int FMT>
+__global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict__ x,
+                                                          uint2* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          int64_t nchunks) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+    const uint4 v = x[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      amax = max(amax, abs_bits_bf16(uint16_t(w[k] & 0xffffu)));
+      amax = max(amax, abs_bits_bf16(uint16_t(w[k] >> 16)));
+    }
+    amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
+    amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
+    const int X = scale_exp<FMT>(amax);
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = encode<FMT>(w[k] << 16, X);
+      const uint32_t hi = encode<FMT>(w[k] & 0xffff0000u, X);
+      out[k >> 1] |= (lo | (hi << 8)) << (16 * (k & 1));
+    }
+    codes[c] = make_uint2(out[0], out[1]);
+    if ((c & 3) == 0) scales[c >> 2] = uint8_t(X + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quant_cols: a thread owns 8 adjacent columns and one group of 32 rows.
+template <int FMT>
+__global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restrict__ x,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          int64_t rows, int64_t cols) {
+  const int64_t c0 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  const int64_t g = blockIdx.y;
+  if (c0 >= cols) return;
+  const int ncol = cols - c0 >= 8 ? 8 : int(cols - c0);
+  uint32_t amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = 0; r < 32; ++r) {
+    const uint16_t* row = x + (g * 32 + r) * cols + c0;
+    for (int k = 0; k < ncol; ++k) amax[k] = max(amax[k], abs_bits_bf16(row[k]));
+  }
+  int X[8];
+  for (int k = 0; k < ncol; ++k) {
+    X[k] = scale_exp<FMT>(amax[k]);
+    scales[g * cols + c0 + k] = uint8_t(X[k] + 127);
+  }
+  for (int r = 0; r < 32; ++r) {
+    const uint16_t* row = x + (g * 32 + r) * cols + c0;
+    uint8_t* crow = codes + (g * 32 + r) * cols + c0;
+    for (int k = 0; k < ncol; ++k) crow[k] = uint8_t(encode<FMT>(uint32_t(row[k]) << 16, X[k]));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quant_tok: tile of 128 logical rows x 128 columns staged in LDS as bf16.
+// Logical row r reads source row idx[r] (or r without an index); a source
+// outside [0, src_rows) contributes zeros (a padding slot).  With a row scale,
+// the staged value is bf16(fp32(scale[r] * v)).  Output: codes_t [cols][rows]
+// and scales_t [cols][rows/32]; rows % 32 == 0 and cols % 8 == 0.
+constexpr int kTokRows = 128;
+constexpr int kTokCols = 128;
+
+template <int FMT, bool GATHER, bool ROWSCALE>
+__global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restrict__ x,
+                                                         int64_t src_rows, int64_t cols,
+                                                         const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ rowscale,
+                                                         int64_t rows, uint8_t* __restrict__ codes_t,
+                                                         uint8_t* __restrict__ scales_t) {
+  __shared__ uint32_t tile[kTokRows][kTokCols / 2 + 1];   // bf16 pairs; +1 word breaks bank aliasing
+  const int tid = threadIdx.x;
+  const int64_t r0 = int64_t(blockIdx.y) * kTokRows;
+  const int64_t c0 = int64_t(blockIdx.x) * kTokCols;
+  // load: 16 lanes per row segment (256 B), 16 rows per pass, 8 passes
+  {
+    const int chunk = tid & 15;
+    const int64_t col = c0 + chunk * 8;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int rr = (tid >> 4) + pass * 16;
+      const int64_t r = r0 + rr;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < rows && col < cols) {
+        const int64_t src = GATHER ? int64_t(idx[r]) : r;
+        if (src >= 0 && src < src_rows) {
+          v = *reinterpret_cast<const uint4*>(x + src * cols + col);
+          if (ROWSCALE) {
+            const float a = rowscale[r];
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t lo = f32_to_bf16(a * __uint_as_float(w[k] << 16));
+              const uint32_t hi = f32_to_bf16(a * __uint_as_float(w[k] & 0xffff0000u));
+              w[k] = lo | (hi << 16);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+      tile[rr][chunk * 4 + 0] = v.x;
+      tile[rr][chunk * 4 + 1] = v.y;
+      tile[rr][chunk * 4 + 2] = v.z;
+      tile[rr][chunk * 4 + 3] = v.w;
+    }
+  }
+  __syncthreads();
+  // quantise: lane -> column pair, wave -> group of 32 rows
+  const int cp = tid & 63;
+  const int grp = tid >> 6;
+  const int64_t row0 = r0 + grp * 32;
+  const int64_t colA = c0 + 2 * cp;
+  if (row0 >= rows || colA >= cols) return;
+  uint32_t amax0 = 0, amax1 = 0;
+  for (int r = 0; r < 32; ++r) {
+    const uint32_t w = tile[grp * 32 + r][cp];
+    amax0 = max(amax0, abs_bits_bf16(uint16_t(w & 0xffffu)));
+    amax1 = max(amax1, abs_bits_bf16(uint16_t(w >> 16)));
+  }
+  const int X0 = scale_exp<FMT>(amax0), X1 = scale_exp<FMT>(amax1);
+  uint32_t p0[8], p1[8];
+  for (int q = 0; q < 8; ++q) {
+    uint32_t a = 0, b = 0;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = tile[grp * 32 + q * 4 + k][cp];
+      a |= encode<FMT>(w << 16, X0) << (8 * k);
+      b |= encode<FMT>(w & 0xffff0000u, X1) << (8 * k);
+    }
+    p0[q] = a;
+    p1[q] = b;
+  }
+  uint4* dst0 = reinterpret_cast<uint4*>(codes_t + colA * rows + row0);
+  uint4* dst1 = reinterpret_cast<uint4*>(codes_t + (colA + 1) * rows + row0);
+  dst0[0] = make_uint4(p0[0], p0[1], p0[2], p0[3]);
+  dst0[1] = make_uint4(p0[4], p0[5], p0[6], p0[7]);
+  dst1[0] = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+  dst1[1] = make_uint4(p1[4], p1[5], p1[6], p1[7]);
+  scales_t[colA * (rows / 32) + row0 / 32] = uint8_t(X0 + 127);
+  scales_t[(colA + 1) * (rows / 32) + row0 / 32] = uint8_t(X1 + 127);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
+                             uint8_t* scales, hipStream_t st) {
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks == 0) return hipSuccess;
+  const int64_t want = (nchunks + 255) / 256;
+  const int blocks = int(want < 65536 ? want : 65536);
+  if (fmt == kE4M3)
+    quant_rows_kernel<kE4M3><<<blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(x),
+                                                      reinterpret_cast<uint2*>(codes), scales, nchunks);
+  else
+    quant_rows_kernel<kE5M2><<<blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(x),
+                                                      reinterpret_cast<uint2*>(codes), scales, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
+                             uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid(unsigned((cols + 8 * 256 - 1) / (8 * 256)), unsigned(rows / 32));
+  if (fmt == kE4M3)
+    quant_cols_kernel<kE4M3><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+  else
+    quant_cols_kernel<kE5M2><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
+                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct) {
+  if (idx && rs)
+    quant_tok_kernel<FMT, true, true><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+  else if (idx)
+    quant_tok_kernel<FMT, true, false><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+  else if (rs)
+    quant_tok_kernel<FMT, false, true><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+  else
+    quant_tok_kernel<FMT, false, false><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+}
+
+hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
+                            const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
+                            uint8_t* scales_t, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid(unsigned((cols + kTokCols - 1) / kTokCols), unsigned((rows + kTokRows - 1) / kTokRows));
+  if (fmt == kE4M3)
+    tok_dispatch<kE4M3>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+  else
+    tok_dispatch<kE5M2>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+  return hipGetLastError();
+}
+
+}  // namespace mx
