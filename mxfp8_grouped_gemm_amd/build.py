@@ -19,7 +19,7 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-SOURCES = ["api.cpp", "quantize.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm_dense.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -1,0 +1,87 @@
+"""matmul_mxfp8_bwd on the GPU against the oracle (P2's dX = dY W, dW = dY^T X).
+
+Bar: quantised operands in the workspace bit-exact; dX and dW within relative
+Frobenius error 2e-3 (fp32 accumulation vs the oracle's exact sums, both then
+rounded to bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from helpers import bf, rel_fro
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _mx():
+    import mxfp8_grouped_gemm_amd as mx
+    return mx
+
+
+def _inputs(M, N, K, seed):
+    cfg = S.DenseConfig("t", M, N, K, seed=seed)
+    return S.dense_tensors(cfg, "cuda")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 96, 128), (256, 320, 192), (96, 160, 544), (512, 384, 640),
+                                   (32, 32, 32), (288, 544, 96)])
+def test_dense_small_full_parity(M, N, K):
+    mx = _mx()
+    t = _inputs(M, N, K, seed=M + N + K)
+    ws = torch.zeros(mx.lib().matmul_mxfp8_bwd_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    dx, dw = mx.matmul_mxfp8_bwd(t["dy"], t["w"], t["x"], workspace=ws)
+    torch.cuda.synchronize()
+    dy_b, w_b, x_b = (S.bf16_bits(t[k]) for k in ("dy", "w", "x"))
+    rdx, rdw = oracle.dense_bwd(dy_b, w_b, x_b)
+    assert rel_fro(bf(S.bf16_bits(dx)), bf(rdx)) <= TOL
+    assert rel_fro(bf(S.bf16_bits(dw)), bf(rdw)) <= TOL
+    # quantised operands in the documented workspace regions, bit-exact
+    regs = mx.matmul_workspace_regions(M, N, K)
+    wsh = ws.cpu().numpy()
+    want = [oracle.quantize(dy_b, 1, oracle.E5M2),
+            oracle.quantize(np.ascontiguousarray(w_b.T), 1, oracle.E4M3),
+            oracle.quantize(np.ascontiguousarray(dy_b.T), 1, oracle.E5M2),
+            oracle.quantize(np.ascontiguousarray(x_b.T), 1, oracle.E4M3)]
+    for (co, so), (c, s) in zip(regs, want):
+        assert np.array_equal(wsh[co:co + c.size], c.ravel())
+        assert np.array_equal(wsh[so:so + s.size], s.ravel())
+
+
+@pytest.mark.parametrize("fdy,fw,fx", [(0, 0, 0), (1, 1, 1), (0, 1, 1), (1, 0, 1)])
+def test_dense_format_combinations(fdy, fw, fx):
+    mx = _mx()
+    M, N, K = 192, 256, 320
+    t = _inputs(M, N, K, seed=3)
+    dx, dw = mx.matmul_mxfp8_bwd(t["dy"], t["w"], t["x"], fdy, fw, fx)
+    rdx, rdw = oracle.dense_bwd(*(S.bf16_bits(t[k]) for k in ("dy", "w", "x")), fmt_dy=fdy, fmt_w=fw, fmt_x=fx)
+    assert rel_fro(bf(S.bf16_bits(dx)), bf(rdx)) <= TOL
+    assert rel_fro(bf(S.bf16_bits(dw)), bf(rdw)) <= TOL
+
+
+def test_dense_4096_sampled_rows():
+    """The benchmark's shape and launch configuration; the oracle computes a
+    sample of output rows (each row spans every column tile)."""
+    mx = _mx()
+    cfg = S.DENSE
+    t = S.dense_tensors(cfg, "cuda")
+    dx, dw = mx.matmul_mxfp8_bwd(t["dy"], t["w"], t["x"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 255, 256, 4095], rng.integers(0, 4096, 12)]))
+    rdx, rdw = oracle.dense_bwd(*(S.bf16_bits(t[k]) for k in ("dy", "w", "x")), dx_rows=rows, dw_rows=rows)
+    gdx = bf(S.bf16_bits(dx))[rows]
+    gdw = bf(S.bf16_bits(dw))[rows]
+    assert rel_fro(gdx, bf(rdx)) <= TOL
+    assert rel_fro(gdw, bf(rdw)) <= TOL
+    # every output finite and not identically zero
+    assert torch.isfinite(dx.float()).all() and torch.isfinite(dw.float()).all()
+    assert dx.float().abs().sum() > 0 and dw.float().abs().sum() > 0
+
+
+def test_dense_rejects_bad_shapes():
+    mx = _mx()
+    t = _inputs(64, 64, 64, 1)
+    with pytest.raises(mx.MxError):
+        mx.matmul_mxfp8_bwd(t["dy"][:, :48].contiguous(), t["w"][:48].contiguous(), t["x"])
