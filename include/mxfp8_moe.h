@@ -180,13 +180,14 @@ typedef struct {
  *   dgu_tok_codes/scales      [2I,P] / [2I,P/32]      [dGate;dUp] along slots (Phase 2)
  *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
- *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending.
+ *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
+ *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32.
  * Pad slots hold code 0.  Rows of a region are contiguous; no padding between rows. */
 typedef struct {
   size_t dy_codes, dy_scales, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
       dgu_tok_scales, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
-      expert_block_list, total;
+      expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 
 /* Host.  Fills *layout for the shapes in *args (pointers are not read).

@@ -17,9 +17,10 @@ LIB = os.path.join(HERE, "libmxfp8_moe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
+         "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-SOURCES = ["api.cpp", "quantize.hip", "gemm_dense.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm_dense.hip", "moe_aux.hip", "moe_gemm.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI (include/mxfp8_moe.h): argument validation, workspace
 // carving and the launch sequence on the caller's stream.  No device memory is
 // allocated here and nothing is synchronised.
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -131,6 +132,206 @@ int64_t moe_num_blocks(int64_t T, int64_t K, int64_t E, int64_t B) {
   if (T <= 0 || K <= 0 || E <= 0 || B <= 0 || T * K < E) return -1;
   // P1 "Dimensions": N = (T*TopK - (E-1))/B + E - 1, the division rounded up.
   return (T * K - (E - 1) + B - 1) / B + E - 1;
+}
+
+size_t moe_build_blocks_workspace_size(int64_t E) { return E > 0 ? up256(size_t(E) * 4) : 0; }
+
+int moe_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N, int32_t* tpid,
+                     int32_t* b2e, void* ws, size_t ws_bytes, void* stream) {
+  if (T <= 0 || K <= 0 || E <= 0 || B <= 0 || N <= 0)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks: sizes must be positive");
+  const int64_t need = moe_num_blocks(T, K, E, B);
+  if (need < 0) return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks: T*K (%lld) < E (%lld)", (long long)(T * K), (long long)E);
+  if (N < need)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks: N = %lld is below the worst case %lld", (long long)N,
+                (long long)need);
+  if (!topk || !tpid || !b2e || !ws) return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks: null pointer");
+  if (ws_bytes < moe_build_blocks_workspace_size(E))
+    return fail(MXFP8_ERR_WORKSPACE, "moe_build_blocks: workspace too small");
+  if (T * K > INT32_MAX || N * B > INT32_MAX)
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_build_blocks: sizes beyond int32 indexing");
+  return hip_status(mx::launch_build_blocks(topk, T, K, E, B, N, tpid, b2e, static_cast<int32_t*>(ws),
+                                            static_cast<hipStream_t>(stream)),
+                    "moe_build_blocks");
+}
+
+/* ---- MoE backward -------------------------------------------------------- */
+static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layout* L) {
+  const int64_t T = a->T, H = a->H, I = a->I, E = a->E, N = a->N, B = a->block_size, P = N * B;
+  size_t o = 0;
+  auto put = [&](size_t& field, int64_t bytes) {
+    field = o;
+    o = up256(o + size_t(bytes));
+  };
+  put(L->dy_codes, T * H);
+  put(L->dy_scales, T * H / 32);
+  put(L->x_tok_codes, H * P);
+  put(L->x_tok_scales, H * P / 32);
+  put(L->gy_tok_codes, H * P);
+  put(L->gy_tok_scales, H * P / 32);
+  put(L->inter_tok_codes, I * P);
+  put(L->inter_tok_scales, I * P / 32);
+  put(L->dgu_row_codes, P * 2 * I);
+  put(L->dgu_row_scales, P * 2 * I / 32);
+  put(L->dgu_tok_codes, 2 * I * P);
+  put(L->dgu_tok_scales, 2 * I * P / 32);
+  put(L->dx_acc, T * H * 4);
+  put(L->daff_slot, P * 4);
+  put(L->db1_acc, E * 2 * I * 4);
+  put(L->db2_acc, E * H * 4);
+  put(L->expert_block_offsets, (E + 1) * 4);
+  put(L->expert_block_list, N * 4);
+  put(L->slot_token, P * 4);
+  put(L->slot_affinity, P * 4);
+  put(L->block_flag, N * 4);
+  L->total = o;
+  return MXFP8_OK;
+}
+
+static int moe_check_shapes(const moe_bwd_mxfp8_args* a) {
+  if (!a) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: null args");
+  if (a->T <= 0 || a->H <= 0 || a->I <= 0 || a->E <= 0 || a->N <= 0 || a->block_size <= 0)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: sizes must be positive");
+  if (a->H % 32 || a->I % 32)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: H and I must be multiples of 32 (got %lld, %lld)",
+                (long long)a->H, (long long)a->I);
+  const int64_t B = a->block_size;
+  if (B != 128 && B != 256 && B != 512 && B != 1024)
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: block_size %lld not in {128,256,512,1024}", (long long)B);
+  if (a->N * B > INT32_MAX || a->T * a->E > INT32_MAX)
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: sizes beyond int32 indexing");
+  return MXFP8_OK;
+}
+
+int moe_bwd_mxfp8_workspace_query(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layout* L) {
+  int rc = moe_check_shapes(a);
+  if (rc) return rc;
+  if (!L) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8_workspace_query: null layout");
+  moe_layout(a, L);
+  return ok();
+}
+
+size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* a) {
+  moe_bwd_mxfp8_workspace_layout L;
+  if (moe_bwd_mxfp8_workspace_query(a, &L)) return 0;
+  return L.total;
+}
+
+int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moe_check_shapes(a);
+  if (rc) return rc;
+  if (!valid_fmt(a->fmt_weight) || !valid_fmt(a->fmt_act) || !valid_fmt(a->fmt_grad))
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: formats must be E4M3 (0) or E5M2 (1)");
+  if (a->affinity_on != 0 && a->affinity_on != 1)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: affinity_on must be 0 (H) or 1 (I)");
+  if (a->has_bias != 0 && a->has_bias != 1) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: has_bias must be 0/1");
+  if (a->affinity_on == 1 && a->has_bias)
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: a bias with the affinity on I is not supported");
+  const void* req[] = {a->hidden_states, a->expert_affinities_masked, a->gate_up_codes, a->gate_up_scales,
+                       a->down_codes, a->down_scales, a->token_position_to_id, a->block_to_expert,
+                       a->output_hidden_states_grad, a->gate_up_proj_act_checkpoint_T, a->hidden_states_grad,
+                       a->expert_affinities_masked_grad, a->gate_up_proj_weight_grad, a->down_proj_weight_grad};
+  for (const void* q : req)
+    if (!q) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: a required pointer is null");
+  for (const void* q : req)
+    if (!aligned16(q)) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: tensors must be 16-byte aligned");
+  if (a->has_bias) {
+    if (!a->down_proj_bias || !a->gate_and_up_proj_bias_grad || !a->down_proj_bias_grad)
+      return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: has_bias needs down_proj_bias and both bias grads");
+    if (!aligned16(a->down_proj_bias) || !aligned16(a->gate_and_up_proj_bias_grad) ||
+        !aligned16(a->down_proj_bias_grad))
+      return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: bias tensors must be 16-byte aligned");
+  }
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: workspace must be non-null and 256-byte aligned");
+  moe_bwd_mxfp8_workspace_layout L;
+  moe_layout(a, &L);
+  if (ws_bytes < L.total) return fail(MXFP8_ERR_WORKSPACE, "moe_bwd_mxfp8: workspace %zu < %zu bytes", ws_bytes, L.total);
+
+  const int64_t T = a->T, H = a->H, I = a->I, E = a->E, N = a->N, B = a->block_size, P = N * B;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  auto at = [&](size_t off) { return w + off; };
+  int32_t* slot_tok = reinterpret_cast<int32_t*>(at(L.slot_token));
+  float* slot_aff = reinterpret_cast<float*>(at(L.slot_affinity));
+  int32_t* flag = reinterpret_cast<int32_t*>(at(L.block_flag));
+  int32_t* boff = reinterpret_cast<int32_t*>(at(L.expert_block_offsets));
+  int32_t* blist = reinterpret_cast<int32_t*>(at(L.expert_block_list));
+  float* dx_acc = reinterpret_cast<float*>(at(L.dx_acc));
+  float* daff_slot = reinterpret_cast<float*>(at(L.daff_slot));
+  float* db1_acc = reinterpret_cast<float*>(at(L.db1_acc));
+  float* db2_acc = reinterpret_cast<float*>(at(L.db2_acc));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+#define STEP(call, what) \
+  if ((e = (call)) != hipSuccess) return hip_status(e, what);
+
+  STEP(mx::launch_fill_u32(dx_acc, T * H, 0u, st), "zero dX accumulator");
+  STEP(mx::launch_fill_u32(daff_slot, P, 0u, st), "zero d(affinity) accumulator");
+  if (a->has_bias) {
+    STEP(mx::launch_fill_u32(db1_acc, E * 2 * I, 0u, st), "zero db1 accumulator");
+    STEP(mx::launch_fill_u32(db2_acc, E * H, 0u, st), "zero db2 accumulator");
+  }
+  STEP(mx::launch_slot_setup(a->token_position_to_id, a->block_to_expert, a->expert_affinities_masked, T, E, N, B,
+                             slot_tok, slot_aff, flag, boff, blist, st),
+       "slot setup");
+  // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later)
+  STEP(mx::launch_quant_rows(a->output_hidden_states_grad, T, H, a->fmt_grad, at(L.dy_codes), at(L.dy_scales), st),
+       "quantize dY");
+  // token-axis operands of Phases 2 and 4: X, a*dY (on H) or dY (on I), the intermediate
+  STEP(mx::launch_quant_tok(a->hidden_states, T, H, slot_tok, nullptr, P, a->fmt_act, at(L.x_tok_codes),
+                            at(L.x_tok_scales), st),
+       "gather-quantize X");
+  STEP(mx::launch_quant_tok(a->output_hidden_states_grad, T, H, slot_tok, a->affinity_on == 0 ? slot_aff : nullptr,
+                            P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st),
+       "gather-quantize dY");
+  STEP(mx::launch_inter_tok(a->gate_up_proj_act_checkpoint_T, slot_tok, slot_aff, flag, I, B, N, a->fmt_act,
+                            a->affinity_on, at(L.inter_tok_codes), at(L.inter_tok_scales), st),
+       "intermediate operand");
+  if (a->has_bias)
+    STEP(mx::launch_bias(a->output_hidden_states_grad, a->down_proj_bias, slot_tok, slot_aff, a->block_to_expert,
+                         flag, H, B, N, daff_slot, db2_acc, st),
+         "bias reductions");
+  // Phase 1 + fused SwiGLU-backward epilogue
+  mx::Phase1Args p1{};
+  p1.wd_codes = a->down_codes; p1.wd_scales = a->down_scales;
+  p1.dy_codes = at(L.dy_codes); p1.dy_scales = at(L.dy_scales);
+  p1.slot_tok = slot_tok; p1.slot_aff = slot_aff; p1.b2e = a->block_to_expert; p1.flag = flag;
+  p1.ckpt = a->gate_up_proj_act_checkpoint_T;
+  p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
+  p1.dgu_row_codes = at(L.dgu_row_codes); p1.dgu_row_scales = at(L.dgu_row_scales);
+  p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);
+  p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
+  STEP(mx::launch_phase1(p1, a->fmt_weight, a->fmt_grad, a->has_bias != 0, st), "phase 1");
+  // Phase 3: dX scatter-add
+  mx::Phase3Args p3{};
+  p3.dgu_row_codes = at(L.dgu_row_codes); p3.dgu_row_scales = at(L.dgu_row_scales);
+  p3.wgu_codes = a->gate_up_codes; p3.wgu_scales = a->gate_up_scales;
+  p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
+  p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
+  STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
+  // Phase 2: dW_gate_up[e] = X_tok . dGU_tok^T over the expert's blocks
+  mx::GemmStoreArgs g{};
+  g.a_codes = at(L.x_tok_codes); g.a_scales = at(L.x_tok_scales); g.lda = P;
+  g.b_codes = at(L.dgu_tok_codes); g.b_scales = at(L.dgu_tok_scales); g.ldb = P;
+  g.M = H; g.N = 2 * I; g.K = 0; g.out = a->gate_up_proj_weight_grad; g.ldo = 2 * I; g.out_gstride = H * 2 * I;
+  g.blk_off = boff; g.blk_list = blist; g.blk = int(B);
+  STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 2");
+  // Phase 4: dW_down[e] = inter_tok . gy_tok^T
+  g.a_codes = at(L.inter_tok_codes); g.a_scales = at(L.inter_tok_scales); g.lda = P;
+  g.b_codes = at(L.gy_tok_codes); g.b_scales = at(L.gy_tok_scales); g.ldb = P;
+  g.M = I; g.N = H; g.out = a->down_proj_weight_grad; g.ldo = H; g.out_gstride = I * H;
+  STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 4");
+  // finalisation
+  STEP(mx::launch_f32_to_bf16(dx_acc, a->hidden_states_grad, T * H, st), "dX to bf16");
+  STEP(mx::launch_daff_scatter(daff_slot, slot_tok, a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,
+                               st),
+       "d(affinity) scatter");
+  if (a->has_bias) {
+    STEP(mx::launch_f32_to_bf16(db1_acc, a->gate_and_up_proj_bias_grad, E * 2 * I, st), "db1 to bf16");
+    STEP(mx::launch_f32_to_bf16(db2_acc, a->down_proj_bias_grad, E * H, st), "db2 to bf16");
+  }
+#undef STEP
+  return ok();
 }
 
 }  // extern "C"

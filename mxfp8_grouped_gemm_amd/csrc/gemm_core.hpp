@@ -191,6 +191,167 @@ __device__ __forceinline__ void mx_mainloop(TileOperands<BM, BN, SALIGN>& op, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Precise variant: the same fp8 tiles and LDS staging, but each fragment is
+// converted in registers to bf16 with its E8M0 scale folded in (exact: an
+// fp8 code times a power of two has at most 4 significant bits) and reduced
+// with v_mfma_f32_32x32x16_bf16, which accumulates at fp32 precision.  The
+// scaled fp8 MFMA's internal reduction carries ~1e-5 relative error; that is
+// invisible in a bf16 output but flips e5m2 rounding decisions when a result
+// is requantised (the Phase-1 epilogue), so Phase 1 uses this loop.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);   // 2^(s-127)
+}
+
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pk_bf16(uint32_t codes, float scale) {
+  v2bf r;
+  if (FMT == 0)
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, HI);
+  else
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(codes, scale, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 16 codes (one uint4) -> two bf16 vectors of 8 (codes 0-7, 8-15), times scale.
+template <int FMT>
+__device__ __forceinline__ void cvt16(const uint4& c, float scale, v8bf& lo, v8bf& hi) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = cvt_pk_bf16<FMT, false>(w[k], scale);
+    o[2 * k + 1] = cvt_pk_bf16<FMT, true>(w[k], scale);
+  }
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  lo = __builtin_bit_cast(v8bf, u4v{o[0], o[1], o[2], o[3]});
+  hi = __builtin_bit_cast(v8bf, u4v{o[4], o[5], o[6], o[7]});
+}
+
+// Raw per-row stage scales (4 bytes: the stage's 4 groups) for the precise loop.
+template <int F, bool ALIGNED>
+struct RawScales {
+  const uint8_t* row[F];
+  uint32_t reg[F];
+  __device__ __forceinline__ void load(int64_t kcol, int kvalid) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      uint32_t s = 0;
+      if (row[f]) {
+        if (ALIGNED && kvalid == kBK) {
+          s = *reinterpret_cast<const uint32_t*>(row[f] + (kcol >> 5));
+        } else {
+          for (int g = 0; g < 4; ++g)
+            if (g * 32 < kvalid) s |= uint32_t(row[f][(kcol >> 5) + g]) << (8 * g);
+        }
+      }
+      reg[f] = s;
+    }
+  }
+};
+
+template <int BM, int BN, bool SALIGN>
+struct TileOperandsBf16 {
+  static constexpr int FM = BM / 64, FN = BN / 64;
+  Stager<BM> a;
+  Stager<BN> b;
+  RawScales<FM, SALIGN> sa;
+  RawScales<FN, SALIGN> sb;
+};
+
+template <int BM, int BN, int FA, int FB, bool SALIGN, class KMap>
+__device__ __forceinline__ void mx_mainloop_bf16(TileOperandsBf16<BM, BN, SALIGN>& op, int nstages, const KMap& kmap,
+                                                 uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
+  constexpr int FM = BM / 64, FN = BN / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r = lane & 31;
+  const int wrow = (wave >> 1) * (BM / 2);
+  const int wcol = (wave & 1) * (BN / 2);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nstages <= 0) return;
+
+  uint8_t* buf[2] = {smem, smem + (BM + BN) * kBK};
+  {
+    int64_t kc;
+    int kv;
+    kmap(0, kc, kv);
+    op.a.load(kc, kv);
+    op.b.load(kc, kv);
+    op.sa.load(kc, kv);
+    op.sb.load(kc, kv);
+    op.a.store(buf[0]);
+    op.b.store(buf[0] + BM * kBK);
+  }
+  __syncthreads();
+  uint32_t sa_cur[FM], sb_cur[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) sa_cur[i] = op.sa.reg[i];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) sb_cur[j] = op.sb.reg[j];
+
+  for (int s = 0; s < nstages; ++s) {
+    const bool more = s + 1 < nstages;
+    if (more) {
+      int64_t kc;
+      int kv;
+      kmap(s + 1, kc, kv);
+      op.a.load(kc, kv);
+      op.b.load(kc, kv);
+      op.sa.load(kc, kv);
+      op.sb.load(kc, kv);
+    }
+    const uint8_t* At = buf[s & 1];
+    const uint8_t* Bt = At + BM * kBK;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // lane holds G0[16h, 16h+16) and G1[16h, 16h+16) of the 64-element step;
+      // bf16 step t covers G0[16h, +8), G0[16h+8, +8), G1[16h, +8), G1[16h+8, +8)
+      v8bf af[FM][4], bfv[FN][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wrow + i * 32 + r;
+        const uint4 lo = *reinterpret_cast<const uint4*>(At + lds_off(row, ks * 4 + h));
+        const uint4 hi = *reinterpret_cast<const uint4*>(At + lds_off(row, ks * 4 + 2 + h));
+        cvt16<FA>(lo, e8m0_to_f32((sa_cur[i] >> (16 * ks)) & 0xffu), af[i][0], af[i][1]);
+        cvt16<FA>(hi, e8m0_to_f32((sa_cur[i] >> (16 * ks + 8)) & 0xffu), af[i][2], af[i][3]);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wcol + j * 32 + r;
+        const uint4 lo = *reinterpret_cast<const uint4*>(Bt + lds_off(row, ks * 4 + h));
+        const uint4 hi = *reinterpret_cast<const uint4*>(Bt + lds_off(row, ks * 4 + 2 + h));
+        cvt16<FB>(lo, e8m0_to_f32((sb_cur[j] >> (16 * ks)) & 0xffu), bfv[j][0], bfv[j][1]);
+        cvt16<FB>(hi, e8m0_to_f32((sb_cur[j] >> (16 * ks + 8)) & 0xffu), bfv[j][2], bfv[j][3]);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][t], bfv[j][t], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      op.a.store(buf[(s + 1) & 1]);
+      op.b.store(buf[(s + 1) & 1] + BM * kBK);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa_cur[i] = op.sa.reg[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb_cur[j] = op.sb.reg[j];
+    }
+    __syncthreads();
+  }
+}
+
 // Row / column of accumulator register q of fragment (i, j) for this lane,
 // relative to the block tile origin.
 template <int BM, int BN>

@@ -38,4 +38,58 @@ struct GemmStoreArgs {
 };
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st);
 
+// moe_aux.hip
+hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
+hipError_t launch_fill_u16(void* p, int64_t n, uint16_t v, hipStream_t st);
+hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
+                               int32_t* tpid, int32_t* b2e, int32_t* counts, hipStream_t st);
+hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
+                             int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* flag,
+                             int32_t* off, int32_t* list, hipStream_t st);
+hipError_t launch_inter_tok(const uint16_t* ckpt, const int32_t* slot_tok, const float* slot_aff,
+                            const int32_t* flag, int64_t I, int64_t B, int64_t N, int fmt, int on_i,
+                            uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,
+                       const int32_t* b2e, const int32_t* flag, int64_t H, int64_t B, int64_t N, float* daff_slot,
+                       float* db2_acc, hipStream_t st);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st);
+hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, const int32_t* b2e, int64_t T,
+                               int64_t E, int64_t B, int64_t N, uint16_t* daff, hipStream_t st);
+
+// moe_gemm.hip
+struct Phase1Args {
+  const uint8_t* wd_codes;      // [E][I][H]
+  const uint8_t* wd_scales;     // [E][I][H/32]
+  const uint8_t* dy_codes;      // [T][H]
+  const uint8_t* dy_scales;     // [T][H/32]
+  const int32_t* slot_tok;      // [P]
+  const float* slot_aff;        // [P]
+  const int32_t* b2e;           // [N]
+  const int32_t* flag;          // [N]
+  const uint16_t* ckpt;         // [N][2][I][B]
+  int64_t T, H, I, E, N, B;
+  uint8_t* dgu_row_codes;       // [P][2I]
+  uint8_t* dgu_row_scales;      // [P][2I/32]
+  uint8_t* dgu_tok_codes;       // [2I][P]
+  uint8_t* dgu_tok_scales;      // [2I][P/32]
+  float* daff_slot;             // [P]
+  float* db1_acc;               // [E][2][I]
+  int tiles_m, tiles_n;
+};
+hipError_t launch_phase1(const Phase1Args& p, int fw, int fg, bool bias, hipStream_t st);
+
+struct Phase3Args {
+  const uint8_t* dgu_row_codes;   // [P][2I]
+  const uint8_t* dgu_row_scales;  // [P][2I/32]
+  const uint8_t* wgu_codes;       // [E][H][2I]
+  const uint8_t* wgu_scales;      // [E][H][2I/32]
+  const int32_t* slot_tok;
+  const int32_t* b2e;
+  const int32_t* flag;
+  int64_t H, I, N, B;
+  float* dx_acc;                  // [T][H]
+  int tiles_m, tiles_n;
+};
+hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st);
+
 }  // namespace mx

@@ -1,0 +1,334 @@
+// moe_aux.hip -- the HBM-bound kernels around the MoE GEMMs (gfx950):
+// routing blocks, per-slot routing info, per-expert block lists, the
+// token-axis quantised SwiGLU intermediate, the bias reductions and the
+// finalisation of the fp32 accumulators into bf16 gradients.
+//
+// Routing blocks: P1 ("Blockwise MM Backward MXFP8 Kernel API Reference")
+// parameters token_position_to_id [N*B] and block_to_expert [N].
+// Bias reductions: P3 (sonic-moe functional/backward.py) db2_and_ds_kernel
+// (db2 = sum of a*dY over an expert's slots; the <dY, b2> term of d(a)) and
+// db1_kernel (db1 = sum of the gate/up gradients).
+#include "kernels.hpp"
+#include "mx_device.hpp"
+#include "swiglu.hpp"
+
+namespace mx {
+
+// ---------------------------------------------------------------------------
+// small fills (plain kernels, so they are safe inside captured graphs)
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void fill_u16_kernel(uint16_t* p, int64_t n, uint16_t v) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u16(void* p, int64_t n, uint16_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  fill_u16_kernel<<<unsigned(want < 8192 ? want : 8192), 256, 0, st>>>(static_cast<uint16_t*>(p), n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  fill_u32_kernel<<<unsigned(want < 8192 ? want : 8192), 256, 0, st>>>(static_cast<uint32_t*>(p), n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// moe_build_blocks: count per expert, then one workgroup per expert places its
+// tokens (ascending) into its consecutive blocks.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[4]*/, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < 4; ++w) {
+    const int s = lds[w];
+    if (w < wave) before += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(256) route_count_kernel(const int32_t* __restrict__ topk, int64_t TK, int E,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int red[4];
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int64_t i = threadIdx.x; i < TK; i += 256) c += topk[i] == e;
+  int tot;
+  block_exclusive_scan(c, red, &tot);
+  if (threadIdx.x == 0) counts[e] = tot;
+}
+
+__global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ topk, int64_t T, int K, int E,
+                                                          int B, const int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ tpid, int32_t* __restrict__ b2e) {
+  __shared__ int red[4];
+  const int e = blockIdx.x;
+  int part = 0;
+  for (int q = threadIdx.x; q < e; q += 256) part += (counts[q] + B - 1) / B;
+  int start_blk;
+  block_exclusive_scan(part, red, &start_blk);
+  const int nb = (counts[e] + B - 1) / B;
+  for (int q = threadIdx.x; q < nb; q += 256) b2e[start_blk + q] = e;
+  int64_t base = int64_t(start_blk) * B;
+  for (int64_t t0 = 0; t0 < T; t0 += 256) {
+    const int64_t t = t0 + threadIdx.x;
+    int hit = 0;
+    if (t < T)
+      for (int k = 0; k < K; ++k) hit |= topk[t * K + k] == e;
+    int tot;
+    const int pos = block_exclusive_scan(hit, red, &tot);
+    if (hit) tpid[base + pos] = int32_t(t);
+    base += tot;
+  }
+}
+
+hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
+                               int32_t* tpid, int32_t* b2e, int32_t* counts, hipStream_t st) {
+  hipError_t err;
+  if ((err = launch_fill_u32(tpid, N * B, 0xffffffffu, st)) != hipSuccess) return err;
+  if ((err = launch_fill_u32(b2e, N, uint32_t(E - 1), st)) != hipSuccess) return err;
+  route_count_kernel<<<unsigned(E), 256, 0, st>>>(topk, T * K, int(E), counts);
+  route_place_kernel<<<unsigned(E), 256, 0, st>>>(topk, T, int(K), int(E), int(B), counts, tpid, b2e);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-slot routing info: token (-1 for padding or an invalid block expert) and
+// affinity (0 for padding).  Outside [0,T) is padding.
+__global__ void slot_info_kernel(const int32_t* __restrict__ tpid, const int32_t* __restrict__ b2e,
+                                 const float* __restrict__ aff, int64_t T, int64_t E, int64_t B, int64_t P,
+                                 int32_t* __restrict__ slot_tok, float* __restrict__ slot_aff) {
+  for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < P; s += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t e = b2e[s / B];
+    const int64_t t = tpid[s];
+    const bool ok = t >= 0 && t < T && e >= 0 && e < E;
+    slot_tok[s] = ok ? int32_t(t) : -1;
+    slot_aff[s] = ok ? aff[t * E + e] : 0.f;
+  }
+}
+
+// A block takes part in the GEMMs iff at least one of its slots is routed.
+__global__ void __launch_bounds__(256) block_flag_kernel(const int32_t* __restrict__ slot_tok, int64_t B,
+                                                         int32_t* __restrict__ flag) {
+  __shared__ int red[4];
+  int any = 0;
+  for (int64_t p = threadIdx.x; p < B; p += 256) any |= slot_tok[int64_t(blockIdx.x) * B + p] >= 0;
+  int tot;
+  block_exclusive_scan(any, red, &tot);
+  if (threadIdx.x == 0) flag[blockIdx.x] = tot > 0;
+}
+
+// Per-expert lists of occupied blocks in ascending order (one workgroup).
+__global__ void __launch_bounds__(256) expert_lists_kernel(const int32_t* __restrict__ b2e,
+                                                           const int32_t* __restrict__ flag, int N, int E,
+                                                           int32_t* __restrict__ off, int32_t* __restrict__ list) {
+  __shared__ int red[4];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + threadIdx.x;
+    int c = 0;
+    if (e < E)
+      for (int b = 0; b < N; ++b) c += (b2e[b] == e) & (flag[b] != 0);
+    int tot;
+    const int pos = block_exclusive_scan(c, red, &tot) + carry;
+    if (e < E) {
+      off[e] = pos;
+      int w = pos;
+      for (int b = 0; b < N; ++b)
+        if (b2e[b] == e && flag[b]) list[w++] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) off[E] = carry;
+}
+
+hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
+                             int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* flag,
+                             int32_t* off, int32_t* list, hipStream_t st) {
+  const int64_t P = N * B;
+  const int64_t want = (P + 255) / 256;
+  slot_info_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(tpid, b2e, aff, T, E, B, P, slot_tok,
+                                                                           slot_aff);
+  block_flag_kernel<<<unsigned(N), 256, 0, st>>>(slot_tok, B, flag);
+  expert_lists_kernel<<<1, 256, 0, st>>>(b2e, flag, int(N), int(E), off, list);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token-axis quantised intermediate for Phase 4: inter = bf16(bf16(silu(g)) * u)
+// (affinity on H) or bf16(fp32(a * inter)) (affinity on I), from the gate/up
+// checkpoint [N,2,I,B] (P1 gate_up_proj_act_checkpoint_T).  Groups of 32
+// consecutive slots; 4 lanes per group, 8 slots per lane.  Padding -> 0.
+template <int FMT, bool ON_I>
+__global__ void __launch_bounds__(256) inter_tok_kernel(const uint16_t* __restrict__ ckpt,
+                                                        const int32_t* __restrict__ slot_tok,
+                                                        const float* __restrict__ slot_aff,
+                                                        const int32_t* __restrict__ flag, int64_t I, int64_t B,
+                                                        int64_t N, uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const int64_t chunks_per_row = B / 8;               // per (block, i)
+  const int64_t total = N * I * chunks_per_row;
+  const int64_t P = N * B;
+  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < total; c += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t b = c / (I * chunks_per_row);
+    const int64_t rem = c - b * I * chunks_per_row;
+    const int64_t i = rem / chunks_per_row;
+    const int64_t p0 = (rem - i * chunks_per_row) * 8;
+    float v[8];
+    uint32_t amax = 0;
+    if (flag[b]) {
+      const uint4 g4 = *reinterpret_cast<const uint4*>(ckpt + ((b * 2 + 0) * I + i) * B + p0);
+      const uint4 u4 = *reinterpret_cast<const uint4*>(ckpt + ((b * 2 + 1) * I + i) * B + p0);
+      const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w}, uw[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t s = b * B + p0 + k;
+        const bool ok = slot_tok[s] >= 0;
+        const float g = ok ? bf16_to_f32(uint16_t(gw[k >> 1] >> (16 * (k & 1)))) : 0.f;
+        const float u = ok ? bf16_to_f32(uint16_t(uw[k >> 1] >> (16 * (k & 1)))) : 0.f;
+        float in = swiglu_inter(g, u);
+        if (ON_I) in = bf16_to_f32(f32_to_bf16(slot_aff[s] * in));
+        v[k] = in;
+        amax = max(amax, abs_bits(in));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    }
+    amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
+    amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
+    const int X = scale_exp<FMT>(amax);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w0 |= encode<FMT>(__float_as_uint(v[k]), X) << (8 * k);
+      w1 |= encode<FMT>(__float_as_uint(v[k + 4]), X) << (8 * k);
+    }
+    *reinterpret_cast<uint2*>(codes + i * P + b * B + p0) = make_uint2(w0, w1);
+    if ((p0 & 31) == 0) scales[i * (P / 32) + (b * B + p0) / 32] = uint8_t(X + 127);
+  }
+}
+
+hipError_t launch_inter_tok(const uint16_t* ckpt, const int32_t* slot_tok, const float* slot_aff,
+                            const int32_t* flag, int64_t I, int64_t B, int64_t N, int fmt, int on_i,
+                            uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int64_t total = N * I * (B / 8);
+  const int64_t want = (total + 255) / 256;
+  const unsigned blocks = unsigned(want < 65536 ? want : 65536);
+  if (fmt == kE4M3) {
+    if (on_i) inter_tok_kernel<kE4M3, true><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
+    else inter_tok_kernel<kE4M3, false><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
+  } else {
+    if (on_i) inter_tok_kernel<kE5M2, true><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
+    else inter_tok_kernel<kE5M2, false><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Bias terms (has_bias): per slot <dY_t, b2[e]> added into daff_slot (one wave
+// per slot), and db2[e][h] += sum over a block's slots of a * dY[t][h].
+__global__ void __launch_bounds__(256) bias_dot_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ b2,
+                                                       const int32_t* __restrict__ slot_tok,
+                                                       const int32_t* __restrict__ b2e, int64_t H, int64_t B,
+                                                       int64_t P, float* __restrict__ daff_slot) {
+  const int64_t s = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (s >= P) return;
+  const int64_t t = slot_tok[s];
+  if (t < 0) return;
+  const int64_t e = b2e[s / B];
+  float acc = 0.f;
+  for (int64_t h = lane; h < H; h += 64) acc += bf16_to_f32(dy[t * H + h]) * bf16_to_f32(b2[e * H + h]);
+  acc = wave_sum_xor(acc, 64);
+  if (lane == 0) atomicAdd(daff_slot + s, acc);
+}
+
+__global__ void __launch_bounds__(256) db2_kernel(const uint16_t* __restrict__ dy, const int32_t* __restrict__ slot_tok,
+                                                  const float* __restrict__ slot_aff, const int32_t* __restrict__ b2e,
+                                                  const int32_t* __restrict__ flag, int64_t H, int64_t B,
+                                                  float* __restrict__ db2_acc) {
+  const int64_t b = blockIdx.y;
+  const int64_t h = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (!flag[b] || h >= H) return;
+  const int64_t e = b2e[b];
+  float acc = 0.f;
+  for (int64_t p = 0; p < B; ++p) {
+    const int64_t t = slot_tok[b * B + p];
+    if (t >= 0) acc += slot_aff[b * B + p] * bf16_to_f32(dy[t * H + h]);
+  }
+  atomicAdd(db2_acc + e * H + h, acc);
+}
+
+hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,
+                       const int32_t* b2e, const int32_t* flag, int64_t H, int64_t B, int64_t N, float* daff_slot,
+                       float* db2_acc, hipStream_t st) {
+  const int64_t P = N * B;
+  bias_dot_kernel<<<unsigned((P + 3) / 4), 256, 0, st>>>(dy, b2, slot_tok, b2e, H, B, P, daff_slot);
+  db2_kernel<<<dim3(unsigned((H + 255) / 256), unsigned(N)), 256, 0, st>>>(dy, slot_tok, slot_aff, b2e, flag, H, B,
+                                                                          db2_acc);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Finalisation: fp32 accumulators -> bf16 outputs; d(a) scattered to t*E+e.
+__global__ void f32_to_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n / 4; i += int64_t(gridDim.x) * blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    const uint32_t lo = uint32_t(f32_to_bf16(v.x)) | (uint32_t(f32_to_bf16(v.y)) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16(v.z)) | (uint32_t(f32_to_bf16(v.w)) << 16);
+    reinterpret_cast<uint2*>(dst)[i] = make_uint2(lo, hi);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+    const int64_t i = (n & ~int64_t(3)) + threadIdx.x;
+    dst[i] = f32_to_bf16(src[i]);
+  }
+}
+
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n / 4 + 255) / 256 + 1;
+  f32_to_bf16_kernel<<<unsigned(want < 16384 ? want : 16384), 256, 0, st>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+__global__ void daff_scatter_kernel(const float* __restrict__ daff_slot, const int32_t* __restrict__ slot_tok,
+                                    const int32_t* __restrict__ b2e, int64_t E, int64_t B, int64_t P,
+                                    uint16_t* __restrict__ daff) {
+  for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < P; s += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = slot_tok[s];
+    if (t >= 0) daff[t * E + b2e[s / B]] = f32_to_bf16(daff_slot[s]);
+  }
+}
+
+hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, const int32_t* b2e, int64_t T,
+                               int64_t E, int64_t B, int64_t N, uint16_t* daff, hipStream_t st) {
+  hipError_t err = launch_fill_u16(daff, T * E, 0, st);
+  if (err != hipSuccess) return err;
+  const int64_t P = N * B;
+  const int64_t want = (P + 255) / 256;
+  daff_scatter_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(daff_slot, slot_tok, b2e, E, B, P, daff);
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,181 @@
+"""moe_bwd_mxfp8 (and moe_build_blocks) on the GPU against the oracle.
+
+Bar: routing blocks, weight codes and the quantised input operands (dY rows,
+gathered X and a*dY along slots) bit-exact; every gradient within relative
+Frobenius error 2e-3; exact zeros where the oracle is zero (unrouted pairs,
+empty experts)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from helpers import bf, rel_fro
+from moe_gpu_common import gpu_problem, host, oracle_problem
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+SMALL = {
+    "tiny": S.TINY,
+    "medium_s": S.scaled(S.MEDIUM, T=512, H=256, I=352, E=8, K=4, B=128),
+    "large_s": S.scaled(S.LARGE, T=256, H=256, I=512, E=4, K=2, B=256),
+    "fine_s": S.scaled(S.FINE, T=512, H=192, I=128, E=16, K=4, B=128),
+    "medium_b512": S.scaled(S.MEDIUM, T=640, H=128, I=96, E=4, K=2, B=512),
+}
+
+
+def _check_outputs(cfg, out, ref, unrouted_zero=True):
+    keys = ["dx", "daff", "dwgu", "dwd"] + (["db1", "db2"] if cfg.has_bias else [])
+    errs = {}
+    for k in keys:
+        g = bf(host(out[k])).reshape(-1)
+        r = bf(ref[k]).reshape(-1)
+        errs[k] = rel_fro(g, r)
+        if unrouted_zero:
+            assert np.all(g[r == 0] == 0) or k in ("dx",), f"{k}: nonzero where the oracle is exactly zero"
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_moe_small_full_parity(name):
+    cfg = SMALL[name]
+    gp = gpu_problem(cfg)
+    out = gp["op"].run()
+    torch.cuda.synchronize()
+    p, ex = oracle_problem(gp)
+    # routing blocks and weight codes: bit-exact
+    assert np.array_equal(host(gp["tpid"]), ex["tpid"]) and np.array_equal(host(gp["b2e"]), ex["b2e"])
+    for g, o in zip(gp["wq"], ex["wq"]):
+        assert np.array_equal(host(g).reshape(-1), o.reshape(-1))
+    ref = oracle.moe_bwd(p)
+    _check_outputs(cfg, out, ref)
+    # quantised input operands read back from the workspace: bit-exact
+    op = gp["op"]
+    T, H, P = cfg.T, cfg.H, gp["N"] * cfg.B
+    ws = op.workspace.cpu().numpy()
+    L = op.layout
+    c, s = oracle.quantize(p.dy, 1, oracle.E5M2)
+    assert np.array_equal(ws[L["dy_codes"]:L["dy_codes"] + T * H], c.ravel())
+    assert np.array_equal(ws[L["dy_scales"]:L["dy_scales"] + T * H // 32], s.ravel())
+    for which, name_c, name_s in ((oracle.TOK_X, "x_tok_codes", "x_tok_scales"),
+                                  (oracle.TOK_GY, "gy_tok_codes", "gy_tok_scales")):
+        c, s = oracle.moe_token_operand(p, which)
+        assert np.array_equal(ws[L[name_c]:L[name_c] + H * P], c.ravel()), name_c
+        assert np.array_equal(ws[L[name_s]:L[name_s] + H * P // 32], s.ravel()), name_s
+    # the intermediate operand: silu is evaluated in fp32 on the GPU and in fp64 by the
+    # oracle, so a rare bf16 rounding may differ; codes must agree almost everywhere
+    c, s = oracle.moe_token_operand(p, oracle.TOK_INTER)
+    got = ws[L["inter_tok_codes"]:L["inter_tok_codes"] + cfg.I * P]
+    assert np.mean(got != c.ravel()) < 1e-3
+
+
+def test_moe_build_blocks_bit_exact_and_edge_cases():
+    import mxfp8_grouped_gemm_amd as mx
+    rng = np.random.default_rng(3)
+    for T, K, E, B in ((1000, 3, 7, 128), (64, 1, 64, 128), (4096, 8, 128, 128), (300, 2, 3, 1024)):
+        topk = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+        if E == 7:
+            topk[topk == 5] = 4 if K == 1 else topk[topk == 5]      # keep rows distinct
+        N = oracle.num_blocks(T, K, E, B) + 2                        # extra trailing blocks
+        tp, be = mx.moe_build_blocks(torch.from_numpy(topk).cuda(), E, B, N)
+        rt, rb = oracle.build_blocks(topk, E, B, N)
+        assert np.array_equal(host(tp), rt) and np.array_equal(host(be), rb)
+    with pytest.raises(mx.MxError):
+        mx.moe_build_blocks(torch.zeros((4, 2), dtype=torch.int32, device="cuda"), 4, 128, 1)
+
+
+def test_moe_deterministic_weight_grads_and_dy_scaling():
+    """Phases 2/4 have a fixed summation order: repeated runs give identical dW,
+    and scaling dY by 2^3 scales them by exactly 8 (the E8M0 scales absorb it)."""
+    cfg = SMALL["fine_s"]
+    gp = gpu_problem(cfg)
+    a = {k: v.clone() for k, v in gp["op"].run().items() if v is not None}
+    b = gp["op"].run()
+    for k in ("dwgu", "dwd"):
+        assert torch.equal(a[k], b[k]), k
+    for k in ("dx", "daff", "db1", "db2"):
+        assert rel_fro(bf(host(b[k])), bf(host(a[k]))) < 1e-5, k
+    gp["t"]["dy"].mul_(8.0)
+    c = gp["op"].run()
+    for k in ("dwgu", "dwd"):
+        assert torch.equal(c[k].float(), 8.0 * a[k].float()), k
+    for k in ("dx", "daff", "db1", "db2"):
+        assert rel_fro(bf(host(c[k])), 8.0 * bf(host(a[k]))) < 1e-5, k
+
+
+def test_moe_extra_padding_blocks_change_nothing():
+    cfg = SMALL["tiny"]
+    g1 = gpu_problem(cfg)
+    o1 = {k: v.clone() for k, v in g1["op"].run().items() if v is not None}
+    g2 = gpu_problem(cfg, N=g1["N"] + 3)
+    o2 = g2["op"].run()
+    for k in ("dwgu", "dwd"):
+        assert torch.equal(o1[k], o2[k]), k
+    for k in ("dx", "daff"):
+        assert rel_fro(bf(host(o2[k])), bf(host(o1[k]))) < 1e-5, k
+
+
+def test_moe_rejects_bad_arguments():
+    import mxfp8_grouped_gemm_amd as mx
+    gp = gpu_problem(SMALL["tiny"])
+    args = gp["op"].args
+    saved = args.block_size
+    args.block_size = 96
+    with pytest.raises(mx.MxError) as ei:
+        gp["op"].run()
+    assert ei.value.status == 2
+    args.block_size = saved
+    args.affinity_on = 1
+    args.has_bias = 1
+    with pytest.raises(mx.MxError):
+        gp["op"].run()
+    args.affinity_on, args.has_bias = 0, 0
+    with pytest.raises(mx.MxError) as ei:
+        mx.lib().moe_bwd_mxfp8(mx.C.byref(args), gp["op"].workspace.data_ptr(), 1024, None)
+        raise mx.MxError("x", mx.lib().moe_bwd_mxfp8(mx.C.byref(args), gp["op"].workspace.data_ptr(), 1024, None), "")
+    gp["op"].run()      # still works after the failed calls
+
+
+# ----------------------------------------------------------------------------- full sizes, sampled
+FULL = {"medium": S.MEDIUM, "large": S.LARGE, "fine": S.FINE}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_moe_full_size_sampled(name):
+    """The benchmark's sizes and launch configuration.  The oracle computes
+    sampled outputs: whole dX rows and d(a) entries of a few tokens, and whole
+    dW columns / rows of a few intermediate indices of two experts."""
+    cfg = FULL[name]
+    gp = gpu_problem(cfg)
+    out = gp["op"].run()
+    torch.cuda.synchronize()
+    print(f"{name}: GPU run done", flush=True)
+    p, ex = oracle_problem(gp)
+    assert np.array_equal(host(gp["tpid"]), ex["tpid"]) and np.array_equal(host(gp["b2e"]), ex["b2e"])
+    rng = np.random.default_rng(1)
+    cnt = np.bincount(gp["topk"].ravel(), minlength=cfg.E)
+    tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 6)])).astype(np.int32)
+    dx_r, da_r = oracle.moe_token_rows(p, tokens)
+    gdx = bf(host(out["dx"]))[tokens]
+    gda = bf(host(out["daff"])).reshape(cfg.T, cfg.E)[tokens]
+    e_dx, e_da = rel_fro(gdx, bf(dx_r)), rel_fro(gda, bf(da_r))
+    assert np.all(gda[bf(da_r) == 0] == 0)
+    experts = [int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30)))]
+    icols = np.unique(np.concatenate([[0, cfg.I - 1], rng.integers(0, cfg.I, 2)])).astype(np.int32)
+    errs = {"dx": e_dx, "daff": e_da}
+    for e in experts:
+        r = oracle.moe_expert_cols(p, e, icols)
+        errs[f"dwgu[{e}]"] = rel_fro(bf(host(out["dwgu"][e]))[:, :, icols], bf(r["dwgu"]))
+        errs[f"dwd[{e}]"] = rel_fro(bf(host(out["dwd"][e]))[icols], bf(r["dwd"]))
+        if cfg.has_bias:
+            errs[f"db1[{e}]"] = rel_fro(bf(host(out["db1"][e]))[:, icols], bf(r["db1"]))
+            errs[f"db2[{e}]"] = rel_fro(bf(host(out["db2"][e])), bf(r["db2"]))
+    empty = np.nonzero(cnt == 0)[0]
+    for e in empty:
+        assert not out["dwgu"][e].float().abs().sum().item() and not out["dwd"][e].float().abs().sum().item()
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
