@@ -95,6 +95,14 @@ int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis, int 
  *   each region starting on a 256-byte boundary, in this order, codes first.
  * ------------------------------------------------------------------------- */
 size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
+/* Profiling aid: one stage of matmul_mxfp8_bwd on a workspace a full call has
+ * filled: 0 quantise dY along N and W along N, 1 quantise dY and X along M,
+ * 2 the dX GEMM, 3 the dW GEMM.  INVALID_ARG for another stage. */
+int matmul_mxfp8_bwd_stage(const uint16_t* output_grad, const uint16_t* weights,
+                           const uint16_t* input_activation, int64_t M, int64_t N, int64_t K,
+                           int fmt_output_grad, int fmt_weights, int fmt_input,
+                           uint16_t* input_grad, uint16_t* weight_grad,
+                           void* workspace, size_t workspace_bytes, int stage, void* stream);
 int matmul_mxfp8_bwd(const uint16_t* output_grad, const uint16_t* weights,
                      const uint16_t* input_activation, int64_t M, int64_t N, int64_t K,
                      int fmt_output_grad, int fmt_weights, int fmt_input,
@@ -204,6 +212,20 @@ size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
  * other values are skipped); each (t,e) pair appears in at most one slot. */
 int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* Profiling aid: enqueue only one stage of moe_bwd_mxfp8, on a workspace that a
+ * full call with the same arguments has already filled (stages read what the
+ * earlier ones wrote there).  Running stages in order 0..MOE_BWD_NUM_STAGES-1
+ * is exactly one full call.  Stages:
+ *   0 setup (zero accumulators, slot routing info, per-expert block lists)
+ *   1 quantise dY along H         2 gather-quantise X and a*dY (or dY) along slots
+ *   3 intermediate along slots    4 bias reductions (has_bias only)
+ *   5 Phase 1 + epilogue          6 Phase 3 (dX scatter-add)
+ *   7 Phase 2 (dW_gate_up)        8 Phase 4 (dW_down)          9 finalise to bf16
+ * Errors as for moe_bwd_mxfp8, plus INVALID_ARG for a stage outside the range. */
+#define MOE_BWD_NUM_STAGES 10
+int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
+                        int stage, void* stream);
 
 #ifdef __cplusplus
 }

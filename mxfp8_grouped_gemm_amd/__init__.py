@@ -82,6 +82,9 @@ def _declare(L):
         ("moe_bwd_mxfp8_workspace_query", C.c_int, [C.POINTER(MoeBwdArgs), C.POINTER(MoeWorkspaceLayout)]),
         ("moe_bwd_mxfp8_workspace_size", C.c_size_t, [C.POINTER(MoeBwdArgs)]),
         ("moe_bwd_mxfp8", C.c_int, [C.POINTER(MoeBwdArgs), _p, C.c_size_t, _p]),
+        ("moe_bwd_mxfp8_stage", C.c_int, [C.POINTER(MoeBwdArgs), _p, C.c_size_t, C.c_int, _p]),
+        ("matmul_mxfp8_bwd_stage", C.c_int, [_p, _p, _p, _i64, _i64, _i64, C.c_int, C.c_int, C.c_int, _p, _p,
+                                             _p, C.c_size_t, C.c_int, _p]),
     ):
         if hasattr(L, name):
             f = getattr(L, name)
@@ -157,6 +160,18 @@ def matmul_mxfp8_bwd(output_grad: torch.Tensor, weights: torch.Tensor, input_act
     return dx, dw
 
 
+def matmul_mxfp8_bwd_stage(output_grad, weights, input_activation, stage: int, workspace, out,
+                           fmt_output_grad: int = E5M2, fmt_weights: int = E4M3, fmt_input: int = E4M3):
+    """One stage of matmul_mxfp8_bwd (0/1 quantise, 2 dX GEMM, 3 dW GEMM) on a filled workspace."""
+    M, N = output_grad.shape
+    K = weights.shape[1]
+    dx, dw = out
+    _check(lib().matmul_mxfp8_bwd_stage(output_grad.data_ptr(), weights.data_ptr(), input_activation.data_ptr(), M,
+                                        N, K, fmt_output_grad, fmt_weights, fmt_input, dx.data_ptr(), dw.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel(), stage, _stream(output_grad)),
+           "matmul_mxfp8_bwd_stage")
+
+
 def matmul_workspace_regions(M: int, N: int, K: int):
     """Byte offsets of the dense workspace regions, as documented in the header."""
     def up(v):
@@ -177,15 +192,19 @@ def moe_num_blocks(T: int, K: int, E: int, block_size: int) -> int:
     return int(lib().moe_num_blocks(T, K, E, block_size))
 
 
-def moe_build_blocks(topk_ids: torch.Tensor, E: int, block_size: int, N: Optional[int] = None):
+def moe_build_blocks(topk_ids: torch.Tensor, E: int, block_size: int, N: Optional[int] = None, out=None,
+                     workspace: Optional[torch.Tensor] = None):
     """topk_ids [T,K] int32 -> (token_position_to_id [N*B] int32, block_to_expert [N] int32)."""
     T, K = topk_ids.shape
     if N is None:
         N = moe_num_blocks(T, K, E, block_size)
     L = lib()
-    ws = torch.empty(L.moe_build_blocks_workspace_size(E), dtype=torch.uint8, device=topk_ids.device)
-    tpid = torch.empty(N * block_size, dtype=torch.int32, device=topk_ids.device)
-    b2e = torch.empty(N, dtype=torch.int32, device=topk_ids.device)
+    ws = workspace if workspace is not None else torch.empty(L.moe_build_blocks_workspace_size(E),
+                                                             dtype=torch.uint8, device=topk_ids.device)
+    if out is None:
+        out = (torch.empty(N * block_size, dtype=torch.int32, device=topk_ids.device),
+               torch.empty(N, dtype=torch.int32, device=topk_ids.device))
+    tpid, b2e = out
     _check(L.moe_build_blocks(_dev(topk_ids, torch.int32, "topk_ids"), T, K, E, block_size, N,
                               tpid.data_ptr(), b2e.data_ptr(), ws.data_ptr(), ws.numel(), _stream(topk_ids)),
            "moe_build_blocks")
@@ -247,6 +266,16 @@ class MoeBwd:
                                    C.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)),
                "moe_bwd_mxfp8")
         return self.out
+
+    NUM_STAGES = 10
+    STAGE_NAMES = ("setup", "quantize_dy", "gather_quantize_x_dy", "intermediate", "bias", "phase1",
+                   "phase3", "phase2", "phase4", "finalize")
+
+    def stage(self, s: int):
+        """Re-run one stage on the workspace a full run filled (profiling aid)."""
+        _check(lib().moe_bwd_mxfp8_stage(C.byref(self.args), self.workspace.data_ptr(), self.workspace.numel(), s,
+                                         C.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)),
+               "moe_bwd_mxfp8_stage")
 
     def region(self, name: str, nbytes: int) -> torch.Tensor:
         """A uint8 view of one workspace region (for reading quantised operands back)."""

@@ -82,9 +82,9 @@ size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K) {
   return total;
 }
 
-int matmul_mxfp8_bwd(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N,
-                     int64_t K, int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws,
-                     size_t ws_bytes, void* stream) {
+static int dense_run(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                     int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws, size_t ws_bytes,
+                     void* stream, int lo, int hi) {
   if (M <= 0 || N <= 0 || K <= 0) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: non-positive shape");
   if (M % 32 || N % 32 || K % 32)
     return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: M, N, K must be multiples of 32 (got %lld %lld %lld)",
@@ -102,30 +102,47 @@ int matmul_mxfp8_bwd(const uint16_t* dy, const uint16_t* w, const uint16_t* x, i
     return fail(MXFP8_ERR_WORKSPACE, "matmul_mxfp8_bwd: workspace %zu < %zu bytes", ws_bytes, total);
   uint8_t* base = static_cast<uint8_t*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  // dX = dY W: dY along N [M,N]; W along N, transposed to [K,N]
-  if ((e = mx::launch_quant_rows(dy, M, N, fmt_dy, base + off[0], base + off[1], st)) != hipSuccess)
+  hipError_t e = hipSuccess;
+  // stage 0 -- dX = dY W: dY along N [M,N]; W along N, transposed to [K,N]
+  if (lo <= 0 && 0 <= hi && (e = mx::launch_quant_rows(dy, M, N, fmt_dy, base + off[0], base + off[1], st)) != hipSuccess)
     return hip_status(e, "quantize dY along N");
-  if ((e = mx::launch_quant_tok(w, N, K, nullptr, nullptr, N, fmt_w, base + off[2], base + off[3], st)) !=
+  if (lo <= 0 && 0 <= hi && (e = mx::launch_quant_tok(w, N, K, nullptr, nullptr, N, fmt_w, base + off[2], base + off[3], st)) !=
       hipSuccess)
     return hip_status(e, "quantize W along N");
-  // dW = dY^T X: dY along M, transposed to [N,M]; X along M, transposed to [K,M]
-  if ((e = mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fmt_dy, base + off[4], base + off[5], st)) !=
+  // stage 1 -- dW = dY^T X: dY along M, transposed to [N,M]; X along M, transposed to [K,M]
+  if (lo <= 1 && 1 <= hi && (e = mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fmt_dy, base + off[4], base + off[5], st)) !=
       hipSuccess)
     return hip_status(e, "quantize dY along M");
-  if ((e = mx::launch_quant_tok(x, M, K, nullptr, nullptr, M, fmt_x, base + off[6], base + off[7], st)) !=
+  if (lo <= 1 && 1 <= hi && (e = mx::launch_quant_tok(x, M, K, nullptr, nullptr, M, fmt_x, base + off[6], base + off[7], st)) !=
       hipSuccess)
     return hip_status(e, "quantize X along M");
   mx::GemmStoreArgs g{};
   g.a_codes = base + off[0]; g.a_scales = base + off[1]; g.lda = N;
   g.b_codes = base + off[2]; g.b_scales = base + off[3]; g.ldb = N;
   g.M = M; g.N = K; g.K = N; g.out = dx; g.ldo = K;
-  if ((e = mx::launch_gemm_store(g, 1, fmt_dy, fmt_w, st)) != hipSuccess) return hip_status(e, "dX GEMM");
+  // stage 2 -- dX GEMM
+  if (lo <= 2 && 2 <= hi && (e = mx::launch_gemm_store(g, 1, fmt_dy, fmt_w, st)) != hipSuccess)
+    return hip_status(e, "dX GEMM");
   g.a_codes = base + off[4]; g.a_scales = base + off[5]; g.lda = M;
   g.b_codes = base + off[6]; g.b_scales = base + off[7]; g.ldb = M;
   g.M = N; g.N = K; g.K = M; g.out = dw; g.ldo = K;
-  if ((e = mx::launch_gemm_store(g, 1, fmt_dy, fmt_x, st)) != hipSuccess) return hip_status(e, "dW GEMM");
+  // stage 3 -- dW GEMM
+  if (lo <= 3 && 3 <= hi && (e = mx::launch_gemm_store(g, 1, fmt_dy, fmt_x, st)) != hipSuccess)
+    return hip_status(e, "dW GEMM");
   return ok();
+}
+
+int matmul_mxfp8_bwd(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                     int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return dense_run(dy, w, x, M, N, K, fmt_dy, fmt_w, fmt_x, dx, dw, ws, ws_bytes, stream, 0, 3);
+}
+
+int matmul_mxfp8_bwd_stage(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N,
+                           int64_t K, int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws,
+                           size_t ws_bytes, int stage, void* stream) {
+  if (stage < 0 || stage > 3) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd_stage: stage %d outside [0,4)", stage);
+  return dense_run(dy, w, x, M, N, K, fmt_dy, fmt_w, fmt_x, dx, dw, ws, ws_bytes, stream, stage, stage);
 }
 
 int64_t moe_num_blocks(int64_t T, int64_t K, int64_t E, int64_t B) {
@@ -217,7 +234,7 @@ size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* a) {
   return L.total;
 }
 
-int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* stream) {
+static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* stream, int lo, int hi) {
   int rc = moe_check_shapes(a);
   if (rc) return rc;
   if (!valid_fmt(a->fmt_weight) || !valid_fmt(a->fmt_act) || !valid_fmt(a->fmt_grad))
@@ -262,9 +279,11 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   float* db2_acc = reinterpret_cast<float*>(at(L.db2_acc));
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  int stage = -1;
 #define STEP(call, what) \
-  if ((e = (call)) != hipSuccess) return hip_status(e, what);
+  if (stage >= lo && stage <= hi && (e = (call)) != hipSuccess) return hip_status(e, what);
 
+  stage = 0;
   STEP(mx::launch_fill_u32(dx_acc, T * H, 0u, st), "zero dX accumulator");
   STEP(mx::launch_fill_u32(daff_slot, P, 0u, st), "zero d(affinity) accumulator");
   if (a->has_bias) {
@@ -274,9 +293,11 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   STEP(mx::launch_slot_setup(a->token_position_to_id, a->block_to_expert, a->expert_affinities_masked, T, E, N, B,
                              slot_tok, slot_aff, flag, boff, blist, st),
        "slot setup");
+  stage = 1;
   // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later)
   STEP(mx::launch_quant_rows(a->output_hidden_states_grad, T, H, a->fmt_grad, at(L.dy_codes), at(L.dy_scales), st),
        "quantize dY");
+  stage = 2;
   // token-axis operands of Phases 2 and 4: X, a*dY (on H) or dY (on I), the intermediate
   STEP(mx::launch_quant_tok(a->hidden_states, T, H, slot_tok, nullptr, P, a->fmt_act, at(L.x_tok_codes),
                             at(L.x_tok_scales), st),
@@ -284,13 +305,16 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   STEP(mx::launch_quant_tok(a->output_hidden_states_grad, T, H, slot_tok, a->affinity_on == 0 ? slot_aff : nullptr,
                             P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st),
        "gather-quantize dY");
+  stage = 3;
   STEP(mx::launch_inter_tok(a->gate_up_proj_act_checkpoint_T, slot_tok, slot_aff, flag, I, B, N, a->fmt_act,
                             a->affinity_on, at(L.inter_tok_codes), at(L.inter_tok_scales), st),
        "intermediate operand");
+  stage = 4;
   if (a->has_bias)
     STEP(mx::launch_bias(a->output_hidden_states_grad, a->down_proj_bias, slot_tok, slot_aff, a->block_to_expert,
                          flag, H, B, N, daff_slot, db2_acc, st),
          "bias reductions");
+  stage = 5;
   // Phase 1 + fused SwiGLU-backward epilogue
   mx::Phase1Args p1{};
   p1.wd_codes = a->down_codes; p1.wd_scales = a->down_scales;
@@ -302,6 +326,7 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);
   p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
   STEP(mx::launch_phase1(p1, a->fmt_weight, a->fmt_grad, a->has_bias != 0, st), "phase 1");
+  stage = 6;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};
   p3.dgu_row_codes = at(L.dgu_row_codes); p3.dgu_row_scales = at(L.dgu_row_scales);
@@ -309,6 +334,7 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
+  stage = 7;
   // Phase 2: dW_gate_up[e] = X_tok . dGU_tok^T over the expert's blocks
   mx::GemmStoreArgs g{};
   g.a_codes = at(L.x_tok_codes); g.a_scales = at(L.x_tok_scales); g.lda = P;
@@ -316,11 +342,13 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   g.M = H; g.N = 2 * I; g.K = 0; g.out = a->gate_up_proj_weight_grad; g.ldo = 2 * I; g.out_gstride = H * 2 * I;
   g.blk_off = boff; g.blk_list = blist; g.blk = int(B);
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 2");
+  stage = 8;
   // Phase 4: dW_down[e] = inter_tok . gy_tok^T
   g.a_codes = at(L.inter_tok_codes); g.a_scales = at(L.inter_tok_scales); g.lda = P;
   g.b_codes = at(L.gy_tok_codes); g.b_scales = at(L.gy_tok_scales); g.ldb = P;
   g.M = I; g.N = H; g.out = a->down_proj_weight_grad; g.ldo = H; g.out_gstride = I * H;
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 4");
+  stage = 9;
   // finalisation
   STEP(mx::launch_f32_to_bf16(dx_acc, a->hidden_states_grad, T * H, st), "dX to bf16");
   STEP(mx::launch_daff_scatter(daff_slot, slot_tok, a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,
@@ -332,6 +360,16 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* 
   }
 #undef STEP
   return ok();
+}
+
+int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return moe_run(a, ws, ws_bytes, stream, 0, MOE_BWD_NUM_STAGES - 1);
+}
+
+int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, int stage, void* stream) {
+  if (stage < 0 || stage >= MOE_BWD_NUM_STAGES)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8_stage: stage %d outside [0,%d)", stage, MOE_BWD_NUM_STAGES);
+  return moe_run(a, ws, ws_bytes, stream, stage, stage);
 }
 
 }  // extern "C"
