@@ -181,6 +181,8 @@ typedef struct {
 /* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised
  * operands can be read back from them after a call:
  *   dy_codes/dy_scales        [T,H] / [T,H/32]        dY along H (Phase 1)
+ *   dy_deq                    [T,H] bf16              exact values of those codes
+ *   wd_deq                    [E,I,H] bf16            exact values of the W_down codes
  *   x_tok_codes/scales        [H,P] / [H,P/32]        X along slots (Phase 2), P = N*B
  *   gy_tok_codes/scales       [H,P] / [H,P/32]        a*dY (on H) or dY (on I), Phase 4
  *   inter_tok_codes/scales    [I,P] / [I,P/32]        inter (on H) or a*inter (on I)
@@ -192,7 +194,7 @@ typedef struct {
  *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32.
  * Pad slots hold code 0.  Rows of a region are contiguous; no padding between rows. */
 typedef struct {
-  size_t dy_codes, dy_scales, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
+  size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
       dgu_tok_scales, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;

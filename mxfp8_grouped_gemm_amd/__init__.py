@@ -56,7 +56,7 @@ class MoeBwdArgs(C.Structure):
                 ("gate_and_up_proj_bias_grad", _p), ("down_proj_bias_grad", _p)]
 
 
-LAYOUT_FIELDS = ("dy_codes", "dy_scales", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
+LAYOUT_FIELDS = ("dy_codes", "dy_scales", "dy_deq", "wd_deq", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
                  "inter_tok_codes", "inter_tok_scales", "dgu_row_codes", "dgu_row_scales", "dgu_tok_codes",
                  "dgu_tok_scales", "dx_acc", "daff_slot", "db1_acc", "db2_acc", "expert_block_offsets",
                  "expert_block_list", "slot_token", "slot_affinity", "block_flag", "total")

@@ -182,6 +182,8 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   };
   put(L->dy_codes, T * H);
   put(L->dy_scales, T * H / 32);
+  put(L->dy_deq, T * H * 2);
+  put(L->wd_deq, E * I * H * 2);
   put(L->x_tok_codes, H * P);
   put(L->x_tok_scales, H * P / 32);
   put(L->gy_tok_codes, H * P);
@@ -215,8 +217,8 @@ static int moe_check_shapes(const moe_bwd_mxfp8_args* a) {
   const int64_t B = a->block_size;
   if (B != 128 && B != 256 && B != 512 && B != 1024)
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: block_size %lld not in {128,256,512,1024}", (long long)B);
-  if (a->N * B > INT32_MAX || a->T * a->E > INT32_MAX)
-    return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: sizes beyond int32 indexing");
+  if (a->N * B > INT32_MAX || a->T * a->E > INT32_MAX || a->T * a->H * 2 > INT32_MAX)
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: sizes beyond 32-bit indexing");
   return MXFP8_OK;
 }
 
@@ -295,8 +297,13 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
        "slot setup");
   stage = 1;
   // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later)
-  STEP(mx::launch_quant_rows(a->output_hidden_states_grad, T, H, a->fmt_grad, at(L.dy_codes), at(L.dy_scales), st),
+  STEP(mx::launch_quant_rows(a->output_hidden_states_grad, T, H, a->fmt_grad, at(L.dy_codes), at(L.dy_scales), st,
+                             reinterpret_cast<uint16_t*>(at(L.dy_deq))),
        "quantize dY");
+  // Phase-1 operands in bf16: the exact values of the MX codes (see the Phase-1 kernel)
+  STEP(mx::launch_dequant_rows(a->down_codes, a->down_scales, E * I, H, a->fmt_weight,
+                               reinterpret_cast<uint16_t*>(at(L.wd_deq)), st),
+       "dequantize W_down");
   stage = 2;
   // token-axis operands of Phases 2 and 4: X, a*dY (on H) or dY (on I), the intermediate
   STEP(mx::launch_quant_tok(a->hidden_states, T, H, slot_tok, nullptr, P, a->fmt_act, at(L.x_tok_codes),
@@ -317,15 +324,15 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   stage = 5;
   // Phase 1 + fused SwiGLU-backward epilogue
   mx::Phase1Args p1{};
-  p1.wd_codes = a->down_codes; p1.wd_scales = a->down_scales;
-  p1.dy_codes = at(L.dy_codes); p1.dy_scales = at(L.dy_scales);
+  p1.wd_deq = reinterpret_cast<const uint16_t*>(at(L.wd_deq));
+  p1.dy_deq = reinterpret_cast<const uint16_t*>(at(L.dy_deq));
   p1.slot_tok = slot_tok; p1.slot_aff = slot_aff; p1.b2e = a->block_to_expert; p1.flag = flag;
   p1.ckpt = a->gate_up_proj_act_checkpoint_T;
   p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
   p1.dgu_row_codes = at(L.dgu_row_codes); p1.dgu_row_scales = at(L.dgu_row_scales);
   p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);
   p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
-  STEP(mx::launch_phase1(p1, a->fmt_weight, a->fmt_grad, a->has_bias != 0, st), "phase 1");
+  STEP(mx::launch_phase1(p1, a->fmt_grad, a->has_bias != 0, st), "phase 1");
   stage = 6;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};

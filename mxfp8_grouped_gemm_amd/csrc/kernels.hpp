@@ -9,7 +9,10 @@ namespace mx {
 
 // quantize.hip
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, hipStream_t st);
+                             uint8_t* scales, hipStream_t st, uint16_t* deq = nullptr);
+// codes [rows][cols] + scales [rows][cols/32] (groups along cols) -> exact bf16 values
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, int fmt,
+                               uint16_t* out, hipStream_t st);
 hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
                              uint8_t* scales, hipStream_t st);
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
@@ -58,10 +61,8 @@ hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, 
 
 // moe_gemm.hip
 struct Phase1Args {
-  const uint8_t* wd_codes;      // [E][I][H]
-  const uint8_t* wd_scales;     // [E][I][H/32]
-  const uint8_t* dy_codes;      // [T][H]
-  const uint8_t* dy_scales;     // [T][H/32]
+  const uint16_t* wd_deq;       // [E][I][H] bf16: dequantised W_down (exact)
+  const uint16_t* dy_deq;       // [T][H] bf16: dequantised Q_H(dY) (exact)
   const int32_t* slot_tok;      // [P]
   const float* slot_aff;        // [P]
   const int32_t* b2e;           // [N]
@@ -76,7 +77,7 @@ struct Phase1Args {
   float* db1_acc;               // [E][2][I]
   int tiles_m, tiles_n;
 };
-hipError_t launch_phase1(const Phase1Args& p, int fw, int fg, bool bias, hipStream_t st);
+hipError_t launch_phase1(const Phase1Args& p, int fg, bool bias, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]

@@ -4,8 +4,10 @@
 // and _up_projection_backward_act).
 //
 // Phase 1, per block b of expert e (tile rows = intermediate index i,
-// tile columns = block slot p, contraction over H; the fp8 tiles are reduced
-// with bf16 MFMAs at fp32 precision, see mx_mainloop_bf16):
+// tile columns = block slot p, contraction over H; the operands are the
+// exactly dequantised MX values in bf16, reduced with bf16 MFMAs whose fp32
+// accumulation is exact enough that requantising the result below makes the
+// same rounding decisions as an exact sum would):
 //   dS[i][p]   = sum_h deq(W_down[e])[i][h] * deq(dY[tok_p])[h]   (dY rows are
 //                quantised along H once and gathered here by token id)
 //   epilogue:  ga = bf16(silu(g)), inter = bf16(ga*u)   (g,u from the checkpoint)
@@ -19,72 +21,60 @@
 // contraction over 2I):
 //   dX[tok_p][h] += sum_{j,i} deq(dGU)[p][j][i] * deq(W_gate_up[e])[h][j][i]
 //   as fp32 atomic adds (a token's top-k slots sit in different blocks).
-#include "gemm_core.hpp"
+#include "gemm_v2.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
 #include "swiglu.hpp"
 
 namespace mx {
 
+using v2::v16f;
+
 struct KMapPlain {
-  int64_t K;
-  __device__ __forceinline__ void operator()(int s, int64_t& kc, int& kv) const {
-    kc = int64_t(s) * kBK;
-    const int64_t rem = K - kc;
-    kv = rem < kBK ? int(rem) : kBK;
+  int64_t K;   // bytes
+  __device__ __forceinline__ void operator()(int s, uint32_t& kc, int& kv) const {
+    kc = uint32_t(int64_t(s) * v2::BK);
+    const int64_t rem = K - int64_t(kc);
+    kv = rem < v2::BK ? int(rem) : v2::BK;
   }
 };
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int FW, int FG, bool BIAS, bool SALIGN>
-__global__ void __launch_bounds__(kThreads) phase1_kernel(Phase1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * kBK];
+template <int BM, int BN, int FG, bool BIAS, bool GENERIC>
+__global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
   constexpr int FM = BM / 64, FN = BN / 64;
   const int per_blk = p.tiles_m * p.tiles_n;
-  const int b = blockIdx.x / per_blk;
-  const int t = blockIdx.x - b * per_blk;
-  const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+  const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
+  const int b = id / per_blk;
+  int tm, tn;
+  v2::grouped_tile<8>(id - b * per_blk, p.tiles_m, p.tiles_n, tm, tn);
   if (!p.flag[b]) return;
   const int64_t e = p.b2e[b];
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;   // m: i, n: slot within block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t P = p.N * p.B;
   const int64_t sbase = int64_t(b) * p.B;
-  const int64_t H32 = p.H / 32;
 
-  TileOperandsBf16<BM, BN, SALIGN> op;
-#pragma unroll
-  for (int q = 0; q < BM / 32; ++q) {
-    const int64_t i = m0 + (threadIdx.x >> 3) + 32 * q;
-    op.a.row[q] = i < p.I ? p.wd_codes + (e * p.I + i) * p.H : nullptr;
-  }
-#pragma unroll
-  for (int q = 0; q < BN / 32; ++q) {
-    const int64_t s = n0 + (threadIdx.x >> 3) + 32 * q;
-    const int64_t tok = s < p.B ? p.slot_tok[sbase + s] : -1;
-    op.b.row[q] = tok >= 0 ? p.dy_codes + tok * p.H : nullptr;
-  }
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    const int64_t i = m0 + (wave >> 1) * (BM / 2) + f * 32 + (lane & 31);
-    op.sa.row[f] = i < p.I ? p.wd_scales + (e * p.I + i) * H32 : nullptr;
-  }
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int64_t s = n0 + (wave & 1) * (BN / 2) + f * 32 + (lane & 31);
-    const int64_t tok = s < p.B ? p.slot_tok[sbase + s] : -1;
-    op.sb.row[f] = tok >= 0 ? p.dy_scales + tok * H32 : nullptr;
-  }
+  // A: dequantised W_down[e] rows i; B: dequantised dY rows gathered by token
+  v2::Operand<BM, FM> A;
+  v2::Operand<BN, FN> B;
+  v2::setup_rows(A, reinterpret_cast<const uint8_t*>(p.wd_deq + e * p.I * p.H), nullptr, m0, p.I, 2 * p.H, 0,
+                 (wave >> 1) * (BM / 2));
+  const int32_t* st = p.slot_tok + sbase;
+  const int64_t B_ = p.B;
+  v2::setup_gather(B, reinterpret_cast<const uint8_t*>(p.dy_deq), nullptr, p.T, 2 * p.H, 0, (wave & 1) * (BN / 2),
+                   [&](int r) -> int64_t { const int64_t s = n0 + r; return s < B_ ? int64_t(st[s]) : -1; });
   v16f acc[FM][FN];
-  // fp32-precise reduction: the result is requantised to the gradient format below
-  mx_mainloop_bf16<BM, BN, FW, FG, SALIGN>(op, int((p.H + kBK - 1) / kBK), KMapPlain{p.H}, smem, acc);
+  v2::mainloop<BM, BN, v2::kBf16, 0, 0, GENERIC>(A, B, int((2 * p.H + v2::BK - 1) / v2::BK), KMapPlain{2 * p.H},
+                                                  smem, acc);
 
   // ---- epilogue -------------------------------------------------------------
   const int h = lane >> 5;
   const int64_t twoI = 2 * p.I;
 #pragma unroll
   for (int fj = 0; fj < FN; ++fj) {
-    const int64_t s = n0 + acc_col<BM, BN>(fj);               // this lane's slot
+    const int64_t s = n0 + v2::acc_col<BM, BN>(fj);           // this lane's slot
     const bool in_blk = s < p.B;
     const int64_t slot = sbase + (in_blk ? s : 0);
     const bool valid = in_blk && p.slot_tok[slot] >= 0;
@@ -178,101 +168,92 @@ __global__ void __launch_bounds__(kThreads) phase1_kernel(Phase1Args p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int FG, int FW, bool SALIGN>
-__global__ void __launch_bounds__(kThreads) phase3_kernel(Phase3Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * kBK];
+template <int BM, int BN, int FG, int FW, bool GENERIC>
+__global__ void __launch_bounds__(v2::kThreads) phase3_kernel(Phase3Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
   constexpr int FM = BM / 64, FN = BN / 64;
   const int per_blk = p.tiles_m * p.tiles_n;
-  const int b = blockIdx.x / per_blk;
-  const int t = blockIdx.x - b * per_blk;
-  const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+  const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
+  const int b = id / per_blk;
+  int tm, tn;
+  v2::grouped_tile<8>(id - b * per_blk, p.tiles_m, p.tiles_n, tm, tn);
   if (!p.flag[b]) return;
   const int64_t e = p.b2e[b];
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;   // m: slot within block, n: h
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   const int64_t sbase = int64_t(b) * p.B;
   const int64_t twoI = 2 * p.I;
 
-  TileOperands<BM, BN, SALIGN> op;
-#pragma unroll
-  for (int q = 0; q < BM / 32; ++q) {
-    const int64_t s = m0 + (threadIdx.x >> 3) + 32 * q;
-    const bool ok = s < p.B && p.slot_tok[sbase + s] >= 0;
-    op.a.row[q] = ok ? p.dgu_row_codes + (sbase + s) * twoI : nullptr;
-  }
-#pragma unroll
-  for (int q = 0; q < BN / 32; ++q) {
-    const int64_t hh = n0 + (threadIdx.x >> 3) + 32 * q;
-    op.b.row[q] = hh < p.H ? p.wgu_codes + (e * p.H + hh) * twoI : nullptr;
-  }
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    const int64_t s = m0 + (wave >> 1) * (BM / 2) + f * 32 + (lane & 31);
-    const bool ok = s < p.B && p.slot_tok[sbase + s] >= 0;
-    op.sa.row[f] = ok ? p.dgu_row_scales + (sbase + s) * (twoI / 32) : nullptr;
-  }
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int64_t hh = n0 + (wave & 1) * (BN / 2) + f * 32 + (lane & 31);
-    op.sb.row[f] = hh < p.H ? p.wgu_scales + (e * p.H + hh) * (twoI / 32) : nullptr;
-  }
+  // A: the block's rows of dGU quantised along I; B: W_gate_up[e] viewed [H][2I]
+  v2::Operand<BM, FM> A;
+  v2::Operand<BN, FN> B;
+  v2::setup_rows(A, p.dgu_row_codes + sbase * twoI, p.dgu_row_scales + sbase * (twoI / 32), m0, p.B, twoI,
+                 twoI / 32, (wave >> 1) * (BM / 2));
+  v2::setup_rows(B, p.wgu_codes + e * p.H * twoI, p.wgu_scales + e * p.H * (twoI / 32), n0, p.H, twoI, twoI / 32,
+                 (wave & 1) * (BN / 2));
   v16f acc[FM][FN];
-  mx_mainloop<BM, BN, FG, FW, SALIGN>(op, int((twoI + kBK - 1) / kBK), KMapPlain{twoI}, smem, acc);
+  v2::mainloop<BM, BN, v2::kFp8, FG, FW, GENERIC>(A, B, int((twoI + v2::BK - 1) / v2::BK), KMapPlain{twoI}, smem,
+                                                   acc);
 
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int64_t s = m0 + acc_row<BM, BN>(fi, q);
+      const int64_t s = m0 + v2::acc_row<BM, BN>(fi, q);
       const int64_t tok = s < p.B ? p.slot_tok[sbase + s] : -1;
       if (tok < 0) continue;
       float* dst = p.dx_acc + tok * p.H;
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj) {
-        const int64_t hh = n0 + acc_col<BM, BN>(fj);
+        const int64_t hh = n0 + v2::acc_col<BM, BN>(fj);
         if (hh < p.H) atomicAdd(dst + hh, acc[fi][fj][q]);
       }
     }
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool SALIGN>
-static hipError_t phase1_launch(Phase1Args p, int fw, int fg, bool bias, hipStream_t st) {
+template <int BM, int BN, bool G>
+static hipError_t phase1_launch(Phase1Args p, int fg, bool bias, hipStream_t st) {
   p.tiles_m = int((p.I + BM - 1) / BM);
   p.tiles_n = int((p.B + BN - 1) / BN);
   const unsigned blocks = unsigned(int64_t(p.tiles_m) * p.tiles_n * p.N);
-#define P1_LAUNCH(FW_, FG_)                                                                  \
-  if (bias) phase1_kernel<BM, BN, FW_, FG_, true, SALIGN><<<blocks, kThreads, 0, st>>>(p); \
-  else phase1_kernel<BM, BN, FW_, FG_, false, SALIGN><<<blocks, kThreads, 0, st>>>(p);
-  if (fw == 0 && fg == 0) { P1_LAUNCH(0, 0) }
-  else if (fw == 0) { P1_LAUNCH(0, 1) }
-  else if (fg == 0) { P1_LAUNCH(1, 0) }
-  else { P1_LAUNCH(1, 1) }
-#undef P1_LAUNCH
+  if (fg == 0) {
+    if (bias) phase1_kernel<BM, BN, 0, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
+    else phase1_kernel<BM, BN, 0, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  } else {
+    if (bias) phase1_kernel<BM, BN, 1, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
+    else phase1_kernel<BM, BN, 1, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
-// Scale rows are read as 32-bit words when their stride (K/32 bytes) keeps them aligned.
-hipError_t launch_phase1(const Phase1Args& p, int fw, int fg, bool bias, hipStream_t st) {
-  if (p.H % kBK == 0) return phase1_launch<128, 128, true>(p, fw, fg, bias, st);
-  return phase1_launch<128, 128, false>(p, fw, fg, bias, st);
+// Tile shape: 256 along a dimension when it is at least 256, else 128.
+hipError_t launch_phase1(const Phase1Args& p, int fg, bool bias, hipStream_t st) {
+  const bool g = (2 * p.H) % v2::BK != 0;      // a ragged last K stage
+  if (p.I >= 256 && p.B >= 256)
+    return g ? phase1_launch<256, 256, true>(p, fg, bias, st) : phase1_launch<256, 256, false>(p, fg, bias, st);
+  if (p.I >= 256)
+    return g ? phase1_launch<256, 128, true>(p, fg, bias, st) : phase1_launch<256, 128, false>(p, fg, bias, st);
+  return g ? phase1_launch<128, 128, true>(p, fg, bias, st) : phase1_launch<128, 128, false>(p, fg, bias, st);
 }
 
-template <int BM, int BN, bool SALIGN>
+template <int BM, int BN, bool G>
 static hipError_t phase3_launch(Phase3Args p, int fg, int fw, hipStream_t st) {
   p.tiles_m = int((p.B + BM - 1) / BM);
   p.tiles_n = int((p.H + BN - 1) / BN);
   const unsigned blocks = unsigned(int64_t(p.tiles_m) * p.tiles_n * p.N);
-  if (fg == 0 && fw == 0) phase3_kernel<BM, BN, 0, 0, SALIGN><<<blocks, kThreads, 0, st>>>(p);
-  else if (fg == 0) phase3_kernel<BM, BN, 0, 1, SALIGN><<<blocks, kThreads, 0, st>>>(p);
-  else if (fw == 0) phase3_kernel<BM, BN, 1, 0, SALIGN><<<blocks, kThreads, 0, st>>>(p);
-  else phase3_kernel<BM, BN, 1, 1, SALIGN><<<blocks, kThreads, 0, st>>>(p);
+  if (fg == 0 && fw == 0) phase3_kernel<BM, BN, 0, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else if (fg == 0) phase3_kernel<BM, BN, 0, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else if (fw == 0) phase3_kernel<BM, BN, 1, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else phase3_kernel<BM, BN, 1, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st) {
-  if ((2 * p.I) % kBK == 0) return phase3_launch<128, 128, true>(p, fg, fw, st);
-  return phase3_launch<128, 128, false>(p, fg, fw, st);
+  const bool g = (2 * p.I) % v2::BK != 0;      // unaligned scale rows / ragged last K stage
+  if (p.B >= 256 && p.H >= 256)
+    return g ? phase3_launch<256, 256, true>(p, fg, fw, st) : phase3_launch<256, 256, false>(p, fg, fw, st);
+  return g ? phase3_launch<128, 256, true>(p, fg, fw, st) : phase3_launch<128, 256, false>(p, fg, fw, st);
 }
 
 }  // namespace mx

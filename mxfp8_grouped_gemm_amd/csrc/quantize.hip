@@ -18,11 +18,23 @@ namespace mx {
 // ---------------------------------------------------------------------------
 // quant_rows: 4 lanes per group, 8 bf16 (16 B) per lane.  A wave covers 16
 // groups = 1 KiB of input per load instruction, fully coalesced.
-template <int FMT>
+// fp8 codes -> bf16 values times 2^X (exact: at most 4 significant bits).
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float pow2_f32(int X) {
+  return X > -127 ? __uint_as_float(uint32_t(X + 127) << 23) : __uint_as_float(0x00400000u);
+}
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t deq_pk(uint32_t codes, float scale) {
+  v2bf_t r = FMT == kE4M3 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, HI)
+                          : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(codes, scale, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int FMT, bool DEQ>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict__ x,
                                                           uint2* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
-                                                          int64_t nchunks) {
+                                                          int64_t nchunks, uint4* __restrict__ deq) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
     const uint4 v = x[c];
@@ -45,6 +57,27 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict
     }
     codes[c] = make_uint2(out[0], out[1]);
     if ((c & 3) == 0) scales[c >> 2] = uint8_t(X + 127);
+    if (DEQ) {
+      const float sc = pow2_f32(X);
+      deq[c] = make_uint4(deq_pk<FMT, false>(out[0], sc), deq_pk<FMT, true>(out[0], sc),
+                          deq_pk<FMT, false>(out[1], sc), deq_pk<FMT, true>(out[1], sc));
+    }
+  }
+}
+
+// codes [rows][cols] with scales along cols -> bf16; one thread per 16 codes.
+template <int FMT>
+__global__ void __launch_bounds__(256) dequant_rows_kernel(const uint4* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales, int64_t n16,
+                                                            uint4* __restrict__ out) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < n16; c += stride) {
+    const uint4 v = codes[c];
+    const float sc = pow2_f32(int(scales[c >> 1]) - 127);
+    out[2 * c] = make_uint4(deq_pk<FMT, false>(v.x, sc), deq_pk<FMT, true>(v.x, sc), deq_pk<FMT, false>(v.y, sc),
+                            deq_pk<FMT, true>(v.y, sc));
+    out[2 * c + 1] = make_uint4(deq_pk<FMT, false>(v.z, sc), deq_pk<FMT, true>(v.z, sc),
+                                deq_pk<FMT, false>(v.w, sc), deq_pk<FMT, true>(v.w, sc));
   }
 }
 
@@ -164,17 +197,36 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // host launchers
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, hipStream_t st) {
+                             uint8_t* scales, hipStream_t st, uint16_t* deq) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
   const int64_t want = (nchunks + 255) / 256;
   const int blocks = int(want < 65536 ? want : 65536);
+  const uint4* xs = reinterpret_cast<const uint4*>(x);
+  uint2* cs = reinterpret_cast<uint2*>(codes);
+  uint4* ds = reinterpret_cast<uint4*>(deq);
+  if (fmt == kE4M3) {
+    if (deq) quant_rows_kernel<kE4M3, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
+    else quant_rows_kernel<kE4M3, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
+  } else {
+    if (deq) quant_rows_kernel<kE5M2, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
+    else quant_rows_kernel<kE5M2, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, int fmt,
+                               uint16_t* out, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  if (n16 == 0) return hipSuccess;
+  const int64_t want = (n16 + 255) / 256;
+  const int blocks = int(want < 65536 ? want : 65536);
   if (fmt == kE4M3)
-    quant_rows_kernel<kE4M3><<<blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(x),
-                                                      reinterpret_cast<uint2*>(codes), scales, nchunks);
+    dequant_rows_kernel<kE4M3><<<blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(codes), scales, n16,
+                                                        reinterpret_cast<uint4*>(out));
   else
-    quant_rows_kernel<kE5M2><<<blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(x),
-                                                      reinterpret_cast<uint2*>(codes), scales, nchunks);
+    dequant_rows_kernel<kE5M2><<<blocks, 256, 0, st>>>(reinterpret_cast<const uint4*>(codes), scales, n16,
+                                                        reinterpret_cast<uint4*>(out));
   return hipGetLastError();
 }
 
