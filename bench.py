@@ -54,9 +54,9 @@ def stage_work(cfg, N):
     q = 1 + 1 / 32                      # bytes per quantised element (code + its share of a scale)
     return {
         "setup": ("hbm", T * H * 4 + P * 12),
-        "quantize_dy": ("hbm", T * H * (2 + q)),
+        # dY: bf16 in, codes + scales + exact bf16 values out; W_down: codes in, bf16 values out
+        "quantize_dy": ("hbm", T * H * (2 + q + 2) + E * I * H * (q + 2)),
         "gather_quantize_x_dy": ("hbm", 2 * (TK * H * 2 + P * H * q)),
-        "intermediate": ("hbm", P * I * (4 + q)),
         "bias": ("hbm", 2 * TK * H * 2 if cfg.has_bias else 0),
         "phase1": ("mfma_bf16", 2 * TK * H * I),
         "phase3": ("mfma", 4 * TK * H * I),

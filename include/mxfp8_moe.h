@@ -221,11 +221,12 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
  * is exactly one full call.  Stages:
  *   0 setup (zero accumulators, slot routing info, per-expert block lists)
  *   1 quantise dY along H         2 gather-quantise X and a*dY (or dY) along slots
- *   3 intermediate along slots    4 bias reductions (has_bias only)
- *   5 Phase 1 + epilogue          6 Phase 3 (dX scatter-add)
- *   7 Phase 2 (dW_gate_up)        8 Phase 4 (dW_down)          9 finalise to bf16
+ *   3 bias reductions (has_bias only)
+ *   4 Phase 1 + epilogue (also the intermediate quantised along slots)
+ *   5 Phase 3 (dX scatter-add)    6 Phase 2 (dW_gate_up)       7 Phase 4 (dW_down)
+ *   8 finalise to bf16
  * Errors as for moe_bwd_mxfp8, plus INVALID_ARG for a stage outside the range. */
-#define MOE_BWD_NUM_STAGES 10
+#define MOE_BWD_NUM_STAGES 9
 int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
                         int stage, void* stream);
 

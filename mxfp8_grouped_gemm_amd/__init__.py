@@ -267,9 +267,9 @@ class MoeBwd:
                "moe_bwd_mxfp8")
         return self.out
 
-    NUM_STAGES = 10
-    STAGE_NAMES = ("setup", "quantize_dy", "gather_quantize_x_dy", "intermediate", "bias", "phase1",
-                   "phase3", "phase2", "phase4", "finalize")
+    NUM_STAGES = 9
+    STAGE_NAMES = ("setup", "quantize_dy", "gather_quantize_x_dy", "bias", "phase1", "phase3", "phase2",
+                   "phase4", "finalize")
 
     def stage(self, s: int):
         """Re-run one stage on the workspace a full run filled (profiling aid)."""

@@ -305,7 +305,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
                                reinterpret_cast<uint16_t*>(at(L.wd_deq)), st),
        "dequantize W_down");
   stage = 2;
-  // token-axis operands of Phases 2 and 4: X, a*dY (on H) or dY (on I), the intermediate
+  // token-axis operands of Phases 2 and 4: X, a*dY (on H) or dY (on I); the intermediate
+  // operand comes out of the Phase-1 epilogue
   STEP(mx::launch_quant_tok(a->hidden_states, T, H, slot_tok, nullptr, P, a->fmt_act, at(L.x_tok_codes),
                             at(L.x_tok_scales), st),
        "gather-quantize X");
@@ -313,16 +314,12 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
                             P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st),
        "gather-quantize dY");
   stage = 3;
-  STEP(mx::launch_inter_tok(a->gate_up_proj_act_checkpoint_T, slot_tok, slot_aff, flag, I, B, N, a->fmt_act,
-                            a->affinity_on, at(L.inter_tok_codes), at(L.inter_tok_scales), st),
-       "intermediate operand");
-  stage = 4;
   if (a->has_bias)
     STEP(mx::launch_bias(a->output_hidden_states_grad, a->down_proj_bias, slot_tok, slot_aff, a->block_to_expert,
                          flag, H, B, N, daff_slot, db2_acc, st),
          "bias reductions");
-  stage = 5;
-  // Phase 1 + fused SwiGLU-backward epilogue
+  stage = 4;
+  // Phase 1 + fused SwiGLU-backward epilogue (also writes the intermediate operand)
   mx::Phase1Args p1{};
   p1.wd_deq = reinterpret_cast<const uint16_t*>(at(L.wd_deq));
   p1.dy_deq = reinterpret_cast<const uint16_t*>(at(L.dy_deq));
@@ -331,9 +328,11 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
   p1.dgu_row_codes = at(L.dgu_row_codes); p1.dgu_row_scales = at(L.dgu_row_scales);
   p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);
+  p1.inter_tok_codes = at(L.inter_tok_codes); p1.inter_tok_scales = at(L.inter_tok_scales);
   p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
-  STEP(mx::launch_phase1(p1, a->fmt_grad, a->has_bias != 0, st), "phase 1");
-  stage = 6;
+  p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias;
+  STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_act, st), "phase 1");
+  stage = 5;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};
   p3.dgu_row_codes = at(L.dgu_row_codes); p3.dgu_row_scales = at(L.dgu_row_scales);
@@ -341,7 +340,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
-  stage = 7;
+  stage = 6;
   // Phase 2: dW_gate_up[e] = X_tok . dGU_tok^T over the expert's blocks
   mx::GemmStoreArgs g{};
   g.a_codes = at(L.x_tok_codes); g.a_scales = at(L.x_tok_scales); g.lda = P;
@@ -349,13 +348,13 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   g.M = H; g.N = 2 * I; g.K = 0; g.out = a->gate_up_proj_weight_grad; g.ldo = 2 * I; g.out_gstride = H * 2 * I;
   g.blk_off = boff; g.blk_list = blist; g.blk = int(B);
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 2");
-  stage = 8;
+  stage = 7;
   // Phase 4: dW_down[e] = inter_tok . gy_tok^T
   g.a_codes = at(L.inter_tok_codes); g.a_scales = at(L.inter_tok_scales); g.lda = P;
   g.b_codes = at(L.gy_tok_codes); g.b_scales = at(L.gy_tok_scales); g.ldb = P;
   g.M = I; g.N = H; g.out = a->down_proj_weight_grad; g.ldo = H; g.out_gstride = I * H;
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 4");
-  stage = 9;
+  stage = 8;
   // finalisation
   STEP(mx::launch_f32_to_bf16(dx_acc, a->hidden_states_grad, T * H, st), "dX to bf16");
   STEP(mx::launch_daff_scatter(daff_slot, slot_tok, a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,

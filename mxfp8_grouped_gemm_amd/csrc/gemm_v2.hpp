@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mx {
 namespace v2 {
 
@@ -304,6 +306,18 @@ template <int BM, int BN>
 __device__ __forceinline__ int acc_col(int j) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   return (wave & 1) * (BN / 2) + j * 32 + (lane & 31);
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): a loop over
+// fragments whose index is a compile-time constant however large the body, so
+// accumulator fragments are always addressed statically (stay in registers).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_(f, std::make_integer_sequence<int, N>{});
 }
 
 // Tile order: consecutive workgroups land on different XCDs (round-robin over

@@ -49,9 +49,6 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* flag,
                              int32_t* off, int32_t* list, hipStream_t st);
-hipError_t launch_inter_tok(const uint16_t* ckpt, const int32_t* slot_tok, const float* slot_aff,
-                            const int32_t* flag, int64_t I, int64_t B, int64_t N, int fmt, int on_i,
-                            uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,
                        const int32_t* b2e, const int32_t* flag, int64_t H, int64_t B, int64_t N, float* daff_slot,
                        float* db2_acc, hipStream_t st);
@@ -73,11 +70,15 @@ struct Phase1Args {
   uint8_t* dgu_row_scales;      // [P][2I/32]
   uint8_t* dgu_tok_codes;       // [2I][P]
   uint8_t* dgu_tok_scales;      // [2I][P/32]
+  uint8_t* inter_tok_codes;     // [I][P]: the intermediate (times a with the affinity on I), slot groups
+  uint8_t* inter_tok_scales;    // [I][P/32]
   float* daff_slot;             // [P]
   float* db1_acc;               // [E][2][I]
+  int affinity_on_i;            // 1: the intermediate operand carries the affinity
+  int has_bias;                 // 1: accumulate db1
   int tiles_m, tiles_n;
 };
-hipError_t launch_phase1(const Phase1Args& p, int fg, bool bias, hipStream_t st);
+hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, int fmt_act, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]

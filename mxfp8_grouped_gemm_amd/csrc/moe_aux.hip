@@ -179,72 +179,6 @@ hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const floa
 // (affinity on H) or bf16(fp32(a * inter)) (affinity on I), from the gate/up
 // checkpoint [N,2,I,B] (P1 gate_up_proj_act_checkpoint_T).  Groups of 32
 // consecutive slots; 4 lanes per group, 8 slots per lane.  Padding -> 0.
-template <int FMT, bool ON_I>
-__global__ void __launch_bounds__(256) inter_tok_kernel(const uint16_t* __restrict__ ckpt,
-                                                        const int32_t* __restrict__ slot_tok,
-                                                        const float* __restrict__ slot_aff,
-                                                        const int32_t* __restrict__ flag, int64_t I, int64_t B,
-                                                        int64_t N, uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales) {
-  const int64_t chunks_per_row = B / 8;               // per (block, i)
-  const int64_t total = N * I * chunks_per_row;
-  const int64_t P = N * B;
-  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < total; c += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t b = c / (I * chunks_per_row);
-    const int64_t rem = c - b * I * chunks_per_row;
-    const int64_t i = rem / chunks_per_row;
-    const int64_t p0 = (rem - i * chunks_per_row) * 8;
-    float v[8];
-    uint32_t amax = 0;
-    if (flag[b]) {
-      const uint4 g4 = *reinterpret_cast<const uint4*>(ckpt + ((b * 2 + 0) * I + i) * B + p0);
-      const uint4 u4 = *reinterpret_cast<const uint4*>(ckpt + ((b * 2 + 1) * I + i) * B + p0);
-      const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w}, uw[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int64_t s = b * B + p0 + k;
-        const bool ok = slot_tok[s] >= 0;
-        const float g = ok ? bf16_to_f32(uint16_t(gw[k >> 1] >> (16 * (k & 1)))) : 0.f;
-        const float u = ok ? bf16_to_f32(uint16_t(uw[k >> 1] >> (16 * (k & 1)))) : 0.f;
-        float in = swiglu_inter(g, u);
-        if (ON_I) in = bf16_to_f32(f32_to_bf16(slot_aff[s] * in));
-        v[k] = in;
-        amax = max(amax, abs_bits(in));
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = 0.f;
-    }
-    amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
-    amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
-    const int X = scale_exp<FMT>(amax);
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      w0 |= encode<FMT>(__float_as_uint(v[k]), X) << (8 * k);
-      w1 |= encode<FMT>(__float_as_uint(v[k + 4]), X) << (8 * k);
-    }
-    *reinterpret_cast<uint2*>(codes + i * P + b * B + p0) = make_uint2(w0, w1);
-    if ((p0 & 31) == 0) scales[i * (P / 32) + (b * B + p0) / 32] = uint8_t(X + 127);
-  }
-}
-
-hipError_t launch_inter_tok(const uint16_t* ckpt, const int32_t* slot_tok, const float* slot_aff,
-                            const int32_t* flag, int64_t I, int64_t B, int64_t N, int fmt, int on_i,
-                            uint8_t* codes, uint8_t* scales, hipStream_t st) {
-  const int64_t total = N * I * (B / 8);
-  const int64_t want = (total + 255) / 256;
-  const unsigned blocks = unsigned(want < 65536 ? want : 65536);
-  if (fmt == kE4M3) {
-    if (on_i) inter_tok_kernel<kE4M3, true><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
-    else inter_tok_kernel<kE4M3, false><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
-  } else {
-    if (on_i) inter_tok_kernel<kE5M2, true><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
-    else inter_tok_kernel<kE5M2, false><<<blocks, 256, 0, st>>>(ckpt, slot_tok, slot_aff, flag, I, B, N, codes, scales);
-  }
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // Bias terms (has_bias): per slot <dY_t, b2[e]> added into daff_slot (one wave
 // per slot), and db2[e][h] += sum over a block's slots of a * dY[t][h].

@@ -40,21 +40,49 @@ struct KMapPlain {
 };
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int FG, bool BIAS, bool GENERIC>
+// Phase 1.  Epilogue data flow per wave (wave tile (BM/2) i-rows x (BN/2) slots):
+//   for each 32-row fragment row fi:
+//     for each fragment fj: SwiGLU backward on the 16 values a lane holds (one
+//       slot, 16 of the 32 rows; lane^32 holds the other 16), the I-axis MX
+//       groups (one xor-32 exchange for the amax), stores of dGU quantised
+//       along I, and staging of dG|dU and the intermediate in LDS;
+//     then each lane takes one staged row i and 32-slot groups of it, so the
+//       slot-axis MX groups (dGU and the intermediate operand of Phase 4) are
+//       reduced and encoded in registers and stored as 32-byte runs.
+// The LDS of the main loop is reused for staging after a barrier.
+template <int BM, int BN, int FG, int FA, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
+  constexpr int SMEM = 2 * (BM + BN) * v2::BK;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   constexpr int FM = BM / 64, FN = BN / 64;
+  constexpr int WN = BN / 2;            // slots per wave
+  constexpr int GS = WN * 4 + 16;       // staged row of dG | dU << 16 words (padding spreads rows over banks)
+  constexpr int IS = WN * 2 + 16;       // staged row of intermediate bf16 values
+  static_assert(4 * 32 * (GS + IS) <= SMEM, "per-wave staging must fit in the main-loop LDS");
   const int per_blk = p.tiles_m * p.tiles_n;
   const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
   const int b = id / per_blk;
   int tm, tn;
   v2::grouped_tile<8>(id - b * per_blk, p.tiles_m, p.tiles_n, tm, tn);
-  if (!p.flag[b]) return;
-  const int64_t e = p.b2e[b];
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;   // m: i, n: slot within block
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t P = p.N * p.B;
   const int64_t sbase = int64_t(b) * p.B;
+  if (!p.flag[b]) {
+    // a block without tokens: its intermediate operand is all zeros (codes 0, scale byte 0)
+    for (int k = threadIdx.x; k < BM * (BN / 16); k += v2::kThreads) {
+      const int64_t i = m0 + k / (BN / 16);
+      if (i < p.I)
+        *reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + sbase + n0 + (k % (BN / 16)) * 16) = uint4{0, 0, 0, 0};
+    }
+    for (int k = threadIdx.x; k < BM * (BN / 128); k += v2::kThreads) {
+      const int64_t i = m0 + k / (BN / 128);
+      if (i < p.I)
+        *reinterpret_cast<uint32_t*>(p.inter_tok_scales + i * (P / 32) + (sbase + n0) / 32 + (k % (BN / 128)) * 4) = 0u;
+    }
+    return;
+  }
+  const int64_t e = p.b2e[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   // A: dequantised W_down[e] rows i; B: dequantised dY rows gathered by token
   v2::Operand<BM, FM> A;
@@ -70,101 +98,177 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
                                                   smem, acc);
 
   // ---- epilogue -------------------------------------------------------------
-  const int h = lane >> 5;
+  __syncthreads();   // every wave has read the last stage: the LDS is free for staging
+  const int h = lane >> 5, r = lane & 31;
+  const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
+  uint8_t* stg_gu = smem + wave * 32 * (GS + IS);
+  uint8_t* stg_in = stg_gu + 32 * GS;
   const int64_t twoI = 2 * p.I;
-#pragma unroll
-  for (int fj = 0; fj < FN; ++fj) {
-    const int64_t s = n0 + v2::acc_col<BM, BN>(fj);           // this lane's slot
-    const bool in_blk = s < p.B;
-    const int64_t slot = sbase + (in_blk ? s : 0);
-    const bool valid = in_blk && p.slot_tok[slot] >= 0;
-    const float a = valid ? p.slot_aff[slot] : 0.f;
-    float daff = 0.f;
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi) {
-      const int64_t i0 = m0 + (wave >> 1) * (BM / 2) + fi * 32;   // first row of the fragment
-      if (i0 >= p.I) continue;                                     // uniform per wave
-      float dg[16], du[16];
-      uint32_t amg = 0, amu = 0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t i = i0 + 8 * (q >> 2) + 4 * h + (q & 3);
-        float g = 0.f, u = 0.f;
-        if (valid) {
-          g = bf16_to_f32(p.ckpt[((int64_t(b) * 2 + 0) * p.I + i) * p.B + s]);
-          u = bf16_to_f32(p.ckpt[((int64_t(b) * 2 + 1) * p.I + i) * p.B + s]);
-        }
-        const float ga = swiglu_gate_act(g);
-        const float inter = bf16_to_f32(f32_to_bf16(ga * u));
-        const float ds = acc[fi][fj][q];
-        daff += ds * inter;
-        const float dinter = a * ds;
-        dg[q] = bf16_to_f32(f32_to_bf16(dinter * u * dsilu_f32(g)));
-        du[q] = bf16_to_f32(f32_to_bf16(dinter * ga));
-        amg = max(amg, abs_bits(dg[q]));
-        amu = max(amu, abs_bits(du[q]));
-      }
-      // along I: the 32 rows of this fragment are this lane's 16 and lane^32's 16
-      amg = max(amg, uint32_t(__shfl_xor(int(amg), 32, 64)));
-      amu = max(amu, uint32_t(__shfl_xor(int(amu), 32, 64)));
-      if (in_blk) {
-        const int Xg = scale_exp<FG>(amg), Xu = scale_exp<FG>(amu);
+  // the block's checkpoint [2][I][B] bf16 through a buffer: padding slots read as zeros
+  [[maybe_unused]] const v2::Buf ck = v2::make_rsrc(p.ckpt + int64_t(b) * 2 * p.I * p.B, uint32_t(4 * p.I * p.B));
+  [[maybe_unused]] const uint32_t up_plane = uint32_t(2 * p.I * p.B);
+  float aff[FN], daff[FN];
+  uint32_t ckoff[FN];
+  v2::static_for<FN>([&](auto FJ) {
+    constexpr int fj = FJ;
+    const int64_t s = n0 + wcol + fj * 32 + r;
+    const bool ok = st[s] >= 0;
+    aff[fj] = ok ? p.slot_aff[sbase + s] : 0.f;
+    daff[fj] = 0.f;
+    ckoff[fj] = ok ? uint32_t((4 * h * p.B + s) * 2) : v2::kOOB;   // row 4h of a fragment, this slot
+  });
+
+  v2::static_for<FM>([&](auto FI) {
+    constexpr int fi = FI;
+    const int64_t i0 = m0 + wrow + fi * 32;   // first row of the fragment row; I % 32 == 0
+    if (i0 < p.I) {                           // wave-uniform
+      v2::static_for<FN>([&](auto FJ) {
+        constexpr int fj = FJ;
+        uint16_t gb[16], ub[16];
+#if defined(__HIP_DEVICE_COMPILE__)
+        const auto rs = MX_RSRC(ck);
+        v2::static_for<16>([&](auto Q) {
+          constexpr int q = Q;
+          const uint32_t so =
+              __builtin_amdgcn_readfirstlane(uint32_t((i0 + 8 * (q >> 2) + (q & 3)) * p.B * 2));
+          gb[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, ckoff[fj], so, 0);
+          ub[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, ckoff[fj], so + up_plane, 0);
+        });
+#endif
+        float dg[16], du[16], it[16];
+        float amg = 0.f, amu = 0.f;
+        v2::static_for<16>([&](auto Q) {
+          constexpr int q = Q;
+          const float g = bf16_to_f32(gb[q]), u = bf16_to_f32(ub[q]);
+          const float sg = 1.f / (1.f + expf(-g));
+          const float ga = bf16_round(g * sg);           // silu(g)
+          const float in = bf16_round(ga * u);           // intermediate
+          const float ds = acc[fi][fj][q];
+          daff[fj] += ds * in;
+          const float di = aff[fj] * ds;                 // d(intermediate)
+          dg[q] = bf16_round(di * u * (sg * (1.f + g * (1.f - sg))));
+          du[q] = bf16_round(di * ga);
+          it[q] = p.affinity_on_i ? bf16_round(aff[fj] * in) : in;
+          amg = fmaxf(amg, fabsf(dg[q]));
+          amu = fmaxf(amu, fabsf(du[q]));
+        });
+        // I-axis groups: the fragment's 32 rows are this lane's 16 and lane^32's 16
+        amg = fmaxf(amg, __shfl_xor(amg, 32, 64));
+        amu = fmaxf(amu, __shfl_xor(amu, 32, 64));
+        const int Xg = scale_exp<FG>(__float_as_uint(amg)), Xu = scale_exp<FG>(__float_as_uint(amu));
+        const float ig = inv_scale(Xg), iu = inv_scale(Xu);
+        const int64_t slot = sbase + n0 + wcol + fj * 32 + r;
         uint8_t* rg = p.dgu_row_codes + slot * twoI + i0 + 4 * h;
         uint8_t* ru = rg + p.I;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t wg = 0, wu = 0;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            wg |= encode<FG>(__float_as_uint(dg[4 * k + c]), Xg) << (8 * c);
-            wu |= encode<FG>(__float_as_uint(du[4 * k + c]), Xu) << (8 * c);
-          }
-          *reinterpret_cast<uint32_t*>(rg + 8 * k) = wg;
-          *reinterpret_cast<uint32_t*>(ru + 8 * k) = wu;
-        }
+        v2::static_for<4>([&](auto K) {
+          constexpr int k = K;
+          *reinterpret_cast<uint32_t*>(rg + 8 * k) =
+              encode4<FG>(dg[4 * k], dg[4 * k + 1], dg[4 * k + 2], dg[4 * k + 3], ig);
+          *reinterpret_cast<uint32_t*>(ru + 8 * k) =
+              encode4<FG>(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3], iu);
+        });
         if (h == 0) {
           p.dgu_row_scales[slot * (twoI / 32) + i0 / 32] = uint8_t(Xg + 127);
           p.dgu_row_scales[slot * (twoI / 32) + (p.I + i0) / 32] = uint8_t(Xu + 127);
         }
-      }
-      // along the slots: a group is the 32 columns of this fragment (lanes of one half)
-      const int64_t p0 = sbase + n0 + (wave & 1) * (BN / 2) + fj * 32;   // first slot of the group
-      if (n0 + (wave & 1) * (BN / 2) + fj * 32 < p.B) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int64_t i = i0 + 8 * (q >> 2) + 4 * h + (q & 3);
-          uint32_t mg = abs_bits(dg[q]), mu = abs_bits(du[q]);
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) {
-            mg = max(mg, uint32_t(__shfl_xor(int(mg), o, 64)));
-            mu = max(mu, uint32_t(__shfl_xor(int(mu), o, 64)));
-          }
-          const int Xg = scale_exp<FG>(mg), Xu = scale_exp<FG>(mu);
-          p.dgu_tok_codes[i * P + p0 + (lane & 31)] = uint8_t(encode<FG>(__float_as_uint(dg[q]), Xg));
-          p.dgu_tok_codes[(p.I + i) * P + p0 + (lane & 31)] = uint8_t(encode<FG>(__float_as_uint(du[q]), Xu));
-          if ((lane & 31) == 0) {
-            p.dgu_tok_scales[i * (P / 32) + p0 / 32] = uint8_t(Xg + 127);
-            p.dgu_tok_scales[(p.I + i) * (P / 32) + p0 / 32] = uint8_t(Xu + 127);
-          }
-          if (BIAS) {
-            float sg = dg[q], su = du[q];
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) {
-              sg += __shfl_xor(sg, o, 64);
-              su += __shfl_xor(su, o, 64);
+        // staging for the slot-axis groups
+        v2::static_for<16>([&](auto Q) {
+          constexpr int q = Q;
+          const int row = 8 * (q >> 2) + 4 * h + (q & 3), col = fj * 32 + r;
+          *reinterpret_cast<uint32_t*>(stg_gu + row * GS + col * 4) =
+              uint32_t(bf16_rne(dg[q])) | (uint32_t(bf16_rne(du[q])) << 16);
+          *reinterpret_cast<uint16_t*>(stg_in + row * IS + col * 2) = bf16_rne(it[q]);
+        });
+      });
+      // the staging writes of this wave are visible to its own later reads (LDS is in order per wave)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // slot-axis groups: lane takes row r of the fragment row, groups h, h+2, ...
+      const int64_t i = i0 + r;
+      v2::static_for<FN / 2>([&](auto C) {
+        const int c = h + 2 * int(C);
+        const int64_t p0 = sbase + n0 + wcol + c * 32;
+        uint4 w[8];
+        v2::static_for<8>([&](auto J) {
+          w[J] = *reinterpret_cast<const uint4*>(stg_gu + r * GS + c * 128 + 16 * int(J));
+        });
+        uint32_t mg = 0, mu = 0;
+        float sg = 0.f, su = 0.f;
+        v2::static_for<8>([&](auto J) {
+          const uint32_t x[4] = {w[J].x, w[J].y, w[J].z, w[J].w};
+          v2::static_for<4>([&](auto T) {
+            mg = max(mg, (x[T] << 16) & 0x7fffffffu);
+            mu = max(mu, x[T] & 0x7fff0000u);
+            if (p.has_bias) {
+              sg += __uint_as_float(x[T] << 16);
+              su += __uint_as_float(x[T] & 0xffff0000u);
             }
-            if ((lane & 31) == 0) {
-              atomicAdd(p.db1_acc + (e * 2 + 0) * p.I + i, sg);
-              atomicAdd(p.db1_acc + (e * 2 + 1) * p.I + i, su);
-            }
-          }
+          });
+        });
+        const int Xg = scale_exp<FG>(mg), Xu = scale_exp<FG>(mu);
+        const float ig = inv_scale(Xg), iu = inv_scale(Xu);
+        uint32_t cg[8], cu[8];
+        v2::static_for<8>([&](auto J) {
+          const uint32_t x[4] = {w[J].x, w[J].y, w[J].z, w[J].w};
+          cg[J] = encode4<FG>(__uint_as_float(x[0] << 16), __uint_as_float(x[1] << 16), __uint_as_float(x[2] << 16),
+                              __uint_as_float(x[3] << 16), ig);
+          cu[J] = encode4<FG>(__uint_as_float(x[0] & 0xffff0000u), __uint_as_float(x[1] & 0xffff0000u),
+                              __uint_as_float(x[2] & 0xffff0000u), __uint_as_float(x[3] & 0xffff0000u), iu);
+        });
+        uint4* og = reinterpret_cast<uint4*>(p.dgu_tok_codes + i * P + p0);
+        uint4* ou = reinterpret_cast<uint4*>(p.dgu_tok_codes + (p.I + i) * P + p0);
+        og[0] = uint4{cg[0], cg[1], cg[2], cg[3]};
+        og[1] = uint4{cg[4], cg[5], cg[6], cg[7]};
+        ou[0] = uint4{cu[0], cu[1], cu[2], cu[3]};
+        ou[1] = uint4{cu[4], cu[5], cu[6], cu[7]};
+        p.dgu_tok_scales[i * (P / 32) + p0 / 32] = uint8_t(Xg + 127);
+        p.dgu_tok_scales[(p.I + i) * (P / 32) + p0 / 32] = uint8_t(Xu + 127);
+        if (p.has_bias) {
+          atomicAdd(p.db1_acc + (e * 2 + 0) * p.I + i, sg);
+          atomicAdd(p.db1_acc + (e * 2 + 1) * p.I + i, su);
         }
-      }
+        // the intermediate operand (activation format)
+        uint4 v[4];
+        v2::static_for<4>([&](auto J) {
+          v[J] = *reinterpret_cast<const uint4*>(stg_in + r * IS + c * 64 + 16 * int(J));
+        });
+        uint32_t mi = 0;
+        v2::static_for<4>([&](auto J) {
+          const uint32_t x[4] = {v[J].x, v[J].y, v[J].z, v[J].w};
+          v2::static_for<4>([&](auto T) {
+            mi = max(mi, (x[T] << 16) & 0x7fffffffu);
+            mi = max(mi, x[T] & 0x7fff0000u);
+          });
+        });
+        const int Xi = scale_exp<FA>(mi);
+        const float ii = inv_scale(Xi);
+        uint32_t ci[8];
+        v2::static_for<4>([&](auto J) {
+          const uint32_t x[4] = {v[J].x, v[J].y, v[J].z, v[J].w};
+          ci[2 * J] = encode4<FA>(__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                                  __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u), ii);
+          ci[2 * J + 1] = encode4<FA>(__uint_as_float(x[2] << 16), __uint_as_float(x[2] & 0xffff0000u),
+                                      __uint_as_float(x[3] << 16), __uint_as_float(x[3] & 0xffff0000u), ii);
+        });
+        uint4* oi = reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + p0);
+        oi[0] = uint4{ci[0], ci[1], ci[2], ci[3]};
+        oi[1] = uint4{ci[4], ci[5], ci[6], ci[7]};
+        p.inter_tok_scales[i * (P / 32) + p0 / 32] = uint8_t(Xi + 127);
+      });
+      // the next fragment row overwrites the staging only after these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // d(a): combine the two lane halves (same slot), then one atomic per slot
-    daff += __shfl_xor(daff, 32, 64);
-    if (valid && h == 0) atomicAdd(p.daff_slot + slot, daff);
-  }
+  });
+  // d(a): the two lane halves hold the same slot; one atomic per slot and wave
+  v2::static_for<FN>([&](auto FJ) {
+    constexpr int fj = FJ;
+    const float d = daff[fj] + __shfl_xor(daff[fj], 32, 64);
+    const int64_t s = n0 + wcol + fj * 32 + r;
+    if (h == 0 && st[s] >= 0) atomicAdd(p.daff_slot + sbase + s, d);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -213,28 +317,26 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_kernel(Phase3Args p) {
 
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool G>
-static hipError_t phase1_launch(Phase1Args p, int fg, bool bias, hipStream_t st) {
+static hipError_t phase1_launch(Phase1Args p, int fg, int fa, hipStream_t st) {
   p.tiles_m = int((p.I + BM - 1) / BM);
   p.tiles_n = int((p.B + BN - 1) / BN);
   const unsigned blocks = unsigned(int64_t(p.tiles_m) * p.tiles_n * p.N);
-  if (fg == 0) {
-    if (bias) phase1_kernel<BM, BN, 0, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
-    else phase1_kernel<BM, BN, 0, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  } else {
-    if (bias) phase1_kernel<BM, BN, 1, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
-    else phase1_kernel<BM, BN, 1, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  }
+  if (fg == 0 && fa == 0) phase1_kernel<BM, BN, 0, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else if (fg == 0) phase1_kernel<BM, BN, 0, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else if (fa == 0) phase1_kernel<BM, BN, 1, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else phase1_kernel<BM, BN, 1, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
-// Tile shape: 256 along a dimension when it is at least 256, else 128.
-hipError_t launch_phase1(const Phase1Args& p, int fg, bool bias, hipStream_t st) {
+// Tile shape: 256 along a dimension when it is at least 256, else 128.  The
+// block size B is a power of two >= 128, so every tile lies inside one block.
+hipError_t launch_phase1(const Phase1Args& p, int fg, int fa, hipStream_t st) {
   const bool g = (2 * p.H) % v2::BK != 0;      // a ragged last K stage
   if (p.I >= 256 && p.B >= 256)
-    return g ? phase1_launch<256, 256, true>(p, fg, bias, st) : phase1_launch<256, 256, false>(p, fg, bias, st);
+    return g ? phase1_launch<256, 256, true>(p, fg, fa, st) : phase1_launch<256, 256, false>(p, fg, fa, st);
   if (p.I >= 256)
-    return g ? phase1_launch<256, 128, true>(p, fg, bias, st) : phase1_launch<256, 128, false>(p, fg, bias, st);
-  return g ? phase1_launch<128, 128, true>(p, fg, bias, st) : phase1_launch<128, 128, false>(p, fg, bias, st);
+    return g ? phase1_launch<256, 128, true>(p, fg, fa, st) : phase1_launch<256, 128, false>(p, fg, fa, st);
+  return g ? phase1_launch<128, 128, true>(p, fg, fa, st) : phase1_launch<128, 128, false>(p, fg, fa, st);
 }
 
 template <int BM, int BN, bool G>

@@ -90,6 +90,38 @@ __device__ __forceinline__ uint32_t encode(uint32_t vbits, int X) {
   return sign | rne_shr(sig, s);
 }
 
+// 2^-X in fp32 for a scale exponent that scale_exp can return (X <= 127 - emax,
+// so the result is a normal number).
+__device__ __forceinline__ float inv_scale(int X) { return __uint_as_float(uint32_t(127 - X) << 23); }
+
+// Four codes packed little-endian into a word, through the hardware converter:
+// y = v * 2^-X is exact (a power-of-two scale of a value inside its group
+// stays normal or underflows far below the format's smallest subnormal), the
+// clamp to +-max finite is the encoder's saturation, and v_cvt_pk_fp8_f32 /
+// v_cvt_pk_bf8_f32 round to nearest-even into the OCP formats.  Equal to
+// encode<FMT> for every finite fp32 input and every scale the group rule can
+// produce (checked exhaustively over all bf16 patterns and all such scales).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3, float inv) {
+  constexpr float M = FMT == kE4M3 ? 448.f : 57344.f;
+  const float y0 = fminf(fmaxf(v0 * inv, -M), M), y1 = fminf(fmaxf(v1 * inv, -M), M);
+  const float y2 = fminf(fmaxf(v2 * inv, -M), M), y3 = fminf(fmaxf(v3 * inv, -M), M);
+  int w;
+  if (FMT == kE4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, w, true);
+  }
+  return uint32_t(w);
+}
+
+// bf16 round-to-nearest-even through the hardware converter (finite inputs;
+// equal to f32_to_bf16 there).
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(bf16_rne(f)); }
+
 // Runtime-format dispatch.
 __device__ __forceinline__ int scale_exp_rt(int fmt, uint32_t amax_bits) {
   return fmt == kE4M3 ? scale_exp<kE4M3>(amax_bits) : scale_exp<kE5M2>(amax_bits);
