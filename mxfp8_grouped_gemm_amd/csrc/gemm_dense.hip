@@ -9,6 +9,7 @@
 //     where the K columns of expert e are the slots of the blocks
 //     list[off[e] .. off[e+1]) (B slots each).
 #include "gemm_v2.hpp"
+#include "gemm_v3.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
@@ -38,7 +39,9 @@ struct KMapGrouped {
 
 template <int BM, int BN, int FA, int FB, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) gemm_store_kernel(GemmStoreArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
+  // GENERIC: ragged K or unaligned scale rows (v2 loop); otherwise the ring (v3 loop)
+  constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   constexpr int FM = BM / 64, FN = BN / 64;
   const int per_group = p.tiles_m * p.tiles_n;
   const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
@@ -47,21 +50,38 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_kernel(GemmStoreArgs 
   v2::grouped_tile<8>(id - g * per_group, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int wave = threadIdx.x >> 6;
-
-  v2::Operand<BM, FM> A;
-  v2::Operand<BN, FN> B;
-  v2::setup_rows(A, p.a_codes, p.a_scales, m0, p.M, p.lda, p.lda / 32, (wave >> 1) * (BM / 2));
-  v2::setup_rows(B, p.b_codes, p.b_scales, n0, p.N, p.ldb, p.ldb / 32, (wave & 1) * (BN / 2));
-  KMapGrouped km{p.blk_list, 0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v2::BK) | 1u), p.K};
-  int nstages;
-  if (p.blk_list) {
-    km.b0 = p.blk_off[g];
-    nstages = int((int64_t(p.blk_off[g + 1] - km.b0) * p.blk) / v2::BK);
-  } else {
-    nstages = int((p.K + v2::BK - 1) / v2::BK);
-  }
   v2::v16f acc[FM][FN];
-  v2::mainloop<BM, BN, v2::kFp8, FA, FB, GENERIC>(A, B, nstages, km, smem, acc);
+
+  if constexpr (GENERIC) {
+    v2::Operand<BM, FM> A;
+    v2::Operand<BN, FN> B;
+    v2::setup_rows(A, p.a_codes, p.a_scales, m0, p.M, p.lda, p.lda / 32, (wave >> 1) * (BM / 2));
+    v2::setup_rows(B, p.b_codes, p.b_scales, n0, p.N, p.ldb, p.ldb / 32, (wave & 1) * (BN / 2));
+    KMapGrouped km{p.blk_list, 0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v2::BK) | 1u), p.K};
+    int nstages;
+    if (p.blk_list) {
+      km.b0 = p.blk_off[g];
+      nstages = int((int64_t(p.blk_off[g + 1] - km.b0) * p.blk) / v2::BK);
+    } else {
+      nstages = int((p.K + v2::BK - 1) / v2::BK);
+    }
+    v2::mainloop<BM, BN, v2::kFp8, FA, FB, true>(A, B, nstages, km, smem, acc);
+  } else {
+    v3::Op<BM> A;
+    v3::Op<BN> B;
+    v3::ScaleDma<BM, BN> sd;
+    v3::setup_rows(A, p.a_codes, m0, p.M, p.lda);
+    v3::setup_rows(B, p.b_codes, n0, p.N, p.ldb);
+    v3::setup_scales(sd, p.a_scales, m0, p.M, p.lda / 32, p.b_scales, n0, p.N, p.ldb / 32);
+    if (p.blk_list) {
+      const int b0 = p.blk_off[g];
+      const int nstages = int((int64_t(p.blk_off[g + 1] - b0) * p.blk) / v3::SK);
+      const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
+      v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, km, smem, acc);
+    } else {
+      v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, int(p.K / v3::SK), v3::KMapPlain{}, smem, acc);
+    }
+  }
 
   uint16_t* out = p.out + int64_t(g) * p.out_gstride;
 #pragma unroll

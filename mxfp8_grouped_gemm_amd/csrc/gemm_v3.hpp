@@ -1,0 +1,366 @@
+// gemm_v3.hpp -- MX GEMM main loop for gfx950 with a four-stage LDS ring.
+//
+// Same contraction and element modes as gemm_v2.hpp (C[m][n] = sum_k A[m][k] *
+// B[n][k]; fp8 codes with E8M0 scales on v_mfma_scale_f32_32x32x64_f8f6f4, or
+// exact bf16 values on v_mfma_f32_32x32x16_bf16), for operands whose code rows
+// are 128-byte aligned and whose K is a multiple of 128 bytes.
+//
+// Why a ring: a CU streams L2 -> LDS at ~55 B/clk with buffer_load ... lds,
+// but a stage can only start when the slowest of its ~500 cache lines has
+// landed, and a few percent of them miss L2.  With one stage in flight the
+// loop runs at that miss latency; with three it runs at the stream rate.
+//
+// Stage = 64 bytes of K (one 64-element fp8 MFMA step, two 16-element bf16
+// steps).  LDS: NBUF code slots of (BM + BN) rows x 64 B (16-byte chunks
+// XOR-swizzled by row so that 8 consecutive rows reading one logical chunk hit
+// distinct banks), then NBUF scale slots holding, for a pair of stages, one
+// 4-byte word per row (the pair's four E8M0 groups).
+//
+// Loads are issued with inline asm (s_mov_b32 m0 + buffer_load_dword{,x4} ...
+// lds) because the compiler's wait-count pass treats every LDS read after an
+// LDS DMA builtin as possibly aliased and waits for all outstanding loads,
+// which would serialise the ring.  The asm loads are invisible to that pass;
+// the loop waits on them explicitly (vmcnt) and they only ever write LDS.
+// The asm sets m0 itself; m0 is reserved (not allocatable), and code built on
+// this core has no other m0 users, so no compiler value lives there across it.
+//
+// Iteration t (fragments of stage t already in registers F[t & 1]):
+//   wait until stage t+1 has landed (loads of t+2 and t+3 may remain), barrier
+//     (also: every wave has finished reading stage t's slot);
+//   DMA stage t+4 into slot (t+4) % 4 == t % 4 (and the scales of pair
+//     (t+4)/2 when t+4 is even);
+//   MFMAs of stage t from F[t & 1], interleaved with the reads of stage t+1
+//     into F[(t+1) & 1].
+// The iteration is straight-line code (no branch for the ring's tail), so the
+// compiler keeps this order.
+#pragma once
+#include "gemm_v2.hpp"
+
+namespace mx {
+namespace v3 {
+
+using v2::Buf;
+using v2::v16f;
+using v2::v8bf;
+using v2::v8i;
+using v2::kBf16;
+using v2::kFp8;
+
+constexpr int SK = 64;          // bytes of K per stage
+constexpr int NBUF = 4;         // ring depth (stages in LDS)
+constexpr int kThreads = 256;
+constexpr uint32_t kOOB = 0x80000000u;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// LDS bytes of a tile's ring.
+__host__ __device__ constexpr int code_slot(int BM, int BN) { return (BM + BN) * SK; }
+__host__ __device__ constexpr int scale_chunks(int BM, int BN) { return 4 * ((BM + BN + 255) / 256); }
+__host__ __device__ constexpr int scale_slot(int BM, int BN) { return scale_chunks(BM, BN) * 256; }
+__host__ __device__ constexpr int smem_bytes(int BM, int BN) { return NBUF * (code_slot(BM, BN) + scale_slot(BM, BN)); }
+
+// s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt left alone.
+__host__ __device__ constexpr int waitcnt(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ v4i rsrc(const Buf& b) {
+  const uint64_t a = reinterpret_cast<uint64_t>(b.base);
+  v4i r;
+  r[0] = int(__builtin_amdgcn_readfirstlane(uint32_t(a)));
+  r[1] = int(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu));   // stride 0
+  r[2] = int(__builtin_amdgcn_readfirstlane(b.bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+// 16 bytes per lane into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const v4i& rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+// 4 bytes per lane into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(const v4i& rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+#endif
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>(p));   // low half of the generic address = LDS offset
+}
+
+// One operand's code rows: buffer and this lane's DMA offsets.  Instruction j
+// of wave w fills rows w*ROWS/4 + 16j .. +16 of a slot; lane l fills row
+// +(l >> 2), physical chunk l & 3, fetching the logical chunk stored there.
+template <int ROWS>
+struct Op {
+  Buf codes;
+  uint32_t off[ROWS / 64];
+};
+
+template <int ROWS>
+__device__ __forceinline__ int dma_row(int j) {
+  return (threadIdx.x >> 6) * (ROWS / 4) + 16 * j + ((threadIdx.x & 63) >> 2);
+}
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+template <int ROWS>
+__device__ __forceinline__ void setup_rows(Op<ROWS>& op, const uint8_t* codes, int64_t row0, int64_t nrows,
+                                           int64_t ld) {
+  const int64_t have = nrows - row0 < ROWS ? nrows - row0 : ROWS;
+  op.codes = v2::make_rsrc(codes + row0 * ld, uint32_t(have * ld));
+#pragma unroll
+  for (int j = 0; j < ROWS / 64; ++j) {
+    const int r = dma_row<ROWS>(j);
+    const int lc = (threadIdx.x & 3) ^ swz(r);
+    op.off[j] = r < have ? uint32_t(r * ld + 16 * lc) : kOOB;
+  }
+}
+
+// Gathered rows: tile row r reads source row rowid(r) (negative: zeros).
+template <int ROWS, class RowId>
+__device__ __forceinline__ void setup_gather(Op<ROWS>& op, const uint8_t* codes, int64_t src_rows, int64_t ld,
+                                             const RowId& rowid) {
+  op.codes = v2::make_rsrc(codes, uint32_t(src_rows * ld));
+#pragma unroll
+  for (int j = 0; j < ROWS / 64; ++j) {
+    const int r = dma_row<ROWS>(j);
+    const int64_t t = rowid(r);
+    const int lc = (threadIdx.x & 3) ^ swz(r);
+    op.off[j] = t >= 0 ? uint32_t(t * ld + 16 * lc) : kOOB;
+  }
+}
+
+// Scale rows of both operands, in 64-row chunks: chunk c (A rows first, then
+// B rows) is loaded by wave c % 4 as its instruction c / 4; chunks past the
+// tile's rows load zeros into the slot's tail so every wave issues the same
+// number of instructions.
+template <int BM, int BN>
+struct ScaleDma {
+  static constexpr int NS = scale_chunks(BM, BN) / 4;
+  Buf buf[NS];
+  uint32_t off[NS];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void setup_scales(ScaleDma<BM, BN>& sd, const uint8_t* a_scales, int64_t a_row0,
+                                             int64_t a_rows, int64_t a_sld, const uint8_t* b_scales, int64_t b_row0,
+                                             int64_t b_rows, int64_t b_sld) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t ha = a_rows - a_row0 < BM ? a_rows - a_row0 : BM;
+  const int64_t hb = b_rows - b_row0 < BN ? b_rows - b_row0 : BN;
+  const Buf ba = v2::make_rsrc(a_scales + a_row0 * a_sld, uint32_t(ha * a_sld));
+  const Buf bb = v2::make_rsrc(b_scales + b_row0 * b_sld, uint32_t(hb * b_sld));
+#pragma unroll
+  for (int i = 0; i < ScaleDma<BM, BN>::NS; ++i) {
+    const int c = wave + 4 * i;
+    if (c < BM / 64) {
+      const int r = 64 * c + lane;
+      sd.buf[i] = ba;
+      sd.off[i] = r < ha ? uint32_t(r * a_sld) : kOOB;
+    } else if (c < (BM + BN) / 64) {
+      const int r = 64 * (c - BM / 64) + lane;
+      sd.buf[i] = bb;
+      sd.off[i] = r < hb ? uint32_t(r * b_sld) : kOOB;
+    } else {
+      sd.buf[i] = ba;
+      sd.off[i] = kOOB;
+    }
+  }
+}
+
+// K map with 64-byte stages.  Plain: [0, K).  Grouped: the K columns of a
+// group are the blocks list[b0 ..] of blk columns each (blk a power of two >=
+// 128, so a scale word never straddles two blocks).
+struct KMapPlain {
+  __device__ __forceinline__ uint32_t operator()(int s) const { return uint32_t(s) * SK; }
+};
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+struct KMapList {
+  const int32_t* list;
+  int b0, blk, shift;   // shift = log2(blk / 64)
+  __device__ __forceinline__ uint32_t operator()(int s) const {
+    const int blkid = ((const_i32_ptr)(uintptr_t)list)[b0 + (s >> shift)];
+    return uint32_t(blkid) * uint32_t(blk) + uint32_t(s & ((1 << shift) - 1)) * SK;
+  }
+};
+
+template <int ELEM, int FA, int FB, int OPS>
+__device__ __forceinline__ v16f mma(const uint4 (&a)[2], const uint4 (&b)[2], const v16f& c, int sa, int sb,
+                                    int half) {
+  if (ELEM == kFp8) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v2::as_v8i(a[0], a[1]), v2::as_v8i(b[0], b[1]), c, FA, FB,
+                                                           OPS, sa, OPS, sb);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(v2::as_v8bf(a[half]), v2::as_v8bf(b[half]), c, 0, 0, 0);
+  }
+}
+
+// The K loop over nstages 64-byte stages (nstages even).  sd may be null in
+// bf16 mode.
+template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
+__device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const ScaleDma<BM, BN>* sd, int nstages,
+                                         const KMap& kmap, uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
+  constexpr int FM = BM / 64, FN = BN / 64;
+  constexpr int CS = code_slot(BM, BN), SSB = scale_slot(BM, BN);
+  constexpr int NCI = (BM + BN) / 64;                       // code DMA instructions per wave per stage
+  constexpr int NS = ScaleDma<BM, BN>::NS;                  // scale DMA instructions per wave per pair
+  constexpr int VM_STEADY = 2 * NCI + (ELEM == kFp8 ? NS : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r = lane & 31;
+  const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  if (nstages <= 0) return;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t lds0 = lds_addr(smem);
+  const v4i rsa = rsrc(A.codes), rsb = rsrc(B.codes);
+  v4i rss[NS];
+  if (ELEM == kFp8) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) rss[i] = rsrc(sd->buf[i]);
+  }
+  // DMA for stage t into ring slot t % NBUF (and the scales of its pair when
+  // t is even).  Stages past the end are issued too, through descriptors with
+  // no records (the hardware returns zeros without a memory access), so every
+  // iteration issues the same loads and the wait counts stay fixed.
+  auto issue = [&](int t) {
+    const bool live = t < nstages;
+    const uint32_t kc = kmap(live ? t : 0);
+    const uint32_t slot = lds0 + uint32_t(t & (NBUF - 1)) * CS;
+    v4i ra = rsa, rb = rsb;
+    ra[2] = live ? ra[2] : 0;
+    rb[2] = live ? rb[2] : 0;
+#pragma unroll
+    for (int j = 0; j < BM / 64; ++j) dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * j) * SK, A.off[j], kc);
+#pragma unroll
+    for (int j = 0; j < BN / 64; ++j)
+      dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * j) * SK, B.off[j], kc);
+    if (ELEM == kFp8 && (t & 1) == 0) {
+      const uint32_t ss = lds0 + NBUF * CS + uint32_t((t >> 1) & (NBUF - 1)) * SSB;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        v4i rs = rss[i];
+        rs[2] = live ? rs[2] : 0;
+        dma4(rs, ss + uint32_t(wave + 4 * i) * 256, sd->off[i], kc >> 5);
+      }
+    }
+  };
+#else
+  auto issue = [&](int) {};
+#endif
+
+  uint4 fa[2][FM][2], fb[2][FN][2];
+  uint32_t sa[2][FM], sb[2][FN];
+  // fragments and raw scale words of stage t into set P (the words are shifted
+  // to this lane's group where they are used, so nothing here waits on the reads)
+  auto read = [&](int t, auto Pc) {
+    constexpr int P = decltype(Pc)::value;
+    const uint8_t* cs = smem + (t & (NBUF - 1)) * CS;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wrow + 32 * i + r;
+      fa[P][i][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
+      fa[P][i][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wcol + 32 * j + r;
+      fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
+      fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
+    }
+    if (ELEM == kFp8) {
+      const uint8_t* ss = smem + NBUF * CS + ((t >> 1) & (NBUF - 1)) * SSB;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wrow + 32 * i + r;
+        sa[P][i] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = BM + wcol + 32 * j + r;
+        sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
+      }
+    }
+  };
+  // MFMAs of half H of the fragments in set P; OPS = scale byte of the stage within its pair
+  auto compute = [&](auto Pc, auto Hc, auto OPSc) {
+    constexpr int P = decltype(Pc)::value, H = decltype(Hc)::value, OPS = decltype(OPSc)::value;
+    if (ELEM == kFp8) {
+      constexpr int I0 = H * FM / 2, I1 = (H + 1) * FM / 2;
+#pragma unroll
+      for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mma<ELEM, FA, FB, OPS>(fa[P][i], fb[P][j], acc[i][j], int(sa[P][i] >> (8 * h)),
+                                             int(sb[P][j] >> (8 * h)), 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma<ELEM, FA, FB, 0>(fa[P][i], fb[P][j], acc[i][j], 0, 0, H);
+    }
+  };
+
+  // One stage t with its fragments in set P (P == t & 1).  With READ: wait
+  // until stage t+1 has landed (t+2, t+3 may still be in flight) and every
+  // wave has finished reading stage t's slot (barrier), DMA stage t+4 into
+  // that slot, then read stage t+1 into set P ^ 1 interleaved with the MFMAs
+  // of stage t (an LDS queue holds at most 15 reads, so issuing them all first
+  // would stall the MFMAs behind them).
+  auto step = [&](int t, auto Pc, auto READc) {
+    constexpr int P = decltype(Pc)::value;
+    constexpr bool READ = decltype(READc)::value;
+    if (READ) {
+      __builtin_amdgcn_s_waitcnt(waitcnt(VM_STEADY, 0));
+      __builtin_amdgcn_s_barrier();
+      issue(t + NBUF);
+      __builtin_amdgcn_sched_barrier(0);
+      read(t + 1, std::integral_constant<int, P ^ 1>{});
+    }
+    compute(std::integral_constant<int, P>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * P>{});
+    compute(std::integral_constant<int, P>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2 * P>{});
+    if (READ) {
+      constexpr int NMF = FM * FN * (ELEM == kFp8 ? 1 : 2);                  // MFMAs of a stage
+      constexpr int NRD = 2 * (FM + FN) + (ELEM == kFp8 ? FM + FN : 0);      // LDS reads of a stage
+      constexpr int PER = (NRD + NMF - 1) / NMF;
+#pragma unroll
+      for (int k = 0; k < NMF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: stages 0 .. 3 in flight, then stage 0 into registers
+#pragma unroll
+  for (int t = 0; t < NBUF; ++t) issue(t);
+  __builtin_amdgcn_s_waitcnt(waitcnt(3 * NCI + (ELEM == kFp8 ? NS : 0), 15));
+  __builtin_amdgcn_s_barrier();
+  read(0, std::integral_constant<int, 0>{});
+  // nstages is even (K is a multiple of 128 bytes); the last pair is peeled so
+  // that the steady-state loop has no path that skips the reads
+  int t = 0;
+  for (; t + 2 < nstages; t += 2) {
+    step(t, std::integral_constant<int, 0>{}, std::true_type{});
+    step(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  step(t, std::integral_constant<int, 0>{}, std::true_type{});
+  step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+}
+
+}  // namespace v3
+}  // namespace mx

@@ -22,6 +22,7 @@
 //   dX[tok_p][h] += sum_{j,i} deq(dGU)[p][j][i] * deq(W_gate_up[e])[h][j][i]
 //   as fp32 atomic adds (a token's top-k slots sit in different blocks).
 #include "gemm_v2.hpp"
+#include "gemm_v3.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
 #include "swiglu.hpp"
@@ -52,7 +53,8 @@ struct KMapPlain {
 // The LDS of the main loop is reused for staging after a barrier.
 template <int BM, int BN, int FG, int FA, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
-  constexpr int SMEM = 2 * (BM + BN) * v2::BK;
+  // GENERIC: 2H not a multiple of 128 bytes (v2 loop); otherwise the ring (v3 loop)
+  constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   constexpr int FM = BM / 64, FN = BN / 64;
   constexpr int WN = BN / 2;            // slots per wave
@@ -85,17 +87,27 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   // A: dequantised W_down[e] rows i; B: dequantised dY rows gathered by token
-  v2::Operand<BM, FM> A;
-  v2::Operand<BN, FN> B;
-  v2::setup_rows(A, reinterpret_cast<const uint8_t*>(p.wd_deq + e * p.I * p.H), nullptr, m0, p.I, 2 * p.H, 0,
-                 (wave >> 1) * (BM / 2));
+  const uint8_t* wd = reinterpret_cast<const uint8_t*>(p.wd_deq + e * p.I * p.H);
+  const uint8_t* dyd = reinterpret_cast<const uint8_t*>(p.dy_deq);
   const int32_t* st = p.slot_tok + sbase;
   const int64_t B_ = p.B;
-  v2::setup_gather(B, reinterpret_cast<const uint8_t*>(p.dy_deq), nullptr, p.T, 2 * p.H, 0, (wave & 1) * (BN / 2),
-                   [&](int r) -> int64_t { const int64_t s = n0 + r; return s < B_ ? int64_t(st[s]) : -1; });
+  auto tok_of = [&](int r) -> int64_t { const int64_t s = n0 + r; return s < B_ ? int64_t(st[s]) : -1; };
   v16f acc[FM][FN];
-  v2::mainloop<BM, BN, v2::kBf16, 0, 0, GENERIC>(A, B, int((2 * p.H + v2::BK - 1) / v2::BK), KMapPlain{2 * p.H},
-                                                  smem, acc);
+  if constexpr (GENERIC) {
+    v2::Operand<BM, FM> A;
+    v2::Operand<BN, FN> B;
+    v2::setup_rows(A, wd, nullptr, m0, p.I, 2 * p.H, 0, (wave >> 1) * (BM / 2));
+    v2::setup_gather(B, dyd, nullptr, p.T, 2 * p.H, 0, (wave & 1) * (BN / 2), tok_of);
+    v2::mainloop<BM, BN, v2::kBf16, 0, 0, true>(A, B, int((2 * p.H + v2::BK - 1) / v2::BK), KMapPlain{2 * p.H},
+                                                 smem, acc);
+  } else {
+    v3::Op<BM> A;
+    v3::Op<BN> B;
+    v3::setup_rows(A, wd, m0, p.I, 2 * p.H);
+    v3::setup_gather(B, dyd, p.T, 2 * p.H, tok_of);
+    v3::mainloop<BM, BN, v3::kBf16, 0, 0>(A, B, static_cast<const v3::ScaleDma<BM, BN>*>(nullptr),
+                                           int(2 * p.H / v3::SK), v3::KMapPlain{}, smem, acc);
+  }
 
   // ---- epilogue -------------------------------------------------------------
   __syncthreads();   // every wave has read the last stage: the LDS is free for staging
@@ -274,7 +286,9 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int FG, int FW, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) phase3_kernel(Phase3Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
+  // GENERIC: 2I not a multiple of 128 bytes (v2 loop); otherwise the ring (v3 loop)
+  constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   constexpr int FM = BM / 64, FN = BN / 64;
   const int per_blk = p.tiles_m * p.tiles_n;
   const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
@@ -289,15 +303,27 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_kernel(Phase3Args p) {
   const int64_t twoI = 2 * p.I;
 
   // A: the block's rows of dGU quantised along I; B: W_gate_up[e] viewed [H][2I]
-  v2::Operand<BM, FM> A;
-  v2::Operand<BN, FN> B;
-  v2::setup_rows(A, p.dgu_row_codes + sbase * twoI, p.dgu_row_scales + sbase * (twoI / 32), m0, p.B, twoI,
-                 twoI / 32, (wave >> 1) * (BM / 2));
-  v2::setup_rows(B, p.wgu_codes + e * p.H * twoI, p.wgu_scales + e * p.H * (twoI / 32), n0, p.H, twoI, twoI / 32,
-                 (wave & 1) * (BN / 2));
+  const uint8_t* ac = p.dgu_row_codes + sbase * twoI;
+  const uint8_t* as = p.dgu_row_scales + sbase * (twoI / 32);
+  const uint8_t* bc = p.wgu_codes + e * p.H * twoI;
+  const uint8_t* bs = p.wgu_scales + e * p.H * (twoI / 32);
   v16f acc[FM][FN];
-  v2::mainloop<BM, BN, v2::kFp8, FG, FW, GENERIC>(A, B, int((twoI + v2::BK - 1) / v2::BK), KMapPlain{twoI}, smem,
-                                                   acc);
+  if constexpr (GENERIC) {
+    v2::Operand<BM, FM> A;
+    v2::Operand<BN, FN> B;
+    v2::setup_rows(A, ac, as, m0, p.B, twoI, twoI / 32, (wave >> 1) * (BM / 2));
+    v2::setup_rows(B, bc, bs, n0, p.H, twoI, twoI / 32, (wave & 1) * (BN / 2));
+    v2::mainloop<BM, BN, v2::kFp8, FG, FW, true>(A, B, int((twoI + v2::BK - 1) / v2::BK), KMapPlain{twoI}, smem,
+                                                  acc);
+  } else {
+    v3::Op<BM> A;
+    v3::Op<BN> B;
+    v3::ScaleDma<BM, BN> sd;
+    v3::setup_rows(A, ac, m0, p.B, twoI);
+    v3::setup_rows(B, bc, n0, p.H, twoI);
+    v3::setup_scales(sd, as, m0, p.B, twoI / 32, bs, n0, p.H, twoI / 32);
+    v3::mainloop<BM, BN, v3::kFp8, FG, FW>(A, B, &sd, int(twoI / v3::SK), v3::KMapPlain{}, smem, acc);
+  }
 
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi)
