@@ -14,6 +14,13 @@ Printed: one JSON line on stdout (progress goes to stderr).  Besides the step
 throughput it carries the roofline of the dominant kernel (timed live with HIP
 events on the library's stream), the dense MXFP8 backward (4096^3) and the
 quantiser throughput, and the CPU oracle timed on a bounded sample.
+
+roofline.traffic is the dominant kernel's HBM bytes per launch from two
+rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on
+a copy of known size; it is read from profiles/<kernel>_<workload>_traffic.txt
+and reported only while the kernel sources still hash to the value recorded
+there (null otherwise).  Those passes run this script with --kernel-only and
+--copy-calibration.
 """
 from __future__ import annotations
 
@@ -29,6 +36,40 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense MXFP8 / FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = os.path.join(ROOT, "mxfp8_grouped_gemm_amd", "csrc")
+
+
+def sources_sha256():
+    """Hash of the HIP sources (kernels and their headers), to tell whether
+    counters taken earlier still describe the kernels being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch recorded for (kernel, workload), or None when there
+    is no record or the sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("sources_sha256") != sources_sha256() or "traffic_bytes_per_launch" not in rec:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
 
 
 def log(*a):
@@ -77,7 +118,9 @@ def roofline_of(kind, work, ms):
             "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
-def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
+def build_problem(cfg, keep_w01=False):
+    """Seeded synthetic inputs of cfg resident on the GPU, weights quantised by
+    the library, routing blocks built, the backward operator bound."""
     import torch
     import mxfp8_grouped_gemm_amd as mx
     import synthetic as S
@@ -103,6 +146,15 @@ def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
     op = mx.MoeBwd(t["hidden"], aff_d, gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32), d_c.view(E, I, H),
                    d_s.view(E, I, H // 32), tpid, b2e, t["dy"], cfg.B, t["ckpt"], down_proj_bias=t["b2"],
                    affinity_on=cfg.affinity_on)
+    return dict(op=op, N=N, topk=topk, aff=aff, topk_d=topk_d, tpid=tpid, b2e=b2e, rb_ws=rb_ws, t=t, w01=w01)
+
+
+def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
+    import torch
+    import mxfp8_grouped_gemm_amd as mx
+
+    pb = build_problem(cfg, keep_w01)
+    op, N, topk_d, tpid, b2e, rb_ws = pb["op"], pb["N"], pb["topk_d"], pb["tpid"], pb["b2e"], pb["rb_ws"]
     log(f"[bench] {cfg.name}: N={N} blocks, workspace {op.workspace.numel() / 2**30:.2f} GiB")
 
     def step():
@@ -139,13 +191,14 @@ def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
     dom = max((k for k in stages if k in work), key=lambda k: stages[k])
     kind, w = work[dom]
     roof = roofline_of(kind, w, stages[dom])
-    roof.update({"kernel": dom, "launch_ms": round(stages[dom], 4), "traffic": None})
+    roof.update({"kernel": dom, "launch_ms": round(stages[dom], 4), "traffic": recorded_traffic(dom, cfg.name)})
     per_stage = {k: {"ms": round(v, 4), **({} if k not in work or not work[k][1] else
                                            {kk: vv for kk, vv in roofline_of(work[k][0], work[k][1], v).items()
                                             if kk in ("achieved", "unit", "frac")})}
                  for k, v in stages.items()}
     log(f"[bench] stages: " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
-    return dict(ms=ms, wall=wall, roof=roof, stages=per_stage, N=N, topk=topk, aff=aff, tensors=t, w01=w01)
+    return dict(ms=ms, wall=wall, roof=roof, stages=per_stage, N=N, topk=pb["topk"], aff=pb["aff"], tensors=pb["t"],
+                w01=pb["w01"])
 
 
 def run_dense(reps):
@@ -230,6 +283,35 @@ def cpu_baseline(cfg, moe, nthreads, n_tokens, n_cols):
                        f"{t2 - t1:.1f} s); {flops / 1e9:.1f} GFLOP in {secs:.1f} s")}
 
 
+def kernel_only(cfg, stage_name, reps):
+    """Set the workload up, run the backward once, then launch one stage reps
+    times (the program rocprofv3 --pmc wraps for that stage's counters)."""
+    import torch
+    import mxfp8_grouped_gemm_amd as mx
+    op = build_problem(cfg)["op"]
+    op.run()
+    torch.cuda.synchronize()
+    s = op.STAGE_NAMES.index(stage_name)
+    for _ in range(reps):
+        op.stage(s)
+    torch.cuda.synchronize()
+    log(f"[bench] kernel-only: {stage_name} x{reps} on {cfg.name} (library {mx.version()})")
+
+
+def copy_calibration(nbytes):
+    """One device-to-device copy of nbytes by a plain copy kernel (torch's
+    elementwise copy), after a warm-up copy: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {nbytes} bytes read and written")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,8 +322,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
-    ap.add_argument("--cpu-tokens", type=int, default=192)
-    ap.add_argument("--cpu-cols", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-cols", type=int, default=128)
+    ap.add_argument("--kernel-only", metavar="STAGE", help="set up, then launch one stage (for rocprofv3 --pmc)")
+    ap.add_argument("--copy-calibration", type=int, metavar="BYTES", help="one copy of BYTES (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -253,6 +337,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     cfg = S.MOE_CONFIGS[args.workload]
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.kernel_only:
+        kernel_only(cfg, args.kernel_only, max(1, args.steps))
+        return
     moe = run_moe(cfg, args.steps, args.warmup, args.profile_reps, keep_w01=not args.no_cpu_baseline)
     value = cfg.flops / moe["ms"] / 1e9
     out = {
