@@ -330,8 +330,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);
   p1.inter_tok_codes = at(L.inter_tok_codes); p1.inter_tok_scales = at(L.inter_tok_scales);
   p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
-  p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias;
-  STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_act, st), "phase 1");
+  p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias; p1.fmt_act = a->fmt_act;
+  STEP(mx::launch_phase1(p1, a->fmt_grad, st), "phase 1");
   stage = 5;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};

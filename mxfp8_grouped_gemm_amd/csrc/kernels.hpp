@@ -76,9 +76,10 @@ struct Phase1Args {
   float* db1_acc;               // [E][2][I]
   int affinity_on_i;            // 1: the intermediate operand carries the affinity
   int has_bias;                 // 1: accumulate db1
+  int fmt_act;                  // format of the intermediate operand (activation format)
   int tiles_m, tiles_n;
 };
-hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, int fmt_act, hipStream_t st);
+hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]

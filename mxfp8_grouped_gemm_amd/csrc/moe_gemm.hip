@@ -51,7 +51,7 @@ struct KMapPlain {
 //       slot-axis MX groups (dGU and the intermediate operand of Phase 4) are
 //       reduced and encoded in registers and stored as 32-byte runs.
 // The LDS of the main loop is reused for staging after a barrier.
-template <int BM, int BN, int FG, int FA, bool GENERIC>
+template <int BM, int BN, int FG, bool ON_I, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   // GENERIC: 2H not a multiple of 128 bytes (v2 loop); otherwise the ring (v3 loop)
   constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
@@ -147,22 +147,22 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
           ub[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, ckoff[fj], so + up_plane, 0);
         });
 #endif
-        float dg[16], du[16], it[16];
+        uint32_t gu[16];        // bf16(dGate) | bf16(dUp) << 16
+        uint16_t it[16];        // bf16 intermediate operand (times a with the affinity on I)
         float amg = 0.f, amu = 0.f;
         v2::static_for<16>([&](auto Q) {
           constexpr int q = Q;
           const float g = bf16_to_f32(gb[q]), u = bf16_to_f32(ub[q]);
-          const float sg = 1.f / (1.f + expf(-g));
+          const float sg = sigmoid_fast(g);
           const float ga = bf16_round(g * sg);           // silu(g)
           const float in = bf16_round(ga * u);           // intermediate
           const float ds = acc[fi][fj][q];
           daff[fj] += ds * in;
           const float di = aff[fj] * ds;                 // d(intermediate)
-          dg[q] = bf16_round(di * u * (sg * (1.f + g * (1.f - sg))));
-          du[q] = bf16_round(di * ga);
-          it[q] = p.affinity_on_i ? bf16_round(aff[fj] * in) : in;
-          amg = fmaxf(amg, fabsf(dg[q]));
-          amu = fmaxf(amu, fabsf(du[q]));
+          gu[q] = bf16x2_rne(di * u * dsilu_from(g, sg), di * ga);
+          it[q] = ON_I ? bf16_rne(aff[fj] * in) : uint16_t(__float_as_uint(in) >> 16);
+          amg = fmaxf(amg, fabsf(lo_bf16(gu[q])));
+          amu = fmaxf(amu, fabsf(hi_bf16(gu[q])));
         });
         // I-axis groups: the fragment's 32 rows are this lane's 16 and lane^32's 16
         amg = fmaxf(amg, __shfl_xor(amg, 32, 64));
@@ -174,10 +174,10 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
         uint8_t* ru = rg + p.I;
         v2::static_for<4>([&](auto K) {
           constexpr int k = K;
-          *reinterpret_cast<uint32_t*>(rg + 8 * k) =
-              encode4<FG>(dg[4 * k], dg[4 * k + 1], dg[4 * k + 2], dg[4 * k + 3], ig);
-          *reinterpret_cast<uint32_t*>(ru + 8 * k) =
-              encode4<FG>(du[4 * k], du[4 * k + 1], du[4 * k + 2], du[4 * k + 3], iu);
+          *reinterpret_cast<uint32_t*>(rg + 8 * k) = encode4<FG>(lo_bf16(gu[4 * k]), lo_bf16(gu[4 * k + 1]),
+                                                                 lo_bf16(gu[4 * k + 2]), lo_bf16(gu[4 * k + 3]), ig);
+          *reinterpret_cast<uint32_t*>(ru + 8 * k) = encode4<FG>(hi_bf16(gu[4 * k]), hi_bf16(gu[4 * k + 1]),
+                                                                 hi_bf16(gu[4 * k + 2]), hi_bf16(gu[4 * k + 3]), iu);
         });
         if (h == 0) {
           p.dgu_row_scales[slot * (twoI / 32) + i0 / 32] = uint8_t(Xg + 127);
@@ -187,9 +187,8 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
         v2::static_for<16>([&](auto Q) {
           constexpr int q = Q;
           const int row = 8 * (q >> 2) + 4 * h + (q & 3), col = fj * 32 + r;
-          *reinterpret_cast<uint32_t*>(stg_gu + row * GS + col * 4) =
-              uint32_t(bf16_rne(dg[q])) | (uint32_t(bf16_rne(du[q])) << 16);
-          *reinterpret_cast<uint16_t*>(stg_in + row * IS + col * 2) = bf16_rne(it[q]);
+          *reinterpret_cast<uint32_t*>(stg_gu + row * GS + col * 4) = gu[q];
+          *reinterpret_cast<uint16_t*>(stg_in + row * IS + col * 2) = it[q];
         });
       });
       // the staging writes of this wave are visible to its own later reads (LDS is in order per wave)
@@ -253,15 +252,19 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
             mi = max(mi, x[T] & 0x7fff0000u);
           });
         });
-        const int Xi = scale_exp<FA>(mi);
+        const bool e5 = p.fmt_act == kE5M2;   // wave-uniform
+        const int Xi = e5 ? scale_exp<kE5M2>(mi) : scale_exp<kE4M3>(mi);
         const float ii = inv_scale(Xi);
         uint32_t ci[8];
         v2::static_for<4>([&](auto J) {
           const uint32_t x[4] = {v[J].x, v[J].y, v[J].z, v[J].w};
-          ci[2 * J] = encode4<FA>(__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
-                                  __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u), ii);
-          ci[2 * J + 1] = encode4<FA>(__uint_as_float(x[2] << 16), __uint_as_float(x[2] & 0xffff0000u),
-                                      __uint_as_float(x[3] << 16), __uint_as_float(x[3] & 0xffff0000u), ii);
+          if (e5) {
+            ci[2 * J] = encode4<kE5M2>(lo_bf16(x[0]), hi_bf16(x[0]), lo_bf16(x[1]), hi_bf16(x[1]), ii);
+            ci[2 * J + 1] = encode4<kE5M2>(lo_bf16(x[2]), hi_bf16(x[2]), lo_bf16(x[3]), hi_bf16(x[3]), ii);
+          } else {
+            ci[2 * J] = encode4<kE4M3>(lo_bf16(x[0]), hi_bf16(x[0]), lo_bf16(x[1]), hi_bf16(x[1]), ii);
+            ci[2 * J + 1] = encode4<kE4M3>(lo_bf16(x[2]), hi_bf16(x[2]), lo_bf16(x[3]), hi_bf16(x[3]), ii);
+          }
         });
         uint4* oi = reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + p0);
         oi[0] = uint4{ci[0], ci[1], ci[2], ci[3]};
@@ -343,26 +346,29 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_kernel(Phase3Args p) {
 
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool G>
-static hipError_t phase1_launch(Phase1Args p, int fg, int fa, hipStream_t st) {
+static hipError_t phase1_launch(Phase1Args p, int fg, hipStream_t st) {
   p.tiles_m = int((p.I + BM - 1) / BM);
   p.tiles_n = int((p.B + BN - 1) / BN);
   const unsigned blocks = unsigned(int64_t(p.tiles_m) * p.tiles_n * p.N);
-  if (fg == 0 && fa == 0) phase1_kernel<BM, BN, 0, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  else if (fg == 0) phase1_kernel<BM, BN, 0, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  else if (fa == 0) phase1_kernel<BM, BN, 1, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  else phase1_kernel<BM, BN, 1, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  const bool on_i = p.affinity_on_i != 0;
+  if (fg == kE4M3) {
+    if (on_i) phase1_kernel<BM, BN, kE4M3, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
+    else phase1_kernel<BM, BN, kE4M3, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  } else {
+    if (on_i) phase1_kernel<BM, BN, kE5M2, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
+    else phase1_kernel<BM, BN, kE5M2, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
 // Tile shape: 256 along a dimension when it is at least 256, else 128.  The
 // block size B is a power of two >= 128, so every tile lies inside one block.
-hipError_t launch_phase1(const Phase1Args& p, int fg, int fa, hipStream_t st) {
-  const bool g = (2 * p.H) % v2::BK != 0;      // a ragged last K stage
-  if (p.I >= 256 && p.B >= 256)
-    return g ? phase1_launch<256, 256, true>(p, fg, fa, st) : phase1_launch<256, 256, false>(p, fg, fa, st);
-  if (p.I >= 256)
-    return g ? phase1_launch<256, 128, true>(p, fg, fa, st) : phase1_launch<256, 128, false>(p, fg, fa, st);
-  return g ? phase1_launch<128, 128, true>(p, fg, fa, st) : phase1_launch<128, 128, false>(p, fg, fa, st);
+// 2H not a multiple of 128 bytes (a ragged last K stage): the v2 loop, 128 x 128.
+hipError_t launch_phase1(const Phase1Args& p, int fg, hipStream_t st) {
+  if ((2 * p.H) % v2::BK != 0) return phase1_launch<128, 128, true>(p, fg, st);
+  if (p.I >= 256 && p.B >= 256) return phase1_launch<256, 256, false>(p, fg, st);
+  if (p.I >= 256) return phase1_launch<256, 128, false>(p, fg, st);
+  return phase1_launch<128, 128, false>(p, fg, st);
 }
 
 template <int BM, int BN, bool G>
