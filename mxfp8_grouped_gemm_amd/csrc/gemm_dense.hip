@@ -8,6 +8,8 @@
 //       dW_down[e]    [I,H]  = inter_tok [I,P] . gy_tok [H,P]^T
 //     where the K columns of expert e are the slots of the blocks
 //     list[off[e] .. off[e+1]) (B slots each).
+#include <utility>
+
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
 #include "kernels.hpp"
@@ -83,19 +85,28 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_kernel(GemmStoreArgs 
     }
   }
 
+  // The launcher swaps the operands, so this tile is C^T: tile row m is an
+  // output column and tile column n an output row.  A lane's registers 4k..4k+3
+  // are four consecutive tile rows, i.e. four adjacent output columns: one
+  // 8-byte store.  M and N are multiples of 32, so such a group is wholly
+  // inside or outside the output.
   uint16_t* out = p.out + int64_t(g) * p.out_gstride;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + v2::acc_col<BM, BN>(j);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + v2::acc_row<BM, BN>(i, q);
-        if (row < p.M) out[row * p.ldo + col] = f32_to_bf16(acc[i][j][q]);
+  v2::static_for<FM>([&](auto I) {
+    v2::static_for<FN>([&](auto J) {
+      const int64_t orow = n0 + v2::acc_col<BM, BN>(J);
+      if (orow < p.N) {
+        uint16_t* dst = out + orow * p.ldo + m0;
+        v2::static_for<4>([&](auto K) {
+          const int ocol = v2::acc_row<BM, BN>(I, 4 * K);
+          if (m0 + ocol < p.M) {
+            const uint32_t lo = bf16x2_pack(acc[I][J][4 * K], acc[I][J][4 * K + 1]);
+            const uint32_t hi = bf16x2_pack(acc[I][J][4 * K + 2], acc[I][J][4 * K + 3]);
+            *reinterpret_cast<uint2*>(dst + ocol) = make_uint2(lo, hi);
+          }
+        });
       }
-    }
+    });
+  });
 }
 
 template <int BM, int BN, bool G>
@@ -108,6 +119,12 @@ static void launch_fmt(const GemmStoreArgs& p, int fa, int fb, unsigned blocks, 
 
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || groups <= 0) return hipSuccess;
+  // compute C^T = B . A^T so that the store is along the output's rows (see the kernel)
+  std::swap(p.a_codes, p.b_codes);
+  std::swap(p.a_scales, p.b_scales);
+  std::swap(p.lda, p.ldb);
+  std::swap(p.M, p.N);
+  std::swap(fa, fb);
   // Larger tiles once there are enough of them to fill the chip (256 CUs).
   const bool big = (p.M >= 256 && p.N >= 256 &&
                     ((p.M + 255) / 256) * ((p.N + 255) / 256) * int64_t(groups) >= 200);

@@ -122,6 +122,14 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(bf16_rne(f)); }
 
+// Two fp32 values rounded to bf16 (nearest even) and packed, a in the low half:
+// one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_pack(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 // Runtime-format dispatch.
 __device__ __forceinline__ int scale_exp_rt(int fmt, uint32_t amax_bits) {
   return fmt == kE4M3 ? scale_exp<kE4M3>(amax_bits) : scale_exp<kE5M2>(amax_bits);

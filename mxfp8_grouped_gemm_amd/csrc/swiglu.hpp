@@ -23,12 +23,7 @@ __device__ __forceinline__ float sigmoid_fast(float g) {
 // silu'(g) from s = sigmoid(g)
 __device__ __forceinline__ float dsilu_from(float g, float s) { return s * (1.f + g * (1.f - s)); }
 
-// Two fp32 values rounded to bf16 (nearest even) and packed: a in the low half.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-}
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) { return bf16x2_pack(a, b); }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
