@@ -8,6 +8,7 @@
 //       dW_down[e]    [I,H]  = inter_tok [I,P] . gy_tok [H,P]^T
 //     where the K columns of expert e are the slots of the blocks
 //     list[off[e] .. off[e+1]) (B slots each).
+#include <type_traits>
 #include <utility>
 
 #include "gemm_v2.hpp"
@@ -39,60 +40,17 @@ struct KMapGrouped {
   }
 };
 
-template <int BM, int BN, int FA, int FB, bool GENERIC>
-__global__ void __launch_bounds__(v2::kThreads) gemm_store_kernel(GemmStoreArgs p) {
-  // GENERIC: ragged K or unaligned scale rows (v2 loop); otherwise the ring (v3 loop)
-  constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  constexpr int FM = BM / 64, FN = BN / 64;
-  const int per_group = p.tiles_m * p.tiles_n;
-  const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
-  const int g = id / per_group;
-  int tm, tn;
-  v2::grouped_tile<8>(id - g * per_group, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
-  const int wave = threadIdx.x >> 6;
-  v2::v16f acc[FM][FN];
-
-  if constexpr (GENERIC) {
-    v2::Operand<BM, FM> A;
-    v2::Operand<BN, FN> B;
-    v2::setup_rows(A, p.a_codes, p.a_scales, m0, p.M, p.lda, p.lda / 32, (wave >> 1) * (BM / 2));
-    v2::setup_rows(B, p.b_codes, p.b_scales, n0, p.N, p.ldb, p.ldb / 32, (wave & 1) * (BN / 2));
-    KMapGrouped km{p.blk_list, 0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v2::BK) | 1u), p.K};
-    int nstages;
-    if (p.blk_list) {
-      km.b0 = p.blk_off[g];
-      nstages = int((int64_t(p.blk_off[g + 1] - km.b0) * p.blk) / v2::BK);
-    } else {
-      nstages = int((p.K + v2::BK - 1) / v2::BK);
-    }
-    v2::mainloop<BM, BN, v2::kFp8, FA, FB, true>(A, B, nstages, km, smem, acc);
-  } else {
-    v3::Op<BM> A;
-    v3::Op<BN> B;
-    v3::ScaleDma<BM, BN> sd;
-    v3::setup_rows(A, p.a_codes, m0, p.M, p.lda);
-    v3::setup_rows(B, p.b_codes, n0, p.N, p.ldb);
-    v3::setup_scales(sd, p.a_scales, m0, p.M, p.lda / 32, p.b_scales, n0, p.N, p.ldb / 32);
-    if (p.blk_list) {
-      const int b0 = p.blk_off[g];
-      const int nstages = int((int64_t(p.blk_off[g + 1] - b0) * p.blk) / v3::SK);
-      const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
-      v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, km, smem, acc);
-    } else {
-      v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, int(p.K / v3::SK), v3::KMapPlain{}, smem, acc);
-    }
-  }
-
-  // The launcher swaps the operands, so this tile is C^T: tile row m is an
-  // output column and tile column n an output row.  A lane's registers 4k..4k+3
-  // are four consecutive tile rows, i.e. four adjacent output columns: one
-  // 8-byte store.  M and N are multiples of 32, so such a group is wholly
-  // inside or outside the output.
+// Output tile store.  The launcher swaps the operands, so a tile is C^T: tile
+// row m is an output column and tile column n an output row.  A lane's
+// registers 4k..4k+3 are four consecutive tile rows, i.e. four adjacent output
+// columns: one 8-byte store.  M and N are multiples of 32, so such a group is
+// wholly inside or outside the output.
+template <int BM, int BN>
+__device__ __forceinline__ void store_tile(const GemmStoreArgs& p, int g, int64_t m0, int64_t n0,
+                                           const v2::v16f (&acc)[BM / 64][BN / 64]) {
   uint16_t* out = p.out + int64_t(g) * p.out_gstride;
-  v2::static_for<FM>([&](auto I) {
-    v2::static_for<FN>([&](auto J) {
+  v2::static_for<BM / 64>([&](auto I) {
+    v2::static_for<BN / 64>([&](auto J) {
       const int64_t orow = n0 + v2::acc_col<BM, BN>(J);
       if (orow < p.N) {
         uint16_t* dst = out + orow * p.ldo + m0;
@@ -109,38 +67,121 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_kernel(GemmStoreArgs 
   });
 }
 
-template <int BM, int BN, bool G>
-static void launch_fmt(const GemmStoreArgs& p, int fa, int fb, unsigned blocks, hipStream_t st) {
-  if (fa == 0 && fb == 0) gemm_store_kernel<BM, BN, 0, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  else if (fa == 0) gemm_store_kernel<BM, BN, 0, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  else if (fb == 0) gemm_store_kernel<BM, BN, 1, 0, G><<<blocks, v2::kThreads, 0, st>>>(p);
-  else gemm_store_kernel<BM, BN, 1, 1, G><<<blocks, v2::kThreads, 0, st>>>(p);
+// Workgroup id -> (group, first row, first column).  Hardware hands out
+// workgroup ids round robin over the 8 XCDs, so ids are remapped to give each
+// XCD a contiguous range, walked GM tile-rows at a time (co-resident tiles
+// share operand rows in that XCD's L2).
+struct TilePos {
+  int g;
+  int64_t m0, n0;
+};
+template <int BM, int BN>
+__device__ __forceinline__ TilePos tile_pos(const GemmStoreArgs& p, int tile) {
+  const int per_group = p.tiles_m * p.tiles_n;
+  const int id = v2::xcd_remap(tile, p.total);
+  const int g = id / per_group;
+  int tm, tn;
+  v2::grouped_tile<8>(id - g * per_group, p.tiles_m, p.tiles_n, tm, tn);
+  return TilePos{g, int64_t(tm) * BM, int64_t(tn) * BN};
+}
+
+// Unaligned shapes (ragged K or scale rows not 4-byte aligned): one tile per
+// workgroup on the two-stage loop.
+template <int BM, int BN, int FA, int FB>
+__global__ void __launch_bounds__(v2::kThreads) gemm_store_generic(GemmStoreArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
+  constexpr int FM = BM / 64, FN = BN / 64;
+  const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x);
+  const int wave = threadIdx.x >> 6;
+  v2::Operand<BM, FM> A;
+  v2::Operand<BN, FN> B;
+  v2::setup_rows(A, p.a_codes, p.a_scales, tp.m0, p.M, p.lda, p.lda / 32, (wave >> 1) * (BM / 2));
+  v2::setup_rows(B, p.b_codes, p.b_scales, tp.n0, p.N, p.ldb, p.ldb / 32, (wave & 1) * (BN / 2));
+  KMapGrouped km{p.blk_list, 0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v2::BK) | 1u), p.K};
+  int nstages;
+  if (p.blk_list) {
+    km.b0 = p.blk_off[tp.g];
+    nstages = int((int64_t(p.blk_off[tp.g + 1] - km.b0) * p.blk) / v2::BK);
+  } else {
+    nstages = int((p.K + v2::BK - 1) / v2::BK);
+  }
+  v2::v16f acc[FM][FN];
+  v2::mainloop<BM, BN, v2::kFp8, FA, FB, true>(A, B, nstages, km, smem, acc);
+  store_tile<BM, BN>(p, tp.g, tp.m0, tp.n0, acc);
+}
+
+// Aligned shapes: one tile per workgroup on the four-stage ring loop.
+// LIST: K runs over each group's block list (MoE Phases 2 and 4).
+template <int BM, int BN, int FA, int FB, bool LIST>
+__global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[v3::smem_bytes(BM, BN)];
+  constexpr int FM = BM / 64, FN = BN / 64;
+  const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x);
+  v3::Op<BM> A;
+  v3::Op<BN> B;
+  v3::ScaleDma<BM, BN> sd;
+  v3::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
+  v3::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
+  v3::setup_scales(sd, p.a_scales, tp.m0, p.M, p.lda / 32, p.b_scales, tp.n0, p.N, p.ldb / 32);
+  v2::v16f acc[FM][FN];
+  if constexpr (LIST) {
+    const int b0 = p.blk_off[tp.g];
+    const int nstages = int((int64_t(p.blk_off[tp.g + 1] - b0) * p.blk) / v3::SK);
+    const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
+    v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, km, smem, acc);
+  } else {
+    v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, int(p.K / v3::SK), v3::KMapPlain{}, smem, acc);
+  }
+  store_tile<BM, BN>(p, tp.g, tp.m0, tp.n0, acc);
+}
+
+template <int BM, int BN>
+static void launch_generic(const GemmStoreArgs& p, int fa, int fb, unsigned grid, hipStream_t st) {
+  if (fa == 0 && fb == 0) gemm_store_generic<BM, BN, 0, 0><<<grid, v2::kThreads, 0, st>>>(p);
+  else if (fa == 0) gemm_store_generic<BM, BN, 0, 1><<<grid, v2::kThreads, 0, st>>>(p);
+  else if (fb == 0) gemm_store_generic<BM, BN, 1, 0><<<grid, v2::kThreads, 0, st>>>(p);
+  else gemm_store_generic<BM, BN, 1, 1><<<grid, v2::kThreads, 0, st>>>(p);
+}
+
+template <int BM, int BN, bool LIST>
+static void launch_ring(const GemmStoreArgs& p, int fa, int fb, unsigned grid, hipStream_t st) {
+  if (fa == 0 && fb == 0) gemm_store_ring<BM, BN, 0, 0, LIST><<<grid, v2::kThreads, 0, st>>>(p);
+  else if (fa == 0) gemm_store_ring<BM, BN, 0, 1, LIST><<<grid, v2::kThreads, 0, st>>>(p);
+  else if (fb == 0) gemm_store_ring<BM, BN, 1, 0, LIST><<<grid, v2::kThreads, 0, st>>>(p);
+  else gemm_store_ring<BM, BN, 1, 1, LIST><<<grid, v2::kThreads, 0, st>>>(p);
 }
 
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || groups <= 0) return hipSuccess;
-  // compute C^T = B . A^T so that the store is along the output's rows (see the kernel)
+  // compute C^T = B . A^T so that the store is along the output's rows (see store_tile)
   std::swap(p.a_codes, p.b_codes);
   std::swap(p.a_scales, p.b_scales);
   std::swap(p.lda, p.ldb);
   std::swap(p.M, p.N);
   std::swap(fa, fb);
-  // Larger tiles once there are enough of them to fill the chip (256 CUs).
-  const bool big = (p.M >= 256 && p.N >= 256 &&
-                    ((p.M + 255) / 256) * ((p.N + 255) / 256) * int64_t(groups) >= 200);
+  // every stage full and scale rows 4-byte aligned -> the ring; otherwise the v2 loop
+  const bool generic = (p.lda % v2::BK) || (p.ldb % v2::BK) || (!p.blk_list && (p.K % v2::BK)) ||
+                       (p.blk_list && (p.blk % v2::BK));
+  // larger tiles once there are enough of them to fill the chip
+  const bool big = !generic && p.M >= 256 && p.N >= 256 &&
+                   ((p.M + 255) / 256) * ((p.N + 255) / 256) * int64_t(groups) >= 200;
   const int BM = big ? 256 : 128, BN = big ? 256 : 128;
   p.tiles_m = int((p.M + BM - 1) / BM);
   p.tiles_n = int((p.N + BN - 1) / BN);
-  const unsigned blocks = unsigned(int64_t(p.tiles_m) * p.tiles_n * groups);
-  // every stage full and scale rows 4-byte aligned -> the straight-line variant
-  const bool generic = (p.lda % v2::BK) || (p.ldb % v2::BK) || (!p.blk_list && (p.K % v2::BK)) ||
-                       (p.blk_list && (p.blk % v2::BK));
+  const int64_t total = int64_t(p.tiles_m) * p.tiles_n * groups;
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  p.total = int(total);
+  if (generic) {
+    launch_generic<128, 128>(p, fa, fb, unsigned(total), st);
+    return hipGetLastError();
+  }
+  const unsigned grid = unsigned(total);
   if (big) {
-    if (generic) launch_fmt<256, 256, true>(p, fa, fb, blocks, st);
-    else launch_fmt<256, 256, false>(p, fa, fb, blocks, st);
+    if (p.blk_list) launch_ring<256, 256, true>(p, fa, fb, grid, st);
+    else launch_ring<256, 256, false>(p, fa, fb, grid, st);
   } else {
-    if (generic) launch_fmt<128, 128, true>(p, fa, fb, blocks, st);
-    else launch_fmt<128, 128, false>(p, fa, fb, blocks, st);
+    if (p.blk_list) launch_ring<128, 128, true>(p, fa, fb, grid, st);
+    else launch_ring<128, 128, false>(p, fa, fb, grid, st);
   }
   return hipGetLastError();
 }

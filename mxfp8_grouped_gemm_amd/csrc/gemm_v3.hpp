@@ -203,72 +203,101 @@ __device__ __forceinline__ v16f mma(const uint4 (&a)[2], const uint4 (&b)[2], co
   }
 }
 
-// The K loop over nstages 64-byte stages (nstages even).  sd may be null in
-// bf16 mode.
-template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
-__device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const ScaleDma<BM, BN>* sd, int nstages,
-                                         const KMap& kmap, uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
-  constexpr int FM = BM / 64, FN = BN / 64;
-  constexpr int CS = code_slot(BM, BN), SSB = scale_slot(BM, BN);
-  constexpr int NCI = (BM + BN) / 64;                       // code DMA instructions per wave per stage
-  constexpr int NS = ScaleDma<BM, BN>::NS;                  // scale DMA instructions per wave per pair
-  constexpr int VM_STEADY = 2 * NCI + (ELEM == kFp8 ? NS : 0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, r = lane & 31;
-  const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  if (nstages <= 0) return;
+// One tile's operands: code rows of A and B, their scale rows (fp8 mode), the
+// K map and the number of 64-byte stages (even: K is a multiple of 128 bytes).
+template <int BM, int BN, class KMap>
+struct Tile {
+  Op<BM> A;
+  Op<BN> B;
+  ScaleDma<BM, BN> sd;
+  KMap km;
+  int nstages;
+};
 
+// The ring, shared by consecutive tiles of one workgroup.  `base` is the ring
+// position of the current tile's stage 0 (always even); stage t of the tile
+// lives in slot (base + t) % NBUF and its pair's scales in slot
+// ((base + t) / 2) % NBUF.  Loads are issued NBUF stages ahead of use.
+//
+// Invariant on entering a tile: positions base .. base + NBUF - 2 are issued
+// (its first stages, or the next tile's when it is shorter, see tail()), in
+// position order.  The tile issues position base + NBUF - 1 itself after a
+// barrier, since that slot held the previous tile's last stage.
+//
+// A tile is run as head() then tail():
+//   head: the stages whose look-ahead stays inside the tile, issuing only
+//         the tile's own operands (straight-line, few live registers);
+//   tail: the last NBUF stages, whose look-ahead would fetch a following
+//         tile's first stages; with no following tile it goes through
+//         descriptors with no records, which the hardware answers with zeros
+//         without touching memory.
+// Every iteration issues the same loads, so the wait counts are fixed.
+// The kernels here run one tile per workgroup (mainloop below).  Chaining
+// tiles through the ring in a persistent grid was measured slower: at 256
+// VGPRs the next tile's descriptors spill, and the reloads' waits drain the
+// ring at every tile boundary.
+template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
+struct Ring {
+  static constexpr int FM = BM / 64, FN = BN / 64;
+  static constexpr int CS = code_slot(BM, BN), SSB = scale_slot(BM, BN);
+  static constexpr int NCI = (BM + BN) / 64;               // code DMA instructions per wave per stage
+  static constexpr int NS = ScaleDma<BM, BN>::NS;          // scale DMA instructions per wave per pair
+  static constexpr int VM_STAGE = NCI;
+  static constexpr int VM_PAIR_SCALES = ELEM == kFp8 ? NS : 0;
+  using T = Tile<BM, BN, KMap>;
+
+  uint8_t* smem;
+  uint32_t base;
+
+  // DMA of stage `stage` of tile x into ring position base + pos (live == false:
+  // a load without records, i.e. zeros, keeping the issue count).
+  __device__ __forceinline__ void issue(const T& x, int stage, int pos, bool live) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t lds0 = lds_addr(smem);
-  const v4i rsa = rsrc(A.codes), rsb = rsrc(B.codes);
-  v4i rss[NS];
-  if (ELEM == kFp8) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i) rss[i] = rsrc(sd->buf[i]);
-  }
-  // DMA for stage t into ring slot t % NBUF (and the scales of its pair when
-  // t is even).  Stages past the end are issued too, through descriptors with
-  // no records (the hardware returns zeros without a memory access), so every
-  // iteration issues the same loads and the wait counts stay fixed.
-  auto issue = [&](int t) {
-    const bool live = t < nstages;
-    const uint32_t kc = kmap(live ? t : 0);
-    const uint32_t slot = lds0 + uint32_t(t & (NBUF - 1)) * CS;
-    v4i ra = rsa, rb = rsb;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t lds0 = lds_addr(smem);
+    const uint32_t kc = x.km(live ? stage : 0);
+    const uint32_t slot = lds0 + ((base + uint32_t(pos)) & (NBUF - 1)) * CS;
+    v4i ra = rsrc(x.A.codes), rb = rsrc(x.B.codes);
     ra[2] = live ? ra[2] : 0;
     rb[2] = live ? rb[2] : 0;
 #pragma unroll
-    for (int j = 0; j < BM / 64; ++j) dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * j) * SK, A.off[j], kc);
+    for (int j = 0; j < BM / 64; ++j) dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * j) * SK, x.A.off[j], kc);
 #pragma unroll
-    for (int j = 0; j < BN / 64; ++j)
-      dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * j) * SK, B.off[j], kc);
-    if (ELEM == kFp8 && (t & 1) == 0) {
-      const uint32_t ss = lds0 + NBUF * CS + uint32_t((t >> 1) & (NBUF - 1)) * SSB;
+    for (int j = 0; j < BN / 64; ++j) dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * j) * SK, x.B.off[j], kc);
+    if (ELEM == kFp8 && (pos & 1) == 0) {
+      const uint32_t ss = lds0 + NBUF * CS + (((base + uint32_t(pos)) >> 1) & (NBUF - 1)) * SSB;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        v4i rs = rss[i];
+        v4i rs = rsrc(x.sd.buf[i]);
         rs[2] = live ? rs[2] : 0;
-        dma4(rs, ss + uint32_t(wave + 4 * i) * 256, sd->off[i], kc >> 5);
+        dma4(rs, ss + uint32_t(wave + 4 * i) * 256, x.sd.off[i], kc >> 5);
       }
     }
-  };
-#else
-  auto issue = [&](int) {};
 #endif
+  }
+  // position pos >= cur.nstages belongs to nxt
+  __device__ __forceinline__ void issue_next(const T& cur, const T& nxt, int pos) const {
+    const int tn = pos - cur.nstages;
+    issue(nxt, tn, pos, tn < nxt.nstages);
+  }
+
+  // Positions 0 .. NBUF-2 of the first tile a workgroup computes.
+  __device__ __forceinline__ void prefetch(const T& first) const {
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t) issue(first, t, t, t < first.nstages);
+  }
 
   uint4 fa[2][FM][2], fb[2][FN][2];
   uint32_t sa[2][FM], sb[2][FN];
+
   // fragments and raw scale words of stage t into set P (the words are shifted
   // to this lane's group where they are used, so nothing here waits on the reads)
-  auto read = [&](int t, auto Pc) {
-    constexpr int P = decltype(Pc)::value;
-    const uint8_t* cs = smem + (t & (NBUF - 1)) * CS;
+  template <int P>
+  __device__ __forceinline__ void read(int t) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = lane >> 5, r = lane & 31;
+    const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
+    const uint8_t* cs = smem + ((base + uint32_t(t)) & (NBUF - 1)) * CS;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wrow + 32 * i + r;
@@ -282,7 +311,7 @@ __device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const
       fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
     }
     if (ELEM == kFp8) {
-      const uint8_t* ss = smem + NBUF * CS + ((t >> 1) & (NBUF - 1)) * SSB;
+      const uint8_t* ss = smem + NBUF * CS + (((base + uint32_t(t)) >> 1) & (NBUF - 1)) * SSB;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = wrow + 32 * i + r;
@@ -294,44 +323,47 @@ __device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const
         sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
       }
     }
-  };
-  // MFMAs of half H of the fragments in set P; OPS = scale byte of the stage within its pair
-  auto compute = [&](auto Pc, auto Hc, auto OPSc) {
-    constexpr int P = decltype(Pc)::value, H = decltype(Hc)::value, OPS = decltype(OPSc)::value;
-    if (ELEM == kFp8) {
-      constexpr int I0 = H * FM / 2, I1 = (H + 1) * FM / 2;
-#pragma unroll
-      for (int i = I0; i < I1; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = mma<ELEM, FA, FB, OPS>(fa[P][i], fb[P][j], acc[i][j], int(sa[P][i] >> (8 * h)),
-                                             int(sb[P][j] >> (8 * h)), 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mma<ELEM, FA, FB, 0>(fa[P][i], fb[P][j], acc[i][j], 0, 0, H);
-    }
-  };
+  }
 
-  // One stage t with its fragments in set P (P == t & 1).  With READ: wait
-  // until stage t+1 has landed (t+2, t+3 may still be in flight) and every
-  // wave has finished reading stage t's slot (barrier), DMA stage t+4 into
-  // that slot, then read stage t+1 into set P ^ 1 interleaved with the MFMAs
-  // of stage t (an LDS queue holds at most 15 reads, so issuing them all first
-  // would stall the MFMAs behind them).
-  auto step = [&](int t, auto Pc, auto READc) {
-    constexpr int P = decltype(Pc)::value;
-    constexpr bool READ = decltype(READc)::value;
-    if (READ) {
-      __builtin_amdgcn_s_waitcnt(waitcnt(VM_STEADY, 0));
-      __builtin_amdgcn_s_barrier();
-      issue(t + NBUF);
-      __builtin_amdgcn_sched_barrier(0);
-      read(t + 1, std::integral_constant<int, P ^ 1>{});
+  // MFMAs of the stage in set P (stage parity P = scale byte within the pair)
+  template <int P>
+  __device__ __forceinline__ void compute(v16f (&acc)[FM][FN]) const {
+    const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int H = 0; H < 2; ++H) {
+      if (ELEM == kFp8) {
+#pragma unroll
+        for (int i = H * FM / 2; i < (H + 1) * FM / 2; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = mma<ELEM, FA, FB, 2 * P>(fa[P][i], fb[P][j], acc[i][j], int(sa[P][i] >> (8 * h)),
+                                                 int(sb[P][j] >> (8 * h)), 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mma<ELEM, FA, FB, 0>(fa[P][i], fb[P][j], acc[i][j], 0, 0, H);
+      }
     }
-    compute(std::integral_constant<int, P>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * P>{});
-    compute(std::integral_constant<int, P>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2 * P>{});
+  }
+
+  // One stage t (fragments in set P == t & 1).  With a look-ahead `ahead`
+  // (a callable issuing position t + NBUF): wait until stage t+1 has landed
+  // (t+2, t+3 may still be in flight) and every wave has finished reading
+  // stage t's slot (barrier), issue, then read stage t+1 into set P ^ 1
+  // interleaved with stage t's MFMAs (an LDS queue holds at most 15 reads, so
+  // issuing them all first would stall the MFMAs behind them).  Without: the
+  // tile's last stage.
+  template <int P, bool READ, class Ahead>
+  __device__ __forceinline__ void step(int t, v16f (&acc)[FM][FN], const Ahead& ahead) {
+    if (READ) {
+      __builtin_amdgcn_s_waitcnt(waitcnt(2 * VM_STAGE + VM_PAIR_SCALES, 0));
+      __builtin_amdgcn_s_barrier();
+      ahead(t + NBUF);
+      __builtin_amdgcn_sched_barrier(0);
+      read<P ^ 1>(t + 1);
+    }
+    compute<P>(acc);
     if (READ) {
       constexpr int NMF = FM * FN * (ELEM == kFp8 ? 1 : 2);                  // MFMAs of a stage
       constexpr int NRD = 2 * (FM + FN) + (ELEM == kFp8 ? FM + FN : 0);      // LDS reads of a stage
@@ -343,23 +375,89 @@ __device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // prologue: stages 0 .. 3 in flight, then stage 0 into registers
-#pragma unroll
-  for (int t = 0; t < NBUF; ++t) issue(t);
-  __builtin_amdgcn_s_waitcnt(waitcnt(3 * NCI + (ELEM == kFp8 ? NS : 0), 15));
-  __builtin_amdgcn_s_barrier();
-  read(0, std::integral_constant<int, 0>{});
-  // nstages is even (K is a multiple of 128 bytes); the last pair is peeled so
-  // that the steady-state loop has no path that skips the reads
-  int t = 0;
-  for (; t + 2 < nstages; t += 2) {
-    step(t, std::integral_constant<int, 0>{}, std::true_type{});
-    step(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
   }
-  step(t, std::integral_constant<int, 0>{}, std::true_type{});
-  step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+
+  // Entry: issue position NBUF-1 (after a barrier: its slot held the previous
+  // tile's last stage), wait for stage 0, read it.
+  template <class Ahead>
+  __device__ __forceinline__ void enter(const Ahead& ahead) {
+    __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
+    __builtin_amdgcn_s_barrier();
+    ahead(NBUF - 1);
+    // stage 0 has landed once at most the three later positions' loads remain
+    __builtin_amdgcn_s_waitcnt(waitcnt(3 * VM_STAGE + VM_PAIR_SCALES, 0));
+    __builtin_amdgcn_s_barrier();
+    read<0>(0);
+  }
+
+  // The stages of cur whose look-ahead stays inside cur.  Returns the first
+  // stage left for tail().
+  __device__ __forceinline__ int head(const T& cur, v16f (&acc)[FM][FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    const int n = cur.nstages;
+    if (n < NBUF) return 0;
+    auto own = [&](int pos) { issue(cur, pos, pos, true); };
+    enter(own);
+    int t = 0;
+    for (; t + NBUF + 1 < n; t += 2) {
+      step<0, true>(t, acc, own);
+      step<1, true>(t + 1, acc, own);
+    }
+    return t;
+  }
+
+  // The last stages of cur (from t0, as head() returned); the look-ahead
+  // fetches nxt's first stages.  Leaves base at nxt's stage 0.
+  __device__ __forceinline__ void tail(const T& cur, const T& nxt, int t0, v16f (&acc)[FM][FN]) {
+    const int n = cur.nstages;
+    auto next = [&](int pos) {
+      if (pos < n) issue(cur, pos, pos, true);
+      else issue_next(cur, nxt, pos);
+    };
+    if (n < NBUF) {
+      // A tile shorter than the ring: positions base + n .. base + NBUF - 2 were
+      // issued without knowing nxt (no records).  Let every load land and every
+      // wave finish the previous tile (barrier), then fetch nxt's stages there,
+      // in position order; later waits can then only over-wait.
+      __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int pos = 0; pos < NBUF - 1; ++pos)
+        if (pos >= n) issue_next(cur, nxt, pos);
+      if (n == 0) return;   // base stays: nxt starts at the same position
+      enter(next);
+    }
+    int t = t0;
+    for (; t + 2 < n; t += 2) {
+      step<0, true>(t, acc, next);
+      step<1, true>(t + 1, acc, next);
+    }
+    step<0, true>(t, acc, next);
+    step<1, false>(t + 1, acc, next);
+    base += uint32_t(n);
+  }
+};
+
+// One tile on its own (no neighbour to prefetch for).  sd may be null in bf16 mode.
+template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
+__device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const ScaleDma<BM, BN>* sd, int nstages,
+                                         const KMap& kmap, uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
+  Tile<BM, BN, KMap> cur{A, B, {}, kmap, nstages};
+  if (ELEM == kFp8) cur.sd = *sd;
+  Tile<BM, BN, KMap> none = cur;
+  none.nstages = 0;
+  Ring<BM, BN, ELEM, FA, FB, KMap> ring{smem, 0u};
+  ring.prefetch(cur);
+  const int t0 = ring.head(cur, acc);
+  ring.tail(cur, none, t0, acc);
+  // the look-ahead loads past the end still write (zeros) into the ring: let
+  // them land before the caller reuses the LDS
+  __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
 }
 
 }  // namespace v3

@@ -38,6 +38,7 @@ struct GemmStoreArgs {
   const int32_t* blk_list;
   int blk;
   int tiles_m, tiles_n;
+  int total;                      // tiles over all groups
 };
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st);
 
@@ -92,6 +93,7 @@ struct Phase3Args {
   int64_t H, I, N, B;
   float* dx_acc;                  // [T][H]
   int tiles_m, tiles_n;
+  int total;                      // tiles over all blocks
 };
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st);
 
