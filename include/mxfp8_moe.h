@@ -92,6 +92,9 @@ int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis, int 
  *     [1]  W^T codes along N [K,N]  + scales [K,N/32]
  *     [2]  dY^T codes along M [N,M] + scales [N,M/32]
  *     [3]  X^T codes along M [K,M]  + scales [K,M/32]
+ *   Scales of [0],[1] are pair-major ([N/128][rows][4]: word (p, r) = row r's
+ *   bytes for elements [128p, 128p+128)) when N % 128 == 0, and those of
+ *   [2],[3] ([M/128][rows][4]) when M % 128 == 0; the region sizes are the same.
  *   each region starting on a 256-byte boundary, in this order, codes first.
  * ------------------------------------------------------------------------- */
 size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
@@ -183,20 +186,26 @@ typedef struct {
  *   dy_codes/dy_scales        [T,H] / [T,H/32]        dY along H (Phase 1)
  *   dy_deq                    [T,H] bf16              exact values of those codes
  *   wd_deq                    [E,I,H] bf16            exact values of the W_down codes
- *   x_tok_codes/scales        [H,P] / [H,P/32]        X along slots (Phase 2), P = N*B
- *   gy_tok_codes/scales       [H,P] / [H,P/32]        a*dY (on H) or dY (on I), Phase 4
- *   inter_tok_codes/scales    [I,P] / [I,P/32]        inter (on H) or a*inter (on I)
- *   dgu_row_codes/scales      [P,2I] / [P,2I/32]      [dGate|dUp] along I (Phase 3)
- *   dgu_tok_codes/scales      [2I,P] / [2I,P/32]      [dGate;dUp] along slots (Phase 2)
+ *   x_tok_codes/scales        [H,P] / P4[P,H]         X along slots (Phase 2), P = N*B
+ *   gy_tok_codes/scales       [H,P] / P4[P,H]         a*dY (on H) or dY (on I), Phase 4
+ *   inter_tok_codes/scales    [I,P] / P4[P,I]         inter (on H) or a*inter (on I)
+ *   dgu_row_codes/scales      [P,2I] / P4[2I,P]       [dGate|dUp] along I (Phase 3);
+ *                                                     scales [P,2I/32] when 2I % 128 != 0
+ *   dgu_tok_codes/scales      [2I,P] / P4[P,2I]       [dGate;dUp] along slots (Phase 2)
+ *   wgu_scales_pairs          P4 of gate_up_scales per expert, [E][2I/128][H][4]
+ *                                                     (written when 2I % 128 == 0)
  *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
  *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32.
- * Pad slots hold code 0.  Rows of a region are contiguous; no padding between rows. */
+ * P4[K,R] is the pair-major scale layout of an operand with R rows contracted
+ * over K elements: [K/128][R][4] bytes, word (p, r) holding row r's E8M0 bytes
+ * for elements [128p, 128p+128) (so one stage pair's words for consecutive rows
+ * are contiguous).  Pad slots hold code 0.  Rows of a region are contiguous. */
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 

@@ -103,18 +103,25 @@ static int dense_run(const uint16_t* dy, const uint16_t* w, const uint16_t* x, i
   uint8_t* base = static_cast<uint8_t*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  // operands of a GEMM whose contraction is a multiple of 128 feed the ring
+  // loop and get pair-major scales
+  const bool pairs_n = N % 128 == 0, pairs_m = M % 128 == 0;
   // stage 0 -- dX = dY W: dY along N [M,N]; W along N, transposed to [K,N]
-  if (lo <= 0 && 0 <= hi && (e = mx::launch_quant_rows(dy, M, N, fmt_dy, base + off[0], base + off[1], st)) != hipSuccess)
+  if (lo <= 0 && 0 <= hi &&
+      (e = mx::launch_quant_rows(dy, M, N, fmt_dy, base + off[0], base + off[1], st, nullptr, pairs_n)) != hipSuccess)
     return hip_status(e, "quantize dY along N");
-  if (lo <= 0 && 0 <= hi && (e = mx::launch_quant_tok(w, N, K, nullptr, nullptr, N, fmt_w, base + off[2], base + off[3], st)) !=
-      hipSuccess)
+  if (lo <= 0 && 0 <= hi &&
+      (e = mx::launch_quant_tok(w, N, K, nullptr, nullptr, N, fmt_w, base + off[2], base + off[3], st, pairs_n)) !=
+          hipSuccess)
     return hip_status(e, "quantize W along N");
   // stage 1 -- dW = dY^T X: dY along M, transposed to [N,M]; X along M, transposed to [K,M]
-  if (lo <= 1 && 1 <= hi && (e = mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fmt_dy, base + off[4], base + off[5], st)) !=
-      hipSuccess)
+  if (lo <= 1 && 1 <= hi &&
+      (e = mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fmt_dy, base + off[4], base + off[5], st, pairs_m)) !=
+          hipSuccess)
     return hip_status(e, "quantize dY along M");
-  if (lo <= 1 && 1 <= hi && (e = mx::launch_quant_tok(x, M, K, nullptr, nullptr, M, fmt_x, base + off[6], base + off[7], st)) !=
-      hipSuccess)
+  if (lo <= 1 && 1 <= hi &&
+      (e = mx::launch_quant_tok(x, M, K, nullptr, nullptr, M, fmt_x, base + off[6], base + off[7], st, pairs_m)) !=
+          hipSuccess)
     return hip_status(e, "quantize X along M");
   mx::GemmStoreArgs g{};
   g.a_codes = base + off[0]; g.a_scales = base + off[1]; g.lda = N;
@@ -194,6 +201,7 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->dgu_row_scales, P * 2 * I / 32);
   put(L->dgu_tok_codes, 2 * I * P);
   put(L->dgu_tok_scales, 2 * I * P / 32);
+  put(L->wgu_scales_pairs, E * H * 2 * I / 32);
   put(L->dx_acc, T * H * 4);
   put(L->daff_slot, P * 4);
   put(L->db1_acc, E * 2 * I * 4);
@@ -304,14 +312,19 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   STEP(mx::launch_dequant_rows(a->down_codes, a->down_scales, E * I, H, a->fmt_weight,
                                reinterpret_cast<uint16_t*>(at(L.wd_deq)), st),
        "dequantize W_down");
+  // Phase 3 on the ring loop reads W_gate_up's scales pair-major
+  const bool gu_pairs = (2 * I) % 128 == 0;
+  if (gu_pairs)
+    STEP(mx::launch_scales_to_pairs(a->gate_up_scales, E, H, 2 * I, at(L.wgu_scales_pairs), st),
+         "W_gate_up scales to pairs");
   stage = 2;
   // token-axis operands of Phases 2 and 4: X, a*dY (on H) or dY (on I); the intermediate
   // operand comes out of the Phase-1 epilogue
   STEP(mx::launch_quant_tok(a->hidden_states, T, H, slot_tok, nullptr, P, a->fmt_act, at(L.x_tok_codes),
-                            at(L.x_tok_scales), st),
+                            at(L.x_tok_scales), st, true),
        "gather-quantize X");
   STEP(mx::launch_quant_tok(a->output_hidden_states_grad, T, H, slot_tok, a->affinity_on == 0 ? slot_aff : nullptr,
-                            P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st),
+                            P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st, true),
        "gather-quantize dY");
   stage = 3;
   if (a->has_bias)
@@ -331,12 +344,13 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.inter_tok_codes = at(L.inter_tok_codes); p1.inter_tok_scales = at(L.inter_tok_scales);
   p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
   p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias; p1.fmt_act = a->fmt_act;
+  p1.dgu_row_pairs = gu_pairs;
   STEP(mx::launch_phase1(p1, a->fmt_grad, st), "phase 1");
   stage = 5;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};
   p3.dgu_row_codes = at(L.dgu_row_codes); p3.dgu_row_scales = at(L.dgu_row_scales);
-  p3.wgu_codes = a->gate_up_codes; p3.wgu_scales = a->gate_up_scales;
+  p3.wgu_codes = a->gate_up_codes; p3.wgu_scales = gu_pairs ? at(L.wgu_scales_pairs) : a->gate_up_scales;
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");

@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p)
   v3::ScaleDma<BM, BN> sd;
   v3::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
   v3::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
-  v3::setup_scales(sd, p.a_scales, tp.m0, p.M, p.lda / 32, p.b_scales, tp.n0, p.N, p.ldb / 32);
+  v3::setup_scales(sd, p.a_scales, tp.m0, p.M, p.M * p.lda / 32, p.b_scales, tp.n0, p.N, p.N * p.ldb / 32);
   v2::v16f acc[FM][FN];
   if constexpr (LIST) {
     const int b0 = p.blk_off[tp.g];

@@ -12,9 +12,10 @@
 //
 // Stage = 64 bytes of K (one 64-element fp8 MFMA step, two 16-element bf16
 // steps).  LDS: NBUF code slots of (BM + BN) rows x 64 B (16-byte chunks
-// XOR-swizzled by row so that 8 consecutive rows reading one logical chunk hit
-// distinct banks), then NBUF scale slots holding, for a pair of stages, one
-// 4-byte word per row (the pair's four E8M0 groups).
+// XOR-swizzled by row so that 16 consecutive rows reading one logical chunk
+// hit distinct banks, see swz), then NBUF scale slots holding, for a pair of
+// stages, one 4-byte word per row (the pair's four E8M0 groups), loaded from
+// pair-major scale arrays (see ScaleDma).
 //
 // Loads are issued with inline asm (s_mov_b32 m0 + buffer_load_dword{,x4} ...
 // lds) because the compiler's wait-count pass treats every LDS read after an
@@ -109,7 +110,14 @@ template <int ROWS>
 __device__ __forceinline__ int dma_row(int j) {
   return (threadIdx.x >> 6) * (ROWS / 4) + 16 * j + ((threadIdx.x & 63) >> 2);
 }
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+// Physical 16-byte chunk of logical chunk c in row `row` is c ^ swz(row).  A
+// fragment read has consecutive lanes on consecutive rows, one chunk each;
+// LDS serves 16 lanes of a 16-byte read per pass on 64 banks, so any 16
+// consecutive rows (four per 256-byte bank line) must fall on 16 distinct
+// 16-byte slots: rows r, r+4, r+8, r+12 need distinct swizzles.  The XOR of
+// bits 1-2 and 3-4 gives that, and also keeps 8 consecutive rows distinct on
+// 32 banks.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 template <int ROWS>
 __device__ __forceinline__ void setup_rows(Op<ROWS>& op, const uint8_t* codes, int64_t row0, int64_t nrows,
@@ -138,40 +146,48 @@ __device__ __forceinline__ void setup_gather(Op<ROWS>& op, const uint8_t* codes,
   }
 }
 
-// Scale rows of both operands, in 64-row chunks: chunk c (A rows first, then
-// B rows) is loaded by wave c % 4 as its instruction c / 4; chunks past the
-// tile's rows load zeros into the slot's tail so every wave issues the same
-// number of instructions.
+// Scale words of both operands.  Scales of an operand with R rows and K
+// contraction elements are stored pair-major, [K/128][R][4]: word (p, r) holds
+// the four E8M0 bytes of row r for K elements [128p, 128p + 128), so the words
+// of a stage pair for consecutive rows are contiguous.  They are loaded in
+// 64-row chunks: chunk c (A rows first, then B rows) by wave c % 4 as its
+// instruction c / 4, one 4-byte word per lane at (row0 + row) * 4 plus the
+// pair's offset p * R * 4; chunks past the tile's rows load zeros into the
+// slot's tail so every wave issues the same number of instructions.
 template <int BM, int BN>
 struct ScaleDma {
   static constexpr int NS = scale_chunks(BM, BN) / 4;
   Buf buf[NS];
-  uint32_t off[NS];
+  uint32_t off[NS];       // this lane's row word (or out of range)
+  uint32_t pstride[NS];   // bytes per pair (R * 4) of the operand the chunk belongs to
 };
 
+// a_scales / b_scales: pair-major scale arrays of the whole operands (a_rows /
+// b_rows rows, a_bytes / b_bytes bytes); the tile covers rows a_row0.. / b_row0..
 template <int BM, int BN>
 __device__ __forceinline__ void setup_scales(ScaleDma<BM, BN>& sd, const uint8_t* a_scales, int64_t a_row0,
-                                             int64_t a_rows, int64_t a_sld, const uint8_t* b_scales, int64_t b_row0,
-                                             int64_t b_rows, int64_t b_sld) {
+                                             int64_t a_rows, int64_t a_bytes, const uint8_t* b_scales,
+                                             int64_t b_row0, int64_t b_rows, int64_t b_bytes) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t ha = a_rows - a_row0 < BM ? a_rows - a_row0 : BM;
-  const int64_t hb = b_rows - b_row0 < BN ? b_rows - b_row0 : BN;
-  const Buf ba = v2::make_rsrc(a_scales + a_row0 * a_sld, uint32_t(ha * a_sld));
-  const Buf bb = v2::make_rsrc(b_scales + b_row0 * b_sld, uint32_t(hb * b_sld));
+  const Buf ba = v2::make_rsrc(a_scales, uint32_t(a_bytes));
+  const Buf bb = v2::make_rsrc(b_scales, uint32_t(b_bytes));
 #pragma unroll
   for (int i = 0; i < ScaleDma<BM, BN>::NS; ++i) {
     const int c = wave + 4 * i;
     if (c < BM / 64) {
-      const int r = 64 * c + lane;
+      const int64_t r = a_row0 + 64 * c + lane;
       sd.buf[i] = ba;
-      sd.off[i] = r < ha ? uint32_t(r * a_sld) : kOOB;
+      sd.off[i] = r < a_rows ? uint32_t(r * 4) : kOOB;
+      sd.pstride[i] = uint32_t(a_rows * 4);
     } else if (c < (BM + BN) / 64) {
-      const int r = 64 * (c - BM / 64) + lane;
+      const int64_t r = b_row0 + 64 * (c - BM / 64) + lane;
       sd.buf[i] = bb;
-      sd.off[i] = r < hb ? uint32_t(r * b_sld) : kOOB;
+      sd.off[i] = r < b_rows ? uint32_t(r * 4) : kOOB;
+      sd.pstride[i] = uint32_t(b_rows * 4);
     } else {
       sd.buf[i] = ba;
       sd.off[i] = kOOB;
+      sd.pstride[i] = 0;
     }
   }
 }
@@ -270,7 +286,7 @@ struct Ring {
       for (int i = 0; i < NS; ++i) {
         v4i rs = rsrc(x.sd.buf[i]);
         rs[2] = live ? rs[2] : 0;
-        dma4(rs, ss + uint32_t(wave + 4 * i) * 256, x.sd.off[i], kc >> 5);
+        dma4(rs, ss + uint32_t(wave + 4 * i) * 256, x.sd.off[i], (kc >> 7) * x.sd.pstride[i]);
       }
     }
 #endif

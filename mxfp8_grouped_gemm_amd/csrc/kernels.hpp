@@ -8,8 +8,10 @@
 namespace mx {
 
 // quantize.hip
+// Scale layouts: row-major [rows][K/32], or pair-major [K/128][rows][4] (pairs
+// = true) for operands of the ring GEMM loop; see gemm_v3.hpp.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, hipStream_t st, uint16_t* deq = nullptr);
+                             uint8_t* scales, hipStream_t st, uint16_t* deq = nullptr, bool pairs = false);
 // codes [rows][cols] + scales [rows][cols/32] (groups along cols) -> exact bf16 values
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, int fmt,
                                uint16_t* out, hipStream_t st);
@@ -17,10 +19,15 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
                              uint8_t* scales, hipStream_t st);
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st);
+                            uint8_t* scales_t, hipStream_t st, bool pairs = false);
+// gate/up weight scales [E][H][2I/32] -> pair-major per expert [E][2I/128][H][4]
+hipError_t launch_scales_to_pairs(const uint8_t* in, int64_t groups, int64_t rows, int64_t k, uint8_t* out,
+                                  hipStream_t st);
 
 // gemm_dense.hip: C[m][n] = sum_k A[m][k] B[n][k] -> bf16 out[g][m][n].
-// A [M][lda] and B [N][ldb] fp8 codes, K-contiguous, scales [rows][ld/32].
+// A [M][lda] and B [N][ldb] fp8 codes, K-contiguous.  Scales pair-major
+// ([ld/128][rows][4]) when lda, ldb and K (or blk) are multiples of 128 (the
+// ring loop), else row-major [rows][ld/32].
 // Without blk_list the contraction is [0, K); with it, group g contracts over
 // the columns of blocks blk_list[blk_off[g] .. blk_off[g+1]) of blk bytes each.
 struct GemmStoreArgs {
@@ -68,25 +75,26 @@ struct Phase1Args {
   const uint16_t* ckpt;         // [N][2][I][B]
   int64_t T, H, I, E, N, B;
   uint8_t* dgu_row_codes;       // [P][2I]
-  uint8_t* dgu_row_scales;      // [P][2I/32]
+  uint8_t* dgu_row_scales;      // pair-major [2I/128][P][4] (dgu_row_pairs) or row-major [P][2I/32]
   uint8_t* dgu_tok_codes;       // [2I][P]
-  uint8_t* dgu_tok_scales;      // [2I][P/32]
+  uint8_t* dgu_tok_scales;      // pair-major [P/128][2I][4]
   uint8_t* inter_tok_codes;     // [I][P]: the intermediate (times a with the affinity on I), slot groups
-  uint8_t* inter_tok_scales;    // [I][P/32]
+  uint8_t* inter_tok_scales;    // pair-major [P/128][I][4]
   float* daff_slot;             // [P]
   float* db1_acc;               // [E][2][I]
   int affinity_on_i;            // 1: the intermediate operand carries the affinity
   int has_bias;                 // 1: accumulate db1
   int fmt_act;                  // format of the intermediate operand (activation format)
+  int dgu_row_pairs;            // 1: dGU along I feeds the ring loop (2I % 128 == 0): pair-major scales
   int tiles_m, tiles_n;
 };
 hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]
-  const uint8_t* dgu_row_scales;  // [P][2I/32]
+  const uint8_t* dgu_row_scales;  // 2I % 128 == 0: pair-major [2I/128][P][4]; else row-major [P][2I/32]
   const uint8_t* wgu_codes;       // [E][H][2I]
-  const uint8_t* wgu_scales;      // [E][H][2I/32]
+  const uint8_t* wgu_scales;      // 2I % 128 == 0: pair-major [E][2I/128][H][4]; else row-major [E][H][2I/32]
   const int32_t* slot_tok;
   const int32_t* b2e;
   const int32_t* flag;

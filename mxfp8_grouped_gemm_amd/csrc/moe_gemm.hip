@@ -70,7 +70,8 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   const int64_t P = p.N * p.B;
   const int64_t sbase = int64_t(b) * p.B;
   if (!p.flag[b]) {
-    // a block without tokens: its intermediate operand is all zeros (codes 0, scale byte 0)
+    // a block without tokens: its intermediate operand is all zeros (codes 0, scale
+    // byte 0; scales pair-major [P/128][I][4])
     for (int k = threadIdx.x; k < BM * (BN / 16); k += v2::kThreads) {
       const int64_t i = m0 + k / (BN / 16);
       if (i < p.I)
@@ -79,7 +80,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
     for (int k = threadIdx.x; k < BM * (BN / 128); k += v2::kThreads) {
       const int64_t i = m0 + k / (BN / 128);
       if (i < p.I)
-        *reinterpret_cast<uint32_t*>(p.inter_tok_scales + i * (P / 32) + (sbase + n0) / 32 + (k % (BN / 128)) * 4) = 0u;
+        *reinterpret_cast<uint32_t*>(p.inter_tok_scales + (((sbase + n0) / 128 + k % (BN / 128)) * p.I + i) * 4) = 0u;
     }
     return;
   }
@@ -180,8 +181,14 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
                                                                  hi_bf16(gu[4 * k + 2]), hi_bf16(gu[4 * k + 3]), iu);
         });
         if (h == 0) {
-          p.dgu_row_scales[slot * (twoI / 32) + i0 / 32] = uint8_t(Xg + 127);
-          p.dgu_row_scales[slot * (twoI / 32) + (p.I + i0) / 32] = uint8_t(Xu + 127);
+          const int64_t gg = i0 / 32, gu_ = (p.I + i0) / 32;
+          if (p.dgu_row_pairs) {   // pair-major [2I/128][P][4]
+            p.dgu_row_scales[((gg >> 2) * P + slot) * 4 + (gg & 3)] = uint8_t(Xg + 127);
+            p.dgu_row_scales[((gu_ >> 2) * P + slot) * 4 + (gu_ & 3)] = uint8_t(Xu + 127);
+          } else {                 // row-major [P][2I/32]
+            p.dgu_row_scales[slot * (twoI / 32) + gg] = uint8_t(Xg + 127);
+            p.dgu_row_scales[slot * (twoI / 32) + gu_] = uint8_t(Xu + 127);
+          }
         }
         // staging for the slot-axis groups
         v2::static_for<16>([&](auto Q) {
@@ -233,8 +240,9 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
         og[1] = uint4{cg[4], cg[5], cg[6], cg[7]};
         ou[0] = uint4{cu[0], cu[1], cu[2], cu[3]};
         ou[1] = uint4{cu[4], cu[5], cu[6], cu[7]};
-        p.dgu_tok_scales[i * (P / 32) + p0 / 32] = uint8_t(Xg + 127);
-        p.dgu_tok_scales[(p.I + i) * (P / 32) + p0 / 32] = uint8_t(Xu + 127);
+        const int64_t g32 = p0 / 32;   // pair-major [P/128][2I][4]
+        p.dgu_tok_scales[((g32 >> 2) * twoI + i) * 4 + (g32 & 3)] = uint8_t(Xg + 127);
+        p.dgu_tok_scales[((g32 >> 2) * twoI + p.I + i) * 4 + (g32 & 3)] = uint8_t(Xu + 127);
         if (p.has_bias) {
           atomicAdd(p.db1_acc + (e * 2 + 0) * p.I + i, sg);
           atomicAdd(p.db1_acc + (e * 2 + 1) * p.I + i, su);
@@ -269,7 +277,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
         uint4* oi = reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + p0);
         oi[0] = uint4{ci[0], ci[1], ci[2], ci[3]};
         oi[1] = uint4{ci[4], ci[5], ci[6], ci[7]};
-        p.inter_tok_scales[i * (P / 32) + p0 / 32] = uint8_t(Xi + 127);
+        p.inter_tok_scales[((g32 >> 2) * p.I + i) * 4 + (g32 & 3)] = uint8_t(Xi + 127);   // [P/128][I][4]
       });
       // the next fragment row overwrites the staging only after these reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -357,8 +365,10 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
   v3::ScaleDma<BM, BN> sd;
   v3::setup_rows(A, p.dgu_row_codes + sbase * twoI, tp.m0, p.B, twoI);
   v3::setup_rows(B, p.wgu_codes + e * p.H * twoI, tp.n0, p.H, twoI);
-  v3::setup_scales(sd, p.dgu_row_scales + sbase * (twoI / 32), tp.m0, p.B, twoI / 32,
-                   p.wgu_scales + e * p.H * (twoI / 32), tp.n0, p.H, twoI / 32);
+  // pair-major scales: dGU along I over all P slots; W_gate_up re-laid per expert
+  const int64_t P = p.N * p.B;
+  v3::setup_scales(sd, p.dgu_row_scales, sbase + tp.m0, P, P * (twoI / 32), p.wgu_scales + e * p.H * (twoI / 32),
+                   tp.n0, p.H, p.H * (twoI / 32));
   v16f acc[FM][FN];
   v3::mainloop<BM, BN, v3::kFp8, FG, FW>(A, B, &sd, int(twoI / v3::SK), v3::KMapPlain{}, smem, acc);
   p3_store<BM, BN>(p, tp, acc);

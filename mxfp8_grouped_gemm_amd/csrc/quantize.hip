@@ -10,6 +10,10 @@
 //                backward's dY^T / W^T / X^T and the MoE token-axis operands.
 // Group size, scale rule and rounding: P1 ("Blockwise MM Backward MXFP8 Kernel
 // API Reference": 32-element MXFP8 quantization groups).
+//
+// Scale layouts: row-major [rows][K/32] (one byte per group), or -- for
+// operands of the ring GEMM loop -- pair-major [K/128][rows][4], where word
+// (p, r) holds row r's four groups of K elements [128p, 128p + 128).
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
@@ -30,11 +34,12 @@ __device__ __forceinline__ uint32_t deq_pk(uint32_t codes, float scale) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <int FMT, bool DEQ>
+template <int FMT, bool DEQ, bool PAIRS>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict__ x,
                                                           uint2* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
-                                                          int64_t nchunks, uint4* __restrict__ deq) {
+                                                          int64_t nchunks, uint4* __restrict__ deq,
+                                                          int64_t rows, int64_t gpr) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
     const uint4 v = x[c];
@@ -56,7 +61,14 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict
       out[k >> 1] |= (lo | (hi << 8)) << (16 * (k & 1));
     }
     codes[c] = make_uint2(out[0], out[1]);
-    if ((c & 3) == 0) scales[c >> 2] = uint8_t(X + 127);
+    if ((c & 3) == 0) {
+      if (PAIRS) {   // group G = row * gpr + g  ->  word (g / 4, row), byte g % 4
+        const int64_t G = c >> 2, row = G / gpr, g = G - row * gpr;
+        scales[((g >> 2) * rows + row) * 4 + (g & 3)] = uint8_t(X + 127);
+      } else {
+        scales[c >> 2] = uint8_t(X + 127);
+      }
+    }
     if (DEQ) {
       const float sc = pow2_f32(X);
       deq[c] = make_uint4(deq_pk<FMT, false>(out[0], sc), deq_pk<FMT, true>(out[0], sc),
@@ -114,11 +126,12 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
 // Logical row r reads source row idx[r] (or r without an index); a source
 // outside [0, src_rows) contributes zeros (a padding slot).  With a row scale,
 // the staged value is bf16(fp32(scale[r] * v)).  Output: codes_t [cols][rows]
-// and scales_t [cols][rows/32]; rows % 32 == 0 and cols % 8 == 0.
+// and scales_t [cols][rows/32] (or pair-major [rows/128][cols][4] with PAIRS);
+// rows % 32 == 0 (% 128 with PAIRS) and cols % 8 == 0.
 constexpr int kTokRows = 128;
 constexpr int kTokCols = 128;
 
-template <int FMT, bool GATHER, bool ROWSCALE>
+template <int FMT, bool GATHER, bool ROWSCALE, bool PAIRS>
 __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restrict__ x,
                                                          int64_t src_rows, int64_t cols,
                                                          const int32_t* __restrict__ idx,
@@ -190,28 +203,64 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
   dst0[1] = make_uint4(p0[4], p0[5], p0[6], p0[7]);
   dst1[0] = make_uint4(p1[0], p1[1], p1[2], p1[3]);
   dst1[1] = make_uint4(p1[4], p1[5], p1[6], p1[7]);
-  scales_t[colA * (rows / 32) + row0 / 32] = uint8_t(X0 + 127);
-  scales_t[(colA + 1) * (rows / 32) + row0 / 32] = uint8_t(X1 + 127);
+  if (PAIRS) {
+    const int64_t g = row0 / 32;
+    scales_t[((g >> 2) * cols + colA) * 4 + (g & 3)] = uint8_t(X0 + 127);
+    scales_t[((g >> 2) * cols + colA + 1) * 4 + (g & 3)] = uint8_t(X1 + 127);
+  } else {
+    scales_t[colA * (rows / 32) + row0 / 32] = uint8_t(X0 + 127);
+    scales_t[(colA + 1) * (rows / 32) + row0 / 32] = uint8_t(X1 + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-major scales of `groups` matrices [rows][k/32] -> pair-major
+// [groups][k/128][rows][4]; k % 128 == 0.  One thread per 4-byte word, reads
+// coalesced.
+__global__ void __launch_bounds__(256) scales_to_pairs_kernel(const uint32_t* __restrict__ in, int64_t groups,
+                                                               int64_t rows, int64_t kp, uint32_t* __restrict__ out) {
+  const int64_t total = groups * rows * kp;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t p = i % kp, gr = i / kp, r = gr % rows, g = gr / rows;
+    out[(g * kp + p) * rows + r] = in[i];
+  }
 }
 
 // ---------------------------------------------------------------------------
 // host launchers
+template <int FMT>
+static void rows_dispatch(int blocks, hipStream_t st, const uint4* xs, uint2* cs, uint8_t* scales, int64_t nchunks,
+                          uint4* ds, int64_t rows, int64_t gpr, bool pairs) {
+  if (ds) quant_rows_kernel<FMT, true, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr);
+  else if (pairs) quant_rows_kernel<FMT, false, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr);
+  else quant_rows_kernel<FMT, false, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr);
+}
+
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, hipStream_t st, uint16_t* deq) {
+                             uint8_t* scales, hipStream_t st, uint16_t* deq, bool pairs) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
+  if (deq && pairs) return hipErrorInvalidValue;   // no caller needs both
   const int64_t want = (nchunks + 255) / 256;
   const int blocks = int(want < 65536 ? want : 65536);
   const uint4* xs = reinterpret_cast<const uint4*>(x);
   uint2* cs = reinterpret_cast<uint2*>(codes);
   uint4* ds = reinterpret_cast<uint4*>(deq);
-  if (fmt == kE4M3) {
-    if (deq) quant_rows_kernel<kE4M3, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
-    else quant_rows_kernel<kE4M3, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
-  } else {
-    if (deq) quant_rows_kernel<kE5M2, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
-    else quant_rows_kernel<kE5M2, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds);
-  }
+  if (fmt == kE4M3) rows_dispatch<kE4M3>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs);
+  else rows_dispatch<kE5M2>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_scales_to_pairs(const uint8_t* in, int64_t groups, int64_t rows, int64_t k, uint8_t* out,
+                                  hipStream_t st) {
+  if (k % 128) return hipErrorInvalidValue;
+  const int64_t total = groups * rows * (k / 128);
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int blocks = int(want < 65536 ? want : 65536);
+  scales_to_pairs_kernel<<<blocks, 256, 0, st>>>(reinterpret_cast<const uint32_t*>(in), groups, rows, k / 128,
+                                                 reinterpret_cast<uint32_t*>(out));
   return hipGetLastError();
 }
 
@@ -241,28 +290,32 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool PAIRS>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
                          const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct) {
   if (idx && rs)
-    quant_tok_kernel<FMT, true, true><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, true, true, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
   else if (idx)
-    quant_tok_kernel<FMT, true, false><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, true, false, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
   else if (rs)
-    quant_tok_kernel<FMT, false, true><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, false, true, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
   else
-    quant_tok_kernel<FMT, false, false><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, false, false, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
 }
 
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st) {
+                            uint8_t* scales_t, hipStream_t st, bool pairs) {
   if (rows == 0 || cols == 0) return hipSuccess;
+  if (pairs && rows % 128) return hipErrorInvalidValue;
   dim3 grid(unsigned((cols + kTokCols - 1) / kTokCols), unsigned((rows + kTokRows - 1) / kTokRows));
-  if (fmt == kE4M3)
-    tok_dispatch<kE4M3>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
-  else
-    tok_dispatch<kE5M2>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+  if (fmt == kE4M3) {
+    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+  } else {
+    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+  }
   return hipGetLastError();
 }
 

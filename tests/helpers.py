@@ -50,3 +50,10 @@ def moe_problem(cfg: S.MoeConfig, nthreads: int = 0, N=None):
                           tpid=tpid, b2e=b2e, dy=bits["dy"], ckpt=bits["ckpt"], b2=bits["b2"],
                           affinity_on=cfg.affinity_on, has_bias=int(cfg.has_bias), nthreads=nthreads)
     return p, dict(topk=topk, bits=bits)
+
+
+def pairs_to_rows(raw, rows: int, k: int) -> np.ndarray:
+    """Scale bytes stored pair-major, [k/128][rows][4] (word (p, r) = row r's
+    bytes for elements [128p, 128p+128)), as row-major [rows][k/32]."""
+    a = np.asarray(raw, dtype=np.uint8).reshape(k // 128, rows, 4)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(rows, k // 32))

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import bf, rel_fro
+from helpers import bf, pairs_to_rows, rel_fro
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -44,9 +44,15 @@ def test_dense_small_full_parity(M, N, K):
             oracle.quantize(np.ascontiguousarray(w_b.T), 1, oracle.E4M3),
             oracle.quantize(np.ascontiguousarray(dy_b.T), 1, oracle.E5M2),
             oracle.quantize(np.ascontiguousarray(x_b.T), 1, oracle.E4M3)]
-    for (co, so), (c, s) in zip(regs, want):
+    # scales of a GEMM whose contraction (N for [0],[1], M for [2],[3]) is a
+    # multiple of 128 are stored pair-major
+    kdim = [N, N, M, M]
+    for (co, so), (c, s), kk in zip(regs, want, kdim):
         assert np.array_equal(wsh[co:co + c.size], c.ravel())
-        assert np.array_equal(wsh[so:so + s.size], s.ravel())
+        got = wsh[so:so + s.size]
+        if kk % 128 == 0:
+            got = pairs_to_rows(got, s.shape[0], kk)
+        assert np.array_equal(got.ravel(), s.ravel())
 
 
 @pytest.mark.parametrize("fdy,fw,fx", [(0, 0, 0), (1, 1, 1), (0, 1, 1), (1, 0, 1)])

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import bf, rel_fro
+from helpers import bf, pairs_to_rows, rel_fro
 from moe_gpu_common import gpu_problem, host, oracle_problem
 
 pytestmark = pytest.mark.gpu
@@ -64,7 +64,9 @@ def test_moe_small_full_parity(name):
                                   (oracle.TOK_GY, "gy_tok_codes", "gy_tok_scales")):
         c, s = oracle.moe_token_operand(p, which)
         assert np.array_equal(ws[L[name_c]:L[name_c] + H * P], c.ravel()), name_c
-        assert np.array_equal(ws[L[name_s]:L[name_s] + H * P // 32], s.ravel()), name_s
+        # token-axis scales are pair-major ([P/128][H][4])
+        got = pairs_to_rows(ws[L[name_s]:L[name_s] + H * P // 32], H, P)
+        assert np.array_equal(got, s.reshape(H, P // 32)), name_s
     # the intermediate operand: silu is evaluated in fp32 on the GPU and in fp64 by the
     # oracle, so a rare bf16 rounding may differ; codes must agree almost everywhere
     c, s = oracle.moe_token_operand(p, oracle.TOK_INTER)
