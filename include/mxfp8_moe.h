@@ -183,9 +183,12 @@ typedef struct {
 
 /* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised
  * operands can be read back from them after a call:
- *   dy_codes/dy_scales        [T,H] / [T,H/32]        dY along H (Phase 1)
+ *   dy_codes/dy_scales        [T,H] / P4[H,T]         dY along H (Phase 1); scales
+ *                                                     [T,H/32] when H % 128 != 0
  *   dy_deq                    [T,H] bf16              exact values of those codes
+ *                                                     (H % 128 != 0; else empty)
  *   wd_deq                    [E,I,H] bf16            exact values of the W_down codes
+ *                                                     (H % 128 != 0; else empty)
  *   x_tok_codes/scales        [H,P] / P4[P,H]         X along slots (Phase 2), P = N*B
  *   gy_tok_codes/scales       [H,P] / P4[P,H]         a*dY (on H) or dY (on I), Phase 4
  *   inter_tok_codes/scales    [I,P] / P4[P,I]         inter (on H) or a*inter (on I)
@@ -194,6 +197,8 @@ typedef struct {
  *   dgu_tok_codes/scales      [2I,P] / P4[P,2I]       [dGate;dUp] along slots (Phase 2)
  *   wgu_scales_pairs          P4 of gate_up_scales per expert, [E][2I/128][H][4]
  *                                                     (written when 2I % 128 == 0)
+ *   wd_scales_pairs           P4 of down_scales per expert, [E][H/128][I][4]
+ *                                                     (H % 128 == 0; else empty)
  *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
@@ -205,7 +210,7 @@ typedef struct {
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, wgu_scales_pairs, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 
@@ -229,7 +234,8 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
  * earlier ones wrote there).  Running stages in order 0..MOE_BWD_NUM_STAGES-1
  * is exactly one full call.  Stages:
  *   0 setup (zero accumulators, slot routing info, per-expert block lists)
- *   1 quantise dY along H         2 gather-quantise X and a*dY (or dY) along slots
+ *   1 quantise dY along H (and lay out W_down's scales for Phase 1)
+ *   2 gather-quantise X and a*dY (or dY) along slots
  *   3 bias reductions (has_bias only)
  *   4 Phase 1 + epilogue (also the intermediate quantised along slots)
  *   5 Phase 3 (dX scatter-add)    6 Phase 2 (dW_gate_up)       7 Phase 4 (dW_down)

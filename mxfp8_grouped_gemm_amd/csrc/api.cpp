@@ -187,10 +187,11 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
     field = o;
     o = up256(o + size_t(bytes));
   };
+  const bool h_pairs = H % 128 == 0;   // Phase 1 reads the codes (else their bf16 values)
   put(L->dy_codes, T * H);
   put(L->dy_scales, T * H / 32);
-  put(L->dy_deq, T * H * 2);
-  put(L->wd_deq, E * I * H * 2);
+  put(L->dy_deq, h_pairs ? 0 : T * H * 2);
+  put(L->wd_deq, h_pairs ? 0 : E * I * H * 2);
   put(L->x_tok_codes, H * P);
   put(L->x_tok_scales, H * P / 32);
   put(L->gy_tok_codes, H * P);
@@ -202,6 +203,7 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->dgu_tok_codes, 2 * I * P);
   put(L->dgu_tok_scales, 2 * I * P / 32);
   put(L->wgu_scales_pairs, E * H * 2 * I / 32);
+  put(L->wd_scales_pairs, h_pairs ? E * I * H / 32 : 0);
   put(L->dx_acc, T * H * 4);
   put(L->daff_slot, P * 4);
   put(L->db1_acc, E * 2 * I * 4);
@@ -304,14 +306,20 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
                              slot_tok, slot_aff, flag, boff, blist, st),
        "slot setup");
   stage = 1;
-  // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later)
+  // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later).
+  // H % 128 == 0: Phase 1 streams the codes with pair-major scales (dY's written so,
+  // W_down's re-laid); otherwise it reads their exact bf16 values.
+  const bool h_pairs = H % 128 == 0;
   STEP(mx::launch_quant_rows(a->output_hidden_states_grad, T, H, a->fmt_grad, at(L.dy_codes), at(L.dy_scales), st,
-                             reinterpret_cast<uint16_t*>(at(L.dy_deq))),
+                             h_pairs ? nullptr : reinterpret_cast<uint16_t*>(at(L.dy_deq)), h_pairs),
        "quantize dY");
-  // Phase-1 operands in bf16: the exact values of the MX codes (see the Phase-1 kernel)
-  STEP(mx::launch_dequant_rows(a->down_codes, a->down_scales, E * I, H, a->fmt_weight,
-                               reinterpret_cast<uint16_t*>(at(L.wd_deq)), st),
-       "dequantize W_down");
+  if (h_pairs) {
+    STEP(mx::launch_scales_to_pairs(a->down_scales, E, I, H, at(L.wd_scales_pairs), st), "W_down scales to pairs");
+  } else {
+    STEP(mx::launch_dequant_rows(a->down_codes, a->down_scales, E * I, H, a->fmt_weight,
+                                 reinterpret_cast<uint16_t*>(at(L.wd_deq)), st),
+         "dequantize W_down");
+  }
   // Phase 3 on the ring loop reads W_gate_up's scales pair-major
   const bool gu_pairs = (2 * I) % 128 == 0;
   if (gu_pairs)
@@ -334,8 +342,13 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   stage = 4;
   // Phase 1 + fused SwiGLU-backward epilogue (also writes the intermediate operand)
   mx::Phase1Args p1{};
-  p1.wd_deq = reinterpret_cast<const uint16_t*>(at(L.wd_deq));
-  p1.dy_deq = reinterpret_cast<const uint16_t*>(at(L.dy_deq));
+  if (h_pairs) {
+    p1.wd_codes = a->down_codes; p1.wd_scales = at(L.wd_scales_pairs);
+    p1.dy_codes = at(L.dy_codes); p1.dy_scales = at(L.dy_scales);
+  } else {
+    p1.wd_deq = reinterpret_cast<const uint16_t*>(at(L.wd_deq));
+    p1.dy_deq = reinterpret_cast<const uint16_t*>(at(L.dy_deq));
+  }
   p1.slot_tok = slot_tok; p1.slot_aff = slot_aff; p1.b2e = a->block_to_expert; p1.flag = flag;
   p1.ckpt = a->gate_up_proj_act_checkpoint_T;
   p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
@@ -345,7 +358,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
   p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias; p1.fmt_act = a->fmt_act;
   p1.dgu_row_pairs = gu_pairs;
-  STEP(mx::launch_phase1(p1, a->fmt_grad, st), "phase 1");
+  STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_weight, st), "phase 1");
   stage = 5;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};

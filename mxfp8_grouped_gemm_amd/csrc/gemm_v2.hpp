@@ -34,6 +34,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kFp8 = 0;
 constexpr int kBf16 = 1;
+constexpr int kFp8Bf16 = 2;   // fp8 codes + scales in memory, exact bf16 values on the MFMA (ring loop only)
 constexpr int BK = 128;         // bytes of K per stage
 constexpr int kThreads = 256;
 constexpr uint32_t kOOB = 0x80000000u;   // offset returned as zeros (>= num_records)

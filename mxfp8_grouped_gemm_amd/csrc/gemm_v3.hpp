@@ -1,9 +1,14 @@
 // gemm_v3.hpp -- MX GEMM main loop for gfx950 with a four-stage LDS ring.
 //
-// Same contraction and element modes as gemm_v2.hpp (C[m][n] = sum_k A[m][k] *
-// B[n][k]; fp8 codes with E8M0 scales on v_mfma_scale_f32_32x32x64_f8f6f4, or
-// exact bf16 values on v_mfma_f32_32x32x16_bf16), for operands whose code rows
-// are 128-byte aligned and whose K is a multiple of 128 bytes.
+// C[m][n] = sum_k A[m][k] * B[n][k] for operands whose code rows are 128-byte
+// aligned and whose K is a multiple of 128 bytes, in three element modes:
+//   kFp8    : fp8 codes + E8M0 scales on v_mfma_scale_f32_32x32x64_f8f6f4;
+//   kBf16   : bf16 values on v_mfma_f32_32x32x16_bf16;
+//   kFp8Bf16: fp8 codes + E8M0 scales moved like kFp8, converted in registers
+//             to their exact bf16 values (v_cvt_scalef32_pk_bf16_fp8/bf8: a
+//             code times a power of two has at most 4 significant bits) and
+//             reduced on the bf16 MFMA, whose accumulation is exact enough
+//             that results requantised afterwards round as an exact sum would.
 //
 // Why a ring: a CU streams L2 -> LDS at ~55 B/clk with buffer_load ... lds,
 // but a stage can only start when the slowest of its ~500 cache lines has
@@ -46,6 +51,7 @@ using v2::v8bf;
 using v2::v8i;
 using v2::kBf16;
 using v2::kFp8;
+using v2::kFp8Bf16;
 
 constexpr int SK = 64;          // bytes of K per stage
 constexpr int NBUF = 4;         // ring depth (stages in LDS)
@@ -163,11 +169,12 @@ struct ScaleDma {
 };
 
 // a_scales / b_scales: pair-major scale arrays of the whole operands (a_rows /
-// b_rows rows, a_bytes / b_bytes bytes); the tile covers rows a_row0.. / b_row0..
-template <int BM, int BN>
-__device__ __forceinline__ void setup_scales(ScaleDma<BM, BN>& sd, const uint8_t* a_scales, int64_t a_row0,
-                                             int64_t a_rows, int64_t a_bytes, const uint8_t* b_scales,
-                                             int64_t b_row0, int64_t b_rows, int64_t b_bytes) {
+// b_rows rows, a_bytes / b_bytes bytes); tile row r of A reads scale row
+// a_row(r), of B b_row(r) (negative: zeros).
+template <int BM, int BN, class ARow, class BRow>
+__device__ __forceinline__ void setup_scales_map(ScaleDma<BM, BN>& sd, const uint8_t* a_scales, int64_t a_rows,
+                                                 int64_t a_bytes, const ARow& a_row, const uint8_t* b_scales,
+                                                 int64_t b_rows, int64_t b_bytes, const BRow& b_row) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const Buf ba = v2::make_rsrc(a_scales, uint32_t(a_bytes));
   const Buf bb = v2::make_rsrc(b_scales, uint32_t(b_bytes));
@@ -175,14 +182,14 @@ __device__ __forceinline__ void setup_scales(ScaleDma<BM, BN>& sd, const uint8_t
   for (int i = 0; i < ScaleDma<BM, BN>::NS; ++i) {
     const int c = wave + 4 * i;
     if (c < BM / 64) {
-      const int64_t r = a_row0 + 64 * c + lane;
+      const int64_t r = a_row(64 * c + lane);
       sd.buf[i] = ba;
-      sd.off[i] = r < a_rows ? uint32_t(r * 4) : kOOB;
+      sd.off[i] = r >= 0 ? uint32_t(r * 4) : kOOB;
       sd.pstride[i] = uint32_t(a_rows * 4);
     } else if (c < (BM + BN) / 64) {
-      const int64_t r = b_row0 + 64 * (c - BM / 64) + lane;
+      const int64_t r = b_row(64 * (c - BM / 64) + lane);
       sd.buf[i] = bb;
-      sd.off[i] = r < b_rows ? uint32_t(r * 4) : kOOB;
+      sd.off[i] = r >= 0 ? uint32_t(r * 4) : kOOB;
       sd.pstride[i] = uint32_t(b_rows * 4);
     } else {
       sd.buf[i] = ba;
@@ -190,6 +197,16 @@ __device__ __forceinline__ void setup_scales(ScaleDma<BM, BN>& sd, const uint8_t
       sd.pstride[i] = 0;
     }
   }
+}
+
+// Both operands as contiguous row ranges: the tile covers rows a_row0.. / b_row0..
+template <int BM, int BN>
+__device__ __forceinline__ void setup_scales(ScaleDma<BM, BN>& sd, const uint8_t* a_scales, int64_t a_row0,
+                                             int64_t a_rows, int64_t a_bytes, const uint8_t* b_scales,
+                                             int64_t b_row0, int64_t b_rows, int64_t b_bytes) {
+  setup_scales_map(
+      sd, a_scales, a_rows, a_bytes, [&](int r) -> int64_t { return a_row0 + r < a_rows ? a_row0 + r : -1; },
+      b_scales, b_rows, b_bytes, [&](int r) -> int64_t { return b_row0 + r < b_rows ? b_row0 + r : -1; });
 }
 
 // K map with 64-byte stages.  Plain: [0, K).  Grouped: the K columns of a
@@ -259,7 +276,8 @@ struct Ring {
   static constexpr int NCI = (BM + BN) / 64;               // code DMA instructions per wave per stage
   static constexpr int NS = ScaleDma<BM, BN>::NS;          // scale DMA instructions per wave per pair
   static constexpr int VM_STAGE = NCI;
-  static constexpr int VM_PAIR_SCALES = ELEM == kFp8 ? NS : 0;
+  static constexpr bool SCALED = ELEM != kBf16;            // codes + scales in memory
+  static constexpr int VM_PAIR_SCALES = SCALED ? NS : 0;
   using T = Tile<BM, BN, KMap>;
 
   uint8_t* smem;
@@ -280,7 +298,7 @@ struct Ring {
     for (int j = 0; j < BM / 64; ++j) dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * j) * SK, x.A.off[j], kc);
 #pragma unroll
     for (int j = 0; j < BN / 64; ++j) dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * j) * SK, x.B.off[j], kc);
-    if (ELEM == kFp8 && (pos & 1) == 0) {
+    if (SCALED && (pos & 1) == 0) {
       const uint32_t ss = lds0 + NBUF * CS + (((base + uint32_t(pos)) >> 1) & (NBUF - 1)) * SSB;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -314,19 +332,42 @@ struct Ring {
     const int h = lane >> 5, r = lane & 31;
     const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
     const uint8_t* cs = smem + ((base + uint32_t(t)) & (NBUF - 1)) * CS;
+    if (ELEM == kFp8Bf16) {
+      // bf16 MFMA layout: step c (elements 16c..16c+15) gives lane half h the
+      // 8 codes 16c + 8h ..; set[0] = steps 0, 1, set[1] = steps 2, 3
+      auto rd = [&](const uint8_t* rowp, int row, uint4(&f)[2]) {
+        const uint2 x0 = *reinterpret_cast<const uint2*>(rowp + 16 * (0 ^ swz(row)) + 8 * h);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(rowp + 16 * (1 ^ swz(row)) + 8 * h);
+        const uint2 x2 = *reinterpret_cast<const uint2*>(rowp + 16 * (2 ^ swz(row)) + 8 * h);
+        const uint2 x3 = *reinterpret_cast<const uint2*>(rowp + 16 * (3 ^ swz(row)) + 8 * h);
+        f[0] = uint4{x0.x, x0.y, x1.x, x1.y};
+        f[1] = uint4{x2.x, x2.y, x3.x, x3.y};
+      };
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wrow + 32 * i + r;
-      fa[P][i][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
-      fa[P][i][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
-    }
+      for (int i = 0; i < FM; ++i) {
+        const int row = wrow + 32 * i + r;
+        rd(cs + row * SK, row, fa[P][i]);
+      }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wcol + 32 * j + r;
-      fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
-      fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
+      for (int j = 0; j < FN; ++j) {
+        const int row = wcol + 32 * j + r;
+        rd(cs + (BM + row) * SK, row, fb[P][j]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wrow + 32 * i + r;
+        fa[P][i][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
+        fa[P][i][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wcol + 32 * j + r;
+        fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
+        fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
+      }
     }
-    if (ELEM == kFp8) {
+    if (SCALED) {
       const uint8_t* ss = smem + NBUF * CS + (((base + uint32_t(t)) >> 1) & (NBUF - 1)) * SSB;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -341,10 +382,46 @@ struct Ring {
     }
   }
 
+  // kFp8Bf16: the exact bf16 values of 8 codes (one 16-element step of a lane)
+  // with scale byte sc (2^(sc - 127); byte 0 is 2^-127, a subnormal float)
+  template <int F>
+  __device__ __forceinline__ static v8bf to_bf16(uint32_t w0, uint32_t w1, uint32_t sc) {
+    const float s = sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u);
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    auto cv = [&](uint32_t w, auto HI) -> uint32_t {
+      if (F == 0) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, decltype(HI)::value));
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, s, decltype(HI)::value));
+    };
+    return __builtin_bit_cast(v8bf, u4v{cv(w0, std::false_type{}), cv(w0, std::true_type{}), cv(w1, std::false_type{}),
+                                        cv(w1, std::true_type{})});
+  }
+
   // MFMAs of the stage in set P (stage parity P = scale byte within the pair)
   template <int P>
   __device__ __forceinline__ void compute(v16f (&acc)[FM][FN]) const {
     const int h = (threadIdx.x & 63) >> 5;
+    if (ELEM == kFp8Bf16) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int sh = 8 * (2 * P + (c >> 1));   // scale byte of this step's 32-element group
+        v8bf av[FM], bv[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const uint4& f = fa[P][i][c >> 1];
+          av[i] = to_bf16<FA>((c & 1) ? f.z : f.x, (c & 1) ? f.w : f.y, (sa[P][i] >> sh) & 0xffu);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint4& f = fb[P][j][c >> 1];
+          bv[j] = to_bf16<FB>((c & 1) ? f.z : f.x, (c & 1) ? f.w : f.y, (sb[P][j] >> sh) & 0xffu);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int H = 0; H < 2; ++H) {
       if (ELEM == kFp8) {
@@ -381,12 +458,13 @@ struct Ring {
     }
     compute<P>(acc);
     if (READ) {
-      constexpr int NMF = FM * FN * (ELEM == kFp8 ? 1 : 2);                  // MFMAs of a stage
-      constexpr int NRD = 2 * (FM + FN) + (ELEM == kFp8 ? FM + FN : 0);      // LDS reads of a stage
+      constexpr int NMF = FM * FN * (ELEM == kFp8 ? 1 : (ELEM == kBf16 ? 2 : 4));   // MFMAs of a stage
+      constexpr int NRD = (ELEM == kFp8Bf16 ? 4 : 2) * (FM + FN) + (SCALED ? FM + FN : 0);   // LDS reads
       constexpr int PER = (NRD + NMF - 1) / NMF;
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);   // LDS reads
+        if (ELEM == kFp8Bf16) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU (conversions)
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
       }
     }
@@ -464,7 +542,7 @@ template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
 __device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const ScaleDma<BM, BN>* sd, int nstages,
                                          const KMap& kmap, uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
   Tile<BM, BN, KMap> cur{A, B, {}, kmap, nstages};
-  if (ELEM == kFp8) cur.sd = *sd;
+  if (ELEM != kBf16) cur.sd = *sd;
   Tile<BM, BN, KMap> none = cur;
   none.nstages = 0;
   Ring<BM, BN, ELEM, FA, FB, KMap> ring{smem, 0u};

@@ -66,8 +66,14 @@ hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, 
 
 // moe_gemm.hip
 struct Phase1Args {
-  const uint16_t* wd_deq;       // [E][I][H] bf16: dequantised W_down (exact)
-  const uint16_t* dy_deq;       // [T][H] bf16: dequantised Q_H(dY) (exact)
+  // H % 128 == 0: the MX operands themselves, scales pair-major
+  const uint8_t* wd_codes;      // [E][I][H]
+  const uint8_t* wd_scales;     // [E][H/128][I][4]
+  const uint8_t* dy_codes;      // [T][H]: Q_H(dY)
+  const uint8_t* dy_scales;     // [H/128][T][4]
+  // otherwise their exact bf16 values
+  const uint16_t* wd_deq;       // [E][I][H] bf16: dequantised W_down
+  const uint16_t* dy_deq;       // [T][H] bf16: dequantised Q_H(dY)
   const int32_t* slot_tok;      // [P]
   const float* slot_aff;        // [P]
   const int32_t* b2e;           // [N]
@@ -88,7 +94,7 @@ struct Phase1Args {
   int dgu_row_pairs;            // 1: dGU along I feeds the ring loop (2I % 128 == 0): pair-major scales
   int tiles_m, tiles_n;
 };
-hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, hipStream_t st);
+hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, int fmt_weight, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]

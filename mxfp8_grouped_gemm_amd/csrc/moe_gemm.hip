@@ -51,9 +51,10 @@ struct KMapPlain {
 //       slot-axis MX groups (dGU and the intermediate operand of Phase 4) are
 //       reduced and encoded in registers and stored as 32-byte runs.
 // The LDS of the main loop is reused for staging after a barrier.
-template <int BM, int BN, int FG, bool ON_I, bool GENERIC>
+template <int BM, int BN, int FG, int FW, bool ON_I, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
-  // GENERIC: 2H not a multiple of 128 bytes (v2 loop); otherwise the ring (v3 loop)
+  // GENERIC: H not a multiple of 128 (v2 loop on the bf16 values); otherwise the
+  // ring (v3 loop) on the codes: fp8 in memory and LDS, exact bf16 on the MFMA
   constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   constexpr int FM = BM / 64, FN = BN / 64;
@@ -87,14 +88,14 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   const int64_t e = p.b2e[b];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // A: dequantised W_down[e] rows i; B: dequantised dY rows gathered by token
-  const uint8_t* wd = reinterpret_cast<const uint8_t*>(p.wd_deq + e * p.I * p.H);
-  const uint8_t* dyd = reinterpret_cast<const uint8_t*>(p.dy_deq);
   const int32_t* st = p.slot_tok + sbase;
   const int64_t B_ = p.B;
   auto tok_of = [&](int r) -> int64_t { const int64_t s = n0 + r; return s < B_ ? int64_t(st[s]) : -1; };
   v16f acc[FM][FN];
   if constexpr (GENERIC) {
+    // A: dequantised W_down[e] rows i; B: dequantised dY rows gathered by token
+    const uint8_t* wd = reinterpret_cast<const uint8_t*>(p.wd_deq + e * p.I * p.H);
+    const uint8_t* dyd = reinterpret_cast<const uint8_t*>(p.dy_deq);
     v2::Operand<BM, FM> A;
     v2::Operand<BN, FN> B;
     v2::setup_rows(A, wd, nullptr, m0, p.I, 2 * p.H, 0, (wave >> 1) * (BM / 2));
@@ -102,12 +103,17 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
     v2::mainloop<BM, BN, v2::kBf16, 0, 0, true>(A, B, int((2 * p.H + v2::BK - 1) / v2::BK), KMapPlain{2 * p.H},
                                                  smem, acc);
   } else {
+    // A: W_down[e] codes rows i; B: Q_H(dY) codes rows gathered by token
     v3::Op<BM> A;
     v3::Op<BN> B;
-    v3::setup_rows(A, wd, m0, p.I, 2 * p.H);
-    v3::setup_gather(B, dyd, p.T, 2 * p.H, tok_of);
-    v3::mainloop<BM, BN, v3::kBf16, 0, 0>(A, B, static_cast<const v3::ScaleDma<BM, BN>*>(nullptr),
-                                           int(2 * p.H / v3::SK), v3::KMapPlain{}, smem, acc);
+    v3::setup_rows(A, p.wd_codes + e * p.I * p.H, m0, p.I, p.H);
+    v3::setup_gather(B, p.dy_codes, p.T, p.H, tok_of);
+    v3::ScaleDma<BM, BN> sd;
+    const int64_t I_ = p.I;
+    v3::setup_scales_map(
+        sd, p.wd_scales + e * p.I * (p.H / 32), p.I, p.I * (p.H / 32),
+        [&](int r) -> int64_t { return m0 + r < I_ ? m0 + r : -1; }, p.dy_scales, p.T, p.T * (p.H / 32), tok_of);
+    v3::mainloop<BM, BN, v3::kFp8Bf16, FW, FG>(A, B, &sd, int(p.H / v3::SK), v3::KMapPlain{}, smem, acc);
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -375,30 +381,41 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
 }
 
 // ---------------------------------------------------------------------------
+template <int BM, int BN, bool G, int FG, int FW>
+static void phase1_go(const Phase1Args& p, unsigned blocks, hipStream_t st) {
+  if (p.affinity_on_i) phase1_kernel<BM, BN, FG, FW, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  else phase1_kernel<BM, BN, FG, FW, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+}
+
 template <int BM, int BN, bool G>
-static hipError_t phase1_launch(Phase1Args p, int fg, hipStream_t st) {
+static hipError_t phase1_launch(Phase1Args p, int fg, int fw, hipStream_t st) {
   p.tiles_m = int((p.I + BM - 1) / BM);
   p.tiles_n = int((p.B + BN - 1) / BN);
-  const unsigned blocks = unsigned(int64_t(p.tiles_m) * p.tiles_n * p.N);
-  const bool on_i = p.affinity_on_i != 0;
-  if (fg == kE4M3) {
-    if (on_i) phase1_kernel<BM, BN, kE4M3, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
-    else phase1_kernel<BM, BN, kE4M3, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+  const int64_t blocks = int64_t(p.tiles_m) * p.tiles_n * p.N;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const unsigned grid = unsigned(blocks);
+  if (G) {   // the bf16 values carry no format
+    if (fg == kE4M3) phase1_go<BM, BN, G, kE4M3, kE4M3>(p, grid, st);
+    else phase1_go<BM, BN, G, kE5M2, kE4M3>(p, grid, st);
+  } else if (fg == kE4M3) {
+    if (fw == kE4M3) phase1_go<BM, BN, G, kE4M3, kE4M3>(p, grid, st);
+    else phase1_go<BM, BN, G, kE4M3, kE5M2>(p, grid, st);
   } else {
-    if (on_i) phase1_kernel<BM, BN, kE5M2, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
-    else phase1_kernel<BM, BN, kE5M2, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
+    if (fw == kE4M3) phase1_go<BM, BN, G, kE5M2, kE4M3>(p, grid, st);
+    else phase1_go<BM, BN, G, kE5M2, kE5M2>(p, grid, st);
   }
   return hipGetLastError();
 }
 
 // Tile shape: 256 along a dimension when it is at least 256, else 128.  The
 // block size B is a power of two >= 128, so every tile lies inside one block.
-// 2H not a multiple of 128 bytes (a ragged last K stage): the v2 loop, 128 x 128.
-hipError_t launch_phase1(const Phase1Args& p, int fg, hipStream_t st) {
-  if ((2 * p.H) % v2::BK != 0) return phase1_launch<128, 128, true>(p, fg, st);
-  if (p.I >= 256 && p.B >= 256) return phase1_launch<256, 256, false>(p, fg, st);
-  if (p.I >= 256) return phase1_launch<256, 128, false>(p, fg, st);
-  return phase1_launch<128, 128, false>(p, fg, st);
+// H not a multiple of 128 (a ragged last K stage, scale rows not in whole
+// pairs): the v2 loop on bf16 values, 128 x 128.
+hipError_t launch_phase1(const Phase1Args& p, int fg, int fw, hipStream_t st) {
+  if (p.H % 128 != 0) return phase1_launch<128, 128, true>(p, fg, fw, st);
+  if (p.I >= 256 && p.B >= 256) return phase1_launch<256, 256, false>(p, fg, fw, st);
+  if (p.I >= 256) return phase1_launch<256, 128, false>(p, fg, fw, st);
+  return phase1_launch<128, 128, false>(p, fg, fw, st);
 }
 
 template <int BM, int BN>

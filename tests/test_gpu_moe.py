@@ -59,7 +59,10 @@ def test_moe_small_full_parity(name):
     L = op.layout
     c, s = oracle.quantize(p.dy, 1, oracle.E5M2)
     assert np.array_equal(ws[L["dy_codes"]:L["dy_codes"] + T * H], c.ravel())
-    assert np.array_equal(ws[L["dy_scales"]:L["dy_scales"] + T * H // 32], s.ravel())
+    got = ws[L["dy_scales"]:L["dy_scales"] + T * H // 32]
+    if H % 128 == 0:   # pair-major ([H/128][T][4]) when Phase 1 streams the codes
+        got = pairs_to_rows(got, T, H)
+    assert np.array_equal(got.ravel(), s.ravel())
     for which, name_c, name_s in ((oracle.TOK_X, "x_tok_codes", "x_tok_scales"),
                                   (oracle.TOK_GY, "gy_tok_codes", "gy_tok_scales")):
         c, s = oracle.moe_token_operand(p, which)
