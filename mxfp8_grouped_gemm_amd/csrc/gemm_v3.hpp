@@ -325,47 +325,31 @@ struct Ring {
   uint32_t sa[2][FM], sb[2][FN];
 
   // fragments and raw scale words of stage t into set P (the words are shifted
-  // to this lane's group where they are used, so nothing here waits on the reads)
+  // to this lane's group where they are used, so nothing here waits on the reads).
+  // Lane half h takes 16-byte chunks h and 2 + h of each row.  The fp8 MFMA
+  // reads them as K positions of its 64-element step; in kFp8Bf16 mode the
+  // chunks are the operands of four bf16 steps: chunk h's low and high 8 bytes
+  // are this lane half's elements of steps 0 and 1, chunk 2 + h's of steps 2
+  // and 3.  A and B are permuted alike, so each step still pairs equal K
+  // indices, and a chunk lies inside one 32-element scale group (h: the
+  // stage's first group, 2 + h: its second).
   template <int P>
   __device__ __forceinline__ void read(int t) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = lane >> 5, r = lane & 31;
     const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
     const uint8_t* cs = smem + ((base + uint32_t(t)) & (NBUF - 1)) * CS;
-    if (ELEM == kFp8Bf16) {
-      // bf16 MFMA layout: step c (elements 16c..16c+15) gives lane half h the
-      // 8 codes 16c + 8h ..; set[0] = steps 0, 1, set[1] = steps 2, 3
-      auto rd = [&](const uint8_t* rowp, int row, uint4(&f)[2]) {
-        const uint2 x0 = *reinterpret_cast<const uint2*>(rowp + 16 * (0 ^ swz(row)) + 8 * h);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(rowp + 16 * (1 ^ swz(row)) + 8 * h);
-        const uint2 x2 = *reinterpret_cast<const uint2*>(rowp + 16 * (2 ^ swz(row)) + 8 * h);
-        const uint2 x3 = *reinterpret_cast<const uint2*>(rowp + 16 * (3 ^ swz(row)) + 8 * h);
-        f[0] = uint4{x0.x, x0.y, x1.x, x1.y};
-        f[1] = uint4{x2.x, x2.y, x3.x, x3.y};
-      };
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wrow + 32 * i + r;
-        rd(cs + row * SK, row, fa[P][i]);
-      }
+    for (int i = 0; i < FM; ++i) {
+      const int row = wrow + 32 * i + r;
+      fa[P][i][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
+      fa[P][i][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
+    }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wcol + 32 * j + r;
-        rd(cs + (BM + row) * SK, row, fb[P][j]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wrow + 32 * i + r;
-        fa[P][i][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
-        fa[P][i][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wcol + 32 * j + r;
-        fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
-        fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
-      }
+    for (int j = 0; j < FN; ++j) {
+      const int row = wcol + 32 * j + r;
+      fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
+      fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
     }
     if (SCALED) {
       const uint8_t* ss = smem + NBUF * CS + (((base + uint32_t(t)) >> 1) & (NBUF - 1)) * SSB;
@@ -383,10 +367,14 @@ struct Ring {
   }
 
   // kFp8Bf16: the exact bf16 values of 8 codes (one 16-element step of a lane)
-  // with scale byte sc (2^(sc - 127); byte 0 is 2^-127, a subnormal float)
+  // with E8M0 scale byte sc.  The converter takes the exponent field of its
+  // fp32 scale operand as the E8M0 byte (2^(sc - 127), byte 0 included: the
+  // float 0.0 scales by 2^-127), so the byte shifted into that field is the
+  // operand.  Checked exhaustively: every code of both formats times every
+  // scale byte 0..254 gives the exact product rounded to bf16.
   template <int F>
   __device__ __forceinline__ static v8bf to_bf16(uint32_t w0, uint32_t w1, uint32_t sc) {
-    const float s = sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u);
+    const float s = __uint_as_float(sc << 23);
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
     auto cv = [&](uint32_t w, auto HI) -> uint32_t {
       if (F == 0) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, decltype(HI)::value));
@@ -459,7 +447,7 @@ struct Ring {
     compute<P>(acc);
     if (READ) {
       constexpr int NMF = FM * FN * (ELEM == kFp8 ? 1 : (ELEM == kBf16 ? 2 : 4));   // MFMAs of a stage
-      constexpr int NRD = (ELEM == kFp8Bf16 ? 4 : 2) * (FM + FN) + (SCALED ? FM + FN : 0);   // LDS reads
+      constexpr int NRD = 2 * (FM + FN) + (SCALED ? FM + FN : 0);   // LDS reads of a stage
       constexpr int PER = (NRD + NMF - 1) / NMF;
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {
