@@ -164,6 +164,17 @@ __device__ __forceinline__ v8i as_v8i(const uint4& lo, const uint4& hi) {
   r[4] = int(hi.x); r[5] = int(hi.y); r[6] = int(hi.z); r[7] = int(hi.w);
   return r;
 }
+// K map over one contiguous byte range [0, K): stage s covers bytes s*BK ..,
+// the last one possibly ragged.
+struct KMapPlain {
+  int64_t K;   // bytes
+  __device__ __forceinline__ void operator()(int s, uint32_t& kc, int& kv) const {
+    kc = uint32_t(int64_t(s) * v2::BK);
+    const int64_t rem = K - int64_t(kc);
+    kv = rem < v2::BK ? int(rem) : v2::BK;
+  }
+};
+
 __device__ __forceinline__ v8bf as_v8bf(const uint4& v) {
   typedef uint32_t u4v __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(v8bf, u4v{v.x, v.y, v.z, v.w});

@@ -64,7 +64,7 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStr
 hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, const int32_t* b2e, int64_t T,
                                int64_t E, int64_t B, int64_t N, uint16_t* daff, hipStream_t st);
 
-// moe_gemm.hip
+// moe_phase1_*.hip, moe_phase3.hip
 struct Phase1Args {
   // H % 128 == 0: the MX operands themselves, scales pair-major
   const uint8_t* wd_codes;      // [E][I][H]

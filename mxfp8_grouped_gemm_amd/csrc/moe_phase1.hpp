@@ -1,13 +1,13 @@
-// moe_gemm.hip -- the token-block GEMMs of the MoE backward with their fused
-// epilogues (P1, "Blockwise MM Backward MXFP8 Kernel API Reference": Phases
-// 1 and 3; P3, sonic-moe functional/backward.py: _down_projection_backward_act
-// and _up_projection_backward_act).
+// moe_phase1.hpp -- Phase 1 of the MoE backward with its fused SwiGLU-backward
+// epilogue (P1, "Blockwise MM Backward MXFP8 Kernel API Reference": Phase 1
+// and the checkpoint parameters; P3, sonic-moe functional/backward.py:
+// _down_projection_backward_act).  The kernel template and its launcher; the
+// tile shapes are instantiated in moe_phase1_*.hip so they compile in parallel.
 //
-// Phase 1, per block b of expert e (tile rows = intermediate index i,
-// tile columns = block slot p, contraction over H; the operands are the
-// exactly dequantised MX values in bf16, reduced with bf16 MFMAs whose fp32
-// accumulation is exact enough that requantising the result below makes the
-// same rounding decisions as an exact sum would):
+// Per block b of expert e (tile rows = intermediate index i, tile columns =
+// block slot p, contraction over H; the operands' exact MX values reduced with
+// bf16 MFMAs, whose fp32 accumulation is exact enough that requantising the
+// result below makes the same rounding decisions as an exact sum would):
 //   dS[i][p]   = sum_h deq(W_down[e])[i][h] * deq(dY[tok_p])[h]   (dY rows are
 //                quantised along H once and gathered here by token id)
 //   epilogue:  ga = bf16(silu(g)), inter = bf16(ga*u)   (g,u from the checkpoint)
@@ -17,10 +17,7 @@
 //              -> quantised along I (Phase-3 A operand, [P][2I])
 //              -> quantised along the slots (Phase-2 B operand, [2I][P])
 //              -> db1 partial sums (with a bias)
-// Phase 3, per block b (tile rows = slot p, columns = hidden index h,
-// contraction over 2I):
-//   dX[tok_p][h] += sum_{j,i} deq(dGU)[p][j][i] * deq(W_gate_up[e])[h][j][i]
-//   as fp32 atomic adds (a token's top-k slots sit in different blocks).
+#pragma once
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
 #include "kernels.hpp"
@@ -30,15 +27,7 @@
 namespace mx {
 
 using v2::v16f;
-
-struct KMapPlain {
-  int64_t K;   // bytes
-  __device__ __forceinline__ void operator()(int s, uint32_t& kc, int& kv) const {
-    kc = uint32_t(int64_t(s) * v2::BK);
-    const int64_t rem = K - int64_t(kc);
-    kv = rem < v2::BK ? int(rem) : v2::BK;
-  }
-};
+using v2::KMapPlain;
 
 // ---------------------------------------------------------------------------
 // Phase 1.  Epilogue data flow per wave (wave tile (BM/2) i-rows x (BN/2) slots):
@@ -301,94 +290,14 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3 tiles: block b, rows = slots m0.., columns = hidden index n0..
-struct P3Pos {
-  int b;
-  int64_t m0, n0;
-};
-template <int BM, int BN>
-__device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int tile) {
-  const int per_blk = p.tiles_m * p.tiles_n;
-  const int id = v2::xcd_remap(tile, p.total);
-  const int b = id / per_blk;
-  int tm, tn;
-  v2::grouped_tile<8>(id - b * per_blk, p.tiles_m, p.tiles_n, tm, tn);
-  return P3Pos{b, int64_t(tm) * BM, int64_t(tn) * BN};
-}
-
-// dX scatter-add of one tile: slot row s of block b adds into its token's row.
-template <int BM, int BN>
-__device__ __forceinline__ void p3_store(const Phase3Args& p, const P3Pos& tp, const v16f (&acc)[BM / 64][BN / 64]) {
-  const int64_t sbase = int64_t(tp.b) * p.B;
-  v2::static_for<BM / 64>([&](auto FI) {
-    v2::static_for<16>([&](auto Q) {
-      const int64_t s = tp.m0 + v2::acc_row<BM, BN>(FI, Q);
-      const int64_t tok = s < p.B ? p.slot_tok[sbase + s] : -1;
-      if (tok >= 0) {
-        float* dst = p.dx_acc + tok * p.H;
-        v2::static_for<BN / 64>([&](auto FJ) {
-          const int64_t hh = tp.n0 + v2::acc_col<BM, BN>(FJ);
-          if (hh < p.H) atomicAdd(dst + hh, acc[FI][FJ][int(Q)]);
-        });
-      }
-    });
-  });
-}
-
-// 2I not a multiple of 128 bytes: one tile per workgroup on the v2 loop.
-template <int BM, int BN, int FG, int FW>
-__global__ void __launch_bounds__(v2::kThreads) phase3_generic(Phase3Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
-  constexpr int FM = BM / 64, FN = BN / 64;
-  const P3Pos tp = p3_pos<BM, BN>(p, blockIdx.x);
-  if (!p.flag[tp.b]) return;
-  const int64_t e = p.b2e[tp.b];
-  const int wave = threadIdx.x >> 6;
-  const int64_t sbase = int64_t(tp.b) * p.B, twoI = 2 * p.I;
-  v2::Operand<BM, FM> A;
-  v2::Operand<BN, FN> B;
-  v2::setup_rows(A, p.dgu_row_codes + sbase * twoI, p.dgu_row_scales + sbase * (twoI / 32), tp.m0, p.B, twoI,
-                 twoI / 32, (wave >> 1) * (BM / 2));
-  v2::setup_rows(B, p.wgu_codes + e * p.H * twoI, p.wgu_scales + e * p.H * (twoI / 32), tp.n0, p.H, twoI,
-                 twoI / 32, (wave & 1) * (BN / 2));
-  v16f acc[FM][FN];
-  v2::mainloop<BM, BN, v2::kFp8, FG, FW, true>(A, B, int((twoI + v2::BK - 1) / v2::BK), KMapPlain{twoI}, smem,
-                                                acc);
-  p3_store<BM, BN>(p, tp, acc);
-}
-
-// Aligned: one tile per workgroup on the four-stage ring loop.
-template <int BM, int BN, int FG, int FW>
-__global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[v3::smem_bytes(BM, BN)];
-  constexpr int FM = BM / 64, FN = BN / 64;
-  const P3Pos tp = p3_pos<BM, BN>(p, blockIdx.x);
-  if (!p.flag[tp.b]) return;
-  const int64_t e = p.b2e[tp.b];
-  const int64_t sbase = int64_t(tp.b) * p.B, twoI = 2 * p.I;
-  v3::Op<BM> A;
-  v3::Op<BN> B;
-  v3::ScaleDma<BM, BN> sd;
-  v3::setup_rows(A, p.dgu_row_codes + sbase * twoI, tp.m0, p.B, twoI);
-  v3::setup_rows(B, p.wgu_codes + e * p.H * twoI, tp.n0, p.H, twoI);
-  // pair-major scales: dGU along I over all P slots; W_gate_up re-laid per expert
-  const int64_t P = p.N * p.B;
-  v3::setup_scales(sd, p.dgu_row_scales, sbase + tp.m0, P, P * (twoI / 32), p.wgu_scales + e * p.H * (twoI / 32),
-                   tp.n0, p.H, p.H * (twoI / 32));
-  v16f acc[FM][FN];
-  v3::mainloop<BM, BN, v3::kFp8, FG, FW>(A, B, &sd, int(twoI / v3::SK), v3::KMapPlain{}, smem, acc);
-  p3_store<BM, BN>(p, tp, acc);
-}
-
-// ---------------------------------------------------------------------------
 template <int BM, int BN, bool G, int FG, int FW>
-static void phase1_go(const Phase1Args& p, unsigned blocks, hipStream_t st) {
+inline void phase1_go(const Phase1Args& p, unsigned blocks, hipStream_t st) {
   if (p.affinity_on_i) phase1_kernel<BM, BN, FG, FW, true, G><<<blocks, v2::kThreads, 0, st>>>(p);
   else phase1_kernel<BM, BN, FG, FW, false, G><<<blocks, v2::kThreads, 0, st>>>(p);
 }
 
 template <int BM, int BN, bool G>
-static hipError_t phase1_launch(Phase1Args p, int fg, int fw, hipStream_t st) {
+hipError_t phase1_launch(Phase1Args p, int fg, int fw, hipStream_t st) {
   p.tiles_m = int((p.I + BM - 1) / BM);
   p.tiles_n = int((p.B + BN - 1) / BN);
   const int64_t blocks = int64_t(p.tiles_m) * p.tiles_n * p.N;
@@ -405,49 +314,6 @@ static hipError_t phase1_launch(Phase1Args p, int fg, int fw, hipStream_t st) {
     else phase1_go<BM, BN, G, kE5M2, kE5M2>(p, grid, st);
   }
   return hipGetLastError();
-}
-
-// Tile shape: 256 along a dimension when it is at least 256, else 128.  The
-// block size B is a power of two >= 128, so every tile lies inside one block.
-// H not a multiple of 128 (a ragged last K stage, scale rows not in whole
-// pairs): the v2 loop on bf16 values, 128 x 128.
-hipError_t launch_phase1(const Phase1Args& p, int fg, int fw, hipStream_t st) {
-  if (p.H % 128 != 0) return phase1_launch<128, 128, true>(p, fg, fw, st);
-  if (p.I >= 256 && p.B >= 256) return phase1_launch<256, 256, false>(p, fg, fw, st);
-  if (p.I >= 256) return phase1_launch<256, 128, false>(p, fg, fw, st);
-  return phase1_launch<128, 128, false>(p, fg, fw, st);
-}
-
-template <int BM, int BN>
-static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipStream_t st) {
-  p.tiles_m = int((p.B + BM - 1) / BM);
-  p.tiles_n = int((p.H + BN - 1) / BN);
-  const int64_t total = int64_t(p.tiles_m) * p.tiles_n * p.N;
-  if (total > INT32_MAX) return hipErrorInvalidValue;
-  p.total = int(total);
-  if (generic) {
-    const unsigned grid = unsigned(total);
-    if (fg == 0 && fw == 0) phase3_generic<BM, BN, 0, 0><<<grid, v2::kThreads, 0, st>>>(p);
-    else if (fg == 0) phase3_generic<BM, BN, 0, 1><<<grid, v2::kThreads, 0, st>>>(p);
-    else if (fw == 0) phase3_generic<BM, BN, 1, 0><<<grid, v2::kThreads, 0, st>>>(p);
-    else phase3_generic<BM, BN, 1, 1><<<grid, v2::kThreads, 0, st>>>(p);
-  } else {
-    const unsigned grid = unsigned(total);
-    if (fg == 0 && fw == 0) phase3_ring<BM, BN, 0, 0><<<grid, v2::kThreads, 0, st>>>(p);
-    else if (fg == 0) phase3_ring<BM, BN, 0, 1><<<grid, v2::kThreads, 0, st>>>(p);
-    else if (fw == 0) phase3_ring<BM, BN, 1, 0><<<grid, v2::kThreads, 0, st>>>(p);
-    else phase3_ring<BM, BN, 1, 1><<<grid, v2::kThreads, 0, st>>>(p);
-  }
-  return hipGetLastError();
-}
-
-// Tile shape: 256 x 256 when the block and H allow, else 128 x 256; 2I not a
-// multiple of 128 bytes (unaligned scale rows / ragged last K stage): the v2
-// loop at 128 x 256.
-hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st) {
-  const bool g = (2 * p.I) % v2::BK != 0;
-  if (!g && p.B >= 256 && p.H >= 256) return phase3_launch<256, 256>(p, fg, fw, false, st);
-  return phase3_launch<128, 256>(p, fg, fw, g, st);
 }
 
 }  // namespace mx

@@ -1,0 +1,24 @@
+// moe_phase1_128.hip -- Phase 1 at 128 x 128 tiles (I = 128, or H not a multiple of 128 on the
+// bf16-value loop) and the tile-shape dispatch.
+#include "moe_phase1.hpp"
+
+namespace mx {
+
+template hipError_t phase1_launch<128, 128, false>(Phase1Args, int, int, hipStream_t);
+template hipError_t phase1_launch<128, 128, true>(Phase1Args, int, int, hipStream_t);
+extern template hipError_t phase1_launch<256, 256, false>(Phase1Args, int, int, hipStream_t);
+extern template hipError_t phase1_launch<256, 128, false>(Phase1Args, int, int, hipStream_t);
+
+
+// Tile shape: 256 along a dimension when it is at least 256, else 128.  The
+// block size B is a power of two >= 128, so every tile lies inside one block.
+// H not a multiple of 128 (a ragged last K stage, scale rows not in whole
+// pairs): the v2 loop on bf16 values, 128 x 128.
+hipError_t launch_phase1(const Phase1Args& p, int fg, int fw, hipStream_t st) {
+  if (p.H % 128 != 0) return phase1_launch<128, 128, true>(p, fg, fw, st);
+  if (p.I >= 256 && p.B >= 256) return phase1_launch<256, 256, false>(p, fg, fw, st);
+  if (p.I >= 256) return phase1_launch<256, 128, false>(p, fg, fw, st);
+  return phase1_launch<128, 128, false>(p, fg, fw, st);
+}
+
+}  // namespace mx
