@@ -1,9 +1,8 @@
 // gemm_v3.hpp -- MX GEMM main loop for gfx950 with a four-stage LDS ring.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k] for operands whose code rows are 128-byte
-// aligned and whose K is a multiple of 128 bytes, in three element modes:
+// aligned and whose K is a multiple of 128 bytes, in two element modes:
 //   kFp8    : fp8 codes + E8M0 scales on v_mfma_scale_f32_32x32x64_f8f6f4;
-//   kBf16   : bf16 values on v_mfma_f32_32x32x16_bf16;
 //   kFp8Bf16: fp8 codes + E8M0 scales moved like kFp8, converted in registers
 //             to their exact bf16 values (v_cvt_scalef32_pk_bf16_fp8/bf8: a
 //             code times a power of two has at most 4 significant bits) and
@@ -49,7 +48,6 @@ using v2::Buf;
 using v2::v16f;
 using v2::v8bf;
 using v2::v8i;
-using v2::kBf16;
 using v2::kFp8;
 using v2::kFp8Bf16;
 
@@ -225,15 +223,12 @@ struct KMapList {
   }
 };
 
-template <int ELEM, int FA, int FB, int OPS>
-__device__ __forceinline__ v16f mma(const uint4 (&a)[2], const uint4 (&b)[2], const v16f& c, int sa, int sb,
-                                    int half) {
-  if (ELEM == kFp8) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v2::as_v8i(a[0], a[1]), v2::as_v8i(b[0], b[1]), c, FA, FB,
-                                                           OPS, sa, OPS, sb);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(v2::as_v8bf(a[half]), v2::as_v8bf(b[half]), c, 0, 0, 0);
-  }
+// One scaled fp8 MFMA (32 x 32 x 64); OPS selects the scale byte of the
+// operands' words (2 * stage parity; lane half h's word is pre-shifted by h bytes).
+template <int FA, int FB, int OPS>
+__device__ __forceinline__ v16f mma(const uint4 (&a)[2], const uint4 (&b)[2], const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v2::as_v8i(a[0], a[1]), v2::as_v8i(b[0], b[1]), c, FA, FB,
+                                                         OPS, sa, OPS, sb);
 }
 
 // One tile's operands: code rows of A and B, their scale rows (fp8 mode), the
@@ -276,38 +271,54 @@ struct Ring {
   static constexpr int NCI = (BM + BN) / 64;               // code DMA instructions per wave per stage
   static constexpr int NS = ScaleDma<BM, BN>::NS;          // scale DMA instructions per wave per pair
   static constexpr int VM_STAGE = NCI;
-  static constexpr bool SCALED = ELEM != kBf16;            // codes + scales in memory
-  static constexpr int VM_PAIR_SCALES = SCALED ? NS : 0;
+  static constexpr int VM_PAIR_SCALES = NS;
   using T = Tile<BM, BN, KMap>;
 
   uint8_t* smem;
   uint32_t base;
 
-  // DMA of stage `stage` of tile x into ring position base + pos (live == false:
-  // a load without records, i.e. zeros, keeping the issue count).
-  __device__ __forceinline__ void issue(const T& x, int stage, int pos, bool live) const {
+  // A stage's work in items, so a stage can be laid out as regions that each
+  // issue one DMA instruction and read one fragment for the next stage ahead
+  // of a share of the MFMAs (the MFMA pipe keeps running while those issue):
+  //   DMA items j < NCI      code rows (A: j < FM, B: j >= FM), plus scale
+  //                          chunk j (j < NS) on even positions;
+  //   read items j < FM + FN fragment j (A: j < FM, B: j >= FM) and its scale word;
+  //   MFMA items k < NMF     (c, i, j) with k = (c * FM + i) * FN + j, c the
+  //                          16-element step in kFp8Bf16 mode (0 in kFp8 mode).
+  static constexpr int NC = ELEM == kFp8 ? 1 : 4;   // MFMAs per fragment pair and stage
+  static constexpr int NMF = NC * FM * FN;
+  static constexpr int NR = FM + FN;               // regions of a stage (== NCI)
+  static_assert(NR == NCI, "one code DMA instruction per region");
+
+  // DMA item J of tile x into ring position base + pos, from K byte kc (x.km of
+  // the stage; live == false: a load without records, i.e. zeros, keeping the
+  // issue count).
+  template <int J>
+  __device__ __forceinline__ void issue_item(const T& x, int pos, bool live, uint32_t kc) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int wave = threadIdx.x >> 6;
     const uint32_t lds0 = lds_addr(smem);
-    const uint32_t kc = x.km(live ? stage : 0);
     const uint32_t slot = lds0 + ((base + uint32_t(pos)) & (NBUF - 1)) * CS;
-    v4i ra = rsrc(x.A.codes), rb = rsrc(x.B.codes);
-    ra[2] = live ? ra[2] : 0;
-    rb[2] = live ? rb[2] : 0;
-#pragma unroll
-    for (int j = 0; j < BM / 64; ++j) dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * j) * SK, x.A.off[j], kc);
-#pragma unroll
-    for (int j = 0; j < BN / 64; ++j) dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * j) * SK, x.B.off[j], kc);
-    if (SCALED && (pos & 1) == 0) {
+    if (J < FM) {
+      v4i ra = rsrc(x.A.codes);
+      ra[2] = live ? ra[2] : 0;
+      dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * J) * SK, x.A.off[J], kc);
+    } else {
+      v4i rb = rsrc(x.B.codes);
+      rb[2] = live ? rb[2] : 0;
+      dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc);
+    }
+    if (J < NS && (pos & 1) == 0) {
       const uint32_t ss = lds0 + NBUF * CS + (((base + uint32_t(pos)) >> 1) & (NBUF - 1)) * SSB;
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        v4i rs = rsrc(x.sd.buf[i]);
-        rs[2] = live ? rs[2] : 0;
-        dma4(rs, ss + uint32_t(wave + 4 * i) * 256, x.sd.off[i], (kc >> 7) * x.sd.pstride[i]);
-      }
+      v4i rs = rsrc(x.sd.buf[J]);
+      rs[2] = live ? rs[2] : 0;
+      dma4(rs, ss + uint32_t(wave + 4 * J) * 256, x.sd.off[J], (kc >> 7) * x.sd.pstride[J]);
     }
 #endif
+  }
+  __device__ __forceinline__ void issue(const T& x, int stage, int pos, bool live) const {
+    const uint32_t kc = x.km(live ? stage : 0);
+    v2::static_for<NCI>([&](auto J) { issue_item<J>(x, pos, live, kc); });
   }
   // position pos >= cur.nstages belongs to nxt
   __device__ __forceinline__ void issue_next(const T& cur, const T& nxt, int pos) const {
@@ -324,8 +335,9 @@ struct Ring {
   uint4 fa[2][FM][2], fb[2][FN][2];
   uint32_t sa[2][FM], sb[2][FN];
 
-  // fragments and raw scale words of stage t into set P (the words are shifted
-  // to this lane's group where they are used, so nothing here waits on the reads).
+  // Read item J of stage t into set P: fragment J's two 16-byte chunks and its
+  // raw scale word (shifted to this lane's group where it is used, so nothing
+  // here waits on the reads).
   // Lane half h takes 16-byte chunks h and 2 + h of each row.  The fp8 MFMA
   // reads them as K positions of its 64-element step; in kFp8Bf16 mode the
   // chunks are the operands of four bf16 steps: chunk h's low and high 8 bytes
@@ -333,37 +345,29 @@ struct Ring {
   // and 3.  A and B are permuted alike, so each step still pairs equal K
   // indices, and a chunk lies inside one 32-element scale group (h: the
   // stage's first group, 2 + h: its second).
-  template <int P>
-  __device__ __forceinline__ void read(int t) {
+  template <int P, int J>
+  __device__ __forceinline__ void read_item(int t) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = lane >> 5, r = lane & 31;
-    const int wrow = (wave >> 1) * (BM / 2), wcol = (wave & 1) * (BN / 2);
     const uint8_t* cs = smem + ((base + uint32_t(t)) & (NBUF - 1)) * CS;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wrow + 32 * i + r;
-      fa[P][i][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
-      fa[P][i][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wcol + 32 * j + r;
+    const uint8_t* ss = smem + NBUF * CS + (((base + uint32_t(t)) >> 1) & (NBUF - 1)) * SSB;
+    if (J < FM) {
+      const int row = (wave >> 1) * (BM / 2) + 32 * J + r;
+      fa[P][J][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
+      fa[P][J][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
+      sa[P][J] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
+    } else {
+      constexpr int j = J - FM;
+      const int row = (wave & 1) * (BN / 2) + 32 * j + r;
       fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
       fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
+      const int srow = BM + row;
+      sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (srow >> 6) * 256 + (srow & 63) * 4);
     }
-    if (SCALED) {
-      const uint8_t* ss = smem + NBUF * CS + (((base + uint32_t(t)) >> 1) & (NBUF - 1)) * SSB;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wrow + 32 * i + r;
-        sa[P][i] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = BM + wcol + 32 * j + r;
-        sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
-      }
-    }
+  }
+  template <int P>
+  __device__ __forceinline__ void read(int t) {
+    v2::static_for<NR>([&](auto J) { read_item<P, J>(t); });
   }
 
   // kFp8Bf16: the exact bf16 values of 8 codes (one 16-element step of a lane)
@@ -383,80 +387,63 @@ struct Ring {
     return __builtin_bit_cast(v8bf, u4v{cv(w0, std::false_type{}), cv(w0, std::true_type{}), cv(w1, std::false_type{}),
                                         cv(w1, std::true_type{})});
   }
+  // operand of step c from a fragment and its scale word (stage parity P picks
+  // the pair's group: bytes 2P and 2P + 1)
+  template <int F, int P, int C>
+  __device__ __forceinline__ static v8bf step_operand(const uint4 (&f)[2], uint32_t sw) {
+    const uint4& x = f[C >> 1];
+    return to_bf16<F>((C & 1) ? x.z : x.x, (C & 1) ? x.w : x.y, (sw >> (8 * (2 * P + (C >> 1)))) & 0xffu);
+  }
 
-  // MFMAs of the stage in set P (stage parity P = scale byte within the pair)
+  // MFMA item K of the stage in set P (stage parity P = scale byte within the pair)
+  template <int P, int K>
+  __device__ __forceinline__ void mfma_item(v16f (&acc)[FM][FN]) const {
+    constexpr int c = K / (FM * FN), i = (K / FN) % FM, j = K % FN;
+    if (ELEM == kFp8Bf16) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(step_operand<FA, P, c>(fa[P][i], sa[P][i]),
+                                                          step_operand<FB, P, c>(fb[P][j], sb[P][j]), acc[i][j], 0,
+                                                          0, 0);
+    } else {
+      const int h = (threadIdx.x & 63) >> 5;
+      acc[i][j] = mma<FA, FB, 2 * P>(fa[P][i], fb[P][j], acc[i][j], int(sa[P][i] >> (8 * h)),
+                                     int(sb[P][j] >> (8 * h)));
+    }
+  }
   template <int P>
   __device__ __forceinline__ void compute(v16f (&acc)[FM][FN]) const {
-    const int h = (threadIdx.x & 63) >> 5;
-    if (ELEM == kFp8Bf16) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int sh = 8 * (2 * P + (c >> 1));   // scale byte of this step's 32-element group
-        v8bf av[FM], bv[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const uint4& f = fa[P][i][c >> 1];
-          av[i] = to_bf16<FA>((c & 1) ? f.z : f.x, (c & 1) ? f.w : f.y, (sa[P][i] >> sh) & 0xffu);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const uint4& f = fb[P][j][c >> 1];
-          bv[j] = to_bf16<FB>((c & 1) ? f.z : f.x, (c & 1) ? f.w : f.y, (sb[P][j] >> sh) & 0xffu);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-      }
-      return;
-    }
-#pragma unroll
-    for (int H = 0; H < 2; ++H) {
-      if (ELEM == kFp8) {
-#pragma unroll
-        for (int i = H * FM / 2; i < (H + 1) * FM / 2; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = mma<ELEM, FA, FB, 2 * P>(fa[P][i], fb[P][j], acc[i][j], int(sa[P][i] >> (8 * h)),
-                                                 int(sb[P][j] >> (8 * h)), 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mma<ELEM, FA, FB, 0>(fa[P][i], fb[P][j], acc[i][j], 0, 0, H);
-      }
-    }
+    v2::static_for<NMF>([&](auto K) { mfma_item<P, K>(acc); });
   }
 
   // One stage t (fragments in set P == t & 1).  With a look-ahead `ahead`
-  // (a callable issuing position t + NBUF): wait until stage t+1 has landed
-  // (t+2, t+3 may still be in flight) and every wave has finished reading
-  // stage t's slot (barrier), issue, then read stage t+1 into set P ^ 1
-  // interleaved with stage t's MFMAs (an LDS queue holds at most 15 reads, so
-  // issuing them all first would stall the MFMAs behind them).  Without: the
-  // tile's last stage.
+  // (ahead.kc(pos): K byte of position pos; ahead(pos, J, kc): DMA item J of
+  // it): wait until stage t+1 has landed (t+2, t+3 may still be in flight) and
+  // every wave has finished reading stage t's slot (barrier), then NR regions,
+  // region q issuing DMA item q of position t + NBUF and read item q of stage
+  // t+1 (into set P ^ 1) before its share of stage t's MFMAs.  Each region is
+  // fenced, so the issue of the memory instructions sits between MFMAs, which
+  // keep executing while it proceeds.  The K byte comes first: a grouped K map
+  // reads it with a scalar load, which the wait below covers (inside the
+  // regions its wait would also drain the fragment reads).  Without a
+  // look-ahead: the tile's last stage.
   template <int P, bool READ, class Ahead>
   __device__ __forceinline__ void step(int t, v16f (&acc)[FM][FN], const Ahead& ahead) {
     if (READ) {
+      const uint32_t kc = ahead.kc(t + NBUF);
       __builtin_amdgcn_s_waitcnt(waitcnt(2 * VM_STAGE + VM_PAIR_SCALES, 0));
       __builtin_amdgcn_s_barrier();
-      ahead(t + NBUF);
       __builtin_amdgcn_sched_barrier(0);
-      read<P ^ 1>(t + 1);
+      v2::static_for<NR>([&](auto Q) {
+        constexpr int q = Q;
+        ahead(t + NBUF, Q, kc);
+        read_item<P ^ 1, q>(t + 1);
+        constexpr int k0 = q * NMF / NR, k1 = (q + 1) * NMF / NR;
+        v2::static_for<k1 - k0>([&](auto K) { mfma_item<P, k0 + K>(acc); });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+      compute<P>(acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    compute<P>(acc);
-    if (READ) {
-      constexpr int NMF = FM * FN * (ELEM == kFp8 ? 1 : (ELEM == kBf16 ? 2 : 4));   // MFMAs of a stage
-      constexpr int NRD = 2 * (FM + FN) + (SCALED ? FM + FN : 0);   // LDS reads of a stage
-      constexpr int PER = (NRD + NMF - 1) / NMF;
-#pragma unroll
-      for (int k = 0; k < NMF; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);   // LDS reads
-        if (ELEM == kFp8Bf16) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU (conversions)
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Entry: issue position NBUF-1 (after a barrier: its slot held the previous
@@ -465,12 +452,41 @@ struct Ring {
   __device__ __forceinline__ void enter(const Ahead& ahead) {
     __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
     __builtin_amdgcn_s_barrier();
-    ahead(NBUF - 1);
+    const uint32_t kc = ahead.kc(NBUF - 1);
+    v2::static_for<NCI>([&](auto J) { ahead(NBUF - 1, J, kc); });
     // stage 0 has landed once at most the three later positions' loads remain
     __builtin_amdgcn_s_waitcnt(waitcnt(3 * VM_STAGE + VM_PAIR_SCALES, 0));
     __builtin_amdgcn_s_barrier();
     read<0>(0);
   }
+
+  // Look-ahead inside one tile (the head's positions all lie in it).
+  struct AheadOwn {
+    const Ring& r;
+    const T& cur;
+    __device__ __forceinline__ uint32_t kc(int pos) const { return cur.km(pos); }
+    template <class J>
+    __device__ __forceinline__ void operator()(int pos, J, uint32_t kc) const {
+      r.template issue_item<J::value>(cur, pos, true, kc);
+    }
+  };
+  // Look-ahead of a tile's last stages: position pos < cur.nstages is cur's
+  // stage pos, later positions are nxt's first stages (no records past its end).
+  struct Ahead {
+    const Ring& r;
+    const T& cur;
+    const T& nxt;
+    __device__ __forceinline__ uint32_t kc(int pos) const {
+      const int tn = pos - cur.nstages;
+      return pos < cur.nstages ? cur.km(pos) : nxt.km(tn < nxt.nstages ? tn : 0);
+    }
+    template <class J>
+    __device__ __forceinline__ void operator()(int pos, J, uint32_t kc) const {
+      const int tn = pos - cur.nstages;
+      if (pos < cur.nstages) r.template issue_item<J::value>(cur, pos, true, kc);
+      else r.template issue_item<J::value>(nxt, pos, tn < nxt.nstages, kc);
+    }
+  };
 
   // The stages of cur whose look-ahead stays inside cur.  Returns the first
   // stage left for tail().
@@ -483,7 +499,7 @@ struct Ring {
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
     const int n = cur.nstages;
     if (n < NBUF) return 0;
-    auto own = [&](int pos) { issue(cur, pos, pos, true); };
+    AheadOwn own{*this, cur};
     enter(own);
     int t = 0;
     for (; t + NBUF + 1 < n; t += 2) {
@@ -497,10 +513,7 @@ struct Ring {
   // fetches nxt's first stages.  Leaves base at nxt's stage 0.
   __device__ __forceinline__ void tail(const T& cur, const T& nxt, int t0, v16f (&acc)[FM][FN]) {
     const int n = cur.nstages;
-    auto next = [&](int pos) {
-      if (pos < n) issue(cur, pos, pos, true);
-      else issue_next(cur, nxt, pos);
-    };
+    Ahead next{*this, cur, nxt};
     if (n < NBUF) {
       // A tile shorter than the ring: positions base + n .. base + NBUF - 2 were
       // issued without knowing nxt (no records).  Let every load land and every
@@ -525,12 +538,11 @@ struct Ring {
   }
 };
 
-// One tile on its own (no neighbour to prefetch for).  sd may be null in bf16 mode.
+// One tile on its own (no neighbour to prefetch for).
 template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
 __device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const ScaleDma<BM, BN>* sd, int nstages,
                                          const KMap& kmap, uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
-  Tile<BM, BN, KMap> cur{A, B, {}, kmap, nstages};
-  if (ELEM != kBf16) cur.sd = *sd;
+  Tile<BM, BN, KMap> cur{A, B, *sd, kmap, nstages};
   Tile<BM, BN, KMap> none = cur;
   none.nstages = 0;
   Ring<BM, BN, ELEM, FA, FB, KMap> ring{smem, 0u};
