@@ -173,7 +173,8 @@ template <int BM, int BN, class ARow, class BRow>
 __device__ __forceinline__ void setup_scales_map(ScaleDma<BM, BN>& sd, const uint8_t* a_scales, int64_t a_rows,
                                                  int64_t a_bytes, const ARow& a_row, const uint8_t* b_scales,
                                                  int64_t b_rows, int64_t b_bytes, const BRow& b_row) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform chunk choice: descriptors and strides stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const Buf ba = v2::make_rsrc(a_scales, uint32_t(a_bytes));
   const Buf bb = v2::make_rsrc(b_scales, uint32_t(b_bytes));
 #pragma unroll
@@ -242,46 +243,39 @@ struct Tile {
   int nstages;
 };
 
-// The ring, shared by consecutive tiles of one workgroup.  `base` is the ring
-// position of the current tile's stage 0 (always even); stage t of the tile
-// lives in slot (base + t) % NBUF and its pair's scales in slot
-// ((base + t) / 2) % NBUF.  Loads are issued NBUF stages ahead of use.
+// The ring of one tile: stage t lives in code slot t % NBUF, with its pair's
+// scale words (one 4-byte word per row covering K elements [128p, 128p + 128),
+// loaded again for each stage of the pair) in scale slot t % NBUF.  Loads are
+// issued NBUF stages ahead of use: after the prologue (positions 0 .. NBUF-1),
+// step t issues position t + NBUF into stage t's slot once every wave has read
+// that slot.  Positions past the last stage load through descriptors with no
+// records, which the hardware answers with zeros without touching memory, so
+// every step issues the same loads and the wait counts are fixed.
 //
-// Invariant on entering a tile: positions base .. base + NBUF - 2 are issued
-// (its first stages, or the next tile's when it is shorter, see tail()), in
-// position order.  The tile issues position base + NBUF - 1 itself after a
-// barrier, since that slot held the previous tile's last stage.
-//
-// A tile is run as head() then tail():
-//   head: the stages whose look-ahead stays inside the tile, issuing only
-//         the tile's own operands (straight-line, few live registers);
-//   tail: the last NBUF stages, whose look-ahead would fetch a following
-//         tile's first stages; with no following tile it goes through
-//         descriptors with no records, which the hardware answers with zeros
-//         without touching memory.
-// Every iteration issues the same loads, so the wait counts are fixed.
-// The kernels here run one tile per workgroup (mainloop below).  Chaining
-// tiles through the ring in a persistent grid was measured slower: at 256
-// VGPRs the next tile's descriptors spill, and the reloads' waits drain the
-// ring at every tile boundary.
+// The steady state runs NBUF stages per iteration, so every slot index, and
+// with it every LDS address, is a compile-time constant there; the last
+// stages (2 to 6; K is a multiple of 128 bytes, so the count is even) run with
+// run-time slots.  The kernels here run one tile per workgroup: chaining tiles
+// through the ring in a persistent grid was measured slower (at 256 VGPRs the
+// next tile's descriptors spill, and the reloads' waits drain the ring at
+// every tile boundary).
 template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
 struct Ring {
   static constexpr int FM = BM / 64, FN = BN / 64;
   static constexpr int CS = code_slot(BM, BN), SSB = scale_slot(BM, BN);
   static constexpr int NCI = (BM + BN) / 64;               // code DMA instructions per wave per stage
-  static constexpr int NS = ScaleDma<BM, BN>::NS;          // scale DMA instructions per wave per pair
-  static constexpr int VM_STAGE = NCI;
-  static constexpr int VM_PAIR_SCALES = NS;
+  static constexpr int NS = ScaleDma<BM, BN>::NS;          // scale DMA instructions per wave per stage
+  static constexpr int VM_STAGE = NCI + NS;
   using T = Tile<BM, BN, KMap>;
 
   uint8_t* smem;
-  uint32_t base;
+  const T& x;
 
   // A stage's work in items, so a stage can be laid out as regions that each
   // issue one DMA instruction and read one fragment for the next stage ahead
   // of a share of the MFMAs (the MFMA pipe keeps running while those issue):
   //   DMA items j < NCI      code rows (A: j < FM, B: j >= FM), plus scale
-  //                          chunk j (j < NS) on even positions;
+  //                          chunk j (j < NS);
   //   read items j < FM + FN fragment j (A: j < FM, B: j >= FM) and its scale word;
   //   MFMA items k < NMF     (c, i, j) with k = (c * FM + i) * FN + j, c the
   //                          16-element step in kFp8Bf16 mode (0 in kFp8 mode).
@@ -290,67 +284,69 @@ struct Ring {
   static constexpr int NR = FM + FN;               // regions of a stage (== NCI)
   static_assert(NR == NCI, "one code DMA instruction per region");
 
-  // DMA item J of tile x into ring position base + pos, from K byte kc (x.km of
-  // the stage; live == false: a load without records, i.e. zeros, keeping the
-  // issue count).
-  template <int J>
-  __device__ __forceinline__ void issue_item(const T& x, int pos, bool live, uint32_t kc) const {
+  // slot of stage t: S when the caller knows it (S >= 0), else t % NBUF
+  template <int S>
+  __device__ __forceinline__ static uint32_t slot_of(int t) {
+    return S >= 0 ? uint32_t(S) : uint32_t(t) & (NBUF - 1);
+  }
+  __device__ __forceinline__ static int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+  // K byte of position pos (stage 0's for positions past the end: any offset
+  // is harmless there, and a grouped K map must not read past its list)
+  __device__ __forceinline__ uint32_t kc_of(int pos) const { return x.km(pos < x.nstages ? pos : 0); }
+
+  // DMA item J of position pos (slot of stage S, see slot_of) from K byte kc.
+  template <int J, int S>
+  __device__ __forceinline__ void issue_item(int pos, uint32_t kc) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int wave = threadIdx.x >> 6;
-    const uint32_t lds0 = lds_addr(smem);
-    const uint32_t slot = lds0 + ((base + uint32_t(pos)) & (NBUF - 1)) * CS;
+    const bool live = pos < x.nstages;
+    const int wave = wave_id();
+    const uint32_t slot = slot_of<S>(pos);
+    const uint32_t cs = lds_addr(smem) + slot * CS;
     if (J < FM) {
       v4i ra = rsrc(x.A.codes);
       ra[2] = live ? ra[2] : 0;
-      dma16(ra, slot + uint32_t(wave * (BM / 4) + 16 * J) * SK, x.A.off[J], kc);
+      dma16(ra, cs + uint32_t(wave * (BM / 4) + 16 * J) * SK, x.A.off[J], kc);
     } else {
       v4i rb = rsrc(x.B.codes);
       rb[2] = live ? rb[2] : 0;
-      dma16(rb, slot + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc);
+      dma16(rb, cs + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc);
     }
-    if (J < NS && (pos & 1) == 0) {
-      const uint32_t ss = lds0 + NBUF * CS + (((base + uint32_t(pos)) >> 1) & (NBUF - 1)) * SSB;
+    if (J < NS) {
+      const uint32_t ss = lds_addr(smem) + NBUF * CS + slot * SSB;
       v4i rs = rsrc(x.sd.buf[J]);
       rs[2] = live ? rs[2] : 0;
       dma4(rs, ss + uint32_t(wave + 4 * J) * 256, x.sd.off[J], (kc >> 7) * x.sd.pstride[J]);
     }
 #endif
   }
-  __device__ __forceinline__ void issue(const T& x, int stage, int pos, bool live) const {
-    const uint32_t kc = x.km(live ? stage : 0);
-    v2::static_for<NCI>([&](auto J) { issue_item<J>(x, pos, live, kc); });
-  }
-  // position pos >= cur.nstages belongs to nxt
-  __device__ __forceinline__ void issue_next(const T& cur, const T& nxt, int pos) const {
-    const int tn = pos - cur.nstages;
-    issue(nxt, tn, pos, tn < nxt.nstages);
-  }
-
-  // Positions 0 .. NBUF-2 of the first tile a workgroup computes.
-  __device__ __forceinline__ void prefetch(const T& first) const {
-#pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t) issue(first, t, t, t < first.nstages);
+  template <int S>
+  __device__ __forceinline__ void issue(int pos) const {
+    const uint32_t kc = kc_of(pos);
+    v2::static_for<NCI>([&](auto J) { issue_item<J, S>(pos, kc); });
   }
 
   uint4 fa[2][FM][2], fb[2][FN][2];
   uint32_t sa[2][FM], sb[2][FN];
 
-  // Read item J of stage t into set P: fragment J's two 16-byte chunks and its
-  // raw scale word (shifted to this lane's group where it is used, so nothing
-  // here waits on the reads).
+  // Read item J of stage t (slot S, see slot_of) into set P: fragment J's two
+  // 16-byte chunks and its raw scale word (shifted to this lane's group where it
+  // is used, so nothing here waits on the reads).
   // Lane half h takes 16-byte chunks h and 2 + h of each row.  The fp8 MFMA
   // reads them as K positions of its 64-element step; in kFp8Bf16 mode the
   // chunks are the operands of four bf16 steps: chunk h's low and high 8 bytes
   // are this lane half's elements of steps 0 and 1, chunk 2 + h's of steps 2
   // and 3.  A and B are permuted alike, so each step still pairs equal K
   // indices, and a chunk lies inside one 32-element scale group (h: the
-  // stage's first group, 2 + h: its second).
-  template <int P, int J>
+  // stage's first group, 2 + h: its second).  Rows 32 apart share a swizzle,
+  // so a wave's fragments differ by constant offsets.
+  template <int P, int J, int S>
   __device__ __forceinline__ void read_item(int t) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int h = lane >> 5, r = lane & 31;
-    const uint8_t* cs = smem + ((base + uint32_t(t)) & (NBUF - 1)) * CS;
-    const uint8_t* ss = smem + NBUF * CS + (((base + uint32_t(t)) >> 1) & (NBUF - 1)) * SSB;
+    const uint32_t slot = slot_of<S>(t);
+    const uint8_t* cs = smem + slot * CS;
+    const uint8_t* ss = smem + NBUF * CS + slot * SSB;
     if (J < FM) {
       const int row = (wave >> 1) * (BM / 2) + 32 * J + r;
       fa[P][J][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
@@ -364,10 +360,6 @@ struct Ring {
       const int srow = BM + row;
       sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (srow >> 6) * 256 + (srow & 63) * 4);
     }
-  }
-  template <int P>
-  __device__ __forceinline__ void read(int t) {
-    v2::static_for<NR>([&](auto J) { read_item<P, J>(t); });
   }
 
   // kFp8Bf16: the exact bf16 values of 8 codes (one 16-element step of a lane)
@@ -409,146 +401,80 @@ struct Ring {
                                      int(sb[P][j] >> (8 * h)));
     }
   }
-  template <int P>
-  __device__ __forceinline__ void compute(v16f (&acc)[FM][FN]) const {
-    v2::static_for<NMF>([&](auto K) { mfma_item<P, K>(acc); });
-  }
 
-  // One stage t (fragments in set P == t & 1).  With a look-ahead `ahead`
-  // (ahead.kc(pos): K byte of position pos; ahead(pos, J, kc): DMA item J of
-  // it): wait until stage t+1 has landed (t+2, t+3 may still be in flight) and
-  // every wave has finished reading stage t's slot (barrier), then NR regions,
-  // region q issuing DMA item q of position t + NBUF and read item q of stage
-  // t+1 (into set P ^ 1) before its share of stage t's MFMAs.  Each region is
-  // fenced, so the issue of the memory instructions sits between MFMAs, which
-  // keep executing while it proceeds.  The K byte comes first: a grouped K map
-  // reads it with a scalar load, which the wait below covers (inside the
-  // regions its wait would also drain the fragment reads).  Without a
-  // look-ahead: the tile's last stage.
-  template <int P, bool READ, class Ahead>
-  __device__ __forceinline__ void step(int t, v16f (&acc)[FM][FN], const Ahead& ahead) {
+  // One stage t (fragments in set P == t & 1, slot S, see slot_of).  With READ:
+  // wait until stage t+1 has landed (t+2, t+3 may still be in flight) and every
+  // wave has finished reading stage t's slot (barrier), then NR regions, region
+  // q issuing DMA item q of position t + NBUF and read item q of stage t+1
+  // (into set P ^ 1) before its share of stage t's MFMAs.  Each region is
+  // fenced, so the memory instructions issue between MFMAs, which keep
+  // executing meanwhile.  The K byte comes first: a grouped K map reads it with
+  // a scalar load, which the wait below covers (inside the regions its wait
+  // would also drain the fragment reads).  Without READ: the tile's last stage.
+  template <int P, int S, bool READ>
+  __device__ __forceinline__ void step(int t, v16f (&acc)[FM][FN]) {
+    constexpr int SN = S >= 0 ? (S + 1) % NBUF : -1;   // slot of stage t + 1
     if (READ) {
-      const uint32_t kc = ahead.kc(t + NBUF);
-      __builtin_amdgcn_s_waitcnt(waitcnt(2 * VM_STAGE + VM_PAIR_SCALES, 0));
+      const uint32_t kc = kc_of(t + NBUF);
+      __builtin_amdgcn_s_waitcnt(waitcnt(2 * VM_STAGE, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       v2::static_for<NR>([&](auto Q) {
         constexpr int q = Q;
-        ahead(t + NBUF, Q, kc);
-        read_item<P ^ 1, q>(t + 1);
+        issue_item<q, S>(t + NBUF, kc);
+        read_item<P ^ 1, q, SN>(t + 1);
         constexpr int k0 = q * NMF / NR, k1 = (q + 1) * NMF / NR;
         v2::static_for<k1 - k0>([&](auto K) { mfma_item<P, k0 + K>(acc); });
         __builtin_amdgcn_sched_barrier(0);
       });
     } else {
-      compute<P>(acc);
+      v2::static_for<NMF>([&](auto K) { mfma_item<P, K>(acc); });
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Entry: issue position NBUF-1 (after a barrier: its slot held the previous
-  // tile's last stage), wait for stage 0, read it.
-  template <class Ahead>
-  __device__ __forceinline__ void enter(const Ahead& ahead) {
-    __builtin_amdgcn_s_waitcnt(waitcnt(63, 0));
-    __builtin_amdgcn_s_barrier();
-    const uint32_t kc = ahead.kc(NBUF - 1);
-    v2::static_for<NCI>([&](auto J) { ahead(NBUF - 1, J, kc); });
-    // stage 0 has landed once at most the three later positions' loads remain
-    __builtin_amdgcn_s_waitcnt(waitcnt(3 * VM_STAGE + VM_PAIR_SCALES, 0));
-    __builtin_amdgcn_s_barrier();
-    read<0>(0);
-  }
-
-  // Look-ahead inside one tile (the head's positions all lie in it).
-  struct AheadOwn {
-    const Ring& r;
-    const T& cur;
-    __device__ __forceinline__ uint32_t kc(int pos) const { return cur.km(pos); }
-    template <class J>
-    __device__ __forceinline__ void operator()(int pos, J, uint32_t kc) const {
-      r.template issue_item<J::value>(cur, pos, true, kc);
-    }
-  };
-  // Look-ahead of a tile's last stages: position pos < cur.nstages is cur's
-  // stage pos, later positions are nxt's first stages (no records past its end).
-  struct Ahead {
-    const Ring& r;
-    const T& cur;
-    const T& nxt;
-    __device__ __forceinline__ uint32_t kc(int pos) const {
-      const int tn = pos - cur.nstages;
-      return pos < cur.nstages ? cur.km(pos) : nxt.km(tn < nxt.nstages ? tn : 0);
-    }
-    template <class J>
-    __device__ __forceinline__ void operator()(int pos, J, uint32_t kc) const {
-      const int tn = pos - cur.nstages;
-      if (pos < cur.nstages) r.template issue_item<J::value>(cur, pos, true, kc);
-      else r.template issue_item<J::value>(nxt, pos, tn < nxt.nstages, kc);
-    }
-  };
-
-  // The stages of cur whose look-ahead stays inside cur.  Returns the first
-  // stage left for tail().
-  __device__ __forceinline__ int head(const T& cur, v16f (&acc)[FM][FN]) {
+  // The whole tile: positions 0 .. NBUF-1, then every stage.
+  __device__ __forceinline__ void run(v16f (&acc)[FM][FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-    const int n = cur.nstages;
-    if (n < NBUF) return 0;
-    AheadOwn own{*this, cur};
-    enter(own);
+    const int n = x.nstages;
+    issue<0>(0);
+    issue<1>(1);
+    issue<2>(2);
+    issue<3>(3);
+    // stage 0 has landed once at most the three later positions' loads remain
+    __builtin_amdgcn_s_waitcnt(waitcnt(3 * VM_STAGE, 0));
+    __builtin_amdgcn_s_barrier();
+    v2::static_for<NR>([&](auto J) { read_item<0, J, 0>(0); });
     int t = 0;
-    for (; t + NBUF + 1 < n; t += 2) {
-      step<0, true>(t, acc, own);
-      step<1, true>(t + 1, acc, own);
+    // steady state: positions t + NBUF .. t + 2 NBUF - 1 all inside the tile
+    for (; t + 2 * NBUF - 1 < n; t += NBUF) {
+      step<0, 0, true>(t, acc);
+      step<1, 1, true>(t + 1, acc);
+      step<0, 2, true>(t + 2, acc);
+      step<1, 3, true>(t + 3, acc);
     }
-    return t;
-  }
-
-  // The last stages of cur (from t0, as head() returned); the look-ahead
-  // fetches nxt's first stages.  Leaves base at nxt's stage 0.
-  __device__ __forceinline__ void tail(const T& cur, const T& nxt, int t0, v16f (&acc)[FM][FN]) {
-    const int n = cur.nstages;
-    Ahead next{*this, cur, nxt};
-    if (n < NBUF) {
-      // A tile shorter than the ring: positions base + n .. base + NBUF - 2 were
-      // issued without knowing nxt (no records).  Let every load land and every
-      // wave finish the previous tile (barrier), then fetch nxt's stages there,
-      // in position order; later waits can then only over-wait.
-      __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
-      __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int pos = 0; pos < NBUF - 1; ++pos)
-        if (pos >= n) issue_next(cur, nxt, pos);
-      if (n == 0) return;   // base stays: nxt starts at the same position
-      enter(next);
-    }
-    int t = t0;
+    // the last stages (n - t is 2, 4 or 6)
     for (; t + 2 < n; t += 2) {
-      step<0, true>(t, acc, next);
-      step<1, true>(t + 1, acc, next);
+      step<0, -1, true>(t, acc);
+      step<1, -1, true>(t + 1, acc);
     }
-    step<0, true>(t, acc, next);
-    step<1, false>(t + 1, acc, next);
-    base += uint32_t(n);
+    step<0, -1, true>(t, acc);
+    step<1, -1, false>(t + 1, acc);
   }
 };
 
-// One tile on its own (no neighbour to prefetch for).
+// One tile per workgroup.
 template <int BM, int BN, int ELEM, int FA, int FB, class KMap>
 __device__ __forceinline__ void mainloop(const Op<BM>& A, const Op<BN>& B, const ScaleDma<BM, BN>* sd, int nstages,
                                          const KMap& kmap, uint8_t* smem, v16f (&acc)[BM / 64][BN / 64]) {
-  Tile<BM, BN, KMap> cur{A, B, *sd, kmap, nstages};
-  Tile<BM, BN, KMap> none = cur;
-  none.nstages = 0;
-  Ring<BM, BN, ELEM, FA, FB, KMap> ring{smem, 0u};
-  ring.prefetch(cur);
-  const int t0 = ring.head(cur, acc);
-  ring.tail(cur, none, t0, acc);
+  const Tile<BM, BN, KMap> tile{A, B, *sd, kmap, nstages};
+  Ring<BM, BN, ELEM, FA, FB, KMap> ring{smem, tile};
+  ring.run(acc);
   // the look-ahead loads past the end still write (zeros) into the ring: let
   // them land before the caller reuses the LDS
   __builtin_amdgcn_s_waitcnt(waitcnt(0, 15));
