@@ -95,8 +95,11 @@ def stage_work(cfg, N):
     q = 1 + 1 / 32                      # bytes per quantised element (code + its share of a scale)
     return {
         "setup": ("hbm", T * H * 4 + P * 12),
-        # dY: bf16 in, codes + scales + exact bf16 values out; W_down: codes in, bf16 values out
-        "quantize_dy": ("hbm", T * H * (2 + q + 2) + E * I * H * (q + 2)),
+        # dY: bf16 in, codes + scales out; H % 128 == 0: W_down's and W_gate_up's scales
+        # re-laid pair-major (read + write); otherwise Phase 1 reads bf16 values, so dY's
+        # are written too and W_down's codes are read and their bf16 values written
+        "quantize_dy": ("hbm", T * H * (2 + q) + E * H * 2 * I / 32 * 2
+                        + (E * I * H / 32 * 2 if H % 128 == 0 else T * H * 2 + E * I * H * (q + 2))),
         "gather_quantize_x_dy": ("hbm", 2 * (TK * H * 2 + P * H * q)),
         "bias": ("hbm", 2 * TK * H * 2 if cfg.has_bias else 0),
         "phase1": ("mfma_bf16", 2 * TK * H * I),
