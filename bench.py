@@ -103,6 +103,9 @@ def stage_work(cfg, N):
         "gather_quantize_x_dy": ("hbm", 2 * (TK * H * 2 + P * H * q)),
         "bias": ("hbm", 2 * TK * H * 2 if cfg.has_bias else 0),
         "phase1": ("mfma_bf16", 2 * TK * H * I),
+        # per (pair, i): reads g, u and dS; writes dGU quantised along both axes and
+        # the intermediate quantised
+        "phase1_epilogue": ("hbm", TK * I * (4 + 4 + 5 * q)),
         "phase3": ("mfma", 4 * TK * H * I),
         "phase2": ("mfma", 4 * TK * H * I),
         "phase4": ("mfma", 2 * TK * H * I),

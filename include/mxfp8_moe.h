@@ -199,6 +199,7 @@ typedef struct {
  *                                                     (written when 2I % 128 == 0)
  *   wd_scales_pairs           P4 of down_scales per expert, [E][H/128][I][4]
  *                                                     (H % 128 == 0; else empty)
+ *   phase1_ds                 [N,I,B] fp32            Phase 1's product dS per block
  *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
@@ -210,7 +211,7 @@ typedef struct {
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 
@@ -223,7 +224,8 @@ size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
 
 /* Enqueues the whole backward.  Errors: INVALID_ARG (shapes, null required
  * pointers, alignment, formats), UNSUPPORTED (block_size outside the set,
- * affinity on I together with a bias), WORKSPACE (too small).  Device-side
+ * affinity on I together with a bias, sizes beyond 32-bit indexing or
+ * I * block_size * 4 beyond 2 GiB), WORKSPACE (too small).  Device-side
  * preconditions (not checked): block_to_expert entries in [0,E) (blocks with
  * other values are skipped); each (t,e) pair appears in at most one slot. */
 int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
@@ -237,11 +239,13 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
  *   1 quantise dY along H (and lay out W_down's scales for Phase 1)
  *   2 gather-quantise X and a*dY (or dY) along slots
  *   3 bias reductions (has_bias only)
- *   4 Phase 1 + epilogue (also the intermediate quantised along slots)
- *   5 Phase 3 (dX scatter-add)    6 Phase 2 (dW_gate_up)       7 Phase 4 (dW_down)
- *   8 finalise to bf16
+ *   4 Phase 1 (the product dS)
+ *   5 Phase 1 epilogue (SwiGLU backward; dGU along I and along slots, the
+ *     intermediate along slots, d(affinity) and db1 partial sums)
+ *   6 Phase 3 (dX scatter-add)    7 Phase 2 (dW_gate_up)       8 Phase 4 (dW_down)
+ *   9 finalise to bf16
  * Errors as for moe_bwd_mxfp8, plus INVALID_ARG for a stage outside the range. */
-#define MOE_BWD_NUM_STAGES 9
+#define MOE_BWD_NUM_STAGES 10
 int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
                         int stage, void* stream);
 

@@ -204,6 +204,7 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->dgu_tok_scales, 2 * I * P / 32);
   put(L->wgu_scales_pairs, E * H * 2 * I / 32);
   put(L->wd_scales_pairs, h_pairs ? E * I * H / 32 : 0);
+  put(L->phase1_ds, N * I * B * 4);
   put(L->dx_acc, T * H * 4);
   put(L->daff_slot, P * 4);
   put(L->db1_acc, E * 2 * I * 4);
@@ -229,6 +230,9 @@ static int moe_check_shapes(const moe_bwd_mxfp8_args* a) {
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: block_size %lld not in {128,256,512,1024}", (long long)B);
   if (a->N * B > INT32_MAX || a->T * a->E > INT32_MAX || a->T * a->H * 2 > INT32_MAX)
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: sizes beyond 32-bit indexing");
+  if (a->I * B * 4 > INT32_MAX)   // a block's checkpoint / product is read through one buffer
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: I * block_size * 4 = %lld bytes beyond 2 GiB",
+                (long long)(a->I * B * 4));
   return MXFP8_OK;
 }
 
@@ -340,7 +344,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
                          flag, H, B, N, daff_slot, db2_acc, st),
          "bias reductions");
   stage = 4;
-  // Phase 1 + fused SwiGLU-backward epilogue (also writes the intermediate operand)
+  // Phase 1: the product dS, fp32
   mx::Phase1Args p1{};
   if (h_pairs) {
     p1.wd_codes = a->down_codes; p1.wd_scales = at(L.wd_scales_pairs);
@@ -349,6 +353,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
     p1.wd_deq = reinterpret_cast<const uint16_t*>(at(L.wd_deq));
     p1.dy_deq = reinterpret_cast<const uint16_t*>(at(L.dy_deq));
   }
+  p1.ds = reinterpret_cast<float*>(at(L.phase1_ds));
   p1.slot_tok = slot_tok; p1.slot_aff = slot_aff; p1.b2e = a->block_to_expert; p1.flag = flag;
   p1.ckpt = a->gate_up_proj_act_checkpoint_T;
   p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
@@ -360,6 +365,9 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.dgu_row_pairs = gu_pairs;
   STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_weight, st), "phase 1");
   stage = 5;
+  // the SwiGLU backward on dS: dGU along both axes, the intermediate operand, d(a), db1
+  STEP(mx::launch_phase1_epi(p1, a->fmt_grad, st), "phase 1 epilogue");
+  stage = 6;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};
   p3.dgu_row_codes = at(L.dgu_row_codes); p3.dgu_row_scales = at(L.dgu_row_scales);
@@ -367,7 +375,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
-  stage = 6;
+  stage = 7;
   // Phase 2: dW_gate_up[e] = X_tok . dGU_tok^T over the expert's blocks
   mx::GemmStoreArgs g{};
   g.a_codes = at(L.x_tok_codes); g.a_scales = at(L.x_tok_scales); g.lda = P;
@@ -375,13 +383,13 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   g.M = H; g.N = 2 * I; g.K = 0; g.out = a->gate_up_proj_weight_grad; g.ldo = 2 * I; g.out_gstride = H * 2 * I;
   g.blk_off = boff; g.blk_list = blist; g.blk = int(B);
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 2");
-  stage = 7;
+  stage = 8;
   // Phase 4: dW_down[e] = inter_tok . gy_tok^T
   g.a_codes = at(L.inter_tok_codes); g.a_scales = at(L.inter_tok_scales); g.lda = P;
   g.b_codes = at(L.gy_tok_codes); g.b_scales = at(L.gy_tok_scales); g.ldb = P;
   g.M = I; g.N = H; g.out = a->down_proj_weight_grad; g.ldo = H; g.out_gstride = I * H;
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 4");
-  stage = 8;
+  stage = 9;
   // finalisation
   STEP(mx::launch_f32_to_bf16(dx_acc, a->hidden_states_grad, T * H, st), "dX to bf16");
   STEP(mx::launch_daff_scatter(daff_slot, slot_tok, a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,

@@ -64,7 +64,7 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStr
 hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, const int32_t* b2e, int64_t T,
                                int64_t E, int64_t B, int64_t N, uint16_t* daff, hipStream_t st);
 
-// moe_phase1_*.hip, moe_phase3.hip
+// moe_phase1_*.hip (product, epilogue), moe_phase3.hip
 struct Phase1Args {
   // H % 128 == 0: the MX operands themselves, scales pair-major
   const uint8_t* wd_codes;      // [E][I][H]
@@ -74,6 +74,7 @@ struct Phase1Args {
   // otherwise their exact bf16 values
   const uint16_t* wd_deq;       // [E][I][H] bf16: dequantised W_down
   const uint16_t* dy_deq;       // [T][H] bf16: dequantised Q_H(dY)
+  float* ds;                    // [N][I][B] fp32: the product, written by Phase 1, read by its epilogue
   const int32_t* slot_tok;      // [P]
   const float* slot_aff;        // [P]
   const int32_t* b2e;           // [N]
@@ -95,6 +96,7 @@ struct Phase1Args {
   int tiles_m, tiles_n;
 };
 hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, int fmt_weight, hipStream_t st);
+hipError_t launch_phase1_epi(const Phase1Args& p, int fmt_grad, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]
