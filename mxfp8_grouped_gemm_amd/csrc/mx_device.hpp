@@ -101,11 +101,13 @@ __device__ __forceinline__ float inv_scale(int X) { return __uint_as_float(uint3
 // v_cvt_pk_bf8_f32 round to nearest-even into the OCP formats.  Equal to
 // encode<FMT> for every finite fp32 input and every scale the group rule can
 // produce (checked exhaustively over all bf16 patterns and all such scales).
+// encode4s: the same with a scale per value (four groups, e.g. four columns).
 template <int FMT>
-__device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3, float inv) {
+__device__ __forceinline__ uint32_t encode4s(float v0, float v1, float v2, float v3, float i0, float i1, float i2,
+                                             float i3) {
   constexpr float M = FMT == kE4M3 ? 448.f : 57344.f;
-  const float y0 = fminf(fmaxf(v0 * inv, -M), M), y1 = fminf(fmaxf(v1 * inv, -M), M);
-  const float y2 = fminf(fmaxf(v2 * inv, -M), M), y3 = fminf(fmaxf(v3 * inv, -M), M);
+  const float y0 = fminf(fmaxf(v0 * i0, -M), M), y1 = fminf(fmaxf(v1 * i1, -M), M);
+  const float y2 = fminf(fmaxf(v2 * i2, -M), M), y3 = fminf(fmaxf(v3 * i3, -M), M);
   int w;
   if (FMT == kE4M3) {
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
@@ -115,6 +117,10 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
     w = __builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, w, true);
   }
   return uint32_t(w);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3, float inv) {
+  return encode4s<FMT>(v0, v1, v2, v3, inv, inv, inv, inv);
 }
 
 // bf16 round-to-nearest-even through the hardware converter (finite inputs;

@@ -1,6 +1,6 @@
 // quantize.hip -- MXFP8 quantisers for gfx950 (HBM-bound; no MFMA).
 //
-// Three kernels share the encoder of mx_device.hpp:
+// Three kernels share the E8M0 rule and the encoders of mx_device.hpp:
 //   quant_rows : groups of 32 along the contiguous axis (codes in place).
 //   quant_cols : groups of 32 along the strided axis (codes in place).
 //   quant_tok  : groups of 32 along the strided axis, written transposed so the
@@ -53,13 +53,12 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict
     amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
     amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
     const int X = scale_exp<FMT>(amax);
-    uint32_t out[2] = {0, 0};
+    const float inv = inv_scale(X);
+    uint32_t out[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = encode<FMT>(w[k] << 16, X);
-      const uint32_t hi = encode<FMT>(w[k] & 0xffff0000u, X);
-      out[k >> 1] |= (lo | (hi << 8)) << (16 * (k & 1));
-    }
+    for (int k = 0; k < 2; ++k)
+      out[k] = encode4<FMT>(__uint_as_float(w[2 * k] << 16), __uint_as_float(w[2 * k] & 0xffff0000u),
+                            __uint_as_float(w[2 * k + 1] << 16), __uint_as_float(w[2 * k + 1] & 0xffff0000u), inv);
     codes[c] = make_uint2(out[0], out[1]);
     if ((c & 3) == 0) {
       if (PAIRS) {   // group G = row * gpr + g  ->  word (g / 4, row), byte g % 4
@@ -94,8 +93,11 @@ __global__ void __launch_bounds__(256) dequant_rows_kernel(const uint4* __restri
 }
 
 // ---------------------------------------------------------------------------
-// quant_cols: a thread owns 8 adjacent columns and one group of 32 rows.
-template <int FMT>
+// quant_cols: a thread owns 8 adjacent columns and one group of 32 rows.  VEC
+// (cols % 8 == 0, so every row segment is 16-byte aligned): one 16-byte load
+// per row for the amax, a second (from L2) to encode, 8-byte code and scale
+// stores.  Otherwise element by element.
+template <int FMT, bool VEC>
 __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restrict__ x,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
@@ -103,6 +105,44 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
   const int64_t c0 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
   const int64_t g = blockIdx.y;
   if (c0 >= cols) return;
+  if (VEC) {
+    const int64_t ld = cols / 8;   // row stride in 16-byte chunks
+    const uint4* src = reinterpret_cast<const uint4*>(x + g * 32 * cols + c0);
+    uint32_t am[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r) {
+      const uint4 v = src[r * ld];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        am[2 * k] = max(am[2 * k], (w[k] << 16) & 0x7fffffffu);
+        am[2 * k + 1] = max(am[2 * k + 1], w[k] & 0x7fff0000u);
+      }
+    }
+    float inv[8];
+    uint32_t sw[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int X = scale_exp<FMT>(am[k]);
+      inv[k] = inv_scale(X);
+      sw[k >> 2] |= uint32_t(X + 127) << (8 * (k & 3));
+    }
+    *reinterpret_cast<uint2*>(scales + g * cols + c0) = make_uint2(sw[0], sw[1]);
+    uint2* dst = reinterpret_cast<uint2*>(codes + g * 32 * cols + c0);
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r) {
+      const uint4 v = src[r * ld];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t lo = encode4s<FMT>(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                        __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u), inv[0],
+                                        inv[1], inv[2], inv[3]);
+      const uint32_t hi = encode4s<FMT>(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                        __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u), inv[4],
+                                        inv[5], inv[6], inv[7]);
+      dst[r * ld] = make_uint2(lo, hi);
+    }
+    return;
+  }
   const int ncol = cols - c0 >= 8 ? 8 : int(cols - c0);
   uint32_t amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = 0; r < 32; ++r) {
@@ -154,14 +194,11 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
         const int64_t src = GATHER ? int64_t(idx[r]) : r;
         if (src >= 0 && src < src_rows) {
           v = *reinterpret_cast<const uint4*>(x + src * cols + col);
-          if (ROWSCALE) {
+          if (ROWSCALE) {   // bf16(a * x), round to nearest even
             const float a = rowscale[r];
             uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t lo = f32_to_bf16(a * __uint_as_float(w[k] << 16));
-              const uint32_t hi = f32_to_bf16(a * __uint_as_float(w[k] & 0xffff0000u));
-              w[k] = lo | (hi << 16);
-            }
+            for (int k = 0; k < 4; ++k)
+              w[k] = bf16x2_pack(a * __uint_as_float(w[k] << 16), a * __uint_as_float(w[k] & 0xffff0000u));
             v = make_uint4(w[0], w[1], w[2], w[3]);
           }
         }
@@ -186,16 +223,16 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
     amax1 = max(amax1, abs_bits_bf16(uint16_t(w >> 16)));
   }
   const int X0 = scale_exp<FMT>(amax0), X1 = scale_exp<FMT>(amax1);
+  const float i0 = inv_scale(X0), i1 = inv_scale(X1);
   uint32_t p0[8], p1[8];
+#pragma unroll
   for (int q = 0; q < 8; ++q) {
-    uint32_t a = 0, b = 0;
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = tile[grp * 32 + q * 4 + k][cp];
-      a |= encode<FMT>(w << 16, X0) << (8 * k);
-      b |= encode<FMT>(w & 0xffff0000u, X1) << (8 * k);
-    }
-    p0[q] = a;
-    p1[q] = b;
+    const uint32_t w0 = tile[grp * 32 + q * 4 + 0][cp], w1 = tile[grp * 32 + q * 4 + 1][cp];
+    const uint32_t w2 = tile[grp * 32 + q * 4 + 2][cp], w3 = tile[grp * 32 + q * 4 + 3][cp];
+    p0[q] = encode4<FMT>(__uint_as_float(w0 << 16), __uint_as_float(w1 << 16), __uint_as_float(w2 << 16),
+                         __uint_as_float(w3 << 16), i0);
+    p1[q] = encode4<FMT>(__uint_as_float(w0 & 0xffff0000u), __uint_as_float(w1 & 0xffff0000u),
+                         __uint_as_float(w2 & 0xffff0000u), __uint_as_float(w3 & 0xffff0000u), i1);
   }
   uint4* dst0 = reinterpret_cast<uint4*>(codes_t + colA * rows + row0);
   uint4* dst1 = reinterpret_cast<uint4*>(codes_t + (colA + 1) * rows + row0);
@@ -283,10 +320,14 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
                              uint8_t* scales, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   dim3 grid(unsigned((cols + 8 * 256 - 1) / (8 * 256)), unsigned(rows / 32));
-  if (fmt == kE4M3)
-    quant_cols_kernel<kE4M3><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
-  else
-    quant_cols_kernel<kE5M2><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+  const bool vec = cols % 8 == 0;
+  if (fmt == kE4M3) {
+    if (vec) quant_cols_kernel<kE4M3, true><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+    else quant_cols_kernel<kE4M3, false><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+  } else {
+    if (vec) quant_cols_kernel<kE5M2, true><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+    else quant_cols_kernel<kE5M2, false><<<grid, 256, 0, st>>>(x, codes, scales, rows, cols);
+  }
   return hipGetLastError();
 }
 
