@@ -115,13 +115,14 @@ __device__ __forceinline__ int dma_row(int j) {
   return (threadIdx.x >> 6) * (ROWS / 4) + 16 * j + ((threadIdx.x & 63) >> 2);
 }
 // Physical 16-byte chunk of logical chunk c in row `row` is c ^ swz(row).  A
-// fragment read has consecutive lanes on consecutive rows, one chunk each;
-// LDS serves 16 lanes of a 16-byte read per pass on 64 banks, so any 16
-// consecutive rows (four per 256-byte bank line) must fall on 16 distinct
-// 16-byte slots: rows r, r+4, r+8, r+12 need distinct swizzles.  The XOR of
-// bits 1-2 and 3-4 gives that, and also keeps 8 consecutive rows distinct on
-// 32 banks.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// fragment read has lanes r and 32 + r on row r (chunks h and 2 + h for lane
+// half h).  LDS serves a 16-byte read at 256 B per clock, and the swizzle was
+// chosen by measurement (rocprofv3 SQ_LDS_BANK_CONFLICT over the exact
+// fragment access pattern): XOR with row bits 2-3 reads both chunk pairs in
+// 4 clocks per instruction with no conflict cycles, like contiguous data,
+// while any swizzle that also depends on row bit 1 or bit 4 costs a 2-way
+// conflict (8 clocks).  Rows 32 apart share a swizzle.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 template <int ROWS>
 __device__ __forceinline__ void setup_rows(Op<ROWS>& op, const uint8_t* codes, int64_t row0, int64_t nrows,
