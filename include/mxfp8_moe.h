@@ -200,10 +200,14 @@ typedef struct {
  *   wd_scales_pairs           P4 of down_scales per expert, [E][H/128][I][4]
  *                                                     (H % 128 == 0; else empty)
  *   phase1_ds                 [N,I,B] fp32            Phase 1's product dS per block
+ *                                                     (slots past a block's extent unwritten)
+ *   phase1_tiles/phase3_tiles [N+1] int32             first tile of each block over its
+ *                                                     live slot tiles, and the total
  *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
- *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32.
+ *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32
+ *   (one past the block's last routed slot; 0 = no routed slot).
  * P4[K,R] is the pair-major scale layout of an operand with R rows contracted
  * over K elements: [K/128][R][4] bytes, word (p, r) holding row r's E8M0 bytes
  * for elements [128p, 128p+128) (so one stage pair's words for consecutive rows
@@ -211,7 +215,7 @@ typedef struct {
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 

@@ -205,6 +205,8 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->wgu_scales_pairs, E * H * 2 * I / 32);
   put(L->wd_scales_pairs, h_pairs ? E * I * H / 32 : 0);
   put(L->phase1_ds, N * I * B * 4);
+  put(L->phase1_tiles, (N + 1) * 4);
+  put(L->phase3_tiles, (N + 1) * 4);
   put(L->dx_acc, T * H * 4);
   put(L->daff_slot, P * 4);
   put(L->db1_acc, E * 2 * I * 4);
@@ -354,6 +356,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
     p1.dy_deq = reinterpret_cast<const uint16_t*>(at(L.dy_deq));
   }
   p1.ds = reinterpret_cast<float*>(at(L.phase1_ds));
+  p1.tile_start = reinterpret_cast<int32_t*>(at(L.phase1_tiles));
   p1.slot_tok = slot_tok; p1.slot_aff = slot_aff; p1.b2e = a->block_to_expert; p1.flag = flag;
   p1.ckpt = a->gate_up_proj_act_checkpoint_T;
   p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
@@ -373,6 +376,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p3.dgu_row_codes = at(L.dgu_row_codes); p3.dgu_row_scales = at(L.dgu_row_scales);
   p3.wgu_codes = a->gate_up_codes; p3.wgu_scales = gu_pairs ? at(L.wgu_scales_pairs) : a->gate_up_scales;
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
+  p3.tile_start = reinterpret_cast<int32_t*>(at(L.phase3_tiles));
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
   stage = 7;
@@ -382,6 +386,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   g.b_codes = at(L.dgu_tok_codes); g.b_scales = at(L.dgu_tok_scales); g.ldb = P;
   g.M = H; g.N = 2 * I; g.K = 0; g.out = a->gate_up_proj_weight_grad; g.ldo = 2 * I; g.out_gstride = H * 2 * I;
   g.blk_off = boff; g.blk_list = blist; g.blk = int(B);
+  g.blk_ext = flag;   // the expert's last block ends at its last routed slot (rounded up to 128)
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 2");
   stage = 8;
   // Phase 4: dW_down[e] = inter_tok . gy_tok^T

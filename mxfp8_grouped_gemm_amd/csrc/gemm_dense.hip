@@ -125,8 +125,10 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p)
   v3::setup_scales(sd, p.a_scales, tp.m0, p.M, p.M * p.lda / 32, p.b_scales, tp.n0, p.N, p.N * p.ldb / 32);
   v2::v16f acc[FM][FN];
   if constexpr (LIST) {
-    const int b0 = p.blk_off[tp.g];
-    const int nstages = int((int64_t(p.blk_off[tp.g + 1] - b0) * p.blk) / v3::SK);
+    const int b0 = p.blk_off[tp.g], b1 = p.blk_off[tp.g + 1];
+    int64_t kbytes = int64_t(b1 - b0) * p.blk;
+    if (p.blk_ext && b1 > b0) kbytes -= p.blk - ((p.blk_ext[p.blk_list[b1 - 1]] + 127) & ~127);
+    const int nstages = int(kbytes / v3::SK);
     const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
     v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, km, smem, acc);
   } else {

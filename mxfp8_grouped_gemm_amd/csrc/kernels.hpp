@@ -43,6 +43,8 @@ struct GemmStoreArgs {
   int64_t out_gstride;
   const int32_t* blk_off;
   const int32_t* blk_list;
+  const int32_t* blk_ext;   // optional: per block, one past its last routed column; a group's
+                            // last block then contributes only that many columns, rounded up to 128
   int blk;
   int tiles_m, tiles_n;
   int total;                      // tiles over all groups
@@ -54,6 +56,7 @@ hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
 hipError_t launch_fill_u16(void* p, int64_t n, uint16_t v, hipStream_t st);
 hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
                                int32_t* tpid, int32_t* b2e, int32_t* counts, hipStream_t st);
+hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st);
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* flag,
                              int32_t* off, int32_t* list, hipStream_t st);
@@ -78,7 +81,8 @@ struct Phase1Args {
   const int32_t* slot_tok;      // [P]
   const float* slot_aff;        // [P]
   const int32_t* b2e;           // [N]
-  const int32_t* flag;          // [N]
+  const int32_t* flag;          // [N]: the block's extent (one past its last routed slot)
+  int32_t* tile_start;          // [N+1]: tile ranges over the blocks' live slot tiles (moe_tiles.hpp)
   const uint16_t* ckpt;         // [N][2][I][B]
   int64_t T, H, I, E, N, B;
   uint8_t* dgu_row_codes;       // [P][2I]
@@ -105,11 +109,11 @@ struct Phase3Args {
   const uint8_t* wgu_scales;      // 2I % 128 == 0: pair-major [E][2I/128][H][4]; else row-major [E][H][2I/32]
   const int32_t* slot_tok;
   const int32_t* b2e;
-  const int32_t* flag;
+  const int32_t* flag;            // [N]: the block's extent (one past its last routed slot)
+  int32_t* tile_start;            // [N+1]: tile ranges over the blocks' live slot tiles (moe_tiles.hpp)
   int64_t H, I, N, B;
   float* dx_acc;                  // [T][H]
   int tiles_m, tiles_n;
-  int total;                      // tiles over all blocks
 };
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st);
 

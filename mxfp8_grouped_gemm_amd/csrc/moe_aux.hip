@@ -123,15 +123,19 @@ __global__ void slot_info_kernel(const int32_t* __restrict__ tpid, const int32_t
   }
 }
 
-// A block takes part in the GEMMs iff at least one of its slots is routed.
+// A block's extent: one past its last routed slot (0: no routed slot, the block
+// takes no part in the GEMMs).  Slots at or past the extent are padding, so
+// the GEMMs skip tiles that start there.
 __global__ void __launch_bounds__(256) block_flag_kernel(const int32_t* __restrict__ slot_tok, int64_t B,
                                                          int32_t* __restrict__ flag) {
   __shared__ int red[4];
-  int any = 0;
-  for (int64_t p = threadIdx.x; p < B; p += 256) any |= slot_tok[int64_t(blockIdx.x) * B + p] >= 0;
-  int tot;
-  block_exclusive_scan(any, red, &tot);
-  if (threadIdx.x == 0) flag[blockIdx.x] = tot > 0;
+  int ext = 0;
+  for (int64_t p = threadIdx.x; p < B; p += 256)
+    if (slot_tok[int64_t(blockIdx.x) * B + p] >= 0) ext = int(p) + 1;   // p ascends per thread
+  for (int o = 32; o > 0; o >>= 1) ext = max(ext, __shfl_xor(ext, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ext;
+  __syncthreads();
+  if (threadIdx.x == 0) flag[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 // Per-expert lists of occupied blocks in ascending order (one workgroup).
@@ -160,6 +164,32 @@ __global__ void __launch_bounds__(256) expert_lists_kernel(const int32_t* __rest
     __syncthreads();
   }
   if (threadIdx.x == 0) off[E] = carry;
+}
+
+// Tile ranges of a slot-blocked GEMM (see moe_tiles.hpp): start[b] = sum over
+// blocks before b of ceil(extent / W) * other; start[N] = the total.  One workgroup.
+__global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restrict__ ext, int N, int W, int other,
+                                                          int32_t* __restrict__ start) {
+  __shared__ int red[4];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < N; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    const int c = b < N ? (ext[b] + W - 1) / W * other : 0;
+    int tot;
+    const int pos = block_exclusive_scan(c, red, &tot) + carry;
+    if (b < N) start[b] = pos;
+    __syncthreads();
+    if (threadIdx.x == 0) carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) start[N] = carry;
+}
+
+hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st) {
+  tile_ranges_kernel<<<1, 256, 0, st>>>(ext, int(N), W, other, start);
+  return hipGetLastError();
 }
 
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,

@@ -11,11 +11,14 @@
 // epilogue's results makes the same rounding decisions as an exact sum would):
 //   dS[b][i][p] = sum_h deq(W_down[e])[i][h] * deq(dY[tok_p])[h]   (fp32; dY rows
 //                 are quantised along H once and gathered here by token id)
-// Blocks without tokens are skipped.
+// Only tiles holding a slot before the block's extent (one past its last routed
+// slot) run (moe_tiles.hpp); dS stays unwritten past it, and the epilogue
+// treats padding slots as zeros.
 #pragma once
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
 #include "kernels.hpp"
+#include "moe_tiles.hpp"
 #include "mx_device.hpp"
 
 namespace mx {
@@ -34,14 +37,14 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   constexpr int SMEM = GENERIC ? 2 * (BM + BN) * v2::BK : v3::smem_bytes(BM, BN);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   constexpr int FM = BM / 64, FN = BN / 64;
-  const int per_blk = p.tiles_m * p.tiles_n;
-  const int id = v2::xcd_remap(blockIdx.x, gridDim.x);
-  const int b = id / per_blk;
+  // live tiles only: block b's slot tiles up to its extent, times the I tiles
+  BlockTiles bt;
+  if (!block_tile(p.tile_start, int(p.N), p.tiles_m, blockIdx.x, bt)) return;
+  const int b = bt.b;
   int tm, tn;
-  v2::grouped_tile<8>(id - b * per_blk, p.tiles_m, p.tiles_n, tm, tn);
+  v2::grouped_tile<8>(bt.local, p.tiles_m, bt.slots, tm, tn);
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;   // m: i, n: slot within block
   const int64_t sbase = int64_t(b) * p.B;
-  if (!p.flag[b]) return;
   const int64_t e = p.b2e[b];
   const int wave = threadIdx.x >> 6;
 
@@ -95,9 +98,11 @@ template <int BM, int BN, bool G>
 hipError_t phase1_launch(Phase1Args p, int fg, int fw, hipStream_t st) {
   p.tiles_m = int((p.I + BM - 1) / BM);
   p.tiles_n = int((p.B + BN - 1) / BN);
-  const int64_t blocks = int64_t(p.tiles_m) * p.tiles_n * p.N;
+  const int64_t blocks = (int64_t(p.tiles_m) * p.tiles_n * p.N + 7) & ~int64_t(7);   // every tile, rounded to 8
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const unsigned grid = unsigned(blocks);
+  hipError_t e = launch_tile_ranges(p.flag, p.N, BN, p.tiles_m, p.tile_start, st);
+  if (e != hipSuccess) return e;
   if (G) {   // the bf16 values carry no format
     phase1_go<BM, BN, G, kE4M3, kE4M3>(p, grid, st);
   } else if (fg == kE4M3) {

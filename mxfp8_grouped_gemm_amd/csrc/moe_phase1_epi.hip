@@ -92,9 +92,13 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
       uint16_t gb[32], ub[32];
       float dv[32];
 #if defined(__HIP_DEVICE_COMPILE__)
-      const auto rd = MX_RSRC(v2::make_rsrc(p.ds + int64_t(b) * p.I * p.B, uint32_t(p.I * p.B * 4)));
-      const auto rc = MX_RSRC(v2::make_rsrc(p.ckpt + int64_t(b) * 2 * p.I * p.B, uint32_t(p.I * p.B * 4)));
-      const uint32_t vd = uint32_t((s0 + sl) * 4), vc = ok ? uint32_t((s0 + sl) * 2) : v2::kOOB;
+      // a tile past the block's extent is all padding (dS unwritten there): its
+      // descriptors have no records, so every load reads zero without memory traffic
+      const uint32_t live = s0 < p.flag[b] ? 1u : 0u;
+      const auto rd = MX_RSRC(v2::make_rsrc(p.ds + int64_t(b) * p.I * p.B, live * uint32_t(p.I * p.B * 4)));
+      const auto rc = MX_RSRC(v2::make_rsrc(p.ckpt + int64_t(b) * 2 * p.I * p.B, live * uint32_t(p.I * p.B * 4)));
+      // padding slots read dS and the checkpoint as zeros (their dS may be unwritten)
+      const uint32_t vd = ok ? uint32_t((s0 + sl) * 4) : v2::kOOB, vc = ok ? uint32_t((s0 + sl) * 2) : v2::kOOB;
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
         const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + k) * p.B));

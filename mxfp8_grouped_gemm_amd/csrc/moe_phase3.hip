@@ -8,6 +8,7 @@
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
 #include "kernels.hpp"
+#include "moe_tiles.hpp"
 #include "mx_device.hpp"
 
 namespace mx {
@@ -17,18 +18,19 @@ using v2::KMapPlain;
 
 // ---------------------------------------------------------------------------
 // Phase 3 tiles: block b, rows = slots m0.., columns = hidden index n0..
+// Live tiles only (moe_tiles.hpp): block b's slot tiles up to its extent, times
+// the H tiles.  b < 0: no tile.
 struct P3Pos {
   int b;
   int64_t m0, n0;
 };
 template <int BM, int BN>
-__device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int tile) {
-  const int per_blk = p.tiles_m * p.tiles_n;
-  const int id = v2::xcd_remap(tile, p.total);
-  const int b = id / per_blk;
+__device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int wg) {
+  BlockTiles bt;
+  if (!block_tile(p.tile_start, int(p.N), p.tiles_n, wg, bt)) return P3Pos{-1, 0, 0};
   int tm, tn;
-  v2::grouped_tile<8>(id - b * per_blk, p.tiles_m, p.tiles_n, tm, tn);
-  return P3Pos{b, int64_t(tm) * BM, int64_t(tn) * BN};
+  v2::grouped_tile<8>(bt.local, bt.slots, p.tiles_n, tm, tn);
+  return P3Pos{bt.b, int64_t(tm) * BM, int64_t(tn) * BN};
 }
 
 // dX scatter-add of one tile: slot row s of block b adds into its token's row.
@@ -56,7 +58,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_generic(Phase3Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
   constexpr int FM = BM / 64, FN = BN / 64;
   const P3Pos tp = p3_pos<BM, BN>(p, blockIdx.x);
-  if (!p.flag[tp.b]) return;
+  if (tp.b < 0) return;
   const int64_t e = p.b2e[tp.b];
   const int wave = threadIdx.x >> 6;
   const int64_t sbase = int64_t(tp.b) * p.B, twoI = 2 * p.I;
@@ -78,7 +80,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[v3::smem_bytes(BM, BN)];
   constexpr int FM = BM / 64, FN = BN / 64;
   const P3Pos tp = p3_pos<BM, BN>(p, blockIdx.x);
-  if (!p.flag[tp.b]) return;
+  if (tp.b < 0) return;
   const int64_t e = p.b2e[tp.b];
   const int64_t sbase = int64_t(tp.b) * p.B, twoI = 2 * p.I;
   v3::Op<BM> A;
@@ -99,9 +101,10 @@ template <int BM, int BN>
 static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipStream_t st) {
   p.tiles_m = int((p.B + BM - 1) / BM);
   p.tiles_n = int((p.H + BN - 1) / BN);
-  const int64_t total = int64_t(p.tiles_m) * p.tiles_n * p.N;
+  const int64_t total = (int64_t(p.tiles_m) * p.tiles_n * p.N + 7) & ~int64_t(7);   // every tile, rounded to 8
   if (total > INT32_MAX) return hipErrorInvalidValue;
-  p.total = int(total);
+  hipError_t e = launch_tile_ranges(p.flag, p.N, BM, p.tiles_n, p.tile_start, st);
+  if (e != hipSuccess) return e;
   if (generic) {
     const unsigned grid = unsigned(total);
     if (fg == 0 && fw == 0) phase3_generic<BM, BN, 0, 0><<<grid, v2::kThreads, 0, st>>>(p);

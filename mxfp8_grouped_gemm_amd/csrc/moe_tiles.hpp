@@ -1,0 +1,43 @@
+// moe_tiles.hpp -- tile spaces of the slot-blocked MoE GEMMs (Phases 1 and 3).
+//
+// Block b's slots past its extent (one past its last routed slot) are padding,
+// so the block contributes ceil(extent / W) slot tiles of W slots, each times
+// `other` tiles along the GEMM's other dimension.  start[b] (b = 0..N) is the
+// index of block b's first tile and start[N] the total, built on the device
+// before the GEMM (launch_tile_ranges).  The GEMM's grid covers every tile a
+// full block could have; workgroups past the total exit at once.  Being the
+// highest ids, those are spread over all XCDs, and the live ids are remapped
+// so each XCD takes a contiguous range of live tiles: skipped tiles never
+// leave one XCD idle while another still holds its full share.
+#pragma once
+#include "gemm_v2.hpp"
+
+namespace mx {
+
+struct BlockTiles {
+  int b;       // block
+  int local;   // tile index inside the block's range
+  int slots;   // slot tiles of the block
+};
+
+// Maps a workgroup id to its tile; false: no tile (exit).
+__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, int N, int other, int wg,
+                                           BlockTiles& t) {
+  const int total = start[N];
+  const int t8 = (total + 7) & ~7;   // the XCD remap needs a multiple of 8 ids
+  if (wg >= t8) return false;
+  const int id = v2::xcd_remap(wg, t8);
+  if (id >= total) return false;
+  int lo = 0, hi = N;   // start[lo] <= id < start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (start[mid] <= id) lo = mid;
+    else hi = mid;
+  }
+  t.b = lo;
+  t.local = id - start[lo];
+  t.slots = (start[lo + 1] - start[lo]) / other;
+  return true;
+}
+
+}  // namespace mx
