@@ -70,7 +70,10 @@ __device__ __forceinline__ void store_tile(const GemmStoreArgs& p, int g, int64_
 // Workgroup id -> (group, first row, first column).  Hardware hands out
 // workgroup ids round robin over the 8 XCDs, so ids are remapped to give each
 // XCD a contiguous range, walked GM tile-rows at a time (co-resident tiles
-// share operand rows in that XCD's L2).
+// share operand rows in that XCD's L2).  With several groups (experts, whose
+// contraction lengths differ) and a tile count per group divisible by 8, each
+// XCD takes a contiguous eighth of every group instead, so no XCD is left
+// holding the longest group alone; for one group the two maps coincide.
 struct TilePos {
   int g;
   int64_t m0, n0;
@@ -78,7 +81,14 @@ struct TilePos {
 template <int BM, int BN>
 __device__ __forceinline__ TilePos tile_pos(const GemmStoreArgs& p, int tile) {
   const int per_group = p.tiles_m * p.tiles_n;
-  const int id = v2::xcd_remap(tile, p.total);
+  int id;
+  if (per_group % 8 == 0) {
+    const int share = per_group / 8, j = tile / 8;   // j-th workgroup on XCD tile % 8
+    const int gg = j / share;
+    id = gg * per_group + (tile % 8) * share + (j - gg * share);
+  } else {
+    id = v2::xcd_remap(tile, p.total);
+  }
   const int g = id / per_group;
   int tm, tn;
   v2::grouped_tile<8>(id - g * per_group, p.tiles_m, p.tiles_n, tm, tn);
