@@ -203,7 +203,9 @@ typedef struct {
  *                                                     (slots past a block's extent unwritten)
  *   phase1_tiles/phase3_tiles [N+1] int32             first tile of each block over its
  *                                                     live slot tiles, and the total
- *   dx_acc [T,H] fp32, daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
+ *   dx_slot [P,H] fp32 (each routed slot's dX row, summed per token at the end),
+ *   slot_of [T,E] int32 (the slot of pair (t, e), -1 = none),
+ *   daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
  *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32
@@ -215,7 +217,7 @@ typedef struct {
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_acc, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_slot, slot_of, daff_slot, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 
@@ -246,8 +248,8 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
  *   4 Phase 1 (the product dS)
  *   5 Phase 1 epilogue (SwiGLU backward; dGU along I and along slots, the
  *     intermediate along slots, d(affinity) and db1 partial sums)
- *   6 Phase 3 (dX scatter-add)    7 Phase 2 (dW_gate_up)       8 Phase 4 (dW_down)
- *   9 finalise to bf16
+ *   6 Phase 3 (dX rows per slot)  7 Phase 2 (dW_gate_up)       8 Phase 4 (dW_down)
+ *   9 finalise (dX summed per token in expert order, the rest to bf16)
  * Errors as for moe_bwd_mxfp8, plus INVALID_ARG for a stage outside the range. */
 #define MOE_BWD_NUM_STAGES 10
 int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,

@@ -207,7 +207,8 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->phase1_ds, N * I * B * 4);
   put(L->phase1_tiles, (N + 1) * 4);
   put(L->phase3_tiles, (N + 1) * 4);
-  put(L->dx_acc, T * H * 4);
+  put(L->dx_slot, N * B * H * 4);
+  put(L->slot_of, T * E * 4);
   put(L->daff_slot, P * 4);
   put(L->db1_acc, E * 2 * I * 4);
   put(L->db2_acc, E * H * 4);
@@ -291,7 +292,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   int32_t* flag = reinterpret_cast<int32_t*>(at(L.block_flag));
   int32_t* boff = reinterpret_cast<int32_t*>(at(L.expert_block_offsets));
   int32_t* blist = reinterpret_cast<int32_t*>(at(L.expert_block_list));
-  float* dx_acc = reinterpret_cast<float*>(at(L.dx_acc));
+  float* dx_slot = reinterpret_cast<float*>(at(L.dx_slot));
+  int32_t* slot_of = reinterpret_cast<int32_t*>(at(L.slot_of));
   float* daff_slot = reinterpret_cast<float*>(at(L.daff_slot));
   float* db1_acc = reinterpret_cast<float*>(at(L.db1_acc));
   float* db2_acc = reinterpret_cast<float*>(at(L.db2_acc));
@@ -302,14 +304,13 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   if (stage >= lo && stage <= hi && (e = (call)) != hipSuccess) return hip_status(e, what);
 
   stage = 0;
-  STEP(mx::launch_fill_u32(dx_acc, T * H, 0u, st), "zero dX accumulator");
   STEP(mx::launch_fill_u32(daff_slot, P, 0u, st), "zero d(affinity) accumulator");
   if (a->has_bias) {
     STEP(mx::launch_fill_u32(db1_acc, E * 2 * I, 0u, st), "zero db1 accumulator");
     STEP(mx::launch_fill_u32(db2_acc, E * H, 0u, st), "zero db2 accumulator");
   }
   STEP(mx::launch_slot_setup(a->token_position_to_id, a->block_to_expert, a->expert_affinities_masked, T, E, N, B,
-                             slot_tok, slot_aff, flag, boff, blist, st),
+                             slot_tok, slot_aff, slot_of, flag, boff, blist, st),
        "slot setup");
   stage = 1;
   // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later).
@@ -377,7 +378,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p3.wgu_codes = a->gate_up_codes; p3.wgu_scales = gu_pairs ? at(L.wgu_scales_pairs) : a->gate_up_scales;
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.tile_start = reinterpret_cast<int32_t*>(at(L.phase3_tiles));
-  p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_acc = dx_acc;
+  p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_slot = dx_slot;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
   stage = 7;
   // Phase 2: dW_gate_up[e] = X_tok . dGU_tok^T over the expert's blocks
@@ -396,7 +397,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   STEP(mx::launch_gemm_store(g, int(E), a->fmt_act, a->fmt_grad, st), "phase 4");
   stage = 9;
   // finalisation
-  STEP(mx::launch_f32_to_bf16(dx_acc, a->hidden_states_grad, T * H, st), "dX to bf16");
+  STEP(mx::launch_dx_reduce(dx_slot, slot_of, T, E, H, a->hidden_states_grad, st), "dX per-token sums");
   STEP(mx::launch_daff_scatter(daff_slot, slot_tok, a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,
                                st),
        "d(affinity) scatter");

@@ -110,16 +110,20 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
 
 // ---------------------------------------------------------------------------
 // Per-slot routing info: token (-1 for padding or an invalid block expert) and
-// affinity (0 for padding).  Outside [0,T) is padding.
+// affinity (0 for padding), and the inverse map slot_of[t*E + e] = the slot
+// of pair (t, e) (a pair occupies at most one slot; -1 where none, filled
+// beforehand).  Outside [0,T) is padding.
 __global__ void slot_info_kernel(const int32_t* __restrict__ tpid, const int32_t* __restrict__ b2e,
                                  const float* __restrict__ aff, int64_t T, int64_t E, int64_t B, int64_t P,
-                                 int32_t* __restrict__ slot_tok, float* __restrict__ slot_aff) {
+                                 int32_t* __restrict__ slot_tok, float* __restrict__ slot_aff,
+                                 int32_t* __restrict__ slot_of) {
   for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < P; s += int64_t(gridDim.x) * blockDim.x) {
     const int64_t e = b2e[s / B];
     const int64_t t = tpid[s];
     const bool ok = t >= 0 && t < T && e >= 0 && e < E;
     slot_tok[s] = ok ? int32_t(t) : -1;
     slot_aff[s] = ok ? aff[t * E + e] : 0.f;
+    if (ok) slot_of[t * E + e] = int32_t(s);
   }
 }
 
@@ -193,12 +197,14 @@ hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, i
 }
 
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
-                             int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* flag,
-                             int32_t* off, int32_t* list, hipStream_t st) {
+                             int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* slot_of,
+                             int32_t* flag, int32_t* off, int32_t* list, hipStream_t st) {
   const int64_t P = N * B;
   const int64_t want = (P + 255) / 256;
+  hipError_t err = launch_fill_u32(reinterpret_cast<uint32_t*>(slot_of), T * E, 0xffffffffu, st);
+  if (err != hipSuccess) return err;
   slot_info_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(tpid, b2e, aff, T, E, B, P, slot_tok,
-                                                                           slot_aff);
+                                                                           slot_aff, slot_of);
   block_flag_kernel<<<unsigned(N), 256, 0, st>>>(slot_tok, B, flag);
   expert_lists_kernel<<<1, 256, 0, st>>>(b2e, flag, int(N), int(E), off, list);
   return hipGetLastError();
@@ -273,6 +279,60 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStr
   if (n <= 0) return hipSuccess;
   const int64_t want = (n / 4 + 255) / 256 + 1;
   f32_to_bf16_kernel<<<unsigned(want < 16384 ? want : 16384), 256, 0, st>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+// dX[t] = sum over t's routed slots, in expert order, of the slot's Phase-3 row
+// (fp32), rounded to bf16; a token without slots gets zeros.  One workgroup
+// per token; H % 32 == 0.  The token's slots are compacted into LDS 256
+// experts at a time (a block scan keeps expert order), then each thread sums
+// up to four 4-column groups over them.
+__global__ void __launch_bounds__(256) dx_reduce_kernel(const float* __restrict__ dx_slot,
+                                                        const int32_t* __restrict__ slot_of, int64_t E, int64_t H,
+                                                        uint16_t* __restrict__ dx) {
+  __shared__ int red[4];
+  __shared__ int32_t list[256];
+  const int64_t t = blockIdx.x;
+  const int32_t* so = slot_of + t * E;
+  const int64_t C = H / 4;   // 4-column groups
+  for (int64_t c0 = 0; c0 < C; c0 += 4 * 256) {
+    float4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t e0 = 0; e0 < E; e0 += 256) {
+      const int64_t e = e0 + threadIdx.x;
+      const int32_t s = e < E ? so[e] : -1;
+      int n;
+      const int pos = block_exclusive_scan(s >= 0 ? 1 : 0, red, &n);
+      if (s >= 0) list[pos] = s;
+      __syncthreads();
+      for (int k = 0; k < n; ++k) {
+        const float4* row = reinterpret_cast<const float4*>(dx_slot + int64_t(list[k]) * H);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t c = c0 + threadIdx.x + 256 * j;
+          if (c < C) {
+            const float4 v = row[c];
+            acc[j].x += v.x; acc[j].y += v.y; acc[j].z += v.z; acc[j].w += v.w;
+          }
+        }
+      }
+      __syncthreads();   // the list is rewritten by the next chunk
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = c0 + threadIdx.x + 256 * j;
+      if (c < C)
+        reinterpret_cast<uint2*>(dx + t * H)[c] =
+            make_uint2(bf16x2_pack(acc[j].x, acc[j].y), bf16x2_pack(acc[j].z, acc[j].w));
+    }
+  }
+}
+
+hipError_t launch_dx_reduce(const float* dx_slot, const int32_t* slot_of, int64_t T, int64_t E, int64_t H,
+                            uint16_t* dx, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  dx_reduce_kernel<<<unsigned(T), 256, 0, st>>>(dx_slot, slot_of, E, H, dx);
   return hipGetLastError();
 }
 

@@ -3,8 +3,9 @@
 // _up_projection_backward_act, the input-gradient product).
 //
 // Per block b (tile rows = slot p, columns = hidden index h, contraction over 2I):
-//   dX[tok_p][h] += sum_{j,i} deq(dGU)[p][j][i] * deq(W_gate_up[e])[h][j][i]
-//   as fp32 atomic adds (a token's top-k slots sit in different blocks).
+//   dX_slot[p][h] = sum_{j,i} deq(dGU)[p][j][i] * deq(W_gate_up[e])[h][j][i]
+//   stored per slot in fp32; the finalisation sums each token's slots (they
+//   sit in different blocks) in expert order, so dX is deterministic.
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
 #include "kernels.hpp"
@@ -33,7 +34,7 @@ __device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int wg) {
   return P3Pos{bt.b, int64_t(tm) * BM, int64_t(tn) * BN};
 }
 
-// dX scatter-add of one tile: slot row s of block b adds into its token's row.
+// dX rows of one tile: routed slot s of block b stores its row.
 template <int BM, int BN>
 __device__ __forceinline__ void p3_store(const Phase3Args& p, const P3Pos& tp, const v16f (&acc)[BM / 64][BN / 64]) {
   const int64_t sbase = int64_t(tp.b) * p.B;
@@ -42,10 +43,10 @@ __device__ __forceinline__ void p3_store(const Phase3Args& p, const P3Pos& tp, c
       const int64_t s = tp.m0 + v2::acc_row<BM, BN>(FI, Q);
       const int64_t tok = s < p.B ? p.slot_tok[sbase + s] : -1;
       if (tok >= 0) {
-        float* dst = p.dx_acc + tok * p.H;
+        float* dst = p.dx_slot + (sbase + s) * p.H;
         v2::static_for<BN / 64>([&](auto FJ) {
           const int64_t hh = tp.n0 + v2::acc_col<BM, BN>(FJ);
-          if (hh < p.H) atomicAdd(dst + hh, acc[FI][FJ][int(Q)]);
+          if (hh < p.H) dst[hh] = acc[FI][FJ][int(Q)];
         });
       }
     });
