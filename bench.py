@@ -94,7 +94,9 @@ def stage_work(cfg, N):
     TK, P = T * K, N * B
     q = 1 + 1 / 32                      # bytes per quantised element (code + its share of a scale)
     return {
-        "setup": ("hbm", T * H * 4 + P * 12),
+        # slot routing info (token, affinity, the (token, expert) -> slot map, block
+        # extents and lists) and the zeroed d(a) accumulator
+        "setup": ("hbm", P * 20 + T * E * 8),
         # dY: bf16 in, codes + scales out; H % 128 == 0: W_down's and W_gate_up's scales
         # re-laid pair-major (read + write); otherwise Phase 1 reads bf16 values, so dY's
         # are written too and W_down's codes are read and their bf16 values written
@@ -109,7 +111,8 @@ def stage_work(cfg, N):
         "phase3": ("mfma", 4 * TK * H * I),
         "phase2": ("mfma", 4 * TK * H * I),
         "phase4": ("mfma", 2 * TK * H * I),
-        "finalize": ("hbm", T * H * (4 + 2) + P * 4 + T * E * 2),
+        # dX: each routed pair's fp32 row read, the token's bf16 row written; d(a)
+        "finalize": ("hbm", TK * H * 4 + T * H * 2 + P * 4 + T * E * (4 + 2)),
     }
 
 
