@@ -142,32 +142,53 @@ __global__ void __launch_bounds__(256) block_flag_kernel(const int32_t* __restri
   if (threadIdx.x == 0) flag[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
-// Per-expert lists of occupied blocks in ascending order (one workgroup).
-__global__ void __launch_bounds__(256) expert_lists_kernel(const int32_t* __restrict__ b2e,
-                                                           const int32_t* __restrict__ flag, int N, int E,
-                                                           int32_t* __restrict__ off, int32_t* __restrict__ list) {
+// Per-expert lists of occupied blocks in ascending order: counts (one
+// workgroup per expert, coalesced scans of the blocks), offsets (one
+// workgroup), then each expert's list in block order (one workgroup each).
+__global__ void __launch_bounds__(256) expert_count_kernel(const int32_t* __restrict__ b2e,
+                                                           const int32_t* __restrict__ flag, int N,
+                                                           int32_t* __restrict__ cnt) {
+  __shared__ int red[4];
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int b = threadIdx.x; b < N; b += 256) c += (b2e[b] == e) & (flag[b] != 0);
+  int tot;
+  block_exclusive_scan(c, red, &tot);
+  if (threadIdx.x == 0) cnt[e] = tot;
+}
+
+__global__ void __launch_bounds__(256) expert_offsets_kernel(const int32_t* __restrict__ cnt, int E,
+                                                             int32_t* __restrict__ off) {
   __shared__ int red[4];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   for (int e0 = 0; e0 < E; e0 += 256) {
     const int e = e0 + threadIdx.x;
-    int c = 0;
-    if (e < E)
-      for (int b = 0; b < N; ++b) c += (b2e[b] == e) & (flag[b] != 0);
     int tot;
-    const int pos = block_exclusive_scan(c, red, &tot) + carry;
-    if (e < E) {
-      off[e] = pos;
-      int w = pos;
-      for (int b = 0; b < N; ++b)
-        if (b2e[b] == e && flag[b]) list[w++] = b;
-    }
+    const int pos = block_exclusive_scan(e < E ? cnt[e] : 0, red, &tot) + carry;
+    if (e < E) off[e] = pos;
     __syncthreads();
     if (threadIdx.x == 0) carry += tot;
     __syncthreads();
   }
   if (threadIdx.x == 0) off[E] = carry;
+}
+
+__global__ void __launch_bounds__(256) expert_list_kernel(const int32_t* __restrict__ b2e,
+                                                          const int32_t* __restrict__ flag, int N,
+                                                          const int32_t* __restrict__ off, int32_t* __restrict__ list) {
+  __shared__ int red[4];
+  const int e = blockIdx.x;
+  int w = off[e];
+  for (int b0 = 0; b0 < N; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    const int hit = b < N && b2e[b] == e && flag[b] != 0;
+    int tot;
+    const int pos = block_exclusive_scan(hit, red, &tot);
+    if (hit) list[w + pos] = b;
+    w += tot;
+  }
 }
 
 // Tile ranges of a slot-blocked GEMM (see moe_tiles.hpp): start[b] = sum over
@@ -206,7 +227,12 @@ hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const floa
   slot_info_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(tpid, b2e, aff, T, E, B, P, slot_tok,
                                                                            slot_aff, slot_of);
   block_flag_kernel<<<unsigned(N), 256, 0, st>>>(slot_tok, B, flag);
-  expert_lists_kernel<<<1, 256, 0, st>>>(b2e, flag, int(N), int(E), off, list);
+  // the counts go to off[1..E] and become offsets in place: in each 256-expert
+  // chunk every count is read before the scan's barrier and every offset
+  // written after it, and a chunk writes only indices the later chunks do not read
+  expert_count_kernel<<<unsigned(E), 256, 0, st>>>(b2e, flag, int(N), off + 1);
+  expert_offsets_kernel<<<1, 256, 0, st>>>(off + 1, int(E), off);
+  expert_list_kernel<<<unsigned(E), 256, 0, st>>>(b2e, flag, int(N), off, list);
   return hipGetLastError();
 }
 
@@ -218,6 +244,7 @@ hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const floa
 // ---------------------------------------------------------------------------
 // Bias terms (has_bias): per slot <dY_t, b2[e]> added into daff_slot (one wave
 // per slot), and db2[e][h] += sum over a block's slots of a * dY[t][h].
+// H % 32 == 0 and dY / b2 rows 16-byte aligned: 8 values per lane and load.
 __global__ void __launch_bounds__(256) bias_dot_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ b2,
                                                        const int32_t* __restrict__ slot_tok,
                                                        const int32_t* __restrict__ b2e, int64_t H, int64_t B,
@@ -228,8 +255,15 @@ __global__ void __launch_bounds__(256) bias_dot_kernel(const uint16_t* __restric
   const int64_t t = slot_tok[s];
   if (t < 0) return;
   const int64_t e = b2e[s / B];
+  const uint4* yr = reinterpret_cast<const uint4*>(dy + t * H);
+  const uint4* br = reinterpret_cast<const uint4*>(b2 + e * H);
   float acc = 0.f;
-  for (int64_t h = lane; h < H; h += 64) acc += bf16_to_f32(dy[t * H + h]) * bf16_to_f32(b2[e * H + h]);
+  for (int64_t c = lane; c < H / 8; c += 64) {
+    const uint4 y = yr[c], w = br[c];
+    const uint32_t ya[4] = {y.x, y.y, y.z, y.w}, wa[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += lo_bf16(ya[k]) * lo_bf16(wa[k]) + hi_bf16(ya[k]) * hi_bf16(wa[k]);
+  }
   acc = wave_sum_xor(acc, 64);
   if (lane == 0) atomicAdd(daff_slot + s, acc);
 }
@@ -242,12 +276,15 @@ __global__ void __launch_bounds__(256) db2_kernel(const uint16_t* __restrict__ d
   const int64_t h = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (!flag[b] || h >= H) return;
   const int64_t e = b2e[b];
-  float acc = 0.f;
-  for (int64_t p = 0; p < B; ++p) {
-    const int64_t t = slot_tok[b * B + p];
-    if (t >= 0) acc += slot_aff[b * B + p] * bf16_to_f32(dy[t * H + h]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four independent chains keep four loads in flight
+  for (int64_t p = 0; p < B; p += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = slot_tok[b * B + p + k];
+      if (t >= 0) acc[k] += slot_aff[b * B + p + k] * bf16_to_f32(dy[t * H + h]);
+    }
   }
-  atomicAdd(db2_acc + e * H + h, acc);
+  atomicAdd(db2_acc + e * H + h, (acc[0] + acc[1]) + (acc[2] + acc[3]));
 }
 
 hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,
