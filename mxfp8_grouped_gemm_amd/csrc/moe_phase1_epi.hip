@@ -196,9 +196,15 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
       const int64_t g32 = p0 / 32;   // pair-major [P/128][2I][4]
       p.dgu_tok_scales[((g32 >> 2) * twoI + i) * 4 + (g32 & 3)] = uint8_t(Xg + 127);
       p.dgu_tok_scales[((g32 >> 2) * twoI + p.I + i) * 4 + (g32 & 3)] = uint8_t(Xu + 127);
-      if (p.has_bias) {
-        atomicAdd(p.db1_acc + (e * 2 + 0) * p.I + i, sg);
-        atomicAdd(p.db1_acc + (e * 2 + 1) * p.I + i, su);
+      if (p.has_bias) {   // the row's NG groups sit in consecutive lanes: one atomic per row
+        for (int o = 1; o < NG; o <<= 1) {
+          sg += __shfl_xor(sg, o, 64);
+          su += __shfl_xor(su, o, 64);
+        }
+        if (c == 0) {
+          atomicAdd(p.db1_acc + (e * 2 + 0) * p.I + i, sg);
+          atomicAdd(p.db1_acc + (e * 2 + 1) * p.I + i, su);
+        }
       }
       // the intermediate operand (activation format)
       const uint16_t* isrc = stg_in + r * ISH + 34 * c;
