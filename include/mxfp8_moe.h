@@ -205,7 +205,8 @@ typedef struct {
  *                                                     live slot tiles, and the total
  *   dx_slot [P,H] fp32 (each routed slot's dX row, summed per token at the end),
  *   slot_of [T,E] int32 (the slot of pair (t, e), -1 = none),
- *   daff_slot [P] fp32, db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
+ *   daff_slot [P] fp32 (the <dY, b2> term), daff_part [I/32,P] fp32 (d(a) partials
+ *   per 32 rows i), db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
  *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32
@@ -217,7 +218,7 @@ typedef struct {
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_slot, slot_of, daff_slot, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_slot, slot_of, daff_slot, daff_part, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 

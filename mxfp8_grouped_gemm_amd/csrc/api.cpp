@@ -210,6 +210,7 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->dx_slot, N * B * H * 4);
   put(L->slot_of, T * E * 4);
   put(L->daff_slot, P * 4);
+  put(L->daff_part, I / 32 * P * 4);
   put(L->db1_acc, E * 2 * I * 4);
   put(L->db2_acc, E * H * 4);
   put(L->expert_block_offsets, (E + 1) * 4);
@@ -304,7 +305,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   if (stage >= lo && stage <= hi && (e = (call)) != hipSuccess) return hip_status(e, what);
 
   stage = 0;
-  STEP(mx::launch_fill_u32(daff_slot, P, 0u, st), "zero d(affinity) accumulator");
+  STEP(mx::launch_fill_u32(daff_slot, P, 0u, st), "zero the d(affinity) bias term");
   if (a->has_bias) {
     STEP(mx::launch_fill_u32(db1_acc, E * 2 * I, 0u, st), "zero db1 accumulator");
     STEP(mx::launch_fill_u32(db2_acc, E * H, 0u, st), "zero db2 accumulator");
@@ -364,7 +365,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.dgu_row_codes = at(L.dgu_row_codes); p1.dgu_row_scales = at(L.dgu_row_scales);
   p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);
   p1.inter_tok_codes = at(L.inter_tok_codes); p1.inter_tok_scales = at(L.inter_tok_scales);
-  p1.daff_slot = daff_slot; p1.db1_acc = db1_acc;
+  p1.daff_part = reinterpret_cast<float*>(at(L.daff_part)); p1.db1_acc = db1_acc;
   p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias; p1.fmt_act = a->fmt_act;
   p1.dgu_row_pairs = gu_pairs;
   STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_weight, st), "phase 1");
@@ -398,7 +399,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   stage = 9;
   // finalisation
   STEP(mx::launch_dx_reduce(dx_slot, slot_of, T, E, H, a->hidden_states_grad, st), "dX per-token sums");
-  STEP(mx::launch_daff_scatter(daff_slot, slot_tok, a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,
+  STEP(mx::launch_daff_scatter(daff_slot, reinterpret_cast<const float*>(at(L.daff_part)), I / 32, slot_tok,
+                               a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,
                                st),
        "d(affinity) scatter");
   if (a->has_bias) {

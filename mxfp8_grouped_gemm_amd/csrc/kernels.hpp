@@ -66,8 +66,9 @@ hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* sl
                        const int32_t* b2e, const int32_t* flag, int64_t H, int64_t B, int64_t N, float* daff_slot,
                        float* db2_acc, hipStream_t st);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st);
-hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, const int32_t* b2e, int64_t T,
-                               int64_t E, int64_t B, int64_t N, uint16_t* daff, hipStream_t st);
+hipError_t launch_daff_scatter(const float* daff_slot, const float* daff_part, int64_t nparts,
+                               const int32_t* slot_tok, const int32_t* b2e, int64_t T, int64_t E, int64_t B,
+                               int64_t N, uint16_t* daff, hipStream_t st);
 
 // moe_phase1_*.hip (product, epilogue), moe_phase3.hip
 struct Phase1Args {
@@ -93,7 +94,7 @@ struct Phase1Args {
   uint8_t* dgu_tok_scales;      // pair-major [P/128][2I][4]
   uint8_t* inter_tok_codes;     // [I][P]: the intermediate (times a with the affinity on I), slot groups
   uint8_t* inter_tok_scales;    // pair-major [P/128][I][4]
-  float* daff_slot;             // [P]
+  float* daff_part;             // [I/32][P]: d(a) partial sums per 32 rows i
   float* db1_acc;               // [E][2][I]
   int affinity_on_i;            // 1: the intermediate operand carries the affinity
   int has_bias;                 // 1: accumulate db1

@@ -242,7 +242,7 @@ hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const floa
 // checkpoint [N,2,I,B] (P1 gate_up_proj_act_checkpoint_T).  Groups of 32
 // consecutive slots; 4 lanes per group, 8 slots per lane.  Padding -> 0.
 // ---------------------------------------------------------------------------
-// Bias terms (has_bias): per slot <dY_t, b2[e]> added into daff_slot (one wave
+// Bias terms (has_bias): per slot <dY_t, b2[e]> stored in daff_slot (one wave
 // per slot), and db2[e][h] += sum over a block's slots of a * dY[t][h].
 // H % 32 == 0 and dY / b2 rows 16-byte aligned: 8 values per lane and load.
 __global__ void __launch_bounds__(256) bias_dot_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ b2,
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(256) bias_dot_kernel(const uint16_t* __restric
     for (int k = 0; k < 4; ++k) acc += lo_bf16(ya[k]) * lo_bf16(wa[k]) + hi_bf16(ya[k]) * hi_bf16(wa[k]);
   }
   acc = wave_sum_xor(acc, 64);
-  if (lane == 0) atomicAdd(daff_slot + s, acc);
+  if (lane == 0) daff_slot[s] = acc;   // the slot's <dY, b2> term
 }
 
 __global__ void __launch_bounds__(256) db2_kernel(const uint16_t* __restrict__ dy, const int32_t* __restrict__ slot_tok,
@@ -373,22 +373,42 @@ hipError_t launch_dx_reduce(const float* dx_slot, const int32_t* slot_of, int64_
   return hipGetLastError();
 }
 
-__global__ void daff_scatter_kernel(const float* __restrict__ daff_slot, const int32_t* __restrict__ slot_tok,
-                                    const int32_t* __restrict__ b2e, int64_t E, int64_t B, int64_t P,
-                                    uint16_t* __restrict__ daff) {
-  for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < P; s += int64_t(gridDim.x) * blockDim.x) {
+// d(a) of each routed slot: its bias term (0 without a bias) plus the
+// epilogue's partials over the rows i, to bf16 at t*E+e.  A workgroup takes 64
+// slots; wave w sums partials w, w+4, ... (coalesced over the slots), and the
+// four sums are added in wave order, so the result does not vary run to run.
+__global__ void __launch_bounds__(256) daff_scatter_kernel(const float* __restrict__ daff_slot,
+                                                           const float* __restrict__ daff_part, int64_t nparts,
+                                                           const int32_t* __restrict__ slot_tok,
+                                                           const int32_t* __restrict__ b2e, int64_t E, int64_t B,
+                                                           int64_t P, uint16_t* __restrict__ daff) {
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t s = int64_t(blockIdx.x) * 64 + lane;
+  float acc = 0.f;
+  if (s < P) {
+#pragma unroll 8
+    for (int64_t g = w; g < nparts; g += 4) acc += daff_part[g * P + s];
+  }
+  part[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && s < P) {
     const int64_t t = slot_tok[s];
-    if (t >= 0) daff[t * E + b2e[s / B]] = f32_to_bf16(daff_slot[s]);
+    if (t >= 0) {
+      const float d = daff_slot[s] + ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]));
+      daff[t * E + b2e[s / B]] = f32_to_bf16(d);
+    }
   }
 }
 
-hipError_t launch_daff_scatter(const float* daff_slot, const int32_t* slot_tok, const int32_t* b2e, int64_t T,
-                               int64_t E, int64_t B, int64_t N, uint16_t* daff, hipStream_t st) {
+hipError_t launch_daff_scatter(const float* daff_slot, const float* daff_part, int64_t nparts,
+                               const int32_t* slot_tok, const int32_t* b2e, int64_t T, int64_t E, int64_t B,
+                               int64_t N, uint16_t* daff, hipStream_t st) {
   hipError_t err = launch_fill_u16(daff, T * E, 0, st);
   if (err != hipSuccess) return err;
   const int64_t P = N * B;
-  const int64_t want = (P + 255) / 256;
-  daff_scatter_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(daff_slot, slot_tok, b2e, E, B, P, daff);
+  daff_scatter_kernel<<<unsigned((P + 63) / 64), 256, 0, st>>>(daff_slot, daff_part, nparts, slot_tok, b2e, E, B, P,
+                                                                daff);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // Per slot p of block b (token t, affinity a_p; padding slots contribute zeros)
 // and intermediate index i, from dS = Phase 1's product and the checkpoint g, u:
 //   ga = bf16(silu(g)), inter = bf16(ga * u)
-//   d(a)_p += sum_i dS * inter                  (fp32 atomics per slot)
+//   d(a)_p  = sum_i dS * inter                  (a partial per 32 rows i, summed
+//                                                at the end in order)
 //   dInter = a_p * dS
 //   dGate = bf16(dInter * u * silu'(g)), dUp = bf16(dInter * ga)
 //   -> quantised along I        (Phase-3 A operand, dgu_row [P][2I])
@@ -18,7 +19,7 @@
 // HBM-bound: a workgroup takes a tile of TI rows i x TS slots of one block
 // (TS = min(B, 256), TI * TS = 8192).  Pass 1, one thread per (slot, 32 rows):
 // coalesced loads of dS and the checkpoint, the element-wise math, the I-axis
-// groups in registers and their 32-byte code runs, d(a); dG|dU and the
+// groups in registers and their 32-byte code runs, d(a) partials; dG|dU and the
 // intermediate are staged in LDS.  Pass 2, one thread per (row, 32-slot group):
 // the slot-axis groups from LDS, stored as 32-byte runs.
 #include "kernels.hpp"
@@ -148,7 +149,7 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
         p.dgu_row_scales[slot * (twoI / 32) + gg] = uint8_t(Xg + 127);
         p.dgu_row_scales[slot * (twoI / 32) + gu_] = uint8_t(Xu + 127);
       }
-      if (ok) atomicAdd(p.daff_slot + slot, daff);
+      p.daff_part[(i0 / 32) * P + slot] = daff;   // this 32-row group's share of d(a)
       // staging for the slot-axis groups: consecutive threads, consecutive slots
 #pragma unroll
       for (int k = 0; k < 32; ++k) {

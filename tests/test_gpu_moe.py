@@ -93,22 +93,23 @@ def test_moe_build_blocks_bit_exact_and_edge_cases():
 
 
 def test_moe_deterministic_weight_grads_and_dy_scaling():
-    """Phases 2/4 and the per-token dX sums have a fixed summation order: repeated
-    runs give identical dW and dX, and scaling dY by 2^3 scales them by exactly 8
-    (the E8M0 scales absorb it).  d(a) and the bias sums use atomics."""
+    """Phases 2/4, the per-token dX sums and the d(a) partials have a fixed
+    summation order: repeated runs give identical dW, dX and d(a), and scaling dY
+    by 2^3 scales them by exactly 8 (the E8M0 scales absorb it).  The bias sums
+    use atomics."""
     cfg = SMALL["fine_s"]
     gp = gpu_problem(cfg)
     a = {k: v.clone() for k, v in gp["op"].run().items() if v is not None}
     b = gp["op"].run()
-    for k in ("dwgu", "dwd", "dx"):
+    for k in ("dwgu", "dwd", "dx", "daff"):
         assert torch.equal(a[k], b[k]), k
-    for k in ("daff", "db1", "db2"):
+    for k in ("db1", "db2"):
         assert rel_fro(bf(host(b[k])), bf(host(a[k]))) < 1e-5, k
     gp["t"]["dy"].mul_(8.0)
     c = gp["op"].run()
-    for k in ("dwgu", "dwd", "dx"):
+    for k in ("dwgu", "dwd", "dx", "daff"):
         assert torch.equal(c[k].float(), 8.0 * a[k].float()), k
-    for k in ("daff", "db1", "db2"):
+    for k in ("db1", "db2"):
         assert rel_fro(bf(host(c[k])), 8.0 * bf(host(a[k]))) < 1e-5, k
 
 
@@ -118,10 +119,8 @@ def test_moe_extra_padding_blocks_change_nothing():
     o1 = {k: v.clone() for k, v in g1["op"].run().items() if v is not None}
     g2 = gpu_problem(cfg, N=g1["N"] + 3)
     o2 = g2["op"].run()
-    for k in ("dwgu", "dwd", "dx"):
+    for k in ("dwgu", "dwd", "dx", "daff"):
         assert torch.equal(o1[k], o2[k]), k
-    for k in ("daff",):
-        assert rel_fro(bf(host(o2[k])), bf(host(o1[k]))) < 1e-5, k
 
 
 def test_moe_rejects_bad_arguments():
