@@ -184,3 +184,24 @@ def test_moe_full_size_sampled(name):
     print(name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= TOL, (k, v)
+
+
+def test_moe_stages_in_order_equal_one_call():
+    """The per-stage entry point: stages 0..NUM_STAGES-1 run in order on a fresh
+    workspace produce what one full call produces (bitwise for every output with
+    a fixed summation order; the bias sums use atomics)."""
+    for name in ("medium_s", "fine_s"):
+        cfg = SMALL[name]
+        g1 = gpu_problem(cfg)
+        o1 = {k: v.clone() for k, v in g1["op"].run().items() if v is not None}
+        g2 = gpu_problem(cfg)
+        op = g2["op"]
+        for s in range(op.NUM_STAGES):
+            op.stage(s)
+        torch.cuda.synchronize()
+        o2 = op.out
+        for k in ("dwgu", "dwd", "dx", "daff"):
+            assert torch.equal(o1[k], o2[k]), (name, k)
+        if cfg.has_bias:
+            for k in ("db1", "db2"):
+                assert rel_fro(bf(host(o2[k])), bf(host(o1[k]))) < 1e-5, (name, k)
