@@ -95,7 +95,7 @@ def stage_work(cfg, N):
     q = 1 + 1 / 32                      # bytes per quantised element (code + its share of a scale)
     return {
         # slot routing info (token, affinity, the (token, expert) -> slot map, block
-        # extents and lists) and the zeroed d(a) accumulator
+        # extents and lists) and the zeroed per-slot d(a) bias term
         "setup": ("hbm", P * 20 + T * E * 8),
         # dY: bf16 in, codes + scales out; H % 128 == 0: W_down's and W_gate_up's scales
         # re-laid pair-major (read + write); otherwise Phase 1 reads bf16 values, so dY's
@@ -112,7 +112,7 @@ def stage_work(cfg, N):
         "phase2": ("mfma", 4 * TK * H * I),
         "phase4": ("mfma", 2 * TK * H * I),
         # dX: each routed pair's fp32 row read, the token's bf16 row written; d(a)
-        "finalize": ("hbm", TK * H * 4 + T * H * 2 + P * 4 + T * E * (4 + 2)),
+        "finalize": ("hbm", TK * H * 4 + T * H * 2 + P * 4 * (1 + I // 32) + T * E * (4 + 2)),
     }
 
 
