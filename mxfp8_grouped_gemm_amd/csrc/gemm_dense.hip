@@ -13,6 +13,7 @@
 
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
+#include "gemm_v4.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
@@ -120,29 +121,50 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_generic(GemmStoreArgs
   store_tile<BM, BN>(p, tp.g, tp.m0, tp.n0, acc);
 }
 
-// Aligned shapes: one tile per workgroup on the four-stage ring loop.
+// Aligned shapes: one tile per workgroup on a ring loop, the pair-slot ring
+// (v4) when PAIR, else the four-slot ring (v3).
 // LIST: K runs over each group's block list (MoE Phases 2 and 4).
-template <int BM, int BN, int FA, int FB, bool LIST>
+template <int BM, int BN, int FA, int FB, bool LIST, bool PAIR>
 __global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[v3::smem_bytes(BM, BN)];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PAIR ? v4::smem_bytes(BM, BN) : v3::smem_bytes(BM, BN)];
   constexpr int FM = BM / 64, FN = BN / 64;
   const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x);
-  v3::Op<BM> A;
-  v3::Op<BN> B;
   v3::ScaleDma<BM, BN> sd;
-  v3::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
-  v3::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
   v3::setup_scales(sd, p.a_scales, tp.m0, p.M, p.M * p.lda / 32, p.b_scales, tp.n0, p.N, p.N * p.ldb / 32);
-  v2::v16f acc[FM][FN];
+  // K bytes of the tile's group: its blocks, the last one cut at its extent
+  int64_t kbytes = p.K;
+  int b0 = 0;
   if constexpr (LIST) {
-    const int b0 = p.blk_off[tp.g], b1 = p.blk_off[tp.g + 1];
-    int64_t kbytes = int64_t(b1 - b0) * p.blk;
+    b0 = p.blk_off[tp.g];
+    const int b1 = p.blk_off[tp.g + 1];
+    kbytes = int64_t(b1 - b0) * p.blk;
     if (p.blk_ext && b1 > b0) kbytes -= p.blk - ((p.blk_ext[p.blk_list[b1 - 1]] + 127) & ~127);
-    const int nstages = int(kbytes / v3::SK);
-    const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
-    v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, km, smem, acc);
+  }
+  v2::v16f acc[FM][FN];
+  if constexpr (PAIR) {
+    v4::Op<BM> A;
+    v4::Op<BN> B;
+    v4::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
+    v4::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
+    const int npairs = int(kbytes / v4::PK);
+    if constexpr (LIST) {
+      const v4::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v4::PK))};
+      v4::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, npairs, km, smem, acc);
+    } else {
+      v4::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, npairs, v4::KMapPlain{}, smem, acc);
+    }
   } else {
-    v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, int(p.K / v3::SK), v3::KMapPlain{}, smem, acc);
+    v3::Op<BM> A;
+    v3::Op<BN> B;
+    v3::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
+    v3::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
+    const int nstages = int(kbytes / v3::SK);
+    if constexpr (LIST) {
+      const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
+      v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, km, smem, acc);
+    } else {
+      v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, v3::KMapPlain{}, smem, acc);
+    }
   }
   store_tile<BM, BN>(p, tp.g, tp.m0, tp.n0, acc);
 }
@@ -155,12 +177,12 @@ static void launch_generic(const GemmStoreArgs& p, int fa, int fb, unsigned grid
   else gemm_store_generic<BM, BN, 1, 1><<<grid, v2::kThreads, 0, st>>>(p);
 }
 
-template <int BM, int BN, bool LIST>
+template <int BM, int BN, bool LIST, bool PAIR>
 static void launch_ring(const GemmStoreArgs& p, int fa, int fb, unsigned grid, hipStream_t st) {
-  if (fa == 0 && fb == 0) gemm_store_ring<BM, BN, 0, 0, LIST><<<grid, v2::kThreads, 0, st>>>(p);
-  else if (fa == 0) gemm_store_ring<BM, BN, 0, 1, LIST><<<grid, v2::kThreads, 0, st>>>(p);
-  else if (fb == 0) gemm_store_ring<BM, BN, 1, 0, LIST><<<grid, v2::kThreads, 0, st>>>(p);
-  else gemm_store_ring<BM, BN, 1, 1, LIST><<<grid, v2::kThreads, 0, st>>>(p);
+  if (fa == 0 && fb == 0) gemm_store_ring<BM, BN, 0, 0, LIST, PAIR><<<grid, v2::kThreads, 0, st>>>(p);
+  else if (fa == 0) gemm_store_ring<BM, BN, 0, 1, LIST, PAIR><<<grid, v2::kThreads, 0, st>>>(p);
+  else if (fb == 0) gemm_store_ring<BM, BN, 1, 0, LIST, PAIR><<<grid, v2::kThreads, 0, st>>>(p);
+  else gemm_store_ring<BM, BN, 1, 1, LIST, PAIR><<<grid, v2::kThreads, 0, st>>>(p);
 }
 
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st) {
@@ -189,11 +211,16 @@ hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStr
   }
   const unsigned grid = unsigned(total);
   if (big) {
-    if (p.blk_list) launch_ring<256, 256, true>(p, fa, fb, grid, st);
-    else launch_ring<256, 256, false>(p, fa, fb, grid, st);
+    if (p.blk_list) {
+      if (p.pair) launch_ring<256, 256, true, true>(p, fa, fb, grid, st);
+      else launch_ring<256, 256, true, false>(p, fa, fb, grid, st);
+    } else {
+      if (p.pair) launch_ring<256, 256, false, true>(p, fa, fb, grid, st);
+      else launch_ring<256, 256, false, false>(p, fa, fb, grid, st);
+    }
   } else {
-    if (p.blk_list) launch_ring<128, 128, true>(p, fa, fb, grid, st);
-    else launch_ring<128, 128, false>(p, fa, fb, grid, st);
+    if (p.blk_list) launch_ring<128, 128, true, false>(p, fa, fb, grid, st);
+    else launch_ring<128, 128, false, false>(p, fa, fb, grid, st);
   }
   return hipGetLastError();
 }

@@ -271,6 +271,7 @@ struct Ring {
 
   uint8_t* smem;
   const T& x;
+  v4i dA, dB, dS[NS];   // descriptors, built once (scalar registers)
 
   // A stage's work in items, so a stage can be laid out as regions that each
   // issue one DMA instruction and read one fragment for the next stage ahead
@@ -305,17 +306,17 @@ struct Ring {
     const uint32_t slot = slot_of<S>(pos);
     const uint32_t cs = lds_addr(smem) + slot * CS;
     if (J < FM) {
-      v4i ra = rsrc(x.A.codes);
+      v4i ra = dA;
       ra[2] = live ? ra[2] : 0;
       dma16(ra, cs + uint32_t(wave * (BM / 4) + 16 * J) * SK, x.A.off[J], kc);
     } else {
-      v4i rb = rsrc(x.B.codes);
+      v4i rb = dB;
       rb[2] = live ? rb[2] : 0;
       dma16(rb, cs + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc);
     }
     if (J < NS) {
       const uint32_t ss = lds_addr(smem) + NBUF * CS + slot * SSB;
-      v4i rs = rsrc(x.sd.buf[J]);
+      v4i rs = dS[J < NS ? J : 0];
       rs[2] = live ? rs[2] : 0;
       dma4(rs, ss + uint32_t(wave + 4 * J) * 256, x.sd.off[J], (kc >> 7) * x.sd.pstride[J]);
     }
@@ -436,6 +437,12 @@ struct Ring {
 
   // The whole tile: positions 0 .. NBUF-1, then every stage.
   __device__ __forceinline__ void run(v16f (&acc)[FM][FN]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    dA = rsrc(x.A.codes);
+    dB = rsrc(x.B.codes);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) dS[j] = rsrc(x.sd.buf[j]);
+#endif
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll

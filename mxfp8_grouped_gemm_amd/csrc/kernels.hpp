@@ -46,6 +46,8 @@ struct GemmStoreArgs {
   const int32_t* blk_ext;   // optional: per block, one past its last routed column; a group's
                             // last block then contributes only that many columns, rounded up to 128
   int blk;
+  int pair;                       // 1: 256 x 256 tiles run the pair-slot ring (128-byte rows), 0: the
+                                  // four-slot ring (deeper look-ahead, for operands streamed from HBM)
   int tiles_m, tiles_n;
   int total;                      // tiles over all groups
 };

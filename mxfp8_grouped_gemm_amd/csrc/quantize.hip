@@ -252,15 +252,25 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
 
 // ---------------------------------------------------------------------------
 // Row-major scales of `groups` matrices [rows][k/32] -> pair-major
-// [groups][k/128][rows][4]; k % 128 == 0.  One thread per 4-byte word, reads
-// coalesced.
-__global__ void __launch_bounds__(256) scales_to_pairs_kernel(const uint32_t* __restrict__ in, int64_t groups,
-                                                               int64_t rows, int64_t kp, uint32_t* __restrict__ out) {
-  const int64_t total = groups * rows * kp;
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t p = i % kp, gr = i / kp, r = gr % rows, g = gr / rows;
-    out[(g * kp + p) * rows + r] = in[i];
+// [groups][k/128][rows][4]; k % 128 == 0.  A transpose of 4-byte words
+// ([rows][kp] -> [kp][rows] per group) through LDS: a workgroup moves 64 rows x
+// 32 words, reading 128-byte row runs and writing 256-byte column runs.
+__global__ void __launch_bounds__(256) scales_to_pairs_kernel(const uint32_t* __restrict__ in, int64_t rows,
+                                                              int64_t kp, uint32_t* __restrict__ out) {
+  __shared__ uint32_t tile[32][65];
+  const int64_t p0 = int64_t(blockIdx.x) * 32, r0 = int64_t(blockIdx.y) * 64, g = blockIdx.z;
+  const uint32_t* src = in + g * rows * kp;
+  uint32_t* dst = out + g * rows * kp;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = threadIdx.x + 256 * k, r = i >> 5, p = i & 31;
+    if (r0 + r < rows && p0 + p < kp) tile[p][r] = src[(r0 + r) * kp + p0 + p];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = threadIdx.x + 256 * k, p = i >> 6, r = i & 63;
+    if (r0 + r < rows && p0 + p < kp) dst[(p0 + p) * rows + r0 + r] = tile[p][r];
   }
 }
 
@@ -292,12 +302,12 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int 
 hipError_t launch_scales_to_pairs(const uint8_t* in, int64_t groups, int64_t rows, int64_t k, uint8_t* out,
                                   hipStream_t st) {
   if (k % 128) return hipErrorInvalidValue;
-  const int64_t total = groups * rows * (k / 128);
-  if (total == 0) return hipSuccess;
-  const int64_t want = (total + 255) / 256;
-  const int blocks = int(want < 65536 ? want : 65536);
-  scales_to_pairs_kernel<<<blocks, 256, 0, st>>>(reinterpret_cast<const uint32_t*>(in), groups, rows, k / 128,
-                                                 reinterpret_cast<uint32_t*>(out));
+  const int64_t kp = k / 128;
+  if (groups == 0 || rows == 0 || kp == 0) return hipSuccess;
+  if (groups > 65535 || (rows + 63) / 64 > 65535 || (kp + 31) / 32 > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid(unsigned((kp + 31) / 32), unsigned((rows + 63) / 64), unsigned(groups));
+  scales_to_pairs_kernel<<<grid, 256, 0, st>>>(reinterpret_cast<const uint32_t*>(in), rows, kp,
+                                               reinterpret_cast<uint32_t*>(out));
   return hipGetLastError();
 }
 

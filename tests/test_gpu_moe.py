@@ -70,6 +70,17 @@ def test_moe_small_full_parity(name):
         # token-axis scales are pair-major ([P/128][H][4])
         got = pairs_to_rows(ws[L[name_s]:L[name_s] + H * P // 32], H, P)
         assert np.array_equal(got, s.reshape(H, P // 32)), name_s
+    # the weights' scales re-laid pair-major for the ring loops: the oracle's bytes
+    _, gu_s, _, d_s = ex["wq"]
+    E, I = cfg.E, cfg.I
+    if (2 * I) % 128 == 0:
+        raw = ws[L["wgu_scales_pairs"]:L["wgu_scales_pairs"] + E * H * 2 * I // 32].reshape(E, -1)
+        for e in range(E):
+            assert np.array_equal(pairs_to_rows(raw[e], H, 2 * I), gu_s.reshape(E, H, 2 * I // 32)[e]), e
+    if H % 128 == 0:
+        raw = ws[L["wd_scales_pairs"]:L["wd_scales_pairs"] + E * I * H // 32].reshape(E, -1)
+        for e in range(E):
+            assert np.array_equal(pairs_to_rows(raw[e], I, H), d_s.reshape(E, I, H // 32)[e]), e
     # the intermediate operand: silu is evaluated in fp32 on the GPU and in fp64 by the
     # oracle, so a rare bf16 rounding may differ; codes must agree almost everywhere
     c, s = oracle.moe_token_operand(p, oracle.TOK_INTER)
