@@ -32,7 +32,9 @@
  * 2^(S-127)); each element is an 8-bit OCP E4M3 or E5M2 code.  The scale is
  * X = floor(log2(amax)) - emax (emax 8 for E4M3, 15 for E5M2), clamped to
  * [-127,127], with X = -127 for an all-zero group; codes round v*2^-X to
- * nearest-even and saturate at the format maximum.
+ * nearest-even and saturate at the format maximum.  Inputs are expected to be
+ * finite: the codes and scales of a group holding a NaN or an infinity are
+ * unspecified (no error is raised and other groups are unaffected).
  */
 #ifndef MXFP8_MOE_H
 #define MXFP8_MOE_H

@@ -123,6 +123,54 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
   return encode4s<FMT>(v0, v1, v2, v3, inv, inv, inv, inv);
 }
 
+// Codes of bf16 values, two packed per word (value 2k in the low half), with
+// scale 2^X: v_cvt_scalef32_pk_fp8_bf16 / _bf8_bf16 divide by the E8M0 scale
+// whose byte is the exponent field of their fp32 scale operand (byte 0
+// included: the float 0.0 stands for 2^-127) and round to nearest-even, but
+// return NaN / Inf past the format's largest finite value instead of
+// saturating.  So the magnitudes are clamped first to max * 2^X, in the bf16
+// domain: |bf16| orders like its 15-bit pattern, so one packed 16-bit minimum
+// clamps both halves.  Checked exhaustively on the GPU: every bf16 pair
+// pattern x every scale the group rule can produce gives the codes of
+// encode4 (clamp-and-convert in fp32).
+// bf16 bits of max * 2^X (max = 1.75 * 2^emax in both formats)
+template <int FMT>
+__device__ __forceinline__ uint32_t bf16_limit(int X) {
+  return (uint32_t(X + 127 + (FMT == kE4M3 ? 8 : 15)) << 7) | 0x60u;
+}
+// |w| clamped halfwise to the limits in lim2 (low and high half)
+__device__ __forceinline__ uint32_t clamp_bf16x2(uint32_t w, uint32_t lim2) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 m = __builtin_elementwise_min(__builtin_bit_cast(u16x2, w & 0x7fff7fffu), __builtin_bit_cast(u16x2, lim2));
+  return (w & 0x80008000u) | __builtin_bit_cast(uint32_t, m);
+}
+// halfwise max of |w| and m (packed 16-bit magnitudes)
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t m, uint32_t w) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                                __builtin_bit_cast(u16x2, w & 0x7fff7fffu)));
+}
+// the scale operand of the converters for 2^X
+__device__ __forceinline__ float cvt_scale(int X) { return __uint_as_float(uint32_t(X + 127) << 23); }
+// four codes from two clamped pairs (values 0, 1 in p01; 2, 3 in p23)
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_bf16x4(uint32_t p01, uint32_t p23, float s) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  s16x2 r = {0, 0};
+  if (FMT == kE4M3) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(b16x2, p01), s, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(b16x2, p23), s, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(b16x2, p01), s, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(b16x2, p23), s, true);
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+// low / high halves of two words, packed (a's in the low half)
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
 // bf16 round-to-nearest-even through the hardware converter (finite inputs;
 // equal to f32_to_bf16 there).
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }

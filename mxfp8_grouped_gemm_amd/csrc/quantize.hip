@@ -14,6 +14,7 @@
 // Scale layouts: row-major [rows][K/32] (one byte per group), or -- for
 // operands of the ring GEMM loop -- pair-major [K/128][rows][4], where word
 // (p, r) holds row r's four groups of K elements [128p, 128p + 128).
+#include "gemm_v2.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
@@ -162,77 +163,78 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// quant_tok: tile of 128 logical rows x 128 columns staged in LDS as bf16.
+// quant_tok: a workgroup covers 128 logical rows x 128 columns; wave w takes
+// rows 32w .. 32w+31 (one scale group) and lane l the column pair 2l, 2l+1.
 // Logical row r reads source row idx[r] (or r without an index); a source
 // outside [0, src_rows) contributes zeros (a padding slot).  With a row scale,
-// the staged value is bf16(fp32(scale[r] * v)).  Output: codes_t [cols][rows]
-// and scales_t [cols][rows/32] (or pair-major [rows/128][cols][4] with PAIRS);
+// the value is bf16(fp32(scale[r] * v)).  Output: codes_t [cols][rows] and
+// scales_t [cols][rows/32] (or pair-major [rows/128][cols][4] with PAIRS);
 // rows % 32 == 0 (% 128 with PAIRS) and cols % 8 == 0.
+// A row and its source index are the same for every lane of a wave, so each
+// of the 32 row loads is one 256-byte coalesced read (the index and the row
+// scale are scalar loads); the 32 values a lane needs stay in registers and
+// no LDS staging or barrier stands between the loads and the stores.
 constexpr int kTokRows = 128;
 constexpr int kTokCols = 128;
 
-template <int FMT, bool GATHER, bool ROWSCALE, bool PAIRS>
+template <int FMT, bool GATHER, bool ROWSCALE, bool PAIRS, bool OFF32>
 __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restrict__ x,
                                                          int64_t src_rows, int64_t cols,
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ rowscale,
                                                          int64_t rows, uint8_t* __restrict__ codes_t,
                                                          uint8_t* __restrict__ scales_t) {
-  __shared__ uint32_t tile[kTokRows][kTokCols / 2 + 1];   // bf16 pairs; +1 word breaks bank aliasing
-  const int tid = threadIdx.x;
-  const int64_t r0 = int64_t(blockIdx.y) * kTokRows;
-  const int64_t c0 = int64_t(blockIdx.x) * kTokCols;
-  // load: 16 lanes per row segment (256 B), 16 rows per pass, 8 passes
-  {
-    const int chunk = tid & 15;
-    const int64_t col = c0 + chunk * 8;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int rr = (tid >> 4) + pass * 16;
-      const int64_t r = r0 + rr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < rows && col < cols) {
-        const int64_t src = GATHER ? int64_t(idx[r]) : r;
-        if (src >= 0 && src < src_rows) {
-          v = *reinterpret_cast<const uint4*>(x + src * cols + col);
-          if (ROWSCALE) {   // bf16(a * x), round to nearest even
-            const float a = rowscale[r];
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int k = 0; k < 4; ++k)
-              w[k] = bf16x2_pack(a * __uint_as_float(w[k] << 16), a * __uint_as_float(w[k] & 0xffff0000u));
-            v = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      }
-      tile[rr][chunk * 4 + 0] = v.x;
-      tile[rr][chunk * 4 + 1] = v.y;
-      tile[rr][chunk * 4 + 2] = v.z;
-      tile[rr][chunk * 4 + 3] = v.w;
-    }
-  }
-  __syncthreads();
-  // quantise: lane -> column pair, wave -> group of 32 rows
-  const int cp = tid & 63;
-  const int grp = tid >> 6;
-  const int64_t row0 = r0 + grp * 32;
-  const int64_t colA = c0 + 2 * cp;
+  const int cp = threadIdx.x & 63;
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row0 = int64_t(blockIdx.y) * kTokRows + grp * 32;
+  const int64_t colA = int64_t(blockIdx.x) * kTokCols + 2 * cp;
   if (row0 >= rows || colA >= cols) return;
-  uint32_t amax0 = 0, amax1 = 0;
-  for (int r = 0; r < 32; ++r) {
-    const uint32_t w = tile[grp * 32 + r][cp];
-    amax0 = max(amax0, abs_bits_bf16(uint16_t(w & 0xffffu)));
-    amax1 = max(amax1, abs_bits_bf16(uint16_t(w >> 16)));
+  uint32_t w[32];   // bf16 of columns colA (low half) and colA + 1 (high half), rows row0 ..
+  if (src_rows > 0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // OFF32 (source under 2 GiB): buffer loads at 32-bit offsets, a padding row
+    // at an offset past the buffer, which reads zeros; the 32 row offsets live
+    // in vector registers (as 64-bit scalar addresses they spilled)
+    const auto rx = MX_RSRC(v2::make_rsrc(x, OFF32 ? uint32_t(src_rows * cols * 2) : 0u));
+    const uint32_t row_bytes = uint32_t(cols * 2), lane_bytes = uint32_t(colA * 2);
+#endif
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int64_t src = GATHER ? int64_t(idx[row0 + r]) : row0 + r;
+      const bool ok = src >= 0 && src < src_rows;
+      uint32_t v = 0u;
+#if defined(__HIP_DEVICE_COMPILE__)
+      if (OFF32) {
+        v = __builtin_amdgcn_raw_buffer_load_b32(rx, ok ? uint32_t(src) * row_bytes + lane_bytes : v2::kOOB, 0, 0);
+      } else {
+        // invalid rows read row 0's word and are zeroed: no branch per row
+        v = *reinterpret_cast<const uint32_t*>(x + (ok ? src : 0) * cols + colA);
+        v = ok ? v : 0u;
+      }
+#endif
+      w[r] = v;
+      if (ROWSCALE) {   // bf16(a * x), round to nearest even
+        const float a = rowscale[row0 + r];
+        w[r] = bf16x2_pack(a * __uint_as_float(w[r] << 16), a * __uint_as_float(w[r] & 0xffff0000u));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) w[r] = 0u;
   }
-  const int X0 = scale_exp<FMT>(amax0), X1 = scale_exp<FMT>(amax1);
-  const float i0 = inv_scale(X0), i1 = inv_scale(X1);
+  uint32_t m = 0;   // |bf16| maxima of both columns
+#pragma unroll
+  for (int r = 0; r < 32; ++r) m = absmax_bf16x2(m, w[r]);
+  const int X0 = scale_exp<FMT>(m << 16), X1 = scale_exp<FMT>(m & 0xffff0000u);
+  const uint32_t lim = bf16_limit<FMT>(X0) | (bf16_limit<FMT>(X1) << 16);
+  const float s0 = cvt_scale(X0), s1 = cvt_scale(X1);
   uint32_t p0[8], p1[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const uint32_t w0 = tile[grp * 32 + q * 4 + 0][cp], w1 = tile[grp * 32 + q * 4 + 1][cp];
-    const uint32_t w2 = tile[grp * 32 + q * 4 + 2][cp], w3 = tile[grp * 32 + q * 4 + 3][cp];
-    p0[q] = encode4<FMT>(__uint_as_float(w0 << 16), __uint_as_float(w1 << 16), __uint_as_float(w2 << 16),
-                         __uint_as_float(w3 << 16), i0);
-    p1[q] = encode4<FMT>(__uint_as_float(w0 & 0xffff0000u), __uint_as_float(w1 & 0xffff0000u),
-                         __uint_as_float(w2 & 0xffff0000u), __uint_as_float(w3 & 0xffff0000u), i1);
+    const uint32_t w0 = clamp_bf16x2(w[4 * q], lim), w1 = clamp_bf16x2(w[4 * q + 1], lim);
+    const uint32_t w2 = clamp_bf16x2(w[4 * q + 2], lim), w3 = clamp_bf16x2(w[4 * q + 3], lim);
+    p0[q] = encode_bf16x4<FMT>(lo_halves(w0, w1), lo_halves(w2, w3), s0);
+    p1[q] = encode_bf16x4<FMT>(hi_halves(w0, w1), hi_halves(w2, w3), s1);
   }
   uint4* dst0 = reinterpret_cast<uint4*>(codes_t + colA * rows + row0);
   uint4* dst1 = reinterpret_cast<uint4*>(codes_t + (colA + 1) * rows + row0);
@@ -341,17 +343,25 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
   return hipGetLastError();
 }
 
-template <int FMT, bool PAIRS>
+template <int FMT, bool PAIRS, bool OFF32>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
                          const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct) {
   if (idx && rs)
-    quant_tok_kernel<FMT, true, true, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, true, true, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
   else if (idx)
-    quant_tok_kernel<FMT, true, false, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, true, false, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
   else if (rs)
-    quant_tok_kernel<FMT, false, true, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, false, true, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
   else
-    quant_tok_kernel<FMT, false, false, PAIRS><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, false, false, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+}
+template <int FMT, bool PAIRS>
+static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
+                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct) {
+  if (src_rows * cols * 2 < int64_t(v2::kOOB))
+    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct);
+  else
+    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct);
 }
 
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
