@@ -258,6 +258,49 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
 int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,
                         int stage, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_router_bwd -- the router backward that consumes the affinity gradient
+ * ([P3] sonic-moe functional/backward.py: the softmax-over-top-k, top-k-over-
+ * softmax and top-k scatter backward kernels).  Per token t, with selected
+ * experts idx[t][0..K) (distinct, in [0,E); an entry outside that range is
+ * skipped) and upstream score gradients g[t][k], it writes the gradient of the
+ * router logits d[t][0..E):
+ *   MXFP8_ROUTER_SOFTMAX_OVER_TOPK  scores y = softmax over the K selected
+ *       logits (topk_scores = y, required):
+ *       d[idx_k] = y_k (g_k - sum_m g_m y_m), 0 elsewhere.
+ *   MXFP8_ROUTER_TOPK_OVER_SOFTMAX  p = softmax over all E logits (logits,
+ *       required), scores p[idx_k], or with renorm != 0 s_k = p[idx_k] / S,
+ *       S = sum_k p[idx_k] (topk_scores = s, required with renorm):
+ *       dp_k = g_k, or (g_k - sum_m g_m s_m) / S with renorm;
+ *       d[e] = p_e (dp(e) - sum_k dp_k p[idx_k]) for every e, where dp(e) is
+ *       dp_k at e = idx_k and 0 elsewhere.
+ *   MXFP8_ROUTER_TOPK  scores = the selected logits: d[idx_k] = g_k, 0 elsewhere.
+ * Arguments:
+ *   T, E, K      tokens, experts, selections per token; 1 <= K <= min(E, 32).
+ *   topk_idx     [T,K] int32.
+ *   topk_scores  [T,K] fp32 forward scores (see the modes), else may be NULL.
+ *   logits       [T,E] fp32 router logits (top-k over softmax), else may be NULL.
+ *   dscores      [T,K] fp32 upstream score gradients, or NULL and
+ *   daff         [T,E] bf16 affinity gradient in the masked layout (index
+ *                t*E + e, as moe_bwd_mxfp8 writes expert_affinities_masked_grad),
+ *                read at the selected experts: exactly one of the two.
+ *   renorm       0 or 1; non-zero only with MXFP8_ROUTER_TOPK_OVER_SOFTMAX.
+ *   dlogits      [T,E] fp32 output, every entry written.
+ * Arithmetic is fp32 (exp through the device math library).
+ * Errors: INVALID_ARG for an unknown mode, a shape outside the bounds above,
+ * renorm with another mode, both or neither of dscores/daff, a NULL pointer
+ * for a tensor the mode reads or writes, or a tensor not 16-byte aligned;
+ * HIP if the launch fails. */
+typedef enum {
+  MXFP8_ROUTER_SOFTMAX_OVER_TOPK = 0,
+  MXFP8_ROUTER_TOPK_OVER_SOFTMAX = 1,
+  MXFP8_ROUTER_TOPK = 2
+} mxfp8_router_mode;
+#define MXFP8_ROUTER_MAX_K 32
+int moe_router_bwd(int mode, int64_t T, int64_t E, int64_t K, const int32_t* topk_idx, const float* topk_scores,
+                   const float* logits, const float* dscores, const uint16_t* daff, int renorm, float* dlogits,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,9 @@ import torch
 
 E4M3 = 0
 E5M2 = 1
+ROUTER_SOFTMAX_OVER_TOPK = 0
+ROUTER_TOPK_OVER_SOFTMAX = 1
+ROUTER_TOPK = 2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxfp8_moe.so")
 
@@ -85,6 +88,7 @@ def _declare(L):
         ("moe_bwd_mxfp8_stage", C.c_int, [C.POINTER(MoeBwdArgs), _p, C.c_size_t, C.c_int, _p]),
         ("matmul_mxfp8_bwd_stage", C.c_int, [_p, _p, _p, _i64, _i64, _i64, C.c_int, C.c_int, C.c_int, _p, _p,
                                              _p, C.c_size_t, C.c_int, _p]),
+        ("moe_router_bwd", C.c_int, [C.c_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, C.c_int, _p, _p]),
     ):
         if hasattr(L, name):
             f = getattr(L, name)
@@ -286,3 +290,34 @@ class MoeBwd:
 def moe_bwd_mxfp8(*args, **kw):
     """Functional form: builds a MoeBwd and runs it once; returns the gradient dict."""
     return MoeBwd(*args, **kw).run()
+
+
+# ----------------------------------------------------------------------------- router backward
+def moe_router_bwd(mode: int, topk_idx: torch.Tensor, *, dscores: Optional[torch.Tensor] = None,
+                   daff: Optional[torch.Tensor] = None, topk_scores: Optional[torch.Tensor] = None,
+                   logits: Optional[torch.Tensor] = None, num_experts: Optional[int] = None, renorm: bool = False,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the router logits, [T, E] fp32 (include/mxfp8_moe.h: moe_router_bwd).
+
+    topk_idx [T, K] int32; the upstream score gradients come either as dscores
+    [T, K] fp32 or as daff, the bf16 affinity gradient in the masked layout
+    ([T*E] or [T, E], as moe_bwd_mxfp8 returns it).  topk_scores [T, K] fp32 and
+    logits [T, E] fp32 as the mode requires."""
+    T, K = topk_idx.shape
+    if num_experts is not None:
+        E = int(num_experts)
+    elif logits is not None:
+        E = logits.shape[1]
+    elif daff is not None:
+        E = daff.numel() // max(T, 1)
+    else:
+        raise ValueError("moe_router_bwd: give num_experts (or logits / daff)")
+    dev = topk_idx.device
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _check(lib().moe_router_bwd(mode, T, E, K, _dev(topk_idx, torch.int32, "topk_idx"),
+                                _dev(topk_scores, torch.float32, "topk_scores"), _dev(logits, torch.float32, "logits"),
+                                _dev(dscores, torch.float32, "dscores"), _dev(daff, torch.bfloat16, "daff"),
+                                1 if renorm else 0, _dev(out, torch.float32, "out"), _stream(topk_idx)),
+           "moe_router_bwd")
+    return out

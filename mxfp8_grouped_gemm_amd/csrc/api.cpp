@@ -424,4 +424,32 @@ int moe_bwd_mxfp8_stage(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, 
   return moe_run(a, ws, ws_bytes, stream, stage, stage);
 }
 
+int moe_router_bwd(int mode, int64_t T, int64_t E, int64_t K, const int32_t* topk_idx, const float* topk_scores,
+                   const float* logits, const float* dscores, const uint16_t* daff, int renorm, float* dlogits,
+                   void* stream) {
+  if (mode != MXFP8_ROUTER_SOFTMAX_OVER_TOPK && mode != MXFP8_ROUTER_TOPK_OVER_SOFTMAX && mode != MXFP8_ROUTER_TOPK)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: unknown mode %d", mode);
+  if (T < 0 || E < 1 || K < 1 || K > E || K > MXFP8_ROUTER_MAX_K)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: need T >= 0 and 1 <= K <= min(E, %d) (T %lld, E %lld, K %lld)",
+                MXFP8_ROUTER_MAX_K, (long long)T, (long long)E, (long long)K);
+  if (E > INT32_MAX / 2) return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: E %lld too large", (long long)E);
+  if (renorm && mode != MXFP8_ROUTER_TOPK_OVER_SOFTMAX)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: renorm applies to the top-k-over-softmax mode only");
+  if ((dscores == nullptr) == (daff == nullptr))
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: pass exactly one of dscores and daff");
+  if (T == 0) return ok();
+  const bool need_scores = mode == MXFP8_ROUTER_SOFTMAX_OVER_TOPK || (mode == MXFP8_ROUTER_TOPK_OVER_SOFTMAX && renorm);
+  const bool need_logits = mode == MXFP8_ROUTER_TOPK_OVER_SOFTMAX;
+  if (!topk_idx || !dlogits || (need_scores && !topk_scores) || (need_logits && !logits))
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: null pointer for a tensor this mode reads or writes");
+  const void* ptrs[6] = {topk_idx, topk_scores, logits, dscores, daff, dlogits};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MXFP8_ERR_INVALID_ARG, "moe_router_bwd: tensors must be 16-byte aligned");
+  mx::RouterArgs r{};
+  r.mode = mode; r.renorm = renorm ? 1 : 0; r.T = T; r.E = E; r.K = K;
+  r.idx = topk_idx; r.scores = topk_scores; r.logits = logits; r.dscores = dscores; r.daff = daff;
+  r.dlogits = dlogits;
+  return hip_status(mx::launch_router_bwd(r, static_cast<hipStream_t>(stream)), "router backward");
+}
+
 }  // extern "C"

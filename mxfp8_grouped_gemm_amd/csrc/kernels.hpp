@@ -53,6 +53,23 @@ struct GemmStoreArgs {
 };
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st);
 
+// router.hip -- the router backward (modes as mxfp8_router_mode in the public header)
+constexpr int kRouterSoftmaxOverTopk = 0;
+constexpr int kRouterTopkOverSoftmax = 1;
+constexpr int kRouterTopk = 2;
+struct RouterArgs {
+  int mode;
+  int renorm;                 // top-k over softmax: the selected probabilities were renormalised
+  int64_t T, E, K;
+  const int32_t* idx;         // [T,K] selected experts
+  const float* scores;        // [T,K] forward scores (softmax over top-k; renormalised top-k over softmax)
+  const float* logits;        // [T,E] router logits (top-k over softmax)
+  const float* dscores;       // [T,K] upstream score gradients, or null when
+  const uint16_t* daff;       // [T,E] bf16 affinity gradient is read at idx instead
+  float* dlogits;             // [T,E] output
+};
+hipError_t launch_router_bwd(const RouterArgs& p, hipStream_t st);
+
 // moe_aux.hip
 hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
 hipError_t launch_fill_u16(void* p, int64_t n, uint16_t v, hipStream_t st);

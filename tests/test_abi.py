@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     import mxfp8_grouped_gemm_amd as mx
     L = mx.lib()
     names = _declared()
-    assert {"mxfp8_quantize", "matmul_mxfp8_bwd", "moe_bwd_mxfp8", "moe_build_blocks"} <= names
+    assert {"mxfp8_quantize", "matmul_mxfp8_bwd", "moe_bwd_mxfp8", "moe_build_blocks", "moe_router_bwd"} <= names
     missing = [n for n in sorted(names) if not hasattr(L, n)]
     assert not missing, missing
 
@@ -44,3 +44,15 @@ def test_validation_without_gpu():
     assert L.moe_num_blocks(32768, 8, 128, 128) == 2175
     assert L.moe_num_blocks(2, 1, 4, 128) == -1
     assert mx.version().startswith("mxfp8_moe")
+    # router backward: every bad argument is caught before any launch
+    rb = L.moe_router_bwd
+    assert rb(3, 4, 8, 2, fake, fake, fake, fake, None, 0, fake, None) == 1 and "mode" in mx.last_error()
+    assert rb(0, 4, 8, 9, fake, fake, fake, fake, None, 0, fake, None) == 1              # K > E
+    assert rb(0, 4, 64, 33, fake, fake, fake, fake, None, 0, fake, None) == 1           # K above the bound
+    assert rb(0, 4, 8, 2, fake, fake, fake, fake, None, 1, fake, None) == 1 and "renorm" in mx.last_error()
+    assert rb(2, 4, 8, 2, fake, None, None, fake, fake, 0, fake, None) == 1              # both gradients
+    assert rb(2, 4, 8, 2, fake, None, None, None, None, 0, fake, None) == 1              # neither
+    assert rb(0, 4, 8, 2, fake, None, None, fake, None, 0, fake, None) == 1              # scores missing
+    assert rb(1, 4, 8, 2, fake, None, None, fake, None, 0, fake, None) == 1              # logits missing
+    assert rb(2, 4, 8, 2, C.c_void_p(0x10004), None, None, fake, None, 0, fake, None) == 1 and "aligned" in mx.last_error()
+    assert rb(2, 0, 8, 2, None, None, None, fake, None, 0, None, None) == 0             # no tokens
