@@ -12,8 +12,10 @@ intermediate).  The metric counts algorithmic FLOPs only: 12*H*I per routed
 
 Printed: one JSON line on stdout (progress goes to stderr).  Besides the step
 throughput it carries the roofline of the dominant kernel (timed live with HIP
-events on the library's stream), the dense MXFP8 backward (4096^3) and the
-quantiser throughput, and the CPU oracle timed on a bounded sample.
+events on the library's stream), the dense MXFP8 backward (4096^3), the
+quantiser throughput, the router backward that consumes d(affinity) (every mode
+on the fine workload's 32768 x 128 top-8 router), and the CPU oracle timed on a
+bounded sample.
 
 roofline.traffic is the dominant kernel's HBM bytes per launch from two
 rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on
@@ -42,13 +44,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = os.path.join(ROOT, "mxfp8_grouped_gemm_amd", "csrc")
 
 
+NOT_MOE_SOURCES = ("router.hip",)   # kernels no MoE-backward stage is built from
+
+
 def sources_sha256():
-    """Hash of the HIP sources (kernels and their headers), to tell whether
-    counters taken earlier still describe the kernels being timed."""
+    """Hash of the HIP sources the MoE-backward stages are built from (kernels,
+    headers and the launch code), to tell whether counters taken earlier still
+    describe the kernels being timed."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")) and name not in NOT_MOE_SOURCES:
             h.update(name.encode())
             with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
                 h.update(f.read())
@@ -238,6 +244,37 @@ def run_dense(reps):
     return res, res_q
 
 
+def run_router(reps):
+    """The router backward on the fine workload's router (32768 tokens, 128
+    experts, top-8): every mode, with the algorithmic bytes of one launch
+    (selections and score gradients read, logits read where the mode needs
+    them, every logit gradient written)."""
+    import torch
+    import mxfp8_grouped_gemm_amd as mx
+    T, E, K = 32768, 128, 8
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    logits = torch.randn((T, E), generator=gen, device="cuda", dtype=torch.float32) * 2.0
+    idx = torch.topk(logits, K, dim=1).indices.to(torch.int32).contiguous()
+    g = torch.randn((T, K), generator=gen, device="cuda", dtype=torch.float32)
+    sel = torch.gather(logits, 1, idx.long())
+    y = torch.softmax(sel, dim=1).contiguous()                     # forward scores, softmax over the top-k
+    ps = torch.gather(torch.softmax(logits, dim=1), 1, idx.long())
+    s = (ps / ps.sum(dim=1, keepdim=True)).contiguous()            # forward scores, renormalised top-k of the softmax
+    res = {"workload": f"router_T{T}_E{E}_top{K}"}
+    for name, mode, renorm, sc, lg, nbytes in (
+            ("softmax_over_topk", mx.ROUTER_SOFTMAX_OVER_TOPK, False, y, None, T * (12 * K + 4 * E)),
+            ("topk_over_softmax", mx.ROUTER_TOPK_OVER_SOFTMAX, False, None, logits, T * (8 * K + 8 * E)),
+            ("topk_over_softmax_renorm", mx.ROUTER_TOPK_OVER_SOFTMAX, True, s, logits, T * (12 * K + 8 * E)),
+            ("topk_scatter", mx.ROUTER_TOPK, False, None, None, T * (8 * K + 4 * E))):
+        out = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        call = lambda: mx.moe_router_bwd(mode, idx, dscores=g, topk_scores=sc, logits=lg, num_experts=E,
+                                         renorm=renorm, out=out)
+        call()
+        ms = _events_ms(call, reps)
+        res[name] = {"ms": round(ms, 5), **roofline_of("hbm", nbytes, ms)}
+    return res
+
+
 def cpu_baseline(cfg, moe, nthreads, n_tokens, n_cols):
     """The oracle (as it stands) on a bounded sample of the same workload: whole
     dX rows and d(a) of n_tokens tokens routed only to experts {0,1} (Phases 1
@@ -371,6 +408,9 @@ def main():
         out["dense"] = dense
         out["quantize"] = quant
         log(f"[bench] dense: {dense['TFLOP/s']} TFLOP/s; quantize {quant['achieved']} GB/s")
+        out["router_bwd"] = run_router(args.profile_reps + 5)
+        log("[bench] router backward: " + ", ".join(f"{k} {v['ms']} ms" for k, v in out["router_bwd"].items()
+                                                     if isinstance(v, dict)))
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample) ...")
         out["cpu_baseline"] = cpu_baseline(cfg, moe, args.cpu_threads, args.cpu_tokens, args.cpu_cols)

@@ -15,10 +15,14 @@
 // Every d[t][e] is written.  HBM-bound: a row is E fp32 logits read (top-k over
 // softmax only) and E fp32 gradients written, plus the K selections.
 //
-// Layout of the work: L = min(64, 2^ceil(log2 E)) lanes take one row, so a
-// wave holds 64 / L rows; the row's reductions are butterflies over its lanes.
-// Each lane walks the row's columns lane, lane + L, ..., so a row segment's
-// loads and stores are contiguous across its lanes.
+// Layout of the work: L lanes take one row (L = E/8 rounded to a power of two
+// in [8, 64]), so a wave holds 64 / L rows and each lane EPL = E/L <= 8 of the
+// row's columns, lane, lane + L, ..., in registers: a row's loads and stores
+// are contiguous across its lanes and issue together, and the row's
+// reductions are butterflies over its L lanes.  (One 64-lane wave per row ran
+// the fine workload's router at 9-14% of HBM bandwidth: four rounds of waves,
+// each waiting on its row's chain of dependent loads.)  Rows wider than
+// 64 * 8 columns loop over their columns instead.
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
@@ -41,7 +45,7 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 }  // namespace
 
-template <int L, int MODE, bool RENORM, bool DAFF>
+template <int L, int EPL, int MODE, bool RENORM, bool DAFF>
 __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(RouterArgs p) {
   const int lane = threadIdx.x % L;
   const int64_t t = int64_t(blockIdx.x) * (kRouterThreads / L) + threadIdx.x / L;
@@ -55,23 +59,53 @@ __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(RouterArgs p
     if (e < 0 || e >= E) return 0.f;
     return DAFF ? bf16_to_f32(p.daff[t * p.E + e]) : p.dscores[t * K + k];
   };
-  if (MODE == kRouterSoftmaxOverTopk) {
-    const float* y = p.scores + t * K;
+  // columns of this lane: lane + L * j (j < EPL), or a loop when EPL == 0
+  constexpr int NJ = EPL > 0 ? EPL : 1;
+  if (MODE == kRouterSoftmaxOverTopk || MODE == kRouterTopk) {
     float dot = 0.f;
-    for (int k = 0; k < K; ++k) dot += grad(k) * y[k];
-    for (int e = lane; e < E; e += L) {
+    if (MODE == kRouterSoftmaxOverTopk)
+      for (int k = 0; k < K; ++k) dot += grad(k) * p.scores[t * K + k];
+    // value at column e: selection k's term when e = idx[k], else 0
+    auto value = [&](int e) -> float {
       float v = 0.f;
       for (int k = 0; k < K; ++k)
-        if (idx[k] == e) v = y[k] * (grad(k) - dot);
-      out[e] = v;
+        if (idx[k] == e) v = MODE == kRouterTopk ? grad(k) : p.scores[t * K + k] * (grad(k) - dot);
+      return v;
+    };
+    if (EPL > 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + L * j;
+        if (e < E) out[e] = value(e);
+      }
+    } else {
+      for (int e = lane; e < E; e += L) out[e] = value(e);
     }
-  } else if (MODE == kRouterTopkOverSoftmax) {
+  } else {   // top-k over softmax
     const float* z = p.logits + t * p.E;
+    float zv[NJ];
     float m = -INFINITY;
-    for (int e = lane; e < E; e += L) m = fmaxf(m, z[e]);
+    if (EPL > 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + L * j;
+        zv[j] = e < E ? z[e] : -INFINITY;
+        m = fmaxf(m, zv[j]);
+      }
+    } else {
+      for (int e = lane; e < E; e += L) m = fmaxf(m, z[e]);
+    }
     m = seg_max<L>(m);
     float s = 0.f;
-    for (int e = lane; e < E; e += L) s += expf(z[e] - m);
+    if (EPL > 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        zv[j] = lane + L * j < E ? expf(zv[j] - m) : 0.f;   // unnormalised probabilities
+        s += zv[j];
+      }
+    } else {
+      for (int e = lane; e < E; e += L) s += expf(z[e] - m);
+    }
     s = seg_sum<L>(s);
     const float inv_s = 1.f / s;
     // the selected probabilities and the adjusted gradients at them
@@ -82,56 +116,64 @@ __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(RouterArgs p
       psum += expf(z[e] - m) * inv_s;
       if (RENORM) gdot += grad(k) * p.scores[t * K + k];
     }
+    const float inv_psum = RENORM ? 1.f / psum : 1.f;
     float dot = 0.f;   // sum_k dp_k p[idx_k]
     for (int k = 0; k < K; ++k) {
       const int e = idx[k];
       if (e < 0 || e >= E) continue;
-      const float dpk = RENORM ? (grad(k) - gdot) / psum : grad(k);
+      const float dpk = RENORM ? (grad(k) - gdot) * inv_psum : grad(k);
       dot += dpk * (expf(z[e] - m) * inv_s);
     }
-    for (int e = lane; e < E; e += L) {
+    auto dp_at = [&](int e) -> float {
       float dp = 0.f;
       for (int k = 0; k < K; ++k)
-        if (idx[k] == e) dp = RENORM ? (grad(k) - gdot) / psum : grad(k);
-      out[e] = expf(z[e] - m) * inv_s * (dp - dot);
-    }
-  } else {   // top-k scatter
-    for (int e = lane; e < E; e += L) {
-      float v = 0.f;
-      for (int k = 0; k < K; ++k)
-        if (idx[k] == e) v = grad(k);
-      out[e] = v;
+        if (idx[k] == e) dp = RENORM ? (grad(k) - gdot) * inv_psum : grad(k);
+      return dp;
+    };
+    if (EPL > 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + L * j;
+        if (e < E) out[e] = zv[j] * inv_s * (dp_at(e) - dot);
+      }
+    } else {
+      for (int e = lane; e < E; e += L) out[e] = expf(z[e] - m) * inv_s * (dp_at(e) - dot);
     }
   }
 }
 
-template <int L, int MODE>
+template <int L, int EPL, int MODE>
 static void router_go(const RouterArgs& p, unsigned grid, hipStream_t st) {
   if (MODE == kRouterTopkOverSoftmax && p.renorm) {
-    if (p.daff) router_bwd_kernel<L, MODE, true, true><<<grid, kRouterThreads, 0, st>>>(p);
-    else router_bwd_kernel<L, MODE, true, false><<<grid, kRouterThreads, 0, st>>>(p);
+    if (p.daff) router_bwd_kernel<L, EPL, MODE, true, true><<<grid, kRouterThreads, 0, st>>>(p);
+    else router_bwd_kernel<L, EPL, MODE, true, false><<<grid, kRouterThreads, 0, st>>>(p);
   } else {
-    if (p.daff) router_bwd_kernel<L, MODE, false, true><<<grid, kRouterThreads, 0, st>>>(p);
-    else router_bwd_kernel<L, MODE, false, false><<<grid, kRouterThreads, 0, st>>>(p);
+    if (p.daff) router_bwd_kernel<L, EPL, MODE, false, true><<<grid, kRouterThreads, 0, st>>>(p);
+    else router_bwd_kernel<L, EPL, MODE, false, false><<<grid, kRouterThreads, 0, st>>>(p);
   }
 }
 
-template <int L>
+template <int L, int EPL>
 static void router_mode(const RouterArgs& p, hipStream_t st) {
   const int64_t rows_per_wg = kRouterThreads / L;
   const unsigned grid = unsigned((p.T + rows_per_wg - 1) / rows_per_wg);
-  if (p.mode == kRouterSoftmaxOverTopk) router_go<L, kRouterSoftmaxOverTopk>(p, grid, st);
-  else if (p.mode == kRouterTopkOverSoftmax) router_go<L, kRouterTopkOverSoftmax>(p, grid, st);
-  else router_go<L, kRouterTopk>(p, grid, st);
+  if (p.mode == kRouterSoftmaxOverTopk) router_go<L, EPL, kRouterSoftmaxOverTopk>(p, grid, st);
+  else if (p.mode == kRouterTopkOverSoftmax) router_go<L, EPL, kRouterTopkOverSoftmax>(p, grid, st);
+  else router_go<L, EPL, kRouterTopk>(p, grid, st);
 }
 
 hipError_t launch_router_bwd(const RouterArgs& p, hipStream_t st) {
   if (p.T <= 0) return hipSuccess;
   if ((p.T + 3) / 4 > int64_t(INT32_MAX)) return hipErrorInvalidValue;
-  if (p.E <= 8) router_mode<8>(p, st);
-  else if (p.E <= 16) router_mode<16>(p, st);
-  else if (p.E <= 32) router_mode<32>(p, st);
-  else router_mode<64>(p, st);
+  // L = E/8 rounded up to a power of two, kept in [8, 64]; EPL = columns per lane
+  if (p.E <= 8) router_mode<8, 1>(p, st);
+  else if (p.E <= 16) router_mode<8, 2>(p, st);
+  else if (p.E <= 32) router_mode<8, 4>(p, st);
+  else if (p.E <= 64) router_mode<8, 8>(p, st);
+  else if (p.E <= 128) router_mode<16, 8>(p, st);
+  else if (p.E <= 256) router_mode<32, 8>(p, st);
+  else if (p.E <= 512) router_mode<64, 8>(p, st);
+  else router_mode<64, 0>(p, st);
   return hipGetLastError();
 }
 

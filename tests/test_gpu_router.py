@@ -57,7 +57,7 @@ def _run(mode, renorm, z, idx, g, daff=None):
 
 @pytest.mark.parametrize("mode,renorm", MODES)
 @pytest.mark.parametrize("T,E,K", [(1000, 8, 2), (4096, 128, 8), (333, 64, 6), (257, 16, 4), (50, 300, 32),
-                                   (7, 3, 1), (129, 33, 5)])
+                                   (7, 3, 1), (129, 33, 5), (100, 24, 3), (64, 200, 8), (20, 600, 16)])
 def test_router_bwd_matches_oracle(mode, renorm, T, E, K):
     z, idx, g = _inputs(T, E, K, seed=T + E + K)
     got, ref, S = _run(mode, renorm, z, idx, g)
