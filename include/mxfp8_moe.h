@@ -181,6 +181,19 @@ typedef struct {
   uint16_t* down_proj_weight_grad;                /* [E,I,H] bf16                        */
   uint16_t* gate_and_up_proj_bias_grad;           /* [E,2,I] bf16 (has_bias)             */
   uint16_t* down_proj_bias_grad;                  /* [E,H] bf16 (has_bias)               */
+  /* Optional checkpoints ([P1] "Parameters": gate_act_checkpoint_T,
+   * intermediate_checkpoint_T, scaled_intermediate_checkpoint_T,
+   * down_proj_act_checkpoint).  NULL: the value is recomputed from the
+   * gate/up checkpoint, dY and the affinities.  Supplied: it is read instead;
+   * it must hold the value the recomputation rounds to (padding slots are
+   * ignored), and the gradients are then the same.  All bf16.               */
+  const uint16_t* gate_act_checkpoint_T;          /* [N,I,B] bf16(silu(gate_pre))        */
+  const uint16_t* intermediate_checkpoint_T;      /* [N,I,B] bf16(gate_act * up)         */
+  const uint16_t* scaled_intermediate_checkpoint_T; /* [N,I,B] bf16(a * intermediate);
+                                                     affinity on I only                 */
+  const uint16_t* down_proj_act_checkpoint;       /* [N,B,H] bf16(a * dY[token]) per slot;
+                                                     affinity on H only (the Phase-4
+                                                     operand)                           */
 } moe_bwd_mxfp8_args;
 
 /* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised

@@ -280,6 +280,16 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
         !aligned16(a->down_proj_bias_grad))
       return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: bias tensors must be 16-byte aligned");
   }
+  if (a->scaled_intermediate_checkpoint_T && a->affinity_on != 1)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: scaled_intermediate_checkpoint_T needs the affinity on I");
+  if (a->down_proj_act_checkpoint && a->affinity_on != 0)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: down_proj_act_checkpoint needs the affinity on H");
+  const void* opt[] = {a->gate_act_checkpoint_T, a->intermediate_checkpoint_T, a->scaled_intermediate_checkpoint_T,
+                       a->down_proj_act_checkpoint};
+  for (const void* q : opt)
+    if (q && !aligned16(q)) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: checkpoints must be 16-byte aligned");
+  if (a->down_proj_act_checkpoint && a->N * a->block_size * a->H * 2 >= int64_t(0x80000000u))
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: down_proj_act_checkpoint must be under 2 GiB");
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: workspace must be non-null and 256-byte aligned");
   moe_bwd_mxfp8_workspace_layout L;
@@ -340,9 +350,15 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   STEP(mx::launch_quant_tok(a->hidden_states, T, H, slot_tok, nullptr, P, a->fmt_act, at(L.x_tok_codes),
                             at(L.x_tok_scales), st, true),
        "gather-quantize X");
-  STEP(mx::launch_quant_tok(a->output_hidden_states_grad, T, H, slot_tok, a->affinity_on == 0 ? slot_aff : nullptr,
-                            P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st, true),
-       "gather-quantize dY");
+  if (a->down_proj_act_checkpoint) {   // a*dY supplied per slot: each routed slot reads its own row
+    STEP(mx::launch_quant_tok(a->down_proj_act_checkpoint, P, H, slot_tok, nullptr, P, a->fmt_grad,
+                              at(L.gy_tok_codes), at(L.gy_tok_scales), st, true, true),
+         "quantize the a*dY checkpoint");
+  } else {
+    STEP(mx::launch_quant_tok(a->output_hidden_states_grad, T, H, slot_tok, a->affinity_on == 0 ? slot_aff : nullptr,
+                              P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st, true),
+         "gather-quantize dY");
+  }
   stage = 3;
   if (a->has_bias)
     STEP(mx::launch_bias(a->output_hidden_states_grad, a->down_proj_bias, slot_tok, slot_aff, a->block_to_expert,
@@ -362,6 +378,9 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.tile_start = reinterpret_cast<int32_t*>(at(L.phase1_tiles));
   p1.slot_tok = slot_tok; p1.slot_aff = slot_aff; p1.b2e = a->block_to_expert; p1.flag = flag;
   p1.ckpt = a->gate_up_proj_act_checkpoint_T;
+  p1.ga_ckpt = a->gate_act_checkpoint_T;
+  p1.in_ckpt = a->intermediate_checkpoint_T;
+  p1.sc_ckpt = a->scaled_intermediate_checkpoint_T;
   p1.T = T; p1.H = H; p1.I = I; p1.E = E; p1.N = N; p1.B = B;
   p1.dgu_row_codes = at(L.dgu_row_codes); p1.dgu_row_scales = at(L.dgu_row_scales);
   p1.dgu_tok_codes = at(L.dgu_tok_codes); p1.dgu_tok_scales = at(L.dgu_tok_scales);

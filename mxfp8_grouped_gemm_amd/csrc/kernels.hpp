@@ -19,7 +19,7 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
                              uint8_t* scales, hipStream_t st);
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st, bool pairs = false);
+                            uint8_t* scales_t, hipStream_t st, bool pairs = false, bool self_rows = false);
 // gate/up weight scales [E][H][2I/32] -> pair-major per expert [E][2I/128][H][4]
 hipError_t launch_scales_to_pairs(const uint8_t* in, int64_t groups, int64_t rows, int64_t k, uint8_t* out,
                                   hipStream_t st);
@@ -106,6 +106,12 @@ struct Phase1Args {
   const int32_t* flag;          // [N]: the block's extent (one past its last routed slot)
   int32_t* tile_start;          // [N+1]: tile ranges over the blocks' live slot tiles (moe_tiles.hpp)
   const uint16_t* ckpt;         // [N][2][I][B]
+  // optional checkpoints supplied by the caller ([N][I][B] bf16 each), read in
+  // place of recomputing the value: silu(gate), the intermediate, and the
+  // intermediate times the affinity (affinity on I)
+  const uint16_t* ga_ckpt;
+  const uint16_t* in_ckpt;
+  const uint16_t* sc_ckpt;
   int64_t T, H, I, E, N, B;
   uint8_t* dgu_row_codes;       // [P][2I]
   uint8_t* dgu_row_scales;      // pair-major [2I/128][P][4] (dgu_row_pairs) or row-major [P][2I/32]

@@ -34,7 +34,29 @@ constexpr int kEpiThreads = 256;
 constexpr int kEpiElems = 8192;   // TI * TS
 }  // namespace
 
-template <int FG, bool ON_I, int TS>
+// The element-wise SwiGLU backward of one (slot, i): from dS = d, the
+// checkpoint's g and u and the affinity a, adds this element's share of d(a)
+// and returns bf16(dGate) | bf16(dUp) << 16 and the bf16 intermediate operand.
+// A supplied checkpoint value (HAS_*) replaces the recomputed one; the values
+// are rounded at the same points either way, so consistent checkpoints give
+// the same bits.
+template <bool ON_I>
+__device__ __forceinline__ uint32_t swiglu_bwd(float d, float g, float u, float a, bool has_ga, float ga_in,
+                                               bool has_in, float in_in, bool has_sc, uint16_t sc_in, float& daff,
+                                               uint16_t& it) {
+  const float sg = sigmoid_fast(g);
+  const float ga = has_ga ? ga_in : bf16_round(g * sg);   // silu(g)
+  const float in = has_in ? in_in : bf16_round(ga * u);   // intermediate
+  daff += d * in;
+  const float di = a * d;                                 // d(intermediate)
+  it = ON_I ? (has_sc ? sc_in : bf16_rne(a * in)) : uint16_t(__float_as_uint(in) >> 16);
+  return bf16x2_rne(di * u * dsilu_from(g, sg), di * ga);
+}
+
+// CK: the caller supplied at least one of the [N][I][B] checkpoints (silu(gate),
+// the intermediate, the scaled intermediate); pass 1 then runs its 32 rows in
+// two halves so that the extra loads fit in registers.
+template <int FG, bool ON_I, int TS, bool CK>
 __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
   constexpr int TI = kEpiElems / TS;         // rows of the tile
   constexpr int NG = TS / 32;                // 32-slot groups of a row
@@ -90,8 +112,9 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
       // this lane's; padding slots load through an offset past the buffer, which
       // reads zeros, so no load is conditional (each would be a branch with its
       // own wait, serialising the 96 loads a thread keeps in flight).
-      uint16_t gb[32], ub[32];
-      float dv[32];
+      uint32_t gu[32];   // bf16(dGate) | bf16(dUp) << 16
+      uint16_t it[32];   // bf16 intermediate operand
+      float daff = 0.f, amg = 0.f, amu = 0.f;
 #if defined(__HIP_DEVICE_COMPILE__)
       // a tile past the block's extent is all padding (dS unwritten there): its
       // descriptors have no records, so every load reads zero without memory traffic
@@ -100,30 +123,58 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
       const auto rc = MX_RSRC(v2::make_rsrc(p.ckpt + int64_t(b) * 2 * p.I * p.B, live * uint32_t(p.I * p.B * 4)));
       // padding slots read dS and the checkpoint as zeros (their dS may be unwritten)
       const uint32_t vd = ok ? uint32_t((s0 + sl) * 4) : v2::kOOB, vc = ok ? uint32_t((s0 + sl) * 2) : v2::kOOB;
+      if constexpr (!CK) {
+        uint16_t gb[32], ub[32];
+        float dv[32];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + k) * p.B));
-        dv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, vd, row * 4, 0));
-        gb[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, row * 2, 0);
-        ub[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, (row + uint32_t(p.I * p.B)) * 2, 0);
+        for (int k = 0; k < 32; ++k) {
+          const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + k) * p.B));
+          dv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, vd, row * 4, 0));
+          gb[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, row * 2, 0);
+          ub[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, (row + uint32_t(p.I * p.B)) * 2, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          gu[k] = swiglu_bwd<ON_I>(dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, false, 0.f, false, 0.f, false,
+                                   0, daff, it[k]);
+          amg = fmaxf(amg, fabsf(lo_bf16(gu[k])));
+          amu = fmaxf(amu, fabsf(hi_bf16(gu[k])));
+        }
+      } else {
+        // a checkpoint that was not supplied is read through a descriptor with
+        // no records: zeros, no memory traffic, and the value is recomputed
+        const bool has_ga = p.ga_ckpt != nullptr, has_in = p.in_ckpt != nullptr, has_sc = p.sc_ckpt != nullptr;
+        const int64_t blk = int64_t(b) * p.I * p.B;
+        const uint32_t ck_bytes = live * uint32_t(p.I * p.B * 2);
+        const auto rga = MX_RSRC(v2::make_rsrc(has_ga ? p.ga_ckpt + blk : p.ckpt, has_ga ? ck_bytes : 0u));
+        const auto rin = MX_RSRC(v2::make_rsrc(has_in ? p.in_ckpt + blk : p.ckpt, has_in ? ck_bytes : 0u));
+        const auto rsc = MX_RSRC(v2::make_rsrc(has_sc ? p.sc_ckpt + blk : p.ckpt, has_sc ? ck_bytes : 0u));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint16_t gb[16], ub[16], gab[16], inb[16], scb[16];
+          float dv[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + 16 * hh + k) * p.B));
+            dv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, vd, row * 4, 0));
+            gb[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, row * 2, 0);
+            ub[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, (row + uint32_t(p.I * p.B)) * 2, 0);
+            gab[k] = __builtin_amdgcn_raw_buffer_load_b16(rga, vc, row * 2, 0);
+            inb[k] = __builtin_amdgcn_raw_buffer_load_b16(rin, vc, row * 2, 0);
+            scb[k] = __builtin_amdgcn_raw_buffer_load_b16(rsc, vc, row * 2, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int kk = 16 * hh + k;
+            gu[kk] = swiglu_bwd<ON_I>(dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, has_ga, bf16_to_f32(gab[k]),
+                                      has_in, bf16_to_f32(inb[k]), has_sc, scb[k], daff, it[kk]);
+            amg = fmaxf(amg, fabsf(lo_bf16(gu[kk])));
+            amu = fmaxf(amu, fabsf(hi_bf16(gu[kk])));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #endif
-      uint32_t gu[32];   // bf16(dGate) | bf16(dUp) << 16
-      uint16_t it[32];   // bf16 intermediate operand
-      float daff = 0.f, amg = 0.f, amu = 0.f;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const float d = dv[k], g = bf16_to_f32(gb[k]), u = bf16_to_f32(ub[k]);
-        const float sg = sigmoid_fast(g);
-        const float ga = bf16_round(g * sg);   // silu(g)
-        const float in = bf16_round(ga * u);   // intermediate
-        daff += d * in;
-        const float di = a * d;                // d(intermediate)
-        gu[k] = bf16x2_rne(di * u * dsilu_from(g, sg), di * ga);
-        it[k] = ON_I ? bf16_rne(a * in) : uint16_t(__float_as_uint(in) >> 16);
-        amg = fmaxf(amg, fabsf(lo_bf16(gu[k])));
-        amu = fmaxf(amu, fabsf(hi_bf16(gu[k])));
-      }
       // I-axis groups: the thread's 32 rows are one group of dGate and one of dUp
       const int Xg = scale_exp<FG>(__float_as_uint(amg)), Xu = scale_exp<FG>(__float_as_uint(amu));
       const float ig = inv_scale(Xg), iu = inv_scale(Xu);
@@ -230,20 +281,25 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
   }
 }
 
-template <int TS>
+template <int TS, bool CK>
 static hipError_t epi_launch(const Phase1Args& p, int fg, hipStream_t st) {
   constexpr int TI = kEpiElems / TS;
   const int64_t grid = int64_t(p.N) * ((p.I + TI - 1) / TI) * (p.B / TS);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   const bool on_i = p.affinity_on_i != 0;
   if (fg == kE4M3) {
-    if (on_i) phase1_epi_kernel<kE4M3, true, TS><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
-    else phase1_epi_kernel<kE4M3, false, TS><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    if (on_i) phase1_epi_kernel<kE4M3, true, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    else phase1_epi_kernel<kE4M3, false, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
   } else {
-    if (on_i) phase1_epi_kernel<kE5M2, true, TS><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
-    else phase1_epi_kernel<kE5M2, false, TS><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    if (on_i) phase1_epi_kernel<kE5M2, true, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    else phase1_epi_kernel<kE5M2, false, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
   }
   return hipGetLastError();
+}
+template <int TS>
+static hipError_t epi_launch(const Phase1Args& p, int fg, hipStream_t st) {
+  if (p.ga_ckpt || p.in_ckpt || p.sc_ckpt) return epi_launch<TS, true>(p, fg, st);
+  return epi_launch<TS, false>(p, fg, st);
 }
 
 // Block size B: a power of two >= 128 (tiles of 256 slots, or of the whole block at 128).

@@ -165,8 +165,9 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 // quant_tok: a workgroup covers 128 logical rows x 128 columns; wave w takes
 // rows 32w .. 32w+31 (one scale group) and lane l the column pair 2l, 2l+1.
-// Logical row r reads source row idx[r] (or r without an index); a source
-// outside [0, src_rows) contributes zeros (a padding slot).  With a row scale,
+// Logical row r reads source row idx[r] (or r without an index; with
+// self_rows, row r itself where idx[r] >= 0); a source outside [0, src_rows)
+// contributes zeros (a padding slot).  With a row scale,
 // the value is bf16(fp32(scale[r] * v)).  Output: codes_t [cols][rows] and
 // scales_t [cols][rows/32] (or pair-major [rows/128][cols][4] with PAIRS);
 // rows % 32 == 0 (% 128 with PAIRS) and cols % 8 == 0.
@@ -183,7 +184,7 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ rowscale,
                                                          int64_t rows, uint8_t* __restrict__ codes_t,
-                                                         uint8_t* __restrict__ scales_t) {
+                                                         uint8_t* __restrict__ scales_t, int self_rows) {
   const int cp = threadIdx.x & 63;
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = int64_t(blockIdx.y) * kTokRows + grp * 32;
@@ -200,13 +201,18 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
 #endif
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-      const int64_t src = GATHER ? int64_t(idx[row0 + r]) : row0 + r;
-      const bool ok = src >= 0 && src < src_rows;
       uint32_t v = 0u;
 #if defined(__HIP_DEVICE_COMPILE__)
-      if (OFF32) {
+      if (OFF32) {   // rows and sources fit in 32 bits: one scalar register per row index
+        const int32_t lr = int32_t(row0) + r;
+        const int32_t id = GATHER ? idx[lr] : lr;
+        const int32_t src = self_rows ? (id >= 0 ? lr : -1) : id;
+        const bool ok = src >= 0 && src < src_rows;
         v = __builtin_amdgcn_raw_buffer_load_b32(rx, ok ? uint32_t(src) * row_bytes + lane_bytes : v2::kOOB, 0, 0);
       } else {
+        const int64_t id = GATHER ? int64_t(idx[row0 + r]) : row0 + r;
+        const int64_t src = self_rows ? (id >= 0 ? row0 + r : -1) : id;
+        const bool ok = src >= 0 && src < src_rows;
         // invalid rows read row 0's word and are zeroed: no branch per row
         v = *reinterpret_cast<const uint32_t*>(x + (ok ? src : 0) * cols + colA);
         v = ok ? v : 0u;
@@ -345,37 +351,43 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
 
 template <int FMT, bool PAIRS, bool OFF32>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
-                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct) {
+                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows) {
   if (idx && rs)
-    quant_tok_kernel<FMT, true, true, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, true, true, PAIRS, OFF32>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
   else if (idx)
-    quant_tok_kernel<FMT, true, false, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, true, false, PAIRS, OFF32>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
   else if (rs)
-    quant_tok_kernel<FMT, false, true, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, false, true, PAIRS, OFF32>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
   else
-    quant_tok_kernel<FMT, false, false, PAIRS, OFF32><<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct);
+    quant_tok_kernel<FMT, false, false, PAIRS, OFF32>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
 }
 template <int FMT, bool PAIRS>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
-                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct) {
-  if (src_rows * cols * 2 < int64_t(v2::kOOB))
-    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct);
+                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows) {
+  if (src_rows * cols * 2 < int64_t(v2::kOOB) && rows <= int64_t(INT32_MAX))
+    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
   else
-    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct);
+    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
 }
 
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st, bool pairs) {
+                            uint8_t* scales_t, hipStream_t st, bool pairs, bool self_rows) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (pairs && rows % 128) return hipErrorInvalidValue;
+  if (self_rows && !idx) return hipErrorInvalidValue;
+  const int self = self_rows ? 1 : 0;
   dim3 grid(unsigned((cols + kTokCols - 1) / kTokCols), unsigned((rows + kTokRows - 1) / kTokRows));
   if (fmt == kE4M3) {
-    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
-    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
+    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
   } else {
-    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
-    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t);
+    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
+    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
   }
   return hipGetLastError();
 }

@@ -216,3 +216,97 @@ def test_moe_stages_in_order_equal_one_call():
         if cfg.has_bias:
             for k in ("db1", "db2"):
                 assert rel_fro(bf(host(o2[k])), bf(host(o1[k]))) < 1e-5, (name, k)
+
+
+# ----------------------------------------------------------------------------- supplied checkpoints
+CKPT_CFGS = {"tiny_onH": S.TINY, "medium_s_onH": SMALL["medium_s"], "large_s_onI": SMALL["large_s"]}
+
+
+def _exact_checkpoints(gp, p):
+    """P1's optional checkpoints as the oracle computes them (fp64, rounded to
+    bf16 where the recomputation rounds), laid out [N,I,B] / [N,B,H]; padding
+    slots hold garbage, which the library must ignore."""
+    cfg = gp["cfg"]
+    N, B, I, H, E, T = gp["N"], cfg.B, cfg.I, cfg.H, cfg.E, cfg.T
+    rng = np.random.default_rng(12)
+    tpid = host(gp["tpid"]).reshape(N, B)
+    pad = (tpid < 0) | (tpid >= T)                        # [N,B]
+    b2e = host(gp["b2e"])
+    a = np.where(pad, 0.0, gp["aff"].reshape(T, E)[np.where(pad, 0, tpid), b2e[:, None]]).astype(np.float32)
+    ga = rng.integers(0, 1 << 16, (N, I, B), dtype=np.uint16)
+    inter = rng.integers(0, 1 << 16, (N, I, B), dtype=np.uint16)
+    for b in range(N):
+        d = oracle.moe_block_detail(p, b)
+        ga[b][:, ~pad[b]] = d["ga"].T[:, ~pad[b]]
+        inter[b][:, ~pad[b]] = d["inter"].T[:, ~pad[b]]
+
+    def to_bf16(x32):                                     # fp32 -> bf16 bits, nearest even
+        return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+            .numpy().view(np.uint16)
+
+    inter_f = (inter.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):   # padding slots hold garbage, replaced below
+        scaled = to_bf16(inter_f * a[:, None, :])        # bf16(fp32(a * intermediate))
+    scaled[np.broadcast_to(pad[:, None, :], scaled.shape)] = 0x7fc0
+    dyf = (host(gp["t"]["dy"]).astype(np.uint32) << 16).view(np.float32)
+    ady = to_bf16(dyf[np.where(pad, 0, tpid)] * a[:, :, None])   # bf16(fp32(a * dY[token])), [N,B,H]
+    ady[pad] = rng.integers(0, 1 << 16, (int(pad.sum()), H), dtype=np.uint16)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return dict(gate_act_checkpoint_T=dev(ga), intermediate_checkpoint_T=dev(inter),
+                scaled_intermediate_checkpoint_T=dev(scaled), down_proj_act_checkpoint=dev(ady))
+
+
+@pytest.mark.parametrize("name", list(CKPT_CFGS))
+def test_moe_supplied_checkpoints(name):
+    """P1's optional checkpoints (silu(gate), the intermediate, and the scaled
+    intermediate under the affinity on I or a*dY under the affinity on H) read
+    in place of the recomputation: the gradients keep their parity with the
+    oracle, and the operands built from the checkpoints are the oracle's bit
+    for bit (recomputed on the GPU, the intermediate may differ in a rare
+    bf16 rounding of silu)."""
+    import mxfp8_grouped_gemm_amd as mx
+    cfg = CKPT_CFGS[name]
+    gp = gpu_problem(cfg)
+    base = {k: v.clone() for k, v in gp["op"].run().items() if v is not None}
+    p, ex = oracle_problem(gp)
+    ck = _exact_checkpoints(gp, p)
+    if cfg.affinity_on:
+        del ck["down_proj_act_checkpoint"]
+    else:
+        del ck["scaled_intermediate_checkpoint_T"]
+    t = gp["t"]
+    gu_c, gu_s, d_c, d_s = gp["wq"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    op = mx.MoeBwd(t["hidden"], torch.from_numpy(gp["aff"]).cuda(), gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32),
+                   d_c.view(E, I, H), d_s.view(E, I, H // 32), gp["tpid"], gp["b2e"], t["dy"], cfg.B, t["ckpt"],
+                   down_proj_bias=t["b2"], affinity_on=cfg.affinity_on, **ck)
+    out = op.run()
+    torch.cuda.synchronize()
+    ref = oracle.moe_bwd(p)
+    _check_outputs(cfg, out, ref)
+    for k in base:
+        assert rel_fro(bf(host(out[k])), bf(host(base[k]))) <= 1e-3, k
+    ws = op.workspace.cpu().numpy()
+    L = op.layout
+    P = gp["N"] * cfg.B
+    c, s = oracle.moe_token_operand(p, oracle.TOK_INTER)
+    assert np.array_equal(ws[L["inter_tok_codes"]:L["inter_tok_codes"] + I * P], c.ravel())
+    assert np.array_equal(pairs_to_rows(ws[L["inter_tok_scales"]:L["inter_tok_scales"] + I * P // 32], I, P),
+                          s.reshape(I, P // 32))
+    c, s = oracle.moe_token_operand(p, oracle.TOK_GY)
+    assert np.array_equal(ws[L["gy_tok_codes"]:L["gy_tok_codes"] + H * P], c.ravel())
+
+
+def test_moe_checkpoints_rejected_with_the_wrong_affinity_placement():
+    import mxfp8_grouped_gemm_amd as mx
+    gp = gpu_problem(S.TINY)                       # affinity on H
+    cfg = S.TINY
+    bad = torch.zeros((gp["N"], cfg.I, cfg.B), dtype=torch.bfloat16, device="cuda")
+    t = gp["t"]
+    gu_c, gu_s, d_c, d_s = gp["wq"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    op = mx.MoeBwd(t["hidden"], torch.from_numpy(gp["aff"]).cuda(), gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32),
+                   d_c.view(E, I, H), d_s.view(E, I, H // 32), gp["tpid"], gp["b2e"], t["dy"], cfg.B, t["ckpt"],
+                   affinity_on=0, scaled_intermediate_checkpoint_T=bad)
+    with pytest.raises(mx.MxError):
+        op.run()
