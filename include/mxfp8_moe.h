@@ -194,6 +194,14 @@ typedef struct {
   const uint16_t* down_proj_act_checkpoint;       /* [N,B,H] bf16(a * dY[token]) per slot;
                                                      affinity on H only (the Phase-4
                                                      operand)                           */
+  /* [P1] num_valid_tokens: [1] int32 in device memory, optional (NULL: T).
+   * Only the leading rows hold real tokens; a count above T means T, below 0
+   * means 0.  Slots of tokens at or past the count are padding, so those
+   * tokens' dX rows and d(a) entries are written as 0.  Read on the device by
+   * the first stage, so the count may be produced by earlier work on the
+   * stream.  With E = 1 and token_position_to_id = 0, 1, 2, ... (P1's
+   * single_expert_dense) it is P1's dynamic block loop.                     */
+  const int32_t* num_valid_tokens;
 } moe_bwd_mxfp8_args;
 
 /* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised

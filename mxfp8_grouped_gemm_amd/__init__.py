@@ -58,7 +58,8 @@ class MoeBwdArgs(C.Structure):
                 ("gate_up_proj_weight_grad", _p), ("down_proj_weight_grad", _p),
                 ("gate_and_up_proj_bias_grad", _p), ("down_proj_bias_grad", _p),
                 ("gate_act_checkpoint_T", _p), ("intermediate_checkpoint_T", _p),
-                ("scaled_intermediate_checkpoint_T", _p), ("down_proj_act_checkpoint", _p)]
+                ("scaled_intermediate_checkpoint_T", _p), ("down_proj_act_checkpoint", _p),
+                ("num_valid_tokens", _p)]
 
 
 LAYOUT_FIELDS = ("dy_codes", "dy_scales", "dy_deq", "wd_deq", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
@@ -229,7 +230,7 @@ class MoeBwd:
                  gate_up_proj_act_checkpoint_T, down_proj_bias=None, affinity_on=0, fmt_weight=E4M3,
                  fmt_act=E4M3, fmt_grad=E5M2, workspace=None, gate_act_checkpoint_T=None,
                  intermediate_checkpoint_T=None, scaled_intermediate_checkpoint_T=None,
-                 down_proj_act_checkpoint=None):
+                 down_proj_act_checkpoint=None, num_valid_tokens=None):
         T, H = hidden_states.shape
         E, _, _, I = gate_up_codes.shape
         N = block_to_expert.numel()
@@ -237,7 +238,7 @@ class MoeBwd:
         self.keep = [hidden_states, expert_affinities_masked, gate_up_codes, gate_up_scales, down_codes,
                      down_scales, token_position_to_id, block_to_expert, output_hidden_states_grad,
                      gate_up_proj_act_checkpoint_T, down_proj_bias, gate_act_checkpoint_T, intermediate_checkpoint_T,
-                     scaled_intermediate_checkpoint_T, down_proj_act_checkpoint]
+                     scaled_intermediate_checkpoint_T, down_proj_act_checkpoint, num_valid_tokens]
         has_bias = down_proj_bias is not None
         self.out = dict(
             dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
@@ -264,7 +265,8 @@ class MoeBwd:
             _dev(gate_act_checkpoint_T, torch.bfloat16, "gate_act_checkpoint_T"),
             _dev(intermediate_checkpoint_T, torch.bfloat16, "intermediate_checkpoint_T"),
             _dev(scaled_intermediate_checkpoint_T, torch.bfloat16, "scaled_intermediate_checkpoint_T"),
-            _dev(down_proj_act_checkpoint, torch.bfloat16, "down_proj_act_checkpoint"))
+            _dev(down_proj_act_checkpoint, torch.bfloat16, "down_proj_act_checkpoint"),
+            _dev(num_valid_tokens, torch.int32, "num_valid_tokens"))
         L = lib()
         lay = MoeWorkspaceLayout()
         _check(L.moe_bwd_mxfp8_workspace_query(C.byref(self.args), C.byref(lay)), "moe_bwd_mxfp8_workspace_query")

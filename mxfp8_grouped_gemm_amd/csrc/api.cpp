@@ -288,6 +288,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
                        a->down_proj_act_checkpoint};
   for (const void* q : opt)
     if (q && !aligned16(q)) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: checkpoints must be 16-byte aligned");
+  if (a->num_valid_tokens && (reinterpret_cast<uintptr_t>(a->num_valid_tokens) & 3u))
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: num_valid_tokens must be 4-byte aligned");
   if (a->down_proj_act_checkpoint && a->N * a->block_size * a->H * 2 >= int64_t(0x80000000u))
     return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: down_proj_act_checkpoint must be under 2 GiB");
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
@@ -322,7 +324,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
     STEP(mx::launch_fill_u32(db2_acc, E * H, 0u, st), "zero db2 accumulator");
   }
   STEP(mx::launch_slot_setup(a->token_position_to_id, a->block_to_expert, a->expert_affinities_masked, T, E, N, B,
-                             slot_tok, slot_aff, slot_of, flag, boff, blist, st),
+                             a->num_valid_tokens, slot_tok, slot_aff, slot_of, flag, boff, blist, st),
        "slot setup");
   stage = 1;
   // S1: dY quantised along H per token row (Phase-1 operand, gathered by token later).

@@ -77,8 +77,8 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
                                int32_t* tpid, int32_t* b2e, int32_t* counts, hipStream_t st);
 hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st);
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
-                             int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* slot_of,
-                             int32_t* flag, int32_t* off, int32_t* list, hipStream_t st);
+                             int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,
+                             int32_t* slot_of, int32_t* flag, int32_t* off, int32_t* list, hipStream_t st);
 hipError_t launch_dx_reduce(const float* dx_slot, const int32_t* slot_of, int64_t T, int64_t E, int64_t H,
                             uint16_t* dx, hipStream_t st);
 hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,

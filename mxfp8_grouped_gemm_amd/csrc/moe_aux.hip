@@ -112,15 +112,19 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
 // Per-slot routing info: token (-1 for padding or an invalid block expert) and
 // affinity (0 for padding), and the inverse map slot_of[t*E + e] = the slot
 // of pair (t, e) (a pair occupies at most one slot; -1 where none, filled
-// beforehand).  Outside [0,T) is padding.
+// beforehand).  Outside [0,T) is padding, and with a device count of valid
+// tokens (P1's num_valid_tokens: the real tokens are the leading rows, a count
+// above T means T) so is every token at or past it.
 __global__ void slot_info_kernel(const int32_t* __restrict__ tpid, const int32_t* __restrict__ b2e,
                                  const float* __restrict__ aff, int64_t T, int64_t E, int64_t B, int64_t P,
-                                 int32_t* __restrict__ slot_tok, float* __restrict__ slot_aff,
-                                 int32_t* __restrict__ slot_of) {
+                                 const int32_t* __restrict__ nvalid, int32_t* __restrict__ slot_tok,
+                                 float* __restrict__ slot_aff, int32_t* __restrict__ slot_of) {
+  const int64_t n = nvalid ? int64_t(*nvalid) : T;
+  const int64_t Tv = n < 0 ? 0 : (n < T ? n : T);
   for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < P; s += int64_t(gridDim.x) * blockDim.x) {
     const int64_t e = b2e[s / B];
     const int64_t t = tpid[s];
-    const bool ok = t >= 0 && t < T && e >= 0 && e < E;
+    const bool ok = t >= 0 && t < Tv && e >= 0 && e < E;
     slot_tok[s] = ok ? int32_t(t) : -1;
     slot_aff[s] = ok ? aff[t * E + e] : 0.f;
     if (ok) slot_of[t * E + e] = int32_t(s);
@@ -218,14 +222,14 @@ hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, i
 }
 
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
-                             int64_t N, int64_t B, int32_t* slot_tok, float* slot_aff, int32_t* slot_of,
-                             int32_t* flag, int32_t* off, int32_t* list, hipStream_t st) {
+                             int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,
+                             int32_t* slot_of, int32_t* flag, int32_t* off, int32_t* list, hipStream_t st) {
   const int64_t P = N * B;
   const int64_t want = (P + 255) / 256;
   hipError_t err = launch_fill_u32(reinterpret_cast<uint32_t*>(slot_of), T * E, 0xffffffffu, st);
   if (err != hipSuccess) return err;
-  slot_info_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(tpid, b2e, aff, T, E, B, P, slot_tok,
-                                                                           slot_aff, slot_of);
+  slot_info_kernel<<<unsigned(want < 4096 ? want : 4096), 256, 0, st>>>(tpid, b2e, aff, T, E, B, P, nvalid,
+                                                                           slot_tok, slot_aff, slot_of);
   block_flag_kernel<<<unsigned(N), 256, 0, st>>>(slot_tok, B, flag);
   // the counts go to off[1..E] and become offsets in place: in each 256-expert
   // chunk every count is read before the scan's barrier and every offset

@@ -310,3 +310,45 @@ def test_moe_checkpoints_rejected_with_the_wrong_affinity_placement():
                    affinity_on=0, scaled_intermediate_checkpoint_T=bad)
     with pytest.raises(mx.MxError):
         op.run()
+
+
+# ----------------------------------------------------------------------------- valid-token count
+def _run_with_count(gp, n):
+    import mxfp8_grouped_gemm_amd as mx
+    cfg = gp["cfg"]
+    t = gp["t"]
+    gu_c, gu_s, d_c, d_s = gp["wq"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    nv = torch.tensor([n], dtype=torch.int32, device="cuda")
+    op = mx.MoeBwd(t["hidden"], torch.from_numpy(gp["aff"]).cuda(), gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32),
+                   d_c.view(E, I, H), d_s.view(E, I, H // 32), gp["tpid"], gp["b2e"], t["dy"], cfg.B, t["ckpt"],
+                   down_proj_bias=t["b2"], affinity_on=cfg.affinity_on, num_valid_tokens=nv)
+    out = op.run()
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,counts", [("single_expert_dense", (200, 0, 300, 1000)), ("medium_s", (256, 1))])
+def test_moe_num_valid_tokens(name, counts):
+    """P1's num_valid_tokens: only the leading rows are real tokens (a count
+    above T means T).  The oracle is given the same routing with the slots of
+    tokens at or past the count made padding; those tokens' dX rows and d(a)
+    entries must be exactly 0.  single_expert_dense is E = 1 with every token
+    routed to expert 0 in order (the identity block layout)."""
+    import dataclasses
+    cfg = S.scaled(S.TINY, T=300, E=1, K=1) if name == "single_expert_dense" else SMALL[name]
+    gp = gpu_problem(cfg)
+    p, ex = oracle_problem(gp)
+    for n in counts:
+        out = _run_with_count(gp, n)
+        nv = max(0, min(n, cfg.T))
+        tp = np.where(p.tpid >= nv, -1, p.tpid).astype(np.int32)
+        ref = oracle.moe_bwd(dataclasses.replace(p, tpid=tp))
+        print(name, "count", n, flush=True)
+        # the zeros this test owns are checked below; masking the routing can also
+        # leave a chance exact zero in the oracle's dW (a cancelling sum, e.g.
+        # dW_down[7][178][201] of medium_s at count 256) that fp32 order need not hit
+        _check_outputs(cfg, out, ref, unrouted_zero=False)
+        dx = host(out["dx"]).reshape(cfg.T, cfg.H)
+        da = host(out["daff"]).reshape(cfg.T, cfg.E)
+        assert not dx[nv:].any() and not da[nv:].any()
