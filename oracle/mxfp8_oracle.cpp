@@ -318,7 +318,8 @@ int orc_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64
   for (int64_t t = 0; t < T; ++t)
     for (int64_t k = 0; k < K; ++k) {
       const int32_t e = topk[t * K + k];
-      if (e < 0 || e >= E) return -1;
+      if (e < 0) continue;   // a dropped selection: this token has fewer than K experts
+      if (e >= E) return -1;
       tok[e].push_back(int32_t(t));
     }
   int64_t need = 0;

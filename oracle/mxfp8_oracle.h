@@ -71,9 +71,11 @@ int orc_dense_bwd(const uint16_t* dY, const uint16_t* W, const uint16_t* X,
 
 /* ---- routing blocks (P1 "Dimensions": N = (T*TopK - (E-1))/B + E - 1) ---- */
 int64_t orc_num_blocks(int64_t T, int64_t K, int64_t E, int64_t B);
-/* topk [T][K] expert ids (distinct per row, in [0,E)).  Writes
- * token_position_to_id [N*B] (-1 = padding) and block_to_expert [N].
- * Returns 0, or -1 if N is too small / ids are invalid. */
+/* topk [T][K] expert ids (distinct per row, in [0,E); a negative id is a
+ * dropped selection -- page 3's varlen-K routing, where a token activates
+ * fewer than K experts -- and is skipped).  Writes token_position_to_id
+ * [N*B] (-1 = padding) and block_to_expert [N].
+ * Returns 0, or -1 if N is too small / an id is E or larger. */
 int orc_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B,
                      int64_t N, int32_t* tpid, int32_t* b2e);
 

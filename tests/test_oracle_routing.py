@@ -29,7 +29,7 @@ def test_block_count_formula_is_worst_case():
 
 def _reference_blocks(topk, E, B, N):
     """Brute force: stable sort of the (expert, token) pairs, then pad per expert."""
-    pairs = sorted((int(e), t) for t in range(topk.shape[0]) for e in topk[t])
+    pairs = sorted((int(e), t) for t in range(topk.shape[0]) for e in topk[t] if e >= 0)
     tp, be = [], []
     for e in range(E):
         toks = [t for (ee, t) in pairs if ee == e]
@@ -63,3 +63,22 @@ def test_build_blocks_rejects_small_N_and_bad_ids():
     oracle.build_blocks(topk, 3, 4, N)
     with pytest.raises(ValueError):
         oracle.build_blocks(np.array([[0, 3]], np.int32), 3, 4, N)
+
+
+def test_build_blocks_skips_dropped_selections():
+    """Page 3's varlen-K routing: a token may activate fewer than K experts; a
+    negative id is a dropped selection.  The blocks are those of the routing
+    without it (brute force), and a token with every selection dropped owns no
+    slot."""
+    rng = np.random.default_rng(5)
+    T, K, E, B = 60, 3, 5, 8
+    topk = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    topk[rng.random((T, K)) < 0.3] = -1
+    topk[7] = -1
+    N = oracle.num_blocks(T, K, E, B)
+    tpid, b2e = oracle.build_blocks(topk, E, B, N)
+    rt, rb = _reference_blocks(topk, E, B, N)
+    assert np.array_equal(tpid, rt) and np.array_equal(b2e, rb)
+    assert 7 not in set(tpid.tolist())
+    seen = sorted((int(b2e[s // B]), int(tpid[s])) for s in range(N * B) if tpid[s] >= 0)
+    assert seen == sorted((int(e), t) for t in range(T) for e in topk[t] if e >= 0)
