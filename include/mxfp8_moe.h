@@ -124,8 +124,11 @@ int matmul_mxfp8_bwd(const uint16_t* output_grad, const uint16_t* weights,
  * moe_num_blocks (host) returns P1's N = (T*TopK - (E-1))/B + E - 1 with the
  * division rounded up -- the worst case over all routings -- or -1 when
  * T*K < E or a size is not positive.
- *   topk_ids [T,K] int32, distinct per row, each in [0,E) (ids outside [0,E)
- *   are ignored).  N >= moe_num_blocks(T,K,E,B) (checked).
+ *   topk_ids [T,K] int32, distinct per row, each in [0,E).  A negative id is
+ *   a dropped selection ([P3]'s varlen-K routing: a token may activate fewer
+ *   than K experts, down to none); ids of E or more are ignored as well.  A
+ *   token with no expert gets a zero dX row and zero d(a) from the backward.
+ *   N >= moe_num_blocks(T,K,E,B) (checked).
  *   workspace >= moe_build_blocks_workspace_size(E) bytes.
  * ------------------------------------------------------------------------- */
 int64_t moe_num_blocks(int64_t T, int64_t K, int64_t E, int64_t block_size);

@@ -352,3 +352,44 @@ def test_moe_num_valid_tokens(name, counts):
         dx = host(out["dx"]).reshape(cfg.T, cfg.H)
         da = host(out["daff"]).reshape(cfg.T, cfg.E)
         assert not dx[nv:].any() and not da[nv:].any()
+
+
+# ----------------------------------------------------------------------------- varlen-K routing
+@pytest.mark.parametrize("name", ["tiny", "medium_s"])
+def test_moe_dropped_selections(name):
+    """Page 3's varlen-K routing: tokens activate between 0 and K experts
+    (negative ids in the top-k list are dropped selections).  The routing
+    blocks match the oracle's bit for bit, the gradients keep parity, and a
+    token with no expert gets a zero dX row and zero d(a)."""
+    import dataclasses
+    import mxfp8_grouped_gemm_amd as mx
+    cfg = SMALL[name]
+    gp = gpu_problem(cfg)
+    rng = np.random.default_rng(21)
+    topk = gp["topk"].copy()
+    topk[rng.random(topk.shape) < 0.3] = -1
+    topk[3] = -1                                          # a token with no expert at all
+    N = gp["N"]
+    tpid, b2e = mx.moe_build_blocks(torch.from_numpy(topk).cuda(), cfg.E, cfg.B, N)
+    rt, rb = oracle.build_blocks(topk, cfg.E, cfg.B, N)
+    assert np.array_equal(host(tpid), rt) and np.array_equal(host(b2e), rb)
+    t = gp["t"]
+    gu_c, gu_s, d_c, d_s = gp["wq"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    op = mx.MoeBwd(t["hidden"], torch.from_numpy(gp["aff"]).cuda(), gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32),
+                   d_c.view(E, I, H), d_s.view(E, I, H // 32), tpid, b2e, t["dy"], cfg.B, t["ckpt"],
+                   down_proj_bias=t["b2"], affinity_on=cfg.affinity_on)
+    out = op.run()
+    torch.cuda.synchronize()
+    p, _ = oracle_problem(gp)
+    ref = oracle.moe_bwd(dataclasses.replace(p, tpid=rt, b2e=rb))
+    _check_outputs(cfg, out, ref, unrouted_zero=False)
+    assert not host(out["dx"]).reshape(cfg.T, H)[3].any()
+    da = host(out["daff"]).reshape(cfg.T, E)
+    assert not da[3].any()
+    routed = np.zeros((cfg.T, E), bool)
+    for tt in range(cfg.T):
+        for e in topk[tt]:
+            if e >= 0:
+                routed[tt, e] = True
+    assert not da[~routed].any()                          # dropped pairs get no affinity gradient
