@@ -159,7 +159,9 @@ int64_t moe_num_blocks(int64_t T, int64_t K, int64_t E, int64_t B) {
   return (T * K - (E - 1) + B - 1) / B + E - 1;
 }
 
-size_t moe_build_blocks_workspace_size(int64_t E) { return E > 0 ? up256(size_t(E) * 4) : 0; }
+size_t moe_build_blocks_workspace_size(int64_t E) {
+  return E > 0 ? up256(size_t(mx::build_blocks_workspace_bytes(E))) : 0;
+}
 
 int moe_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N, int32_t* tpid,
                      int32_t* b2e, void* ws, size_t ws_bytes, void* stream) {

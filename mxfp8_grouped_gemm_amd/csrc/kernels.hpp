@@ -73,8 +73,10 @@ hipError_t launch_router_bwd(const RouterArgs& p, hipStream_t st);
 // moe_aux.hip
 hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st);
 hipError_t launch_fill_u16(void* p, int64_t n, uint16_t v, hipStream_t st);
+// ws: build_blocks_workspace_bytes(E) bytes (per expert and token chunk: counts, first slots)
+int64_t build_blocks_workspace_bytes(int64_t E);
 hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
-                               int32_t* tpid, int32_t* b2e, int32_t* counts, hipStream_t st);
+                               int32_t* tpid, int32_t* b2e, int32_t* ws, hipStream_t st);
 hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st);
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,

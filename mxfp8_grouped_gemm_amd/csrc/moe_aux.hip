@@ -41,8 +41,16 @@ hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// moe_build_blocks: count per expert, then one workgroup per expert places its
-// tokens (ascending) into its consecutive blocks.
+// moe_build_blocks: the tokens are cut into C chunks (C <= kRouteChunks).
+// Workgroup (e, c) counts the tokens of chunk c routed to expert e; one
+// workgroup turns the counts into each expert's first block and each (e, c)'s
+// first slot; workgroup (e, c) then places its chunk's tokens of expert e in
+// ascending order from there.  (One workgroup per expert scanning all tokens
+// took 80 us of the large workload's step.)  A token is routed to e when any
+// of its K ids is e; negative ids (dropped selections) and ids >= E match
+// nothing.
+constexpr int kRouteChunks = 32;
+
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[4]*/, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -63,34 +71,61 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[4]*/, int
   return before + x - v;
 }
 
-__global__ void __launch_bounds__(256) route_count_kernel(const int32_t* __restrict__ topk, int64_t TK, int E,
-                                                          int32_t* __restrict__ counts) {
-  __shared__ int red[4];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int64_t i = threadIdx.x; i < TK; i += 256) c += topk[i] == e;
-  int tot;
-  block_exclusive_scan(c, red, &tot);
-  if (threadIdx.x == 0) counts[e] = tot;
+// token t of a chunk routed to expert e?
+__device__ __forceinline__ int routed_to(const int32_t* __restrict__ topk, int64_t t, int K, int e) {
+  int hit = 0;
+  for (int k = 0; k < K; ++k) hit |= topk[t * K + k] == e;
+  return hit;
 }
 
-__global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ topk, int64_t T, int K, int E,
-                                                          int B, const int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ tpid, int32_t* __restrict__ b2e) {
+__global__ void __launch_bounds__(256) route_count_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
+                                                          int64_t CH, int C, int32_t* __restrict__ cnt) {
   __shared__ int red[4];
-  const int e = blockIdx.x;
-  int part = 0;
-  for (int q = threadIdx.x; q < e; q += 256) part += (counts[q] + B - 1) / B;
-  int start_blk;
-  block_exclusive_scan(part, red, &start_blk);
-  const int nb = (counts[e] + B - 1) / B;
-  for (int q = threadIdx.x; q < nb; q += 256) b2e[start_blk + q] = e;
-  int64_t base = int64_t(start_blk) * B;
-  for (int64_t t0 = 0; t0 < T; t0 += 256) {
-    const int64_t t = t0 + threadIdx.x;
-    int hit = 0;
-    if (t < T)
-      for (int k = 0; k < K; ++k) hit |= topk[t * K + k] == e;
+  const int e = blockIdx.x, c = blockIdx.y;
+  const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
+  int n = 0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) n += routed_to(topk, t, K, e);
+  int tot;
+  block_exclusive_scan(n, red, &tot);
+  if (threadIdx.x == 0) cnt[e * C + c] = tot;
+}
+
+// One workgroup: expert e's blocks start after ceil(n_q / B) blocks of every q < e;
+// off[e*C + c] = its first slot + the tokens of e in chunks before c; b2e of used blocks.
+__global__ void __launch_bounds__(256) route_offsets_kernel(const int32_t* __restrict__ cnt, int E, int C, int B,
+                                                            int32_t* __restrict__ off, int32_t* __restrict__ b2e) {
+  __shared__ int red[4];
+  int blk = 0;   // first block of the current expert chunk
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + threadIdx.x;
+    int n = 0;
+    if (e < E)
+      for (int c = 0; c < C; ++c) n += cnt[e * C + c];
+    const int nb = (n + B - 1) / B;
+    int tot;
+    const int first = blk + block_exclusive_scan(nb, red, &tot);
+    if (e < E) {
+      int run = first * B;
+      for (int c = 0; c < C; ++c) {
+        off[e * C + c] = run;
+        run += cnt[e * C + c];
+      }
+      for (int q = 0; q < nb; ++q) b2e[first + q] = e;
+    }
+    blk += tot;
+  }
+}
+
+__global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
+                                                          int64_t CH, int C, const int32_t* __restrict__ off,
+                                                          int32_t* __restrict__ tpid) {
+  __shared__ int red[4];
+  const int e = blockIdx.x, c = blockIdx.y;
+  const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
+  int64_t base = off[e * C + c];
+  for (int64_t tb = t0; tb < t1; tb += 256) {
+    const int64_t t = tb + threadIdx.x;
+    const int hit = t < t1 ? routed_to(topk, t, K, e) : 0;
     int tot;
     const int pos = block_exclusive_scan(hit, red, &tot);
     if (hit) tpid[base + pos] = int32_t(t);
@@ -98,13 +133,23 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
   }
 }
 
+int64_t build_blocks_workspace_bytes(int64_t E) { return E > 0 ? 2 * E * kRouteChunks * 4 : 0; }
+
 hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
-                               int32_t* tpid, int32_t* b2e, int32_t* counts, hipStream_t st) {
+                               int32_t* tpid, int32_t* b2e, int32_t* ws, hipStream_t st) {
   hipError_t err;
   if ((err = launch_fill_u32(tpid, N * B, 0xffffffffu, st)) != hipSuccess) return err;
   if ((err = launch_fill_u32(b2e, N, uint32_t(E - 1), st)) != hipSuccess) return err;
-  route_count_kernel<<<unsigned(E), 256, 0, st>>>(topk, T * K, int(E), counts);
-  route_place_kernel<<<unsigned(E), 256, 0, st>>>(topk, T, int(K), int(E), int(B), counts, tpid, b2e);
+  if (T <= 0) return hipSuccess;
+  // chunks of a multiple of 256 tokens, at most kRouteChunks of them
+  const int64_t per = (T + kRouteChunks - 1) / kRouteChunks;
+  const int64_t CH = (per + 255) / 256 * 256;
+  const int C = int((T + CH - 1) / CH);
+  int32_t* cnt = ws;
+  int32_t* off = ws + E * kRouteChunks;
+  route_count_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, cnt);
+  route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), off, b2e);
+  route_place_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, off, tpid);
   return hipGetLastError();
 }
 
