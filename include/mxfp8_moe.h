@@ -205,6 +205,14 @@ typedef struct {
    * stream.  With E = 1 and token_position_to_id = 0, 1, 2, ... (P1's
    * single_expert_dense) it is P1's dynamic block loop.                     */
   const int32_t* num_valid_tokens;
+  /* [P1] accumulation flag (its meaning is not spelled out there; reading:
+   * accumulate into the gradients instead of initialising them).  0: every
+   * output above is overwritten.  1: each output element becomes
+   * bf16(old + g), the value the caller's buffer holds plus the fp32 gradient,
+   * rounded once; entries the overwrite mode writes as 0 (unrouted tokens and
+   * pairs, empty experts) keep their old value.  For gradient accumulation
+   * over micro-batches.                                                      */
+  int accumulate;
 } moe_bwd_mxfp8_args;
 
 /* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised
@@ -256,7 +264,7 @@ int moe_bwd_mxfp8_workspace_query(const moe_bwd_mxfp8_args* args,
 size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
 
 /* Enqueues the whole backward.  Errors: INVALID_ARG (shapes, null required
- * pointers, alignment, formats), UNSUPPORTED (block_size outside the set,
+ * pointers, alignment, formats, accumulate outside {0,1}), UNSUPPORTED (block_size outside the set,
  * affinity on I together with a bias, sizes beyond 32-bit indexing or
  * I * block_size * 4 beyond 2 GiB), WORKSPACE (too small).  Device-side
  * preconditions (not checked): block_to_expert entries in [0,E) (blocks with

@@ -59,7 +59,7 @@ class MoeBwdArgs(C.Structure):
                 ("gate_and_up_proj_bias_grad", _p), ("down_proj_bias_grad", _p),
                 ("gate_act_checkpoint_T", _p), ("intermediate_checkpoint_T", _p),
                 ("scaled_intermediate_checkpoint_T", _p), ("down_proj_act_checkpoint", _p),
-                ("num_valid_tokens", _p)]
+                ("num_valid_tokens", _p), ("accumulate", C.c_int)]
 
 
 LAYOUT_FIELDS = ("dy_codes", "dy_scales", "dy_deq", "wd_deq", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
@@ -223,14 +223,16 @@ class MoeBwd:
     """One MoE backward problem bound to device tensors (P1's argument list).
 
     Allocates the outputs and the workspace once; ``run()`` enqueues the whole
-    backward on the current stream."""
+    backward on the current stream.  With ``accumulate=True`` the outputs are
+    allocated zeroed and each ``run()`` adds its gradients into what they hold
+    (write priors into ``self.out`` to start from other values)."""
 
     def __init__(self, hidden_states, expert_affinities_masked, gate_up_codes, gate_up_scales, down_codes,
                  down_scales, token_position_to_id, block_to_expert, output_hidden_states_grad, block_size,
                  gate_up_proj_act_checkpoint_T, down_proj_bias=None, affinity_on=0, fmt_weight=E4M3,
                  fmt_act=E4M3, fmt_grad=E5M2, workspace=None, gate_act_checkpoint_T=None,
                  intermediate_checkpoint_T=None, scaled_intermediate_checkpoint_T=None,
-                 down_proj_act_checkpoint=None, num_valid_tokens=None):
+                 down_proj_act_checkpoint=None, num_valid_tokens=None, accumulate=False):
         T, H = hidden_states.shape
         E, _, _, I = gate_up_codes.shape
         N = block_to_expert.numel()
@@ -240,13 +242,14 @@ class MoeBwd:
                      gate_up_proj_act_checkpoint_T, down_proj_bias, gate_act_checkpoint_T, intermediate_checkpoint_T,
                      scaled_intermediate_checkpoint_T, down_proj_act_checkpoint, num_valid_tokens]
         has_bias = down_proj_bias is not None
+        alloc = torch.zeros if accumulate else torch.empty
         self.out = dict(
-            dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
-            daff=torch.empty(T * E, dtype=torch.bfloat16, device=dev),
-            dwgu=torch.empty((E, H, 2, I), dtype=torch.bfloat16, device=dev),
-            dwd=torch.empty((E, I, H), dtype=torch.bfloat16, device=dev),
-            db1=torch.empty((E, 2, I), dtype=torch.bfloat16, device=dev) if has_bias else None,
-            db2=torch.empty((E, H), dtype=torch.bfloat16, device=dev) if has_bias else None)
+            dx=alloc((T, H), dtype=torch.bfloat16, device=dev),
+            daff=alloc(T * E, dtype=torch.bfloat16, device=dev),
+            dwgu=alloc((E, H, 2, I), dtype=torch.bfloat16, device=dev),
+            dwd=alloc((E, I, H), dtype=torch.bfloat16, device=dev),
+            db1=alloc((E, 2, I), dtype=torch.bfloat16, device=dev) if has_bias else None,
+            db2=alloc((E, H), dtype=torch.bfloat16, device=dev) if has_bias else None)
         o = self.out
         self.args = MoeBwdArgs(
             T, H, I, E, N, block_size,
@@ -266,7 +269,7 @@ class MoeBwd:
             _dev(intermediate_checkpoint_T, torch.bfloat16, "intermediate_checkpoint_T"),
             _dev(scaled_intermediate_checkpoint_T, torch.bfloat16, "scaled_intermediate_checkpoint_T"),
             _dev(down_proj_act_checkpoint, torch.bfloat16, "down_proj_act_checkpoint"),
-            _dev(num_valid_tokens, torch.int32, "num_valid_tokens"))
+            _dev(num_valid_tokens, torch.int32, "num_valid_tokens"), int(bool(accumulate)))
         L = lib()
         lay = MoeWorkspaceLayout()
         _check(L.moe_bwd_mxfp8_workspace_query(C.byref(self.args), C.byref(lay)), "moe_bwd_mxfp8_workspace_query")

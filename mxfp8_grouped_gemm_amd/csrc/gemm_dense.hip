@@ -58,9 +58,14 @@ __device__ __forceinline__ void store_tile(const GemmStoreArgs& p, int g, int64_
         v2::static_for<4>([&](auto K) {
           const int ocol = v2::acc_row<BM, BN>(I, 4 * K);
           if (m0 + ocol < p.M) {
-            const uint32_t lo = bf16x2_pack(acc[I][J][4 * K], acc[I][J][4 * K + 1]);
-            const uint32_t hi = bf16x2_pack(acc[I][J][4 * K + 2], acc[I][J][4 * K + 3]);
-            *reinterpret_cast<uint2*>(dst + ocol) = make_uint2(lo, hi);
+            float v0 = acc[I][J][4 * K], v1 = acc[I][J][4 * K + 1];
+            float v2 = acc[I][J][4 * K + 2], v3 = acc[I][J][4 * K + 3];
+            if (p.accumulate) {   // add the output's old values, then round once
+              const uint2 o = *reinterpret_cast<const uint2*>(dst + ocol);
+              v0 += bf16_to_f32(uint16_t(o.x)); v1 += bf16_to_f32(uint16_t(o.x >> 16));
+              v2 += bf16_to_f32(uint16_t(o.y)); v3 += bf16_to_f32(uint16_t(o.y >> 16));
+            }
+            *reinterpret_cast<uint2*>(dst + ocol) = make_uint2(bf16x2_pack(v0, v1), bf16x2_pack(v2, v3));
           }
         });
       }

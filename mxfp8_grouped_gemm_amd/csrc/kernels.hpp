@@ -46,6 +46,7 @@ struct GemmStoreArgs {
   const int32_t* blk_ext;   // optional: per block, one past its last routed column; a group's
                             // last block then contributes only that many columns, rounded up to 128
   int blk;
+  int accumulate;                 // 1: out = bf16(out + C) instead of bf16(C)
   int pair;                       // 1: 256 x 256 tiles run the pair-slot ring (128-byte rows), 0: the
                                   // four-slot ring (deeper look-ahead, for operands streamed from HBM)
   int tiles_m, tiles_n;
@@ -81,15 +82,16 @@ hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, i
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,
                              int32_t* slot_of, int32_t* flag, int32_t* off, int32_t* list, hipStream_t st);
+// accumulate: each bf16 output becomes bf16(old + value) (else bf16(value))
 hipError_t launch_dx_reduce(const float* dx_slot, const int32_t* slot_of, int64_t T, int64_t E, int64_t H,
-                            uint16_t* dx, hipStream_t st);
+                            uint16_t* dx, hipStream_t st, bool accumulate = false);
 hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,
                        const int32_t* b2e, const int32_t* flag, int64_t H, int64_t B, int64_t N, float* daff_slot,
                        float* db2_acc, hipStream_t st);
-hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st, bool accumulate = false);
 hipError_t launch_daff_scatter(const float* daff_slot, const float* daff_part, int64_t nparts,
                                const int32_t* slot_tok, const int32_t* b2e, int64_t T, int64_t E, int64_t B,
-                               int64_t N, uint16_t* daff, hipStream_t st);
+                               int64_t N, uint16_t* daff, hipStream_t st, bool accumulate = false);
 
 // moe_phase1_*.hip (product, epilogue), moe_phase3.hip
 struct Phase1Args {

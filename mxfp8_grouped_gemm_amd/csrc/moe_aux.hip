@@ -348,23 +348,32 @@ hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* sl
 
 // ---------------------------------------------------------------------------
 // Finalisation: fp32 accumulators -> bf16 outputs; d(a) scattered to t*E+e.
+// With ACC the output's old bf16 value is added before the one rounding.
+template <bool ACC>
 __global__ void f32_to_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n / 4; i += int64_t(gridDim.x) * blockDim.x) {
-    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    float4 v = reinterpret_cast<const float4*>(src)[i];
+    if (ACC) {
+      const uint2 o = reinterpret_cast<const uint2*>(dst)[i];
+      v.x += bf16_to_f32(uint16_t(o.x)); v.y += bf16_to_f32(uint16_t(o.x >> 16));
+      v.z += bf16_to_f32(uint16_t(o.y)); v.w += bf16_to_f32(uint16_t(o.y >> 16));
+    }
     const uint32_t lo = uint32_t(f32_to_bf16(v.x)) | (uint32_t(f32_to_bf16(v.y)) << 16);
     const uint32_t hi = uint32_t(f32_to_bf16(v.z)) | (uint32_t(f32_to_bf16(v.w)) << 16);
     reinterpret_cast<uint2*>(dst)[i] = make_uint2(lo, hi);
   }
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
     const int64_t i = (n & ~int64_t(3)) + threadIdx.x;
-    dst[i] = f32_to_bf16(src[i]);
+    dst[i] = f32_to_bf16(src[i] + (ACC ? bf16_to_f32(dst[i]) : 0.f));
   }
 }
 
-hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st) {
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st, bool accumulate) {
   if (n <= 0) return hipSuccess;
   const int64_t want = (n / 4 + 255) / 256 + 1;
-  f32_to_bf16_kernel<<<unsigned(want < 16384 ? want : 16384), 256, 0, st>>>(src, dst, n);
+  const unsigned grid = unsigned(want < 16384 ? want : 16384);
+  if (accumulate) f32_to_bf16_kernel<true><<<grid, 256, 0, st>>>(src, dst, n);
+  else f32_to_bf16_kernel<false><<<grid, 256, 0, st>>>(src, dst, n);
   return hipGetLastError();
 }
 
@@ -373,6 +382,7 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStr
 // per token; H % 32 == 0.  The token's slots are compacted into LDS 256
 // experts at a time (a block scan keeps expert order), then each thread sums
 // up to four 4-column groups over them.
+template <bool ACC>
 __global__ void __launch_bounds__(256) dx_reduce_kernel(const float* __restrict__ dx_slot,
                                                         const int32_t* __restrict__ slot_of, int64_t E, int64_t H,
                                                         uint16_t* __restrict__ dx) {
@@ -408,17 +418,24 @@ __global__ void __launch_bounds__(256) dx_reduce_kernel(const float* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t c = c0 + threadIdx.x + 256 * j;
-      if (c < C)
-        reinterpret_cast<uint2*>(dx + t * H)[c] =
-            make_uint2(bf16x2_pack(acc[j].x, acc[j].y), bf16x2_pack(acc[j].z, acc[j].w));
+      if (c < C) {
+        uint2* dst = reinterpret_cast<uint2*>(dx + t * H) + c;
+        if (ACC) {   // the old value joins after the slot sum, before the one rounding
+          const uint2 o = *dst;
+          acc[j].x += bf16_to_f32(uint16_t(o.x)); acc[j].y += bf16_to_f32(uint16_t(o.x >> 16));
+          acc[j].z += bf16_to_f32(uint16_t(o.y)); acc[j].w += bf16_to_f32(uint16_t(o.y >> 16));
+        }
+        *dst = make_uint2(bf16x2_pack(acc[j].x, acc[j].y), bf16x2_pack(acc[j].z, acc[j].w));
+      }
     }
   }
 }
 
 hipError_t launch_dx_reduce(const float* dx_slot, const int32_t* slot_of, int64_t T, int64_t E, int64_t H,
-                            uint16_t* dx, hipStream_t st) {
+                            uint16_t* dx, hipStream_t st, bool accumulate) {
   if (T <= 0) return hipSuccess;
-  dx_reduce_kernel<<<unsigned(T), 256, 0, st>>>(dx_slot, slot_of, E, H, dx);
+  if (accumulate) dx_reduce_kernel<true><<<unsigned(T), 256, 0, st>>>(dx_slot, slot_of, E, H, dx);
+  else dx_reduce_kernel<false><<<unsigned(T), 256, 0, st>>>(dx_slot, slot_of, E, H, dx);
   return hipGetLastError();
 }
 
@@ -430,7 +447,8 @@ __global__ void __launch_bounds__(256) daff_scatter_kernel(const float* __restri
                                                            const float* __restrict__ daff_part, int64_t nparts,
                                                            const int32_t* __restrict__ slot_tok,
                                                            const int32_t* __restrict__ b2e, int64_t E, int64_t B,
-                                                           int64_t P, uint16_t* __restrict__ daff) {
+                                                           int64_t P, int accumulate,
+                                                           uint16_t* __restrict__ daff) {
   __shared__ float part[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t s = int64_t(blockIdx.x) * 64 + lane;
@@ -444,20 +462,24 @@ __global__ void __launch_bounds__(256) daff_scatter_kernel(const float* __restri
   if (w == 0 && s < P) {
     const int64_t t = slot_tok[s];
     if (t >= 0) {
-      const float d = daff_slot[s] + ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]));
-      daff[t * E + b2e[s / B]] = f32_to_bf16(d);
+      float d = daff_slot[s] + ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]));
+      uint16_t* dst = daff + t * E + b2e[s / B];
+      if (accumulate) d += bf16_to_f32(*dst);
+      *dst = f32_to_bf16(d);
     }
   }
 }
 
 hipError_t launch_daff_scatter(const float* daff_slot, const float* daff_part, int64_t nparts,
                                const int32_t* slot_tok, const int32_t* b2e, int64_t T, int64_t E, int64_t B,
-                               int64_t N, uint16_t* daff, hipStream_t st) {
-  hipError_t err = launch_fill_u16(daff, T * E, 0, st);
-  if (err != hipSuccess) return err;
+                               int64_t N, uint16_t* daff, hipStream_t st, bool accumulate) {
+  if (!accumulate) {   // pairs without a slot are 0; accumulating, they keep their value
+    hipError_t err = launch_fill_u16(daff, T * E, 0, st);
+    if (err != hipSuccess) return err;
+  }
   const int64_t P = N * B;
   daff_scatter_kernel<<<unsigned((P + 63) / 64), 256, 0, st>>>(daff_slot, daff_part, nparts, slot_tok, b2e, E, B, P,
-                                                                daff);
+                                                                accumulate ? 1 : 0, daff);
   return hipGetLastError();
 }
 

@@ -199,7 +199,7 @@ class _MoeProblem(C.Structure):
                 ("wd_codes", _p), ("wd_scales", _p), ("tpid", _p), ("b2e", _p), ("dy", _p),
                 ("ckpt", _p), ("b2", _p), ("affinity_on", C.c_int), ("has_bias", C.c_int),
                 ("fmt_w", C.c_int), ("fmt_act", C.c_int), ("fmt_grad", C.c_int),
-                ("nthreads", C.c_int)]
+                ("nthreads", C.c_int), ("accumulate", C.c_int)]
 
 
 @dataclass
@@ -233,6 +233,7 @@ class MoeProblem:
     fmt_act: int = E4M3
     fmt_grad: int = E5M2
     nthreads: int = 0
+    accumulate: int = 0      # P1's accumulation flag: outputs = bf16(prior + gradient)
 
     def _struct(self):
         keep = {}
@@ -247,40 +248,49 @@ class MoeProblem:
                                                   "wd_codes", "wd_scales", "tpid", "b2e", "dy",
                                                   "ckpt", "b2")],
                         self.affinity_on, self.has_bias, self.fmt_w, self.fmt_act, self.fmt_grad,
-                        self.nthreads)
+                        self.nthreads, self.accumulate)
         return s, keep
 
 
-def moe_bwd(p: MoeProblem):
-    """Full MX-mode backward: dict of bf16-bit arrays dx, daff, dwgu, dwd, db1, db2."""
+def _outputs(shapes, prior):
+    """bf16-bit output arrays: zeros, or copies of prior[name] (the values an
+    accumulating backward adds to)."""
+    return {k: (np.zeros(shp, np.uint16) if prior is None or prior.get(k) is None
+                else np.array(prior[k], np.uint16, order="C").reshape(shp)) for k, shp in shapes.items()}
+
+
+def moe_bwd(p: MoeProblem, prior=None):
+    """Full MX-mode backward: dict of bf16-bit arrays dx, daff, dwgu, dwd, db1, db2.
+    With p.accumulate, prior[name] holds the outputs' values on entry."""
     s, keep = p._struct()
-    out = dict(dx=np.zeros((p.T, p.H), np.uint16), daff=np.zeros(p.T * p.E, np.uint16),
-               dwgu=np.zeros((p.E, p.H, 2, p.I), np.uint16), dwd=np.zeros((p.E, p.I, p.H), np.uint16),
-               db1=np.zeros((p.E, 2, p.I), np.uint16), db2=np.zeros((p.E, p.H), np.uint16))
+    out = _outputs(dict(dx=(p.T, p.H), daff=(p.T * p.E,), dwgu=(p.E, p.H, 2, p.I), dwd=(p.E, p.I, p.H),
+                        db1=(p.E, 2, p.I), db2=(p.E, p.H)), prior)
     _check(lib().orc_moe_bwd(C.byref(s), *[_ptr(out[k]) for k in ("dx", "daff", "dwgu", "dwd", "db1", "db2")]),
            "moe_bwd")
     del keep
     return out
 
 
-def moe_token_rows(p: MoeProblem, tokens):
+def moe_token_rows(p: MoeProblem, tokens, prior=None):
+    """dX rows and d(a) rows ([E] per token) of the given tokens; with
+    p.accumulate, prior = dict(dx=[n,H], daff=[n,E]) of their values on entry."""
     s, keep = p._struct()
     tok = np.ascontiguousarray(tokens, dtype=np.int32)
-    dx = np.zeros((tok.size, p.H), np.uint16)
-    da = np.zeros((tok.size, p.E), np.uint16)
+    o = _outputs(dict(dx=(tok.size, p.H), daff=(tok.size, p.E)), prior)
+    dx, da = o["dx"], o["daff"]
     _check(lib().orc_moe_token_rows(C.byref(s), _ptr(tok), tok.size, _ptr(dx), _ptr(da)), "token_rows")
     del keep
     return dx, da
 
 
-def moe_expert_cols(p: MoeProblem, e: int, icols):
+def moe_expert_cols(p: MoeProblem, e: int, icols, prior=None):
+    """Expert e's weight and bias gradients at intermediate columns icols; with
+    p.accumulate, prior holds their values on entry (same shapes as returned)."""
     s, keep = p._struct()
     ic = np.ascontiguousarray(icols, dtype=np.int32)
     n = ic.size
-    dwgu = np.zeros((p.H, 2, n), np.uint16)
-    dwd = np.zeros((n, p.H), np.uint16)
-    db1 = np.zeros((2, n), np.uint16)
-    db2 = np.zeros(p.H, np.uint16)
+    o = _outputs(dict(dwgu=(p.H, 2, n), dwd=(n, p.H), db1=(2, n), db2=(p.H,)), prior)
+    dwgu, dwd, db1, db2 = o["dwgu"], o["dwd"], o["db1"], o["db2"]
     _check(lib().orc_moe_expert_cols(C.byref(s), e, _ptr(ic), n, _ptr(dwgu), _ptr(dwd), _ptr(db1),
                                      _ptr(db2)), "expert_cols")
     del keep

@@ -111,6 +111,9 @@ double f32r(double x) { return double(float(x)); }  /* value after one fp32 roun
 /* A gradient output: the fp64 sum stands for an fp32 accumulator, so it is
  * rounded once to fp32 and then to bf16 (RNE), as an fp32 result would be. */
 uint16_t out_bf16(double acc) { return to_bf16(f32r(acc)); }
+/* Writes gradient g into an output element: overwritten, or added to the
+ * element's value when accumulating (P1's accumulation flag), one rounding. */
+void put_grad(uint16_t* o, double g, int accumulate) { *o = out_bf16(accumulate ? bf(*o) + g : g); }
 
 /* One MX group (P1: "32-element quantization group").  Scale rule (reading:
  * the OCP MX rule; the pages do not state one): X = floor(log2(amax)) - emax
@@ -479,9 +482,9 @@ int orc_moe_token_rows(const orc_moe_problem* pp, const int32_t* tokens, int64_t
         m.phase3(e, dG, dU, acc);
       }
     if (dx_rows)
-      for (int64_t h = 0; h < p.H; ++h) dx_rows[r * p.H + h] = out_bf16(acc[h]);
+      for (int64_t h = 0; h < p.H; ++h) put_grad(&dx_rows[r * p.H + h], acc[h], p.accumulate);
     if (daff_rows)
-      for (int64_t e = 0; e < p.E; ++e) daff_rows[r * p.E + e] = out_bf16(daff[e]);
+      for (int64_t e = 0; e < p.E; ++e) put_grad(&daff_rows[r * p.E + e], daff[e], p.accumulate);
   });
   return 0;
 }
@@ -541,8 +544,8 @@ int orc_moe_expert_cols(const orc_moe_problem* pp, int64_t e, const int32_t* ico
     for (int64_t c = 0; c < C; ++c) {
       double s0 = 0.0, s1 = 0.0;
       for (int64_t q = 0; q < S; ++q) { s0 += gv[q * C + c]; s1 += uv[q * C + c]; }
-      db1_cols[c] = out_bf16(s0);
-      db1_cols[C + c] = out_bf16(s1);
+      put_grad(&db1_cols[c], s0, p.accumulate);
+      put_grad(&db1_cols[C + c], s1, p.accumulate);
     }
   parallel_for(p.H, p.nthreads, [&](int64_t h) {
     std::vector<double> xs(S), ys(S), xq(S), yq(S);
@@ -566,12 +569,12 @@ int orc_moe_expert_cols(const orc_moe_problem* pp, int64_t e, const int32_t* ico
         s2 += iq[q * C + c] * yq[q];
       }
       if (dwgu_cols) {
-        dwgu_cols[(h * 2 + 0) * C + c] = out_bf16(s0);
-        dwgu_cols[(h * 2 + 1) * C + c] = out_bf16(s1);
+        put_grad(&dwgu_cols[(h * 2 + 0) * C + c], s0, p.accumulate);
+        put_grad(&dwgu_cols[(h * 2 + 1) * C + c], s1, p.accumulate);
       }
-      if (dwd_rows) dwd_rows[c * p.H + h] = out_bf16(s2);
+      if (dwd_rows) put_grad(&dwd_rows[c * p.H + h], s2, p.accumulate);
     }
-    if (db2_row) db2_row[h] = out_bf16(db2);
+    if (db2_row) put_grad(&db2_row[h], db2, p.accumulate);
   });
   return 0;
 }
@@ -583,6 +586,7 @@ int orc_moe_bwd(const orc_moe_problem* pp, uint16_t* dx, uint16_t* daff, uint16_
   std::vector<int32_t> all_t(p.T);
   for (int64_t t = 0; t < p.T; ++t) all_t[t] = int32_t(t);
   std::vector<uint16_t> daff_rows(p.T * p.E);
+  if (p.accumulate && daff) std::memcpy(daff_rows.data(), daff, daff_rows.size() * 2);
   if (orc_moe_token_rows(pp, all_t.data(), p.T, dx, daff_rows.data())) return -1;
   if (daff) std::memcpy(daff, daff_rows.data(), daff_rows.size() * 2);
   std::vector<int32_t> all_i(p.I);

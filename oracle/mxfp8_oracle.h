@@ -95,10 +95,15 @@ typedef struct {
   int has_bias;                                    /* adds <dY, b2[e]> to d(affinity)   */
   int fmt_w, fmt_act, fmt_grad;
   int nthreads;                                    /* 0 = all host cores                */
+  int accumulate;      /* P1's accumulation flag (reading: add into the gradients):
+                          1 = every output element o becomes bf16(fp32(o + g)), the
+                          buffer's value plus the exact gradient, rounded as an fp32
+                          sum would be; 0 = bf16(fp32(g))                        */
 } orc_moe_problem;
 
 /* All outputs bf16.  Full problem: dx [T][H], daff [T*E], dwgu [E][H][2][I],
- * dwd [E][I][H], db1 [E][2][I], db2 [E][H] (any may be NULL). */
+ * dwd [E][I][H], db1 [E][2][I], db2 [E][H] (any may be NULL).  With accumulate
+ * the output buffers hold the values to add to on entry. */
 int orc_moe_bwd(const orc_moe_problem* p, uint16_t* dx, uint16_t* daff, uint16_t* dwgu,
                 uint16_t* dwd, uint16_t* db1, uint16_t* db2);
 

@@ -56,3 +56,25 @@ def test_validation_without_gpu():
     assert rb(1, 4, 8, 2, fake, None, None, fake, None, 0, fake, None) == 1              # logits missing
     assert rb(2, 4, 8, 2, C.c_void_p(0x10004), None, None, fake, None, 0, fake, None) == 1 and "aligned" in mx.last_error()
     assert rb(2, 0, 8, 2, None, None, None, fake, None, 0, None, None) == 0             # no tokens
+
+
+@pytest.mark.parametrize("cls,ctype", [("MoeBwdArgs", "moe_bwd_mxfp8_args"),
+                                       ("MoeWorkspaceLayout", "moe_bwd_mxfp8_workspace_layout")])
+def test_binding_structs_match_the_header(cls, ctype, tmp_path):
+    """The ctypes mirrors of the header's structs: same size and every field at
+    the offset the C compiler gives it."""
+    import subprocess
+    import mxfp8_grouped_gemm_amd as mx
+    S = getattr(mx, cls)
+    lines = [f'printf("size %zu\\n", sizeof({ctype}));']
+    lines += [f'printf("{n} %zu\\n", offsetof({ctype}, {n}));' for n, _ in S._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"mxfp8_moe.h\"\nint main(void) {\n"
+                   + "\n".join(lines) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                 text=True).stdout.splitlines())
+    assert int(got.pop("size")) == C.sizeof(S)
+    for n, _ in S._fields_:
+        assert int(got[n]) == getattr(S, n).offset, n

@@ -393,3 +393,53 @@ def test_moe_dropped_selections(name):
             if e >= 0:
                 routed[tt, e] = True
     assert not da[~routed].any()                          # dropped pairs get no affinity gradient
+
+
+# ----------------------------------------------------------------------------- accumulation
+@pytest.mark.parametrize("name", ["fine_s", "large_s"])
+def test_moe_accumulate(name):
+    """P1's accumulation flag (reading: add into the gradients).  Every output
+    starts from seeded random bf16 values; one call must give bf16(prior + g)
+    and a second call, on top of that, the oracle's accumulation of g onto its
+    own first result.  Pairs without a slot keep the prior bit for bit."""
+    import dataclasses
+    import mxfp8_grouped_gemm_amd as mx
+    cfg = SMALL[name]
+    gp = gpu_problem(cfg)
+    p, _ = oracle_problem(gp)
+    base = oracle.moe_bwd(p)
+    keys = ["dx", "daff", "dwgu", "dwd"] + (["db1", "db2"] if cfg.has_bias else [])
+    rng = np.random.default_rng(61)
+    prior = {}
+    for k in keys:
+        scale = float(np.abs(bf(base[k])).max())
+        x = torch.from_numpy(rng.standard_normal(base[k].shape)).float() * scale
+        prior[k] = S.bf16_bits(x.to(torch.bfloat16))
+    t = gp["t"]
+    gu_c, gu_s, d_c, d_s = gp["wq"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    op = mx.MoeBwd(t["hidden"], torch.from_numpy(gp["aff"]).cuda(), gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32),
+                   d_c.view(E, I, H), d_s.view(E, I, H // 32), gp["tpid"], gp["b2e"], t["dy"], cfg.B, t["ckpt"],
+                   down_proj_bias=t["b2"], affinity_on=cfg.affinity_on, accumulate=True)
+    for k in keys:
+        assert not op.out[k].float().abs().sum().item()          # allocated zeroed
+        op.out[k].view(torch.int16).copy_(torch.from_numpy(prior[k].view(np.int16)).view(op.out[k].shape))
+    pa = dataclasses.replace(p, accumulate=1)
+    ref1 = oracle.moe_bwd(pa, prior=prior)
+    out = op.run()
+    torch.cuda.synchronize()
+    print(name, "first call", flush=True)
+    _check_outputs(cfg, out, ref1, unrouted_zero=False)
+    routed = np.zeros((cfg.T, E), bool)
+    routed[np.arange(cfg.T)[:, None], gp["topk"]] = True
+    da = host(out["daff"]).reshape(cfg.T, E)
+    assert np.array_equal(da[~routed], prior["daff"].reshape(cfg.T, E)[~routed])
+    ref2 = oracle.moe_bwd(pa, prior=ref1)
+    out = op.run()
+    torch.cuda.synchronize()
+    print(name, "second call", flush=True)
+    _check_outputs(cfg, out, ref2, unrouted_zero=False)
+    # the flag must not leak into a later overwriting problem
+    again = gp["op"].run()
+    torch.cuda.synchronize()
+    _check_outputs(cfg, again, base)

@@ -267,3 +267,50 @@ def test_token_operands_match_their_definition():
     gy[valid] = a[valid, None] * bf(p.dy[p.tpid[valid]]).astype(np.float32)      # fp32 product
     c2, s2 = oracle.quantize(np.ascontiguousarray(_bits(gy).T), 1, oracle.E5M2)
     assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+
+
+def test_accumulate_adds_into_the_outputs():
+    """P1's accumulation flag (reading: add into the gradients).  Pins: with zero
+    priors it is the overwrite result bit for bit; onto the negated overwrite
+    result only the rounding residual g - bf16(g) is left (|.| <= 2^-8 |g|),
+    which fails if the prior were ignored, replaced or subtracted, output by
+    output; the restricted evaluators accumulate the same way."""
+    cfg = S.scaled(S.FINE, T=64, H=64, I=64, E=6, K=2, B=32)
+    p, ex = moe_problem(cfg)
+    assert p.has_bias
+    base = oracle.moe_bwd(p)
+    p.accumulate = 1
+    zero = oracle.moe_bwd(p, prior={k: np.zeros_like(v) for k, v in base.items()})
+    for k in KEYS:
+        assert np.array_equal(base[k], zero[k]), k
+    neg = {k: v ^ np.uint16(0x8000) for k, v in base.items()}
+    res = oracle.moe_bwd(p, prior=neg)
+    for k in KEYS:
+        g, r = bf(base[k]), bf(res[k])
+        assert np.all(np.abs(r) <= 2.0 ** -8 * np.abs(g)), k
+        assert np.abs(g).max() > 0, k
+    # a prior of other values: within one rounding of prior + bf16(g)
+    rng = np.random.default_rng(53)
+    prior = {k: oracle_bits(rng.standard_normal(v.shape) * np.abs(bf(v)).max()) for k, v in base.items()}
+    acc = oracle.moe_bwd(p, prior=prior)
+    for k in KEYS:
+        want = bf(prior[k]) + bf(base[k])
+        tol = 2.0 ** -8 * (np.abs(want) + np.abs(bf(base[k]))) + 1e-30
+        assert np.all(np.abs(bf(acc[k]) - want) <= tol), k
+    tok = np.array([5, 0, 63])
+    dx, da = oracle.moe_token_rows(p, tok, prior=dict(dx=prior["dx"][tok],
+                                                      daff=prior["daff"].reshape(cfg.T, cfg.E)[tok]))
+    assert np.array_equal(dx, acc["dx"][tok])
+    assert np.array_equal(da, acc["daff"].reshape(cfg.T, cfg.E)[tok])
+    e, cols = 1, np.array([3, 63, 0])
+    r = oracle.moe_expert_cols(p, e, cols, prior=dict(dwgu=prior["dwgu"][e][:, :, cols], dwd=prior["dwd"][e][cols],
+                                                      db1=prior["db1"][e][:, cols], db2=prior["db2"][e]))
+    assert np.array_equal(r["dwgu"], acc["dwgu"][e][:, :, cols])
+    assert np.array_equal(r["dwd"], acc["dwd"][e][cols])
+    assert np.array_equal(r["db1"], acc["db1"][e][:, cols])
+    assert np.array_equal(r["db2"], acc["db2"][e])
+
+
+def oracle_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns (one RNE rounding)."""
+    return np.vectorize(oracle.double_to_bf16, otypes=[np.uint16])(x)
