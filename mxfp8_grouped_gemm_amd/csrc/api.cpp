@@ -183,6 +183,11 @@ int moe_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64
 }
 
 /* ---- MoE backward -------------------------------------------------------- */
+// An expert weight operand at least this large (8x one XCD's 4 MB L2) is shared
+// by all XCDs through the infinity cache: its GEMM hands tiles out round robin
+// (moe_tiles.hpp).
+constexpr int64_t kRoundRobinWeightBytes = int64_t(32) << 20;
+
 static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layout* L) {
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, N = a->N, B = a->block_size, P = N * B;
   size_t o = 0;
@@ -394,6 +399,9 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.daff_part = reinterpret_cast<float*>(at(L.daff_part)); p1.db1_acc = db1_acc;
   p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias; p1.fmt_act = a->fmt_act;
   p1.dgu_row_pairs = gu_pairs;
+  // Tile order over the XCDs (measured: round robin 2.6% faster on Phase 1 with
+  // 58 MB W_down experts; the contiguous ranges 6% faster with 0.4-3 MB ones)
+  p1.rr_tiles = I * H >= kRoundRobinWeightBytes;
   STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_weight, st), "phase 1");
   stage = 5;
   // the SwiGLU backward on dS: dGU along both axes, the intermediate operand, d(a), db1
@@ -406,6 +414,9 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.tile_start = reinterpret_cast<int32_t*>(at(L.phase3_tiles));
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_slot = dx_slot;
+  // measured: round robin 4.8% faster with 117 MB W_gate_up experts, the
+  // contiguous ranges 6-14% faster with 0.8-6 MB ones
+  p3.rr_tiles = H * 2 * I >= kRoundRobinWeightBytes;
   STEP(mx::launch_phase3(p3, a->fmt_grad, a->fmt_weight, st), "phase 3");
   stage = 7;
   // Phase 2: dW_gate_up[e] = X_tok . dGU_tok^T over the expert's blocks

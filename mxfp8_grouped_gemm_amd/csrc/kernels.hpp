@@ -129,6 +129,7 @@ struct Phase1Args {
   int has_bias;                 // 1: accumulate db1
   int fmt_act;                  // format of the intermediate operand (activation format)
   int dgu_row_pairs;            // 1: dGU along I feeds the ring loop (2I % 128 == 0): pair-major scales
+  int rr_tiles;                 // tile order over the XCDs (moe_tiles.hpp)
   int tiles_m, tiles_n;
 };
 hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, int fmt_weight, hipStream_t st);
@@ -145,6 +146,7 @@ struct Phase3Args {
   int32_t* tile_start;            // [N+1]: tile ranges over the blocks' live slot tiles (moe_tiles.hpp)
   int64_t H, I, N, B;
   float* dx_slot;                 // [P][H] fp32: each routed slot's row of dX
+  int rr_tiles;                   // tile order over the XCDs (moe_tiles.hpp)
   int tiles_m, tiles_n;
 };
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st);

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   constexpr int FM = BM / 64, FN = BN / 64;
   // live tiles only: block b's slot tiles up to its extent, times the I tiles
   BlockTiles bt;
-  if (!block_tile(p.tile_start, int(p.N), p.tiles_m, blockIdx.x, bt)) return;
+  if (!block_tile(p.tile_start, int(p.N), p.tiles_m, blockIdx.x, p.rr_tiles, bt)) return;
   const int b = bt.b;
   int tm, tn;
   v2::grouped_tile<8>(bt.local, p.tiles_m, bt.slots, tm, tn);

@@ -28,7 +28,7 @@ struct P3Pos {
 template <int BM, int BN>
 __device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int wg) {
   BlockTiles bt;
-  if (!block_tile(p.tile_start, int(p.N), p.tiles_n, wg, bt)) return P3Pos{-1, 0, 0};
+  if (!block_tile(p.tile_start, int(p.N), p.tiles_n, wg, p.rr_tiles, bt)) return P3Pos{-1, 0, 0};
   int tm, tn;
   v2::grouped_tile<8>(bt.local, bt.slots, p.tiles_n, tm, tn);
   return P3Pos{bt.b, int64_t(tm) * BM, int64_t(tn) * BN};

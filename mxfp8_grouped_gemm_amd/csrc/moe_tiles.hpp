@@ -20,13 +20,22 @@ struct BlockTiles {
   int slots;   // slot tiles of the block
 };
 
-// Maps a workgroup id to its tile; false: no tile (exit).
-__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, int N, int other, int wg,
+// Maps a workgroup id to its tile; false: no tile (exit).  Two orders:
+//   rr = 0: each XCD takes a contiguous range of tiles, so consecutive blocks
+//     of one expert meet in one XCD's L2 -- the better order while an
+//     expert's weights are small next to the 4 MB L2;
+//   rr = 1: ids as the hardware hands them out, round robin over the XCDs,
+//     so all XCDs work on the same blocks at once and stream one expert's
+//     weights together through the infinity cache -- the better order for
+//     weights many times the L2, which no single XCD can keep.  With a
+//     block's tile count a multiple of 8, each XCD still holds a compact
+//     group of tiles.
+__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, int N, int other, int wg, int rr,
                                            BlockTiles& t) {
   const int total = start[N];
   const int t8 = (total + 7) & ~7;   // the XCD remap needs a multiple of 8 ids
   if (wg >= t8) return false;
-  const int id = v2::xcd_remap(wg, t8);
+  const int id = rr ? wg : v2::xcd_remap(wg, t8);
   if (id >= total) return false;
   int lo = 0, hi = N;   // start[lo] <= id < start[hi]
   while (hi - lo > 1) {
