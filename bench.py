@@ -14,8 +14,10 @@ Printed: one JSON line on stdout (progress goes to stderr).  Besides the step
 throughput it carries the roofline of the dominant kernel (timed live with HIP
 events on the library's stream), the dense MXFP8 backward (4096^3), the
 quantiser throughput, the router backward that consumes d(affinity) (every mode
-on the fine workload's 32768 x 128 top-8 router), and the CPU oracle timed on a
-bounded sample.
+on the fine workload's 32768 x 128 top-8 router), the CPU oracle timed on a
+bounded sample, the step one call at a time with warm and with cold caches
+(median, p10, p90), the same for the tiny, medium and fine workloads, and the
+engine clock read from sysfs with the peak fraction rescaled to it.
 
 roofline.traffic is the dominant kernel's HBM bytes per launch from two
 rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on
@@ -92,6 +94,44 @@ def _events_ms(fn, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def step_distribution(fn, reps, cold, scratch=None):
+    """Per-call durations of fn (HIP events around each call): median, p10 and
+    p90 in ms.  cold: a 512 MiB buffer is written before each call (outside the
+    events), which evicts the L2s and the 256 MB infinity cache."""
+    import numpy as np
+    import torch
+    if cold and scratch is None:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if cold:
+            scratch.fill_(1)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": round(float(np.median(t)), 4), "p10_ms": round(float(np.percentile(t, 10)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4), "reps": reps}
+
+
+def gpu_sclk_mhz():
+    """Current shader clock from sysfs (the starred pp_dpm_sclk level), or None."""
+    import glob
+    import re
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*[Mm]hz", line)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            pass
+    return None
 
 
 def stage_work(cfg, N):
@@ -190,7 +230,11 @@ def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / steps
-    log(f"[bench] timed {steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)")
+    sclk = gpu_sclk_mhz()
+    log(f"[bench] timed {steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s), sclk {sclk} MHz")
+    # the step one at a time: warm caches, then cold (L2 and infinity cache evicted)
+    timing = {"warm": step_distribution(step, 20, False), "cold": step_distribution(step, 20, True)}
+    log(f"[bench] per step: warm {timing['warm']}, cold {timing['cold']}")
 
     # per-stage durations, HIP events on the stream the library launches on
     work = stage_work(cfg, N)
@@ -213,7 +257,40 @@ def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
                  for k, v in stages.items()}
     log(f"[bench] stages: " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
     return dict(ms=ms, wall=wall, roof=roof, stages=per_stage, N=N, topk=pb["topk"], aff=pb["aff"], tensors=pb["t"],
-                w01=pb["w01"])
+                w01=pb["w01"], timing=timing, sclk=sclk)
+
+
+def run_other_configs(skip):
+    """The other MoE workloads, each a full step (routing blocks + backward):
+    warm and cold distributions; TFLOP/s from the cold median for the medium
+    and fine workloads and from the warm one for tiny, which is launch-bound."""
+    import torch
+    import mxfp8_grouped_gemm_amd as mx
+    import synthetic as S
+    res = {}
+    for name, cfg in S.MOE_CONFIGS.items():
+        if cfg.name == skip:
+            continue
+        pb = build_problem(cfg)
+        op, N, topk_d, tpid, b2e, rb_ws = pb["op"], pb["N"], pb["topk_d"], pb["tpid"], pb["b2e"], pb["rb_ws"]
+
+        def step():
+            mx.moe_build_blocks(topk_d, cfg.E, cfg.B, N, out=(tpid, b2e), workspace=rb_ws)
+            op.run()
+
+        for _ in range(5):
+            step()
+        reps = 200 if name == "tiny" else 20
+        warm, cold = step_distribution(step, reps, False), step_distribution(step, reps, True)
+        prim = "warm" if name == "tiny" else "cold"
+        tf = cfg.flops / ({"warm": warm, "cold": cold}[prim]["median_ms"] * 1e9)
+        res[name] = {"workload": cfg.name, "warm": warm, "cold": cold, "primary": prim,
+                     "TFLOP/s": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        log(f"[bench] {cfg.name}: warm {warm['median_ms']} ms, cold {cold['median_ms']} ms, {tf:.1f} TFLOP/s ({prim})")
+        del pb, op
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
 
 
 def run_dense(reps):
@@ -402,6 +479,11 @@ def main():
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
         "roofline": moe["roof"],
         "stages": moe["stages"],
+        "step_timing": moe["timing"],
+        # the 5.0 PFLOP/s peak is quoted at the 2.4 GHz peak engine clock
+        "sclk_mhz": moe["sclk"],
+        "frac_of_fp8_peak_at_sclk": (round(value / (PEAK_FP8_TFLOPS * moe["sclk"] / 2400.0), 4)
+                                     if moe["sclk"] else None),
     }
     if not args.no_extra:
         dense, quant = run_dense(args.profile_reps + 5)
@@ -411,6 +493,7 @@ def main():
         out["router_bwd"] = run_router(args.profile_reps + 5)
         log("[bench] router backward: " + ", ".join(f"{k} {v['ms']} ms" for k, v in out["router_bwd"].items()
                                                      if isinstance(v, dict)))
+        out["other_workloads"] = run_other_configs(cfg.name)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample) ...")
         out["cpu_baseline"] = cpu_baseline(cfg, moe, args.cpu_threads, args.cpu_tokens, args.cpu_cols)

@@ -6,9 +6,10 @@
 // index of block b's first tile and start[N] the total, built on the device
 // before the GEMM (launch_tile_ranges).  The GEMM's grid covers every tile a
 // full block could have; workgroups past the total exit at once.  Being the
-// highest ids, those are spread over all XCDs, and the live ids are remapped
-// so each XCD takes a contiguous range of live tiles: skipped tiles never
-// leave one XCD idle while another still holds its full share.
+// highest ids, those are spread over all XCDs, and the live ids are handed to
+// the XCDs evenly (in contiguous ranges or round robin, see block_tile):
+// skipped tiles never leave one XCD idle while another still holds its full
+// share.
 #pragma once
 #include "gemm_v2.hpp"
 
