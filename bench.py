@@ -204,7 +204,7 @@ def build_problem(cfg, keep_w01=False):
     return dict(op=op, N=N, topk=topk, aff=aff, topk_d=topk_d, tpid=tpid, b2e=b2e, rb_ws=rb_ws, t=t, w01=w01)
 
 
-def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
+def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False, distributions=True):
     import torch
     import mxfp8_grouped_gemm_amd as mx
 
@@ -233,8 +233,10 @@ def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False):
     sclk = gpu_sclk_mhz()
     log(f"[bench] timed {steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s), sclk {sclk} MHz")
     # the step one at a time: warm caches, then cold (L2 and infinity cache evicted)
-    timing = {"warm": step_distribution(step, 20, False), "cold": step_distribution(step, 20, True)}
-    log(f"[bench] per step: warm {timing['warm']}, cold {timing['cold']}")
+    timing = None
+    if distributions:
+        timing = {"warm": step_distribution(step, 20, False), "cold": step_distribution(step, 20, True)}
+        log(f"[bench] per step: warm {timing['warm']}, cold {timing['cold']}")
 
     # per-stage durations, HIP events on the stream the library launches on
     work = stage_work(cfg, N)
@@ -466,7 +468,8 @@ def main():
     if args.kernel_only:
         kernel_only(cfg, args.kernel_only, max(1, args.steps))
         return
-    moe = run_moe(cfg, args.steps, args.warmup, args.profile_reps, keep_w01=not args.no_cpu_baseline)
+    moe = run_moe(cfg, args.steps, args.warmup, args.profile_reps, keep_w01=not args.no_cpu_baseline,
+                  distributions=not args.no_extra)
     value = cfg.flops / moe["ms"] / 1e9
     out = {
         "metric": "MoE backward TFLOP/s (1 MI355X) + % of MXFP8 MFMA peak; quantize GB/s",

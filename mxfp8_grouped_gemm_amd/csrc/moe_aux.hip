@@ -317,23 +317,32 @@ __global__ void __launch_bounds__(256) bias_dot_kernel(const uint16_t* __restric
   if (lane == 0) daff_slot[s] = acc;   // the slot's <dY, b2> term
 }
 
+// db2 of one block: thread = two adjacent columns h (4-byte loads), eight
+// independent chains over the block's slots keep eight loads in flight; one
+// atomic per (block, column).
 __global__ void __launch_bounds__(256) db2_kernel(const uint16_t* __restrict__ dy, const int32_t* __restrict__ slot_tok,
                                                   const float* __restrict__ slot_aff, const int32_t* __restrict__ b2e,
                                                   const int32_t* __restrict__ flag, int64_t H, int64_t B,
                                                   float* __restrict__ db2_acc) {
   const int64_t b = blockIdx.y;
-  const int64_t h = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t h = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 2;
   if (!flag[b] || h >= H) return;
   const int64_t e = b2e[b];
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};   // four independent chains keep four loads in flight
-  for (int64_t p = 0; p < B; p += 4) {
+  float lo[8] = {}, hi[8] = {};
+  for (int64_t p = 0; p < B; p += 8) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       const int64_t t = slot_tok[b * B + p + k];
-      if (t >= 0) acc[k] += slot_aff[b * B + p + k] * bf16_to_f32(dy[t * H + h]);
+      if (t >= 0) {
+        const float a = slot_aff[b * B + p + k];
+        const uint32_t y = *reinterpret_cast<const uint32_t*>(dy + t * H + h);
+        lo[k] += a * lo_bf16(y);
+        hi[k] += a * hi_bf16(y);
+      }
     }
   }
-  atomicAdd(db2_acc + e * H + h, (acc[0] + acc[1]) + (acc[2] + acc[3]));
+  atomicAdd(db2_acc + e * H + h, ((lo[0] + lo[1]) + (lo[2] + lo[3])) + ((lo[4] + lo[5]) + (lo[6] + lo[7])));
+  atomicAdd(db2_acc + e * H + h + 1, ((hi[0] + hi[1]) + (hi[2] + hi[3])) + ((hi[4] + hi[5]) + (hi[6] + hi[7])));
 }
 
 hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* slot_tok, const float* slot_aff,
@@ -341,7 +350,7 @@ hipError_t launch_bias(const uint16_t* dy, const uint16_t* b2, const int32_t* sl
                        float* db2_acc, hipStream_t st) {
   const int64_t P = N * B;
   bias_dot_kernel<<<unsigned((P + 3) / 4), 256, 0, st>>>(dy, b2, slot_tok, b2e, H, B, P, daff_slot);
-  db2_kernel<<<dim3(unsigned((H + 255) / 256), unsigned(N)), 256, 0, st>>>(dy, slot_tok, slot_aff, b2e, flag, H, B,
+  db2_kernel<<<dim3(unsigned((H + 511) / 512), unsigned(N)), 256, 0, st>>>(dy, slot_tok, slot_aff, b2e, flag, H, B,
                                                                           db2_acc);
   return hipGetLastError();
 }
