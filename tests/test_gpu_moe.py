@@ -23,25 +23,28 @@ SMALL = {
     "fine_s": S.scaled(S.FINE, T=512, H=192, I=128, E=16, K=4, B=128),
     "medium_b512": S.scaled(S.MEDIUM, T=640, H=128, I=96, E=4, K=2, B=512),
 }
+# experts of 32 MiB (W_down) and 64 MiB (W_gate_up): Phases 1 and 3 hand their
+# tiles to the XCDs round robin, which no other small case reaches
+ROUND_ROBIN = {"large_rr": S.scaled(S.LARGE, T=256, H=4096, I=8192, E=2, K=1, B=128)}
 
 
-def _check_outputs(cfg, out, ref, unrouted_zero=True):
+def _check_outputs(cfg, out, ref, unrouted_zero=True, zero_keys=None):
     keys = ["dx", "daff", "dwgu", "dwd"] + (["db1", "db2"] if cfg.has_bias else [])
     errs = {}
     for k in keys:
         g = bf(host(out[k])).reshape(-1)
         r = bf(ref[k]).reshape(-1)
         errs[k] = rel_fro(g, r)
-        if unrouted_zero:
+        if unrouted_zero and (zero_keys is None or k in zero_keys):
             assert np.all(g[r == 0] == 0) or k in ("dx",), f"{k}: nonzero where the oracle is exactly zero"
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= TOL, (k, v)
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("name", list(SMALL) + list(ROUND_ROBIN))
 def test_moe_small_full_parity(name):
-    cfg = SMALL[name]
+    cfg = {**SMALL, **ROUND_ROBIN}[name]
     gp = gpu_problem(cfg)
     out = gp["op"].run()
     torch.cuda.synchronize()
@@ -51,7 +54,11 @@ def test_moe_small_full_parity(name):
     for g, o in zip(gp["wq"], ex["wq"]):
         assert np.array_equal(host(g).reshape(-1), o.reshape(-1))
     ref = oracle.moe_bwd(p)
-    _check_outputs(cfg, out, ref)
+    # large_rr has no empty expert, so its only structural zeros are the
+    # unrouted d(a) pairs; with 128 slots per expert the oracle's exact dW sums
+    # can also cancel to 0 by chance (23 of 134M dW_gate_up entries), where a
+    # rare one-step difference in a dGate/dUp code leaves a residue
+    _check_outputs(cfg, out, ref, zero_keys=("daff",) if name in ROUND_ROBIN else None)
     # quantised input operands read back from the workspace: bit-exact
     op = gp["op"]
     T, H, P = cfg.T, cfg.H, gp["N"] * cfg.B
