@@ -78,3 +78,18 @@ def test_binding_structs_match_the_header(cls, ctype, tmp_path):
     assert int(got.pop("size")) == C.sizeof(S)
     for n, _ in S._fields_:
         assert int(got[n]) == getattr(S, n).offset, n
+
+
+def test_moe_bwd_rejects_a_bad_accumulate_flag_without_gpu():
+    """The accumulation flag is 0 or 1; anything else fails in validation,
+    before any device access (the pointers here are never dereferenced)."""
+    import mxfp8_grouped_gemm_amd as mx
+    L = mx.lib()
+    fake = 0x10000
+    T, H, I, E, B = 256, 128, 256, 4, 128
+    N = L.moe_num_blocks(T, 2, E, B)
+    ptrs = [fake] * 10
+    a = mx.MoeBwdArgs(T, H, I, E, N, B, *ptrs, None, 0, 0, mx.E4M3, mx.E4M3, mx.E5M2,
+                      fake, fake, fake, fake, None, None, None, None, None, None, None, 2)
+    assert L.moe_bwd_mxfp8(C.byref(a), C.c_void_p(fake), 1 << 40, None) == 1
+    assert "accumulate" in mx.last_error()
