@@ -4,7 +4,7 @@
 A step is one pass of the hot path over one batch of seeded synthetic input
 already resident in HBM: the routing blocks from the top-k ids
 (moe_build_blocks) and the whole backward (moe_bwd_mxfp8: dY quantisation,
-token-axis gathers, Phase 1 with its fused epilogue, Phases 3, 2 and 4, bias
+token-axis gathers, Phase 1 and its SwiGLU-backward epilogue kernel, Phases 3, 2 and 4, bias
 reductions, finalisation).  The workload is the largest single-GPU MoE
 configuration (T=16384, H=4096, I=14336, E=8, top-2, B=1024, affinity on the
 intermediate).  The metric counts algorithmic FLOPs only: 12*H*I per routed
@@ -173,9 +173,12 @@ def roofline_of(kind, work, ms):
             "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
-def build_problem(cfg, keep_w01=False):
+def build_problem(cfg, keep_w01=False, keep_w_all=False):
     """Seeded synthetic inputs of cfg resident on the GPU, weights quantised by
-    the library, routing blocks built, the backward operator bound."""
+    the library, routing blocks built, the backward operator bound.  keep_w01 /
+    keep_w_all: host copies of the bf16 weights of experts 0 and 1 / of every
+    expert, for the oracle's sample (the generator's output, before the library
+    quantises it)."""
     import torch
     import mxfp8_grouped_gemm_amd as mx
     import synthetic as S
@@ -194,8 +197,9 @@ def build_problem(cfg, keep_w01=False):
     gu_c, gu_s = mx.mxfp8_quantize(t["w_gate_up"].view(E * H * 2, I), 1, mx.E4M3)
     d_c, d_s = mx.mxfp8_quantize(t["w_down"].view(E * I, H), 1, mx.E4M3)
     w01 = None
-    if keep_w01:      # experts 0 and 1 for the CPU-baseline sample (generator output)
-        w01 = {"gu": S.bf16_bits(t["w_gate_up"][:2]), "d": S.bf16_bits(t["w_down"][:2])}
+    if keep_w01 or keep_w_all:      # for the CPU-baseline sample (generator output)
+        n = E if keep_w_all else 2
+        w01 = {"gu": S.bf16_bits(t["w_gate_up"][:n]), "d": S.bf16_bits(t["w_down"][:n])}
     del t["w_gate_up"], t["w_down"]
     aff_d = torch.from_numpy(aff).to(dev)
     op = mx.MoeBwd(t["hidden"], aff_d, gu_c.view(E, H, 2, I), gu_s.view(E, H, 2, I // 32), d_c.view(E, I, H),
@@ -238,42 +242,53 @@ def run_moe(cfg, steps, warmup, profile_reps, keep_w01=False, distributions=True
         timing = {"warm": step_distribution(step, 20, False), "cold": step_distribution(step, 20, True)}
         log(f"[bench] per step: warm {timing['warm']}, cold {timing['cold']}")
 
-    # per-stage durations, HIP events on the stream the library launches on
+    stages, per_stage, dom = time_stages(cfg, pb, profile_reps)
+    kind, w = stage_work(cfg, N)[dom]
+    roof = roofline_of(kind, w, stages[dom])
+    roof.update({"kernel": dom, "launch_ms": round(stages[dom], 4), "traffic": recorded_traffic(dom, cfg.name)})
+    return dict(ms=ms, wall=wall, roof=roof, stages=per_stage, N=N, topk=pb["topk"], aff=pb["aff"], tensors=pb["t"],
+                w01=pb["w01"], timing=timing, sclk=sclk)
+
+
+def time_stages(cfg, pb, reps):
+    """Per-stage durations (HIP events on the stream the library launches on),
+    each with its roofline figure; also the stage with the longest launch."""
+    import torch
+    import mxfp8_grouped_gemm_amd as mx
+    op, N, topk_d, tpid, b2e, rb_ws = pb["op"], pb["N"], pb["topk_d"], pb["tpid"], pb["b2e"], pb["rb_ws"]
     work = stage_work(cfg, N)
     stages = {}
     for s, name in enumerate(op.STAGE_NAMES):
         if name == "bias" and not cfg.has_bias:
             continue
-        stages[name] = _events_ms(lambda s=s: op.stage(s), profile_reps)
+        stages[name] = _events_ms(lambda s=s: op.stage(s), reps)
     stages["build_blocks"] = _events_ms(
-        lambda: mx.moe_build_blocks(topk_d, cfg.E, cfg.B, N, out=(tpid, b2e), workspace=rb_ws), profile_reps)
+        lambda: mx.moe_build_blocks(topk_d, cfg.E, cfg.B, N, out=(tpid, b2e), workspace=rb_ws), reps)
     op.run()
     torch.cuda.synchronize()
     dom = max((k for k in stages if k in work), key=lambda k: stages[k])
-    kind, w = work[dom]
-    roof = roofline_of(kind, w, stages[dom])
-    roof.update({"kernel": dom, "launch_ms": round(stages[dom], 4), "traffic": recorded_traffic(dom, cfg.name)})
     per_stage = {k: {"ms": round(v, 4), **({} if k not in work or not work[k][1] else
                                            {kk: vv for kk, vv in roofline_of(work[k][0], work[k][1], v).items()
                                             if kk in ("achieved", "unit", "frac")})}
                  for k, v in stages.items()}
-    log(f"[bench] stages: " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
-    return dict(ms=ms, wall=wall, roof=roof, stages=per_stage, N=N, topk=pb["topk"], aff=pb["aff"], tensors=pb["t"],
-                w01=pb["w01"], timing=timing, sclk=sclk)
+    log(f"[bench] {cfg.name} stages: " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+    return stages, per_stage, dom
 
 
-def run_other_configs(skip):
+def run_other_configs(skip, cpu_threads=0, profile_reps=5):
     """The other MoE workloads, each a full step (routing blocks + backward):
-    warm and cold distributions; TFLOP/s from the cold median for the medium
-    and fine workloads and from the warm one for tiny, which is launch-bound."""
+    warm and cold distributions, per-stage times, and (cpu_threads > 0) the
+    oracle timed on a bounded sample of the same workload.  TFLOP/s from the
+    cold median for the medium and fine workloads and from the warm one for
+    tiny, which is launch-bound."""
     import torch
     import mxfp8_grouped_gemm_amd as mx
     import synthetic as S
-    res = {}
+    res, cpu = {}, {}
     for name, cfg in S.MOE_CONFIGS.items():
         if cfg.name == skip:
             continue
-        pb = build_problem(cfg)
+        pb = build_problem(cfg, keep_w_all=cpu_threads > 0)
         op, N, topk_d, tpid, b2e, rb_ws = pb["op"], pb["N"], pb["topk_d"], pb["tpid"], pb["b2e"], pb["rb_ws"]
 
         def step():
@@ -286,13 +301,22 @@ def run_other_configs(skip):
         warm, cold = step_distribution(step, reps, False), step_distribution(step, reps, True)
         prim = "warm" if name == "tiny" else "cold"
         tf = cfg.flops / ({"warm": warm, "cold": cold}[prim]["median_ms"] * 1e9)
+        _, per_stage, dom = time_stages(cfg, pb, profile_reps)
         res[name] = {"workload": cfg.name, "warm": warm, "cold": cold, "primary": prim,
-                     "TFLOP/s": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+                     "TFLOP/s": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "stages": per_stage, "longest_stage": dom}
         log(f"[bench] {cfg.name}: warm {warm['median_ms']} ms, cold {cold['median_ms']} ms, {tf:.1f} TFLOP/s ({prim})")
+        if cpu_threads > 0:
+            host = dict(N=N, topk=pb["topk"], aff=pb["aff"], tensors=pb["t"], w01=pb["w01"])
+            cpu[name] = oracle_sample(cfg, host, cpu_threads, all_experts=True,
+                                      **({"full": True} if name == "tiny" else {"n_tokens": 128, "n_cols": 64}))
+            if name == "tiny":     # the whole tiny backward on one thread as well
+                cpu[name]["single_thread"] = oracle_sample(cfg, host, 1, all_experts=True, full=True)
+            log(f"[bench] cpu baseline {name}: {cpu[name]['sample']}")
         del pb, op
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    return res
+    return res, cpu
 
 
 def run_dense(reps):
@@ -354,12 +378,41 @@ def run_router(reps):
     return res
 
 
-def cpu_baseline(cfg, moe, nthreads, n_tokens, n_cols):
-    """The oracle (as it stands) on a bounded sample of the same workload: whole
-    dX rows and d(a) of n_tokens tokens routed only to experts {0,1} (Phases 1
-    and 3 with the epilogue), and n_cols intermediate columns of expert 0's
-    weight gradients (Phases 2 and 4).  Weights of experts 0 and 1 are
-    quantised by the oracle itself (input preparation, not timed)."""
+def host_cpu():
+    """The host the oracle runs on: logical CPUs of the machine, those this
+    process may run on, the thread share the box grants a one-GPU job
+    (OMP_NUM_THREADS there), and the CPU model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or None
+    return {"cpu_model": model, "host_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+            "thread_share": share}
+
+
+def oracle_threads():
+    """Threads for the oracle: every CPU this process may run on, capped at the
+    box's per-GPU thread share when one is set."""
+    h = host_cpu()
+    n = h["affinity_cpus"] or 1
+    return min(n, h["thread_share"]) if h["thread_share"] else n
+
+
+def oracle_sample(cfg, moe, nthreads, n_tokens=0, n_cols=0, all_experts=False, full=False):
+    """The oracle (as it stands, never tuned for timing) on the same workload:
+    full=True the whole backward; otherwise a bounded sample: whole dX rows and
+    d(a) of n_tokens tokens (Phases 1 and 3 with the epilogue) and n_cols
+    intermediate columns of one expert's weight gradients (Phases 2 and 4).
+    With all_experts every expert's weights are quantised by the oracle (input
+    preparation, not timed); otherwise only experts 0 and 1, and the tokens are
+    those routed to no other expert.  The rate counts the algorithmic FLOPs of
+    the sample (12*H*I per routed pair of the rows, 6*H per slot and column)."""
     import numpy as np
     import oracle
     import synthetic as S
@@ -373,39 +426,73 @@ def cpu_baseline(cfg, moe, nthreads, n_tokens, n_cols):
     wgu_s = np.zeros((E, H, 2, I // 32), np.uint8)
     wd_c = np.zeros((E, I, H), np.uint8)
     wd_s = np.zeros((E, I, H // 32), np.uint8)
-    # bf16 weights of experts 0 and 1 as the generator made them, quantised by the oracle
     from concurrent.futures import ThreadPoolExecutor
 
     def q_rows(x, rows):
         return oracle.quantize(np.ascontiguousarray(x[rows]), 1, oracle.E4M3)
 
-    with ThreadPoolExecutor(max_workers=nthreads) as ex:
-        for e in (0, 1):
+    nq = moe["w01"]["gu"].shape[0]
+    with ThreadPoolExecutor(max_workers=max(1, nthreads)) as ex:
+        for e in range(nq):
             gu = moe["w01"]["gu"][e].reshape(H * 2, I)
             dd = moe["w01"]["d"][e].reshape(I, H)
             for src, dst_c, dst_s in ((gu, wgu_c[e].reshape(H * 2, I), wgu_s[e].reshape(H * 2, I // 32)),
                                       (dd, wd_c[e], wd_s[e])):
-                chunks = np.array_split(np.arange(src.shape[0]), nthreads)
+                chunks = np.array_split(np.arange(src.shape[0]), max(1, nthreads))
                 for rows, (c, s) in zip(chunks, ex.map(lambda r, src=src: q_rows(src, r), chunks)):
                     dst_c[rows], dst_s[rows] = c, s
     p = oracle.MoeProblem(T=T, H=H, I=I, E=E, N=N, B=B, hidden=bits["hidden"], aff=moe["aff"], wgu_codes=wgu_c,
                           wgu_scales=wgu_s, wd_codes=wd_c, wd_scales=wd_s, tpid=tpid, b2e=b2e, dy=bits["dy"],
                           ckpt=bits["ckpt"], b2=bits["b2"], affinity_on=cfg.affinity_on,
                           has_bias=int(cfg.has_bias), nthreads=nthreads)
-    only01 = np.nonzero(np.all(np.isin(topk, [0, 1]), axis=1))[0][:n_tokens].astype(np.int32)
-    cols = np.arange(n_cols, dtype=np.int32) * (I // n_cols)
-    slots_e0 = int(np.count_nonzero((tpid >= 0) & (np.repeat(b2e, B) == 0)))
-    t0 = time.perf_counter()
-    oracle.moe_token_rows(p, only01)
-    t1 = time.perf_counter()
-    oracle.moe_expert_cols(p, 0, cols)
-    t2 = time.perf_counter()
-    flops = only01.size * cfg.K * 6 * H * I + n_cols * 6 * H * slots_e0
-    secs = t2 - t0
+    if full:
+        t0 = time.perf_counter()
+        oracle.moe_bwd(p)
+        secs = time.perf_counter() - t0
+        flops = cfg.flops
+        desc = f"{cfg.name}: the whole backward, {flops / 1e9:.2f} GFLOP in {secs:.2f} s on {nthreads} thread(s)"
+    else:
+        if all_experts:
+            toks = np.arange(min(n_tokens, T), dtype=np.int32)
+        else:
+            toks = np.nonzero(np.all(np.isin(topk, [0, 1]), axis=1))[0][:n_tokens].astype(np.int32)
+        cnt = np.bincount(topk[topk >= 0].ravel(), minlength=E)
+        e_cols = int(np.argmax(cnt)) if all_experts else 0
+        cols = np.arange(n_cols, dtype=np.int32) * (I // n_cols)
+        slots = int(np.count_nonzero((tpid >= 0) & (np.repeat(b2e, B) == e_cols)))
+        pairs = int(np.count_nonzero(topk[toks] >= 0))
+        t0 = time.perf_counter()
+        oracle.moe_token_rows(p, toks)
+        t1 = time.perf_counter()
+        oracle.moe_expert_cols(p, e_cols, cols)
+        t2 = time.perf_counter()
+        flops = pairs * 6 * H * I + n_cols * 6 * H * slots
+        secs = t2 - t0
+        desc = (f"{cfg.name}: dX rows + d(affinity) of {toks.size} tokens ({pairs} routed pairs; Phases 1+3, "
+                f"{t1 - t0:.1f} s) and {n_cols} intermediate columns of expert {e_cols}'s dW (Phases 2+4, {slots} "
+                f"slots, {t2 - t1:.1f} s); {flops / 1e9:.1f} GFLOP in {secs:.1f} s on {nthreads} thread(s)")
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
-            "sample": (f"{cfg.name}: dX rows + d(affinity) of {only01.size} tokens (Phases 1+3, {t1 - t0:.1f} s) "
-                       f"and {n_cols} intermediate columns of expert 0's dW (Phases 2+4, {slots_e0} slots, "
-                       f"{t2 - t1:.1f} s); {flops / 1e9:.1f} GFLOP in {secs:.1f} s")}
+            "seconds": round(secs, 3), "sample": desc}
+
+
+def oracle_dense_sample(nthreads, n_rows):
+    """The oracle's dense backward (4096^3) on n_rows rows of dX and of dW: the
+    whole-operand quantisations it needs plus 4*n_rows*4096*4096 FLOPs."""
+    import numpy as np
+    import oracle
+    import synthetic as S
+    cfg = S.DENSE
+    d = S.dense_tensors(cfg, "cpu")
+    dy, w, x = (S.bf16_bits(d[k]) for k in ("dy", "w", "x"))
+    rows = np.arange(n_rows, dtype=np.int64) * (cfg.M // n_rows)
+    t0 = time.perf_counter()
+    oracle.dense_bwd(dy, w, x, dx_rows=rows, dw_rows=rows, nthreads=nthreads)
+    secs = time.perf_counter() - t0
+    flops = 2 * 2 * n_rows * cfg.N * cfg.K
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "seconds": round(secs, 3),
+            "sample": f"{cfg.name}: {n_rows} rows of dX and of dW (with the quantisation of all three operands), "
+                      f"{flops / 1e9:.2f} GFLOP in {secs:.2f} s on {nthreads} thread(s)"}
 
 
 def kernel_only(cfg, stage_name, reps):
@@ -446,7 +533,8 @@ def main():
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (0: every CPU this process may use, capped at the box's thread share)")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--cpu-cols", type=int, default=128)
     ap.add_argument("--kernel-only", metavar="STAGE", help="set up, then launch one stage (for rocprofv3 --pmc)")
@@ -496,11 +584,22 @@ def main():
         out["router_bwd"] = run_router(args.profile_reps + 5)
         log("[bench] router backward: " + ", ".join(f"{k} {v['ms']} ms" for k, v in out["router_bwd"].items()
                                                      if isinstance(v, dict)))
-        out["other_workloads"] = run_other_configs(cfg.name)
+    nthreads = args.cpu_threads or oracle_threads()
+    others_cpu = {}
+    if not args.no_extra:
+        out["other_workloads"], others_cpu = run_other_configs(
+            cfg.name, 0 if args.no_cpu_baseline else nthreads, args.profile_reps)
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle on a bounded sample) ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, moe, args.cpu_threads, args.cpu_tokens, args.cpu_cols)
-        log(f"[bench] cpu baseline: {out['cpu_baseline']['sample']}")
+        log(f"[bench] cpu baseline (oracle on a bounded sample, {nthreads} threads) ...")
+        cb = oracle_sample(cfg, moe, nthreads, args.cpu_tokens, args.cpu_cols)
+        cb.update(host_cpu())
+        if not args.no_extra:
+            dense_st = oracle_dense_sample(1, 16)
+            dense_mt = oracle_dense_sample(nthreads, 64)
+            dense_mt["single_thread"] = dense_st
+            cb["other_workloads"] = {**others_cpu, "dense": dense_mt}
+        out["cpu_baseline"] = cb
+        log(f"[bench] cpu baseline: {cb['sample']}")
     print(json.dumps(out), flush=True)
 
 

@@ -25,7 +25,8 @@
  *    failure the call returns a non-zero mxfp8_status, records a message that
  *    mxfp8_last_error() returns on the calling thread, and leaves every output
  *    untouched.  No C++ exception crosses this interface.
- *  - Outputs are fully overwritten (never accumulated into).
+ *  - Outputs are fully overwritten, except where moe_bwd_mxfp8's `accumulate`
+ *    flag asks for the gradients to be added into them.
  *
  * MXFP8 (P1: "32-element quantization group"): a group of 32 consecutive
  * elements along the quantised axis shares one E8M0 scale byte S (value
@@ -69,9 +70,10 @@ const char* mxfp8_version(void);
  *   axis 0: groups of 32 along rows;  scales [rows/32, cols]  (rows % 32 == 0).
  *   fmt    MXFP8_E4M3 or MXFP8_E5M2.
  *   codes  [rows, cols] u8, in x's layout;  scales: E8M0 bytes as above.
- * Errors: INVALID_ARG for a null pointer, a bad axis/fmt, a non-multiple of 32
- * along the quantised axis or rows*cols == 0 with non-null pointers is fine
- * (nothing is enqueued).
+ * Errors: INVALID_ARG for a negative size, a bad axis or fmt, a size along the
+ * quantised axis that is not a multiple of 32, a null pointer, or x / codes
+ * not 16-byte aligned; HIP if the launch fails.  rows * cols == 0 is not an
+ * error: nothing is enqueued and the pointers are not read (they may be NULL).
  * ------------------------------------------------------------------------- */
 int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis, int fmt,
                    uint8_t* codes, uint8_t* scales, void* stream);
@@ -145,7 +147,8 @@ int moe_build_blocks(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
  *   affinity on H (0): y_t += a * (inter Wd[e] + b2[e])
  *   affinity on I (1): y_t += (a * inter) Wd[e]            (no bias)
  * Backward (P1 phases; P3's epilogue):
- *   Phase 1  dS = dY_t Wd[e]^T (quantised along H), fused epilogue:
+ *   Phase 1  dS = dY_t Wd[e]^T (quantised along H), then the SwiGLU-backward
+ *            epilogue on the fp32 product (a kernel of its own):
  *            d(a) = sum_i dS*inter + <dY_t, b2[e]>,  dInter = a*dS,
  *            dGate = dInter*up*silu'(g),  dUp = dInter*silu(g)
  *   Phase 3  dX_t += [dGate,dUp] Wgu[e]^T    (quantised along I)
@@ -264,9 +267,12 @@ int moe_bwd_mxfp8_workspace_query(const moe_bwd_mxfp8_args* args,
 size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
 
 /* Enqueues the whole backward.  Errors: INVALID_ARG (shapes, null required
- * pointers, alignment, formats, accumulate outside {0,1}), UNSUPPORTED (block_size outside the set,
- * affinity on I together with a bias, sizes beyond 32-bit indexing or
- * I * block_size * 4 beyond 2 GiB), WORKSPACE (too small).  Device-side
+ * pointers, alignment, formats, accumulate outside {0,1}), UNSUPPORTED
+ * (block_size outside the set, affinity on I together with a bias, or sizes
+ * beyond 32-bit indexing: N * block_size or T * E above 2^31 - 1, a [T,H] bf16
+ * tensor of 2 GiB or more, i.e. T * H * 2 > 2^31 - 1, which the gathers
+ * address through one buffer descriptor, or I * block_size * 4 beyond 2 GiB),
+ * WORKSPACE (too small).  Device-side
  * preconditions (not checked): block_to_expert entries in [0,E) (blocks with
  * other values are skipped); each (t,e) pair appears in at most one slot. */
 int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,

@@ -286,11 +286,6 @@ hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const floa
 }
 
 // ---------------------------------------------------------------------------
-// Token-axis quantised intermediate for Phase 4: inter = bf16(bf16(silu(g)) * u)
-// (affinity on H) or bf16(fp32(a * inter)) (affinity on I), from the gate/up
-// checkpoint [N,2,I,B] (P1 gate_up_proj_act_checkpoint_T).  Groups of 32
-// consecutive slots; 4 lanes per group, 8 slots per lane.  Padding -> 0.
-// ---------------------------------------------------------------------------
 // Bias terms (has_bias): per slot <dY_t, b2[e]> stored in daff_slot (one wave
 // per slot), and db2[e][h] += sum over a block's slots of a * dY[t][h].
 // H % 32 == 0 and dY / b2 rows 16-byte aligned: 8 values per lane and load.

@@ -26,11 +26,14 @@ _lib = None
 
 
 def lib():
+    """The loaded oracle library: liboracle.so, or the file MXFP8_ORACLE_LIB
+    names (the sanitizer build, loaded by the sanitizer pin's child process)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("MXFP8_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        _lib = C.CDLL(_build.LIB)
+        _lib = C.CDLL(path)
         _declare(_lib)
     return _lib
 

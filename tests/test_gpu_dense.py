@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import bf, pairs_to_rows, rel_fro
+from helpers import assert_parity, bf, pairs_to_rows, parity_stats, rel_fro
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -35,8 +35,11 @@ def test_dense_small_full_parity(M, N, K):
     torch.cuda.synchronize()
     dy_b, w_b, x_b = (S.bf16_bits(t[k]) for k in ("dy", "w", "x"))
     rdx, rdw = oracle.dense_bwd(dy_b, w_b, x_b)
-    assert rel_fro(bf(S.bf16_bits(dx)), bf(rdx)) <= TOL
-    assert rel_fro(bf(S.bf16_bits(dw)), bf(rdw)) <= TOL
+    sx = parity_stats(bf(S.bf16_bits(dx)), bf(rdx), rows=M)
+    sw = parity_stats(bf(S.bf16_bits(dw)), bf(rdw), rows=N)
+    print((M, N, K), "dX", sx, "dW", sw, flush=True)
+    assert_parity("dX", sx, tol=TOL)
+    assert_parity("dW", sw, tol=TOL)
     # quantised operands in the documented workspace regions, bit-exact
     regs = mx.matmul_workspace_regions(M, N, K)
     wsh = ws.cpu().numpy()
@@ -62,8 +65,8 @@ def test_dense_format_combinations(fdy, fw, fx):
     t = _inputs(M, N, K, seed=3)
     dx, dw = mx.matmul_mxfp8_bwd(t["dy"], t["w"], t["x"], fdy, fw, fx)
     rdx, rdw = oracle.dense_bwd(*(S.bf16_bits(t[k]) for k in ("dy", "w", "x")), fmt_dy=fdy, fmt_w=fw, fmt_x=fx)
-    assert rel_fro(bf(S.bf16_bits(dx)), bf(rdx)) <= TOL
-    assert rel_fro(bf(S.bf16_bits(dw)), bf(rdw)) <= TOL
+    assert_parity("dX", parity_stats(bf(S.bf16_bits(dx)), bf(rdx), rows=M), tol=TOL)
+    assert_parity("dW", parity_stats(bf(S.bf16_bits(dw)), bf(rdw), rows=N), tol=TOL)
 
 
 def test_dense_4096_sampled_rows():
@@ -79,8 +82,11 @@ def test_dense_4096_sampled_rows():
     rdx, rdw = oracle.dense_bwd(*(S.bf16_bits(t[k]) for k in ("dy", "w", "x")), dx_rows=rows, dw_rows=rows)
     gdx = bf(S.bf16_bits(dx))[rows]
     gdw = bf(S.bf16_bits(dw))[rows]
-    assert rel_fro(gdx, bf(rdx)) <= TOL
-    assert rel_fro(gdw, bf(rdw)) <= TOL
+    sx = parity_stats(gdx, bf(rdx), rows=len(rows))
+    sw = parity_stats(gdw, bf(rdw), rows=len(rows))
+    print("dense 4096 sampled rows: dX", sx, "dW", sw, flush=True)
+    assert_parity("dX", sx, tol=TOL)
+    assert_parity("dW", sw, tol=TOL)
     # every output finite and not identically zero
     assert torch.isfinite(dx.float()).all() and torch.isfinite(dw.float()).all()
     assert dx.float().abs().sum() > 0 and dw.float().abs().sum() > 0

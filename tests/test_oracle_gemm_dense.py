@@ -93,3 +93,41 @@ def test_dense_close_to_exact_and_row_selection():
     rows = np.array([5, 0, 77])
     sx, sw = oracle.dense_bwd(dy, w, x, dx_rows=rows, dw_rows=rows)
     assert np.array_equal(sx, dX[rows]) and np.array_equal(sw, dW[rows])
+
+
+def test_dense_finite_differences_of_the_forward():
+    """With quantisation switched off (format hook -1) the oracle's dX and dW are
+    the gradients of L(X, W) = <dY, X W^T> ([P2] Background: Y = X W^T).  Central
+    differences of L, evaluated by numpy's float64 matmul, must match every
+    entry to one bf16 rounding; a transposed operand or a wrong contraction
+    axis fails here."""
+    rng = np.random.default_rng(14)
+    M, N, K = 64, 32, 8
+    dy, w, x = _bits(rng.standard_normal((M, N))), _bits(rng.standard_normal((N, K))), \
+        _bits(rng.standard_normal((M, K)))
+    dX, dW = oracle.dense_bwd(dy, w, x, fmt_dy=oracle.NONE, fmt_w=oracle.NONE, fmt_x=oracle.NONE)
+    dyf, wf, xf = (oracle.bf16_to_float(v).astype(np.float64) for v in (dy, w, x))
+
+    def loss(xv, wv):
+        return float(np.sum(dyf * (xv @ wv.T)))
+
+    h = 0.5
+    fdx = np.zeros((M, K))
+    for m in range(M):
+        for k in range(K):
+            xp, xm = xf.copy(), xf.copy()
+            xp[m, k] += h
+            xm[m, k] -= h
+            fdx[m, k] = (loss(xp, wf) - loss(xm, wf)) / (2 * h)
+    fdw = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            wp, wm = wf.copy(), wf.copy()
+            wp[n, k] += h
+            wm[n, k] -= h
+            fdw[n, k] = (loss(xf, wp) - loss(xf, wm)) / (2 * h)
+    gx = oracle.bf16_to_float(dX).astype(np.float64)
+    gw = oracle.bf16_to_float(dW).astype(np.float64)
+    assert np.all(np.abs(gx - fdx) <= 2.0 ** -8 * np.abs(fdx) + 1e-9)
+    assert np.all(np.abs(gw - fdw) <= 2.0 ** -8 * np.abs(fdw) + 1e-9)
+    assert np.abs(fdx).max() > 1 and np.abs(fdw).max() > 1

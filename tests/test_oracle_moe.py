@@ -314,3 +314,39 @@ def test_accumulate_adds_into_the_outputs():
 def oracle_bits(x: np.ndarray) -> np.ndarray:
     """float64 -> bf16 bit patterns (one RNE rounding)."""
     return np.vectorize(oracle.double_to_bf16, otypes=[np.uint16])(x)
+
+
+@pytest.mark.parametrize("on", [0, 1])
+def test_token_operands_of_the_epilogue_match_their_definition(on):
+    """The other two token-axis operands: the intermediate (mode 2; under the
+    affinity on I it is bf16(fp32(a * intermediate))) and [dGate; dUp] (mode 3),
+    each the 32-slot groups of the per-slot values gathered into [rows, P].
+    The per-slot values come from the block evaluator, whose arithmetic the
+    single-expert identity and the finite-difference pins fix; this pins the
+    gather, the row order (gate rows before up rows), the affinity product and
+    its rounding, the format and the group axis."""
+    cfg = S.scaled(S.TINY, T=64, I=64, H=64, E=4, K=2, B=32)
+    p, _ = moe_problem(cfg)
+    p.affinity_on = on
+    P = p.N * p.B
+    valid = (p.tpid >= 0) & (p.tpid < p.T)
+    e = p.b2e[np.arange(P) // p.B]
+    a = np.where(valid, p.aff[np.where(valid, p.tpid, 0) * p.E + e], 0).astype(np.float32)
+    det = [oracle.moe_block_detail(p, b) for b in range(p.N)]
+    inter = np.concatenate([d["inter"] for d in det])                       # [P, I] bf16 bits
+    dgu = np.concatenate([np.concatenate([d["dG"], d["dU"]], 1) for d in det])   # [P, 2I]
+    inter[~valid] = 0
+    dgu[~valid] = 0
+    if on == 1:
+        inter = _bits(a[:, None] * bf(inter).astype(np.float32))           # fp32 product, one bf16 rounding
+    codes, scales = oracle.moe_token_operand(p, oracle.TOK_INTER)
+    c2, s2 = oracle.quantize(np.ascontiguousarray(inter.T), 1, oracle.E4M3)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    codes, scales = oracle.moe_token_operand(p, oracle.TOK_DGU)
+    c2, s2 = oracle.quantize(np.ascontiguousarray(dgu.T), 1, oracle.E5M2)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    # the affinity really enters mode 2 under the affinity on I (and only there)
+    assert (on == 1) != np.array_equal(
+        oracle.moe_token_operand(p, oracle.TOK_INTER)[0],
+        oracle.quantize(np.ascontiguousarray(np.concatenate([d["inter"] for d in det]).T * valid[None]
+                                             .astype(np.uint16)), 1, oracle.E4M3)[0])
