@@ -309,7 +309,7 @@ def run_other_configs(skip, cpu_threads=0, profile_reps=5):
         if cpu_threads > 0:
             host = dict(N=N, topk=pb["topk"], aff=pb["aff"], tensors=pb["t"], w01=pb["w01"])
             cpu[name] = oracle_sample(cfg, host, cpu_threads, all_experts=True,
-                                      **({"full": True} if name == "tiny" else {"n_tokens": 128, "n_cols": 64}))
+                                      **({"full": True} if name == "tiny" else {"n_tokens": 512, "n_cols": 128}))
             if name == "tiny":     # the whole tiny backward on one thread as well
                 cpu[name]["single_thread"] = oracle_sample(cfg, host, 1, all_experts=True, full=True)
             log(f"[bench] cpu baseline {name}: {cpu[name]['sample']}")
@@ -594,8 +594,8 @@ def main():
         cb = oracle_sample(cfg, moe, nthreads, args.cpu_tokens, args.cpu_cols)
         cb.update(host_cpu())
         if not args.no_extra:
-            dense_st = oracle_dense_sample(1, 16)
-            dense_mt = oracle_dense_sample(nthreads, 64)
+            dense_st = oracle_dense_sample(1, 32)
+            dense_mt = oracle_dense_sample(nthreads, 256)
             dense_mt["single_thread"] = dense_st
             cb["other_workloads"] = {**others_cpu, "dense": dense_mt}
         out["cpu_baseline"] = cb

@@ -102,6 +102,60 @@ int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis, int 
  *   each region starting on a 256-byte boundary, in this order, codes first.
  * ------------------------------------------------------------------------- */
 size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* matmul_mxfp8_bwd_ex -- the same backward with [P2]'s optional pre-quantised
+ * operands ("API Reference": output_grad_scales, weight_scales, input_scales,
+ * use_scale_packing and the *_is_swizzled flags).  Reading: a pre-quantised
+ * operand is given as its codes and E8M0 scales, grouped along the
+ * contraction axis of the product it feeds.  dY feeds two products that
+ * contract different axes, so it takes one set per axis (along N for dX,
+ * along M for dW); either or both may be given, and the bf16 output_grad is
+ * needed only for a set that is not.  An operand given pre-quantised needs no
+ * bf16 tensor (its pointer may be NULL).  The codes' format is the operand's
+ * fmt_*.  Layouts, for an operand with contraction length C:
+ *   not swizzled (what mxfp8_quantize writes):
+ *     output_grad along N  codes [M,N], scales [M, N/32]   (axis 1)
+ *     output_grad along M  codes [M,N], scales [M/32, N]   (axis 0)
+ *     weights (along N)    codes [N,K], scales [N/32, K]   (axis 0)
+ *     input (along M)      codes [M,K], scales [M/32, K]   (axis 0)
+ *   swizzled (*_is_swizzled = 1; the GEMM's operand layout, contraction
+ *   contiguous, as workspace regions [0]-[3] of matmul_mxfp8_bwd hold it):
+ *     output_grad along N  codes [M,N], scales [M, N/32]
+ *     output_grad along M  codes [N,M], scales [N, M/32]
+ *     weights              codes [K,N], scales [K, N/32]
+ *     input                codes [K,M], scales [K, M/32]
+ *   use_scale_packing = 1 (swizzled operands only, C % 128 == 0): the scales
+ *     of every pre-quantised operand are packed as [C/128][rows][4], word
+ *     (p, r) holding row r's E8M0 bytes for elements [128p, 128p + 128).
+ * A swizzled operand (with packed scales, or with C % 128 != 0) is read in
+ * place; any other is rearranged into its workspace region first.
+ * Workspace: matmul_mxfp8_bwd_workspace_size(M, N, K) bytes, as above.
+ * Errors: those of matmul_mxfp8_bwd, and INVALID_ARG for codes without scales
+ * (or the reverse), a flag outside {0,1}, a *_is_swizzled flag or
+ * use_scale_packing without a pre-quantised operand it applies to, packed
+ * scales on an unswizzled operand or with C % 128 != 0, or a missing bf16
+ * tensor that some product still needs.                                     */
+typedef struct {
+  int64_t M, N, K;
+  const uint16_t* output_grad;         /* [M,N] bf16 (NULL if both dY sets are given) */
+  const uint16_t* weights;             /* [N,K] bf16 (NULL if weight_codes is given)  */
+  const uint16_t* input_activation;    /* [M,K] bf16 (NULL if input_codes is given)   */
+  int fmt_output_grad, fmt_weights, fmt_input;
+  const uint8_t* output_grad_codes_n;  /* dY quantised along N (feeds dX), or NULL    */
+  const uint8_t* output_grad_scales_n;
+  const uint8_t* output_grad_codes_m;  /* dY quantised along M (feeds dW), or NULL    */
+  const uint8_t* output_grad_scales_m;
+  const uint8_t* weight_codes;         /* W quantised along N, or NULL               */
+  const uint8_t* weight_scales;
+  const uint8_t* input_codes;          /* X quantised along M, or NULL               */
+  const uint8_t* input_scales;
+  int output_grad_is_swizzled, weights_is_swizzled, input_is_swizzled;
+  int use_scale_packing;
+  uint16_t* input_grad;                /* [M,K] bf16 */
+  uint16_t* weight_grad;               /* [N,K] bf16 */
+} matmul_mxfp8_bwd_args;
+int matmul_mxfp8_bwd_ex(const matmul_mxfp8_bwd_args* args, void* workspace, size_t workspace_bytes,
+                        void* stream);
 /* Profiling aid: one stage of matmul_mxfp8_bwd on a workspace a full call has
  * filled: 0 quantise dY along N and W along N, 1 quantise dY and X along M,
  * 2 the dX GEMM, 3 the dW GEMM.  INVALID_ARG for another stage. */
@@ -142,7 +196,8 @@ int moe_build_blocks(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
 
 /* ---------------------------------------------------------------------------
  * moe_bwd_mxfp8 -- P1's blockwise_mm_bwd_mxfp8: all gradients of a blockwise
- * MoE SwiGLU layer.  Forward, per routed (token t, expert e) with affinity a:
+ * MoE SwiGLU (or GeGLU, see `activation`) layer.  Forward, per routed (token t,
+ * expert e) with affinity a:
  *   g = x_t Wgu[e][:,0,:] (+b1),  u = x_t Wgu[e][:,1,:] (+b1),  inter = silu(g)*u
  *   affinity on H (0): y_t += a * (inter Wd[e] + b2[e])
  *   affinity on I (1): y_t += (a * inter) Wd[e]            (no bias)
@@ -216,7 +271,15 @@ typedef struct {
    * pairs, empty experts) keep their old value.  For gradient accumulation
    * over micro-batches.                                                      */
   int accumulate;
+  /* Gated activation of the gate projection ([P3] _down_projection_backward_act
+   * accepts "swiglu" and "geglu"): MXFP8_ACT_SWIGLU (0, act = silu) or
+   * MXFP8_ACT_GEGLU (1, act = gelu in its erf form, g * Phi(g) with Phi the
+   * standard normal CDF; the pages do not say which GELU, and this is its
+   * definition).  inter = act(gate_pre) * up, dGate = dInter * up * act'(g),
+   * dUp = dInter * act(g); gate_act_checkpoint_T then holds bf16(act(g)).   */
+  int activation;
 } moe_bwd_mxfp8_args;
+typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
 
 /* Byte offsets of the workspace regions (each 256-byte aligned).  The quantised
  * operands can be read back from them after a call:
@@ -267,7 +330,7 @@ int moe_bwd_mxfp8_workspace_query(const moe_bwd_mxfp8_args* args,
 size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
 
 /* Enqueues the whole backward.  Errors: INVALID_ARG (shapes, null required
- * pointers, alignment, formats, accumulate outside {0,1}), UNSUPPORTED
+ * pointers, alignment, formats, accumulate or activation outside {0,1}), UNSUPPORTED
  * (block_size outside the set, affinity on I together with a bias, or sizes
  * beyond 32-bit indexing: N * block_size or T * E above 2^31 - 1, a [T,H] bf16
  * tensor of 2 GiB or more, i.e. T * H * 2 > 2^31 - 1, which the gathers

@@ -14,6 +14,8 @@ import torch
 
 E4M3 = 0
 E5M2 = 1
+ACT_SWIGLU = 0
+ACT_GEGLU = 1
 ROUTER_SOFTMAX_OVER_TOPK = 0
 ROUTER_TOPK_OVER_SOFTMAX = 1
 ROUTER_TOPK = 2
@@ -59,7 +61,7 @@ class MoeBwdArgs(C.Structure):
                 ("gate_and_up_proj_bias_grad", _p), ("down_proj_bias_grad", _p),
                 ("gate_act_checkpoint_T", _p), ("intermediate_checkpoint_T", _p),
                 ("scaled_intermediate_checkpoint_T", _p), ("down_proj_act_checkpoint", _p),
-                ("num_valid_tokens", _p), ("accumulate", C.c_int)]
+                ("num_valid_tokens", _p), ("accumulate", C.c_int), ("activation", C.c_int)]
 
 
 LAYOUT_FIELDS = ("dy_codes", "dy_scales", "dy_deq", "wd_deq", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
@@ -81,6 +83,7 @@ def _declare(L):
     L.moe_num_blocks.argtypes = [_i64, _i64, _i64, _i64]
     for name, res, args in (
         ("matmul_mxfp8_bwd_workspace_size", C.c_size_t, [_i64, _i64, _i64]),
+        ("matmul_mxfp8_bwd_ex", C.c_int, [C.POINTER(MatmulBwdArgs), _p, C.c_size_t, _p]),
         ("matmul_mxfp8_bwd", C.c_int, [_p, _p, _p, _i64, _i64, _i64, C.c_int, C.c_int, C.c_int, _p, _p,
                                        _p, C.c_size_t, _p]),
         ("moe_build_blocks_workspace_size", C.c_size_t, [_i64]),
@@ -167,6 +170,52 @@ def matmul_mxfp8_bwd(output_grad: torch.Tensor, weights: torch.Tensor, input_act
     return dx, dw
 
 
+class MatmulBwdArgs(C.Structure):
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("output_grad", _p), ("weights", _p),
+                ("input_activation", _p), ("fmt_output_grad", C.c_int), ("fmt_weights", C.c_int),
+                ("fmt_input", C.c_int), ("output_grad_codes_n", _p), ("output_grad_scales_n", _p),
+                ("output_grad_codes_m", _p), ("output_grad_scales_m", _p), ("weight_codes", _p),
+                ("weight_scales", _p), ("input_codes", _p), ("input_scales", _p),
+                ("output_grad_is_swizzled", C.c_int), ("weights_is_swizzled", C.c_int),
+                ("input_is_swizzled", C.c_int), ("use_scale_packing", C.c_int), ("input_grad", _p),
+                ("weight_grad", _p)]
+
+
+def matmul_mxfp8_bwd_ex(M: int, N: int, K: int, device, output_grad=None, weights=None, input_activation=None,
+                        fmt_output_grad: int = E5M2, fmt_weights: int = E4M3, fmt_input: int = E4M3,
+                        output_grad_n=None, output_grad_m=None, weight_q=None, input_q=None,
+                        output_grad_is_swizzled=False, weights_is_swizzled=False, input_is_swizzled=False,
+                        use_scale_packing=False, workspace: Optional[torch.Tensor] = None, out=None):
+    """matmul_mxfp8_bwd with [P2]'s optional pre-quantised operands
+    (include/mxfp8_moe.h: matmul_mxfp8_bwd_ex).  output_grad_n / output_grad_m /
+    weight_q / input_q are (codes uint8, scales uint8) pairs in the layouts the
+    header gives, or None to quantise the bf16 tensor."""
+    L = lib()
+    if workspace is None:
+        workspace = torch.empty(L.matmul_mxfp8_bwd_workspace_size(M, N, K), dtype=torch.uint8, device=device)
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.bfloat16, device=device),
+               torch.empty((N, K), dtype=torch.bfloat16, device=device))
+    dx, dw = out
+
+    def q(pair, name):
+        if pair is None:
+            return None, None
+        return _dev(pair[0], torch.uint8, name + " codes"), _dev(pair[1], torch.uint8, name + " scales")
+
+    gn, gm, wq, xq = (q(output_grad_n, "output_grad_n"), q(output_grad_m, "output_grad_m"), q(weight_q, "weights"),
+                      q(input_q, "input"))
+    a = MatmulBwdArgs(M, N, K, _dev(output_grad, torch.bfloat16, "output_grad"), _dev(weights, torch.bfloat16, "weights"),
+                      _dev(input_activation, torch.bfloat16, "input_activation"), fmt_output_grad, fmt_weights,
+                      fmt_input, *gn, *gm, *wq, *xq, int(output_grad_is_swizzled), int(weights_is_swizzled),
+                      int(input_is_swizzled), int(use_scale_packing), _dev(dx, torch.bfloat16, "dx"),
+                      _dev(dw, torch.bfloat16, "dw"))
+    _check(L.matmul_mxfp8_bwd_ex(C.byref(a), workspace.data_ptr(), workspace.numel(),
+                                 C.c_void_p(torch.cuda.current_stream(torch.device(device)).cuda_stream)),
+           "matmul_mxfp8_bwd_ex")
+    return dx, dw
+
+
 def matmul_mxfp8_bwd_stage(output_grad, weights, input_activation, stage: int, workspace, out,
                            fmt_output_grad: int = E5M2, fmt_weights: int = E4M3, fmt_input: int = E4M3):
     """One stage of matmul_mxfp8_bwd (0/1 quantise, 2 dX GEMM, 3 dW GEMM) on a filled workspace."""
@@ -232,7 +281,7 @@ class MoeBwd:
                  gate_up_proj_act_checkpoint_T, down_proj_bias=None, affinity_on=0, fmt_weight=E4M3,
                  fmt_act=E4M3, fmt_grad=E5M2, workspace=None, gate_act_checkpoint_T=None,
                  intermediate_checkpoint_T=None, scaled_intermediate_checkpoint_T=None,
-                 down_proj_act_checkpoint=None, num_valid_tokens=None, accumulate=False):
+                 down_proj_act_checkpoint=None, num_valid_tokens=None, accumulate=False, activation=0):
         T, H = hidden_states.shape
         E, _, _, I = gate_up_codes.shape
         N = block_to_expert.numel()
@@ -269,7 +318,7 @@ class MoeBwd:
             _dev(intermediate_checkpoint_T, torch.bfloat16, "intermediate_checkpoint_T"),
             _dev(scaled_intermediate_checkpoint_T, torch.bfloat16, "scaled_intermediate_checkpoint_T"),
             _dev(down_proj_act_checkpoint, torch.bfloat16, "down_proj_act_checkpoint"),
-            _dev(num_valid_tokens, torch.int32, "num_valid_tokens"), int(bool(accumulate)))
+            _dev(num_valid_tokens, torch.int32, "num_valid_tokens"), int(bool(accumulate)), int(activation))
         L = lib()
         lay = MoeWorkspaceLayout()
         _check(L.moe_bwd_mxfp8_workspace_query(C.byref(self.args), C.byref(lay)), "moe_bwd_mxfp8_workspace_query")

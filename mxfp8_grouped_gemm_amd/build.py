@@ -21,7 +21,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 SOURCES = ["api.cpp", "quantize.hip", "gemm_dense.hip", "moe_aux.hip", "moe_phase1_256.hip", "moe_phase1_256x128.hip",
-           "moe_phase1_128.hip", "moe_phase1_epi.hip", "moe_phase3.hip", "router.hip"]
+           "moe_phase1_128.hip", "moe_phase1_epi.hip", "moe_phase3.hip", "router.hip", "prequant.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

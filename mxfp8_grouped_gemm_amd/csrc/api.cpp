@@ -82,20 +82,69 @@ size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K) {
   return total;
 }
 
-static int dense_run(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N, int64_t K,
-                     int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws, size_t ws_bytes,
-                     void* stream, int lo, int hi) {
+// The four GEMM operand streams of the dense backward: rows, contraction, and
+// the workspace regions (codes, scales) they are built in when the caller does
+// not supply them in the GEMM's layout.
+struct DenseOperand {
+  const uint8_t* codes;    // what the GEMM reads
+  const uint8_t* scales;
+};
+
+static int dense_check(const matmul_mxfp8_bwd_args* a) {
+  if (!a) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: null args");
+  const int64_t M = a->M, N = a->N, K = a->K;
   if (M <= 0 || N <= 0 || K <= 0) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: non-positive shape");
   if (M % 32 || N % 32 || K % 32)
     return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: M, N, K must be multiples of 32 (got %lld %lld %lld)",
                 (long long)M, (long long)N, (long long)K);
-  if (!valid_fmt(fmt_dy) || !valid_fmt(fmt_w) || !valid_fmt(fmt_x))
+  if (!valid_fmt(a->fmt_output_grad) || !valid_fmt(a->fmt_weights) || !valid_fmt(a->fmt_input))
     return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: formats must be E4M3 (0) or E5M2 (1)");
-  if (!dy || !w || !x || !dx || !dw || !ws) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: null pointer");
-  if (!aligned16(dy) || !aligned16(w) || !aligned16(x) || !aligned16(dx) || !aligned16(dw))
-    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: tensors must be 16-byte aligned");
-  if (reinterpret_cast<uintptr_t>(ws) & 255u)
-    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: workspace must be 256-byte aligned");
+  const int flags[4] = {a->output_grad_is_swizzled, a->weights_is_swizzled, a->input_is_swizzled,
+                        a->use_scale_packing};
+  for (int f : flags)
+    if (f != 0 && f != 1) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: flags must be 0 or 1");
+  struct Pre { const uint8_t* c; const uint8_t* s; int swz; int64_t kdim; const char* name; };
+  const Pre pre[4] = {{a->output_grad_codes_n, a->output_grad_scales_n, a->output_grad_is_swizzled, N, "output_grad (along N)"},
+                      {a->weight_codes, a->weight_scales, a->weights_is_swizzled, N, "weights"},
+                      {a->output_grad_codes_m, a->output_grad_scales_m, a->output_grad_is_swizzled, M, "output_grad (along M)"},
+                      {a->input_codes, a->input_scales, a->input_is_swizzled, M, "input_activation"}};
+  for (const Pre& q : pre) {
+    if ((q.c == nullptr) != (q.s == nullptr))
+      return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: %s: pre-quantised codes and scales go together", q.name);
+    if (q.c && (!aligned16(q.c) || !aligned16(q.s)))
+      return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: %s: codes and scales must be 16-byte aligned", q.name);
+    if (q.c && a->use_scale_packing && !q.swz)
+      return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: %s: packed scales come with the swizzled layout", q.name);
+    if (q.c && q.swz && a->use_scale_packing && q.kdim % 128)
+      return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: %s: packed scales need a contraction that is a "
+                  "multiple of 128", q.name);
+  }
+  if (a->output_grad_is_swizzled && !a->output_grad_codes_n && !a->output_grad_codes_m)
+    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: output_grad_is_swizzled without pre-quantised output_grad");
+  if (a->weights_is_swizzled && !a->weight_codes)
+    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: weights_is_swizzled without pre-quantised weights");
+  if (a->input_is_swizzled && !a->input_codes)
+    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: input_is_swizzled without pre-quantised input_activation");
+  if (a->use_scale_packing && !a->output_grad_codes_n && !a->output_grad_codes_m && !a->weight_codes && !a->input_codes)
+    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: use_scale_packing without a pre-quantised input");
+  const bool need_dy = !a->output_grad_codes_n || !a->output_grad_codes_m;
+  if ((need_dy && !a->output_grad) || (!a->weight_codes && !a->weights) || (!a->input_codes && !a->input_activation) ||
+      !a->input_grad || !a->weight_grad)
+    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: null pointer (a bf16 input that is not given pre-quantised, "
+                "or an output)");
+  const void* al[5] = {need_dy ? a->output_grad : nullptr, a->weight_codes ? nullptr : a->weights,
+                       a->input_codes ? nullptr : a->input_activation, a->input_grad, a->weight_grad};
+  for (const void* q : al)
+    if (q && !aligned16(q)) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: tensors must be 16-byte aligned");
+  return MXFP8_OK;
+}
+
+static int dense_run(const matmul_mxfp8_bwd_args* a, void* ws, size_t ws_bytes, void* stream, int lo, int hi) {
+  int rc = dense_check(a);
+  if (rc) return rc;
+  const int64_t M = a->M, N = a->N, K = a->K;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd: workspace must be non-null and 256-byte aligned");
   size_t off[8], total;
   dense_regions(M, N, K, off, &total);
   if (ws_bytes < total)
@@ -103,54 +152,99 @@ static int dense_run(const uint16_t* dy, const uint16_t* w, const uint16_t* x, i
   uint8_t* base = static_cast<uint8_t*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  // operands of a GEMM whose contraction is a multiple of 128 feed the ring
-  // loop and get pair-major scales
-  const bool pairs_n = N % 128 == 0, pairs_m = M % 128 == 0;
-  // stage 0 -- dX = dY W: dY along N [M,N]; W along N, transposed to [K,N]
-  if (lo <= 0 && 0 <= hi &&
-      (e = mx::launch_quant_rows(dy, M, N, fmt_dy, base + off[0], base + off[1], st, nullptr, pairs_n)) != hipSuccess)
-    return hip_status(e, "quantize dY along N");
-  if (lo <= 0 && 0 <= hi &&
-      (e = mx::launch_quant_tok(w, N, K, nullptr, nullptr, N, fmt_w, base + off[2], base + off[3], st, pairs_n)) !=
-          hipSuccess)
-    return hip_status(e, "quantize W along N");
-  // stage 1 -- dW = dY^T X: dY along M, transposed to [N,M]; X along M, transposed to [K,M]
-  if (lo <= 1 && 1 <= hi &&
-      (e = mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fmt_dy, base + off[4], base + off[5], st, pairs_m)) !=
-          hipSuccess)
-    return hip_status(e, "quantize dY along M");
-  if (lo <= 1 && 1 <= hi &&
-      (e = mx::launch_quant_tok(x, M, K, nullptr, nullptr, M, fmt_x, base + off[6], base + off[7], st, pairs_m)) !=
-          hipSuccess)
-    return hip_status(e, "quantize X along M");
+  // Operands of a GEMM whose contraction is a multiple of 128 feed the ring
+  // loop and get pair-major scales.  Stream i of the GEMMs (rows x contraction): 0 dY along N (M x N), 1 W^T
+  // (K x N), 2 dY^T (N x M), 3 X^T (K x M).  Each is quantised from bf16 into
+  // workspace region i, or built there from a pre-quantised operand, or read
+  // in place when the caller's operand already has the GEMM's layout.
+  DenseOperand op[4];
+  for (int i = 0; i < 4; ++i) op[i] = {base + off[2 * i], base + off[2 * i + 1]};
+  const int64_t rows[4] = {M, K, N, K}, kdim[4] = {N, N, M, M};
+  const uint8_t* pc[4] = {a->output_grad_codes_n, a->weight_codes, a->output_grad_codes_m, a->input_codes};
+  const uint8_t* ps[4] = {a->output_grad_scales_n, a->weight_scales, a->output_grad_scales_m, a->input_scales};
+  const int swz[4] = {a->output_grad_is_swizzled, a->weights_is_swizzled, a->output_grad_is_swizzled,
+                      a->input_is_swizzled};
+  // natural (unswizzled) source of streams 1-3: codes [kdim][rows], scales [kdim/32][rows]
+  for (int i = 0; i < 4; ++i) {
+    if (!pc[i]) continue;
+    const bool pairs = kdim[i] % 128 == 0;
+    if (i == 0 || swz[i]) {   // codes already [rows][kdim]
+      op[i].codes = pc[i];
+      if (!pairs || a->use_scale_packing) op[i].scales = ps[i];   // the GEMM's scale layout as given
+    }
+  }
+  const uint16_t* dy = a->output_grad;
+  const int fdy = a->fmt_output_grad, fw = a->fmt_weights, fx = a->fmt_input;
+  auto prep = [&](int i) -> hipError_t {
+    const bool pairs = kdim[i] % 128 == 0;
+    uint8_t* wc = base + off[2 * i];
+    uint8_t* wsc = base + off[2 * i + 1];
+    if (!pc[i]) {   // quantise from bf16 along the contraction
+      switch (i) {
+        case 0: return mx::launch_quant_rows(dy, M, N, fdy, wc, wsc, st, nullptr, pairs);
+        case 1: return mx::launch_quant_tok(a->weights, N, K, nullptr, nullptr, N, fw, wc, wsc, st, pairs);
+        case 2: return mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fdy, wc, wsc, st, pairs);
+        default: return mx::launch_quant_tok(a->input_activation, M, K, nullptr, nullptr, M, fx, wc, wsc, st, pairs);
+      }
+    }
+    if (i == 0 || swz[i]) {   // GEMM layout: at most the row-major scales become pair-major
+      if (pairs && !a->use_scale_packing) return mx::launch_scales_to_pairs(ps[i], 1, rows[i], kdim[i], wsc, st);
+      return hipSuccess;
+    }
+    hipError_t r = mx::launch_transpose_codes(pc[i], kdim[i], rows[i], wc, st);
+    if (r != hipSuccess) return r;
+    return mx::launch_scales_axis0(ps[i], kdim[i], rows[i], wsc, pairs, st);
+  };
+  // stage 0 -- the dX operands (dY along N; W along N); stage 1 -- the dW operands
+  for (int i = 0; i < 4; ++i) {
+    const int stage = i < 2 ? 0 : 1;
+    if (lo <= stage && stage <= hi && (e = prep(i)) != hipSuccess) return hip_status(e, "operand preparation");
+  }
   mx::GemmStoreArgs g{};
-  g.a_codes = base + off[0]; g.a_scales = base + off[1]; g.lda = N;
-  g.b_codes = base + off[2]; g.b_scales = base + off[3]; g.ldb = N;
-  g.M = M; g.N = K; g.K = N; g.out = dx; g.ldo = K;
+  g.a_codes = op[0].codes; g.a_scales = op[0].scales; g.lda = N;
+  g.b_codes = op[1].codes; g.b_scales = op[1].scales; g.ldb = N;
+  g.M = M; g.N = K; g.K = N; g.out = a->input_grad; g.ldo = K;
   g.pair = 1;   // measured 6% faster than the four-slot ring on 8192^3, 5% on 4096^3
   // stage 2 -- dX GEMM
-  if (lo <= 2 && 2 <= hi && (e = mx::launch_gemm_store(g, 1, fmt_dy, fmt_w, st)) != hipSuccess)
+  if (lo <= 2 && 2 <= hi && (e = mx::launch_gemm_store(g, 1, fdy, fw, st)) != hipSuccess)
     return hip_status(e, "dX GEMM");
-  g.a_codes = base + off[4]; g.a_scales = base + off[5]; g.lda = M;
-  g.b_codes = base + off[6]; g.b_scales = base + off[7]; g.ldb = M;
-  g.M = N; g.N = K; g.K = M; g.out = dw; g.ldo = K;
+  g.a_codes = op[2].codes; g.a_scales = op[2].scales; g.lda = M;
+  g.b_codes = op[3].codes; g.b_scales = op[3].scales; g.ldb = M;
+  g.M = N; g.N = K; g.K = M; g.out = a->weight_grad; g.ldo = K;
   // stage 3 -- dW GEMM
-  if (lo <= 3 && 3 <= hi && (e = mx::launch_gemm_store(g, 1, fmt_dy, fmt_x, st)) != hipSuccess)
+  if (lo <= 3 && 3 <= hi && (e = mx::launch_gemm_store(g, 1, fdy, fx, st)) != hipSuccess)
     return hip_status(e, "dW GEMM");
   return ok();
+}
+
+static matmul_mxfp8_bwd_args dense_plain_args(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M,
+                                              int64_t N, int64_t K, int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx,
+                                              uint16_t* dw) {
+  matmul_mxfp8_bwd_args a{};
+  a.M = M; a.N = N; a.K = K;
+  a.output_grad = dy; a.weights = w; a.input_activation = x;
+  a.fmt_output_grad = fmt_dy; a.fmt_weights = fmt_w; a.fmt_input = fmt_x;
+  a.input_grad = dx; a.weight_grad = dw;
+  return a;
 }
 
 int matmul_mxfp8_bwd(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N, int64_t K,
                      int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws, size_t ws_bytes,
                      void* stream) {
-  return dense_run(dy, w, x, M, N, K, fmt_dy, fmt_w, fmt_x, dx, dw, ws, ws_bytes, stream, 0, 3);
+  const matmul_mxfp8_bwd_args a = dense_plain_args(dy, w, x, M, N, K, fmt_dy, fmt_w, fmt_x, dx, dw);
+  return dense_run(&a, ws, ws_bytes, stream, 0, 3);
+}
+
+int matmul_mxfp8_bwd_ex(const matmul_mxfp8_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return dense_run(a, ws, ws_bytes, stream, 0, 3);
 }
 
 int matmul_mxfp8_bwd_stage(const uint16_t* dy, const uint16_t* w, const uint16_t* x, int64_t M, int64_t N,
                            int64_t K, int fmt_dy, int fmt_w, int fmt_x, uint16_t* dx, uint16_t* dw, void* ws,
                            size_t ws_bytes, int stage, void* stream) {
   if (stage < 0 || stage > 3) return fail(MXFP8_ERR_INVALID_ARG, "matmul_mxfp8_bwd_stage: stage %d outside [0,4)", stage);
-  return dense_run(dy, w, x, M, N, K, fmt_dy, fmt_w, fmt_x, dx, dw, ws, ws_bytes, stream, stage, stage);
+  const matmul_mxfp8_bwd_args a = dense_plain_args(dy, w, x, M, N, K, fmt_dy, fmt_w, fmt_x, dx, dw);
+  return dense_run(&a, ws, ws_bytes, stream, stage, stage);
 }
 
 int64_t moe_num_blocks(int64_t T, int64_t K, int64_t E, int64_t B) {
@@ -272,6 +366,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   if (a->has_bias != 0 && a->has_bias != 1) return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: has_bias must be 0/1");
   if (a->accumulate != 0 && a->accumulate != 1)
     return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: accumulate must be 0/1");
+  if (a->activation != MXFP8_ACT_SWIGLU && a->activation != MXFP8_ACT_GEGLU)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_bwd_mxfp8: activation must be 0 (SwiGLU) or 1 (GeGLU)");
   if (a->affinity_on == 1 && a->has_bias)
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: a bias with the affinity on I is not supported");
   const void* req[] = {a->hidden_states, a->expert_affinities_masked, a->gate_up_codes, a->gate_up_scales,
@@ -398,6 +494,7 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p1.inter_tok_codes = at(L.inter_tok_codes); p1.inter_tok_scales = at(L.inter_tok_scales);
   p1.daff_part = reinterpret_cast<float*>(at(L.daff_part)); p1.db1_acc = db1_acc;
   p1.affinity_on_i = a->affinity_on; p1.has_bias = a->has_bias; p1.fmt_act = a->fmt_act;
+  p1.geglu = a->activation == MXFP8_ACT_GEGLU;
   p1.dgu_row_pairs = gu_pairs;
   // Tile order over the XCDs (measured: round robin 2.6% faster on Phase 1 with
   // 58 MB W_down experts; the contiguous ranges 6% faster with 0.4-3 MB ones)

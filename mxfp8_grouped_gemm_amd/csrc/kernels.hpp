@@ -20,6 +20,11 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
                             uint8_t* scales_t, hipStream_t st, bool pairs = false, bool self_rows = false);
+// prequant.hip: an operand quantised along its rows (codes [R][C], scales
+// [R/32][C]) into the GEMM layout: codes [C][R]; scales pair-major
+// [R/128][C][4] (pairs) or row-major [C][R/32]
+hipError_t launch_transpose_codes(const uint8_t* in, int64_t R, int64_t C, uint8_t* out, hipStream_t st);
+hipError_t launch_scales_axis0(const uint8_t* in, int64_t R, int64_t C, uint8_t* out, bool pairs, hipStream_t st);
 // gate/up weight scales [E][H][2I/32] -> pair-major per expert [E][2I/128][H][4]
 hipError_t launch_scales_to_pairs(const uint8_t* in, int64_t groups, int64_t rows, int64_t k, uint8_t* out,
                                   hipStream_t st);
@@ -128,6 +133,7 @@ struct Phase1Args {
   int affinity_on_i;            // 1: the intermediate operand carries the affinity
   int has_bias;                 // 1: accumulate db1
   int fmt_act;                  // format of the intermediate operand (activation format)
+  int geglu;                    // gated activation: 0 SwiGLU (silu), 1 GeGLU (gelu, erf form)
   int dgu_row_pairs;            // 1: dGU along I feeds the ring loop (2I % 128 == 0): pair-major scales
   int rr_tiles;                 // tile order over the XCDs (moe_tiles.hpp)
   int tiles_m, tiles_n;

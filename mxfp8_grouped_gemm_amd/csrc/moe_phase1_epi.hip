@@ -1,15 +1,15 @@
-// moe_phase1_epi.hip -- the SwiGLU backward after Phase 1's product (P1,
+// moe_phase1_epi.hip -- the SwiGLU (or GeGLU) backward after Phase 1's product (P1,
 // "Blockwise MM Backward MXFP8 Kernel API Reference": Phase 1's epilogue and
 // the checkpoint parameters; P3, sonic-moe functional/backward.py:
 // _down_projection_backward_act, the gated-activation backward).
 //
 // Per slot p of block b (token t, affinity a_p; padding slots contribute zeros)
 // and intermediate index i, from dS = Phase 1's product and the checkpoint g, u:
-//   ga = bf16(silu(g)), inter = bf16(ga * u)
+//   ga = bf16(silu(g)) (GeGLU: bf16(gelu(g))), inter = bf16(ga * u)
 //   d(a)_p  = sum_i dS * inter                  (a partial per 32 rows i, summed
 //                                                at the end in order)
 //   dInter = a_p * dS
-//   dGate = bf16(dInter * u * silu'(g)), dUp = bf16(dInter * ga)
+//   dGate = bf16(dInter * u * silu'(g)) (GeGLU: gelu'(g)), dUp = bf16(dInter * ga)
 //   -> quantised along I        (Phase-3 A operand, dgu_row [P][2I])
 //   -> quantised along the slots (Phase-2 B operand, dgu_tok [2I][P])
 //   -> db1 partial sums along the slots (with a bias)
@@ -40,23 +40,34 @@ constexpr int kEpiElems = 8192;   // TI * TS
 // A supplied checkpoint value (HAS_*) replaces the recomputed one; the values
 // are rounded at the same points either way, so consistent checkpoints give
 // the same bits.
-template <bool ON_I>
+// GEGLU: the gate activation is gelu (g * Phi(g)) instead of silu.
+template <bool ON_I, bool GEGLU>
 __device__ __forceinline__ uint32_t swiglu_bwd(float d, float g, float u, float a, bool has_ga, float ga_in,
                                                bool has_in, float in_in, bool has_sc, uint16_t sc_in, float& daff,
                                                uint16_t& it) {
-  const float sg = sigmoid_fast(g);
-  const float ga = has_ga ? ga_in : bf16_round(g * sg);   // silu(g)
-  const float in = has_in ? in_in : bf16_round(ga * u);   // intermediate
-  daff += d * in;
-  const float di = a * d;                                 // d(intermediate)
-  it = ON_I ? (has_sc ? sc_in : bf16_rne(a * in)) : uint16_t(__float_as_uint(in) >> 16);
-  return bf16x2_rne(di * u * dsilu_from(g, sg), di * ga);
+  if constexpr (GEGLU) {
+    const float cdf = normal_cdf(g);
+    const float ga = has_ga ? ga_in : bf16_round(g * cdf);   // gelu(g)
+    const float in = has_in ? in_in : bf16_round(ga * u);    // intermediate
+    daff += d * in;
+    const float di = a * d;                                  // d(intermediate)
+    it = ON_I ? (has_sc ? sc_in : bf16_rne(a * in)) : uint16_t(__float_as_uint(in) >> 16);
+    return bf16x2_rne(di * u * dgelu_from(g, cdf), di * ga);
+  } else {
+    const float sg = sigmoid_fast(g);
+    const float ga = has_ga ? ga_in : bf16_round(g * sg);   // silu(g)
+    const float in = has_in ? in_in : bf16_round(ga * u);   // intermediate
+    daff += d * in;
+    const float di = a * d;                                 // d(intermediate)
+    it = ON_I ? (has_sc ? sc_in : bf16_rne(a * in)) : uint16_t(__float_as_uint(in) >> 16);
+    return bf16x2_rne(di * u * dsilu_from(g, sg), di * ga);
+  }
 }
 
 // CK: the caller supplied at least one of the [N][I][B] checkpoints (silu(gate),
 // the intermediate, the scaled intermediate); pass 1 then runs its 32 rows in
 // two halves so that the extra loads fit in registers.
-template <int FG, bool ON_I, int TS, bool CK>
+template <int FG, bool ON_I, int TS, bool CK, bool GEGLU>
 __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
   constexpr int TI = kEpiElems / TS;         // rows of the tile
   constexpr int NG = TS / 32;                // 32-slot groups of a row
@@ -135,7 +146,7 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
         }
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
-          gu[k] = swiglu_bwd<ON_I>(dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, false, 0.f, false, 0.f, false,
+          gu[k] = swiglu_bwd<ON_I, GEGLU>(dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, false, 0.f, false, 0.f, false,
                                    0, daff, it[k]);
           amg = fmaxf(amg, fabsf(lo_bf16(gu[k])));
           amu = fmaxf(amu, fabsf(hi_bf16(gu[k])));
@@ -166,7 +177,7 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             const int kk = 16 * hh + k;
-            gu[kk] = swiglu_bwd<ON_I>(dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, has_ga, bf16_to_f32(gab[k]),
+            gu[kk] = swiglu_bwd<ON_I, GEGLU>(dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, has_ga, bf16_to_f32(gab[k]),
                                       has_in, bf16_to_f32(inb[k]), has_sc, scb[k], daff, it[kk]);
             amg = fmaxf(amg, fabsf(lo_bf16(gu[kk])));
             amu = fmaxf(amu, fabsf(hi_bf16(gu[kk])));
@@ -281,24 +292,29 @@ __global__ void __launch_bounds__(kEpiThreads) phase1_epi_kernel(Phase1Args p) {
   }
 }
 
-template <int TS, bool CK>
+template <int TS, bool CK, bool GEGLU>
 static hipError_t epi_launch(const Phase1Args& p, int fg, hipStream_t st) {
   constexpr int TI = kEpiElems / TS;
   const int64_t grid = int64_t(p.N) * ((p.I + TI - 1) / TI) * (p.B / TS);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   const bool on_i = p.affinity_on_i != 0;
   if (fg == kE4M3) {
-    if (on_i) phase1_epi_kernel<kE4M3, true, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
-    else phase1_epi_kernel<kE4M3, false, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    if (on_i) phase1_epi_kernel<kE4M3, true, TS, CK, GEGLU><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    else phase1_epi_kernel<kE4M3, false, TS, CK, GEGLU><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
   } else {
-    if (on_i) phase1_epi_kernel<kE5M2, true, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
-    else phase1_epi_kernel<kE5M2, false, TS, CK><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    if (on_i) phase1_epi_kernel<kE5M2, true, TS, CK, GEGLU><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
+    else phase1_epi_kernel<kE5M2, false, TS, CK, GEGLU><<<unsigned(grid), kEpiThreads, 0, st>>>(p);
   }
   return hipGetLastError();
 }
+template <int TS, bool GEGLU>
+static hipError_t epi_launch(const Phase1Args& p, int fg, hipStream_t st) {
+  if (p.ga_ckpt || p.in_ckpt || p.sc_ckpt) return epi_launch<TS, true, GEGLU>(p, fg, st);
+  return epi_launch<TS, false, GEGLU>(p, fg, st);
+}
 template <int TS>
 static hipError_t epi_launch(const Phase1Args& p, int fg, hipStream_t st) {
-  if (p.ga_ckpt || p.in_ckpt || p.sc_ckpt) return epi_launch<TS, true>(p, fg, st);
+  if (p.geglu) return epi_launch<TS, true>(p, fg, st);
   return epi_launch<TS, false>(p, fg, st);
 }
 

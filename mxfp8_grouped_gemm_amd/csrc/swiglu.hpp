@@ -1,4 +1,5 @@
-// swiglu.hpp -- SwiGLU recompute and backward factors for the Phase-1 epilogue.
+// swiglu.hpp -- gated-activation (SwiGLU, GeGLU) recompute and backward
+// factors for the Phase-1 epilogue.
 //
 // P1 ("Blockwise MM Backward MXFP8 Kernel API Reference", the checkpoint
 // parameters): gate_act = SiLU(gate_pre) and intermediate = gate_act * up are
@@ -22,6 +23,16 @@ __device__ __forceinline__ float sigmoid_fast(float g) {
 
 // silu'(g) from s = sigmoid(g)
 __device__ __forceinline__ float dsilu_from(float g, float s) { return s * (1.f + g * (1.f - s)); }
+
+// GeGLU's gate activation (P3 accepts "geglu" beside "swiglu"; the GELU taken
+// is its definition g * Phi(g), Phi the standard normal CDF):
+// Phi(g) = erfc(-g / sqrt 2) / 2 with the device library's erfcf (a few ulp,
+// relative, also for negative g, where 1 + erf would cancel), and
+// gelu'(g) = Phi(g) + g * exp(-g^2 / 2) / sqrt(2 pi) with v_exp_f32.
+__device__ __forceinline__ float normal_cdf(float g) { return 0.5f * erfcf(g * -0.70710678118654752f); }
+__device__ __forceinline__ float dgelu_from(float g, float cdf) {
+  return cdf + g * (0.39894228040143268f * __builtin_amdgcn_exp2f(g * g * -0.72134752044448170f));
+}
 
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) { return bf16x2_pack(a, b); }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }

@@ -21,6 +21,7 @@ from . import build as _build
 E4M3 = 0
 E5M2 = 1
 NONE = -1  # test hook: quantisation disabled
+SWIGLU, GEGLU = 0, 1  # gated activations
 
 _lib = None
 
@@ -202,7 +203,7 @@ class _MoeProblem(C.Structure):
                 ("wd_codes", _p), ("wd_scales", _p), ("tpid", _p), ("b2e", _p), ("dy", _p),
                 ("ckpt", _p), ("b2", _p), ("affinity_on", C.c_int), ("has_bias", C.c_int),
                 ("fmt_w", C.c_int), ("fmt_act", C.c_int), ("fmt_grad", C.c_int),
-                ("nthreads", C.c_int), ("accumulate", C.c_int)]
+                ("nthreads", C.c_int), ("accumulate", C.c_int), ("activation", C.c_int)]
 
 
 @dataclass
@@ -237,6 +238,7 @@ class MoeProblem:
     fmt_grad: int = E5M2
     nthreads: int = 0
     accumulate: int = 0      # P1's accumulation flag: outputs = bf16(prior + gradient)
+    activation: int = 0      # 0 = SwiGLU, 1 = GeGLU (the erf form of GELU)
 
     def _struct(self):
         keep = {}
@@ -251,7 +253,7 @@ class MoeProblem:
                                                   "wd_codes", "wd_scales", "tpid", "b2e", "dy",
                                                   "ckpt", "b2")],
                         self.affinity_on, self.has_bias, self.fmt_w, self.fmt_act, self.fmt_grad,
-                        self.nthreads, self.accumulate)
+                        self.nthreads, self.accumulate, self.activation)
         return s, keep
 
 
@@ -331,7 +333,7 @@ def moe_token_operand(p: MoeProblem, which: int):
 class _MoeExact(C.Structure):
     _fields_ = [("T", _i64), ("H", _i64), ("I", _i64), ("E", _i64), ("N", _i64), ("B", _i64),
                 ("x", _p), ("aff", _p), ("wgu", _p), ("b1", _p), ("wd", _p), ("b2", _p),
-                ("tpid", _p), ("b2e", _p), ("affinity_on", C.c_int)]
+                ("tpid", _p), ("b2e", _p), ("affinity_on", C.c_int), ("activation", C.c_int)]
 
 
 @dataclass
@@ -347,6 +349,7 @@ class MoeExact:
     b1: Optional[np.ndarray] = None
     b2: Optional[np.ndarray] = None
     affinity_on: int = 0
+    activation: int = 0      # 0 = SwiGLU, 1 = GeGLU
 
     def _struct(self):
         T, H = self.x.shape
@@ -359,7 +362,7 @@ class MoeExact:
         keep["b2e"] = np.ascontiguousarray(self.b2e, dtype=np.int32)
         s = _MoeExact(T, H, I, E, N, self.B, *[_ptr(keep[k]) for k in
                                                ("x", "aff", "wgu", "b1", "wd", "b2", "tpid", "b2e")],
-                      self.affinity_on)
+                      self.affinity_on, self.activation)
         return s, keep, (T, H, I, E, N)
 
 

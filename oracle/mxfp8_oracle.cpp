@@ -9,6 +9,7 @@
 #include "mxfp8_oracle.h"
 
 #include <algorithm>
+#define _USE_MATH_DEFINES
 #include <cmath>
 #include <cstring>
 #include <functional>
@@ -170,6 +171,20 @@ double dsilu(double g) {                            /* d/dg [g * sigmoid(g)] */
   const double s = 1.0 / (1.0 + std::exp(-g));
   return s * (1.0 + g * (1.0 - s));
 }
+/* GELU (reading: the defining form g * Phi(g), Phi the standard normal CDF;
+ * P3 names "geglu" as the other gated activation without fixing the GELU
+ * form) and its derivative Phi(g) + g * phi(g).  Phi(g) = erfc(-g / sqrt 2) / 2,
+ * which keeps its relative accuracy for negative g (1 + erf cancels there). */
+double normal_cdf(double g) { return 0.5 * std::erfc(-g / std::sqrt(2.0)); }
+double gelu(double g) { return g * normal_cdf(g); }
+double dgelu(double g) {
+  const double cdf = normal_cdf(g);
+  const double pdf = std::exp(-0.5 * g * g) / std::sqrt(2.0 * M_PI);
+  return cdf + g * pdf;
+}
+/* The gate's activation: 0 = SwiGLU (silu), 1 = GeGLU (gelu). */
+double act(int a, double g) { return a == 1 ? gelu(g) : silu(g); }
+double dact(int a, double g) { return a == 1 ? dgelu(g) : dsilu(g); }
 
 }  // namespace
 
@@ -393,13 +408,13 @@ struct Moe {
     Col c;
     c.g = ckpt(b, 0, i, s, t);
     c.u = ckpt(b, 1, i, s, t);
-    c.ga = bf16r(silu(c.g));
+    c.ga = bf16r(act(p.activation, c.g));
     c.inter = bf16r(c.ga * c.u);
     double acc = 0.0;                                /* Phase 1: dS = Q(dY_t) . Q(W_down[e][i]) */
     for (int64_t h = 0; h < p.H; ++h) acc += dyq[h] * wd(e, i, h);
     c.dS = f32r(acc);
     const double dinter = f32r(affinity(t, e) * c.dS);   /* affinity applied to the fp32 tile */
-    c.dG = bf16r(dinter * c.u * dsilu(c.g));
+    c.dG = bf16r(dinter * c.u * dact(p.activation, c.g));
     c.dU = bf16r(dinter * c.ga);
     return c;
   }
@@ -458,6 +473,7 @@ struct Moe {
 
 bool valid_problem(const orc_moe_problem* p) {
   return p && p->T > 0 && p->H % 32 == 0 && p->I % 32 == 0 && p->B % 32 == 0 && p->E > 0 &&
+         (p->activation == 0 || p->activation == 1) &&
          p->N > 0 && fmt_of(p->fmt_w) && (fmt_of(p->fmt_act) || p->fmt_act == -1) &&
          (fmt_of(p->fmt_grad) || p->fmt_grad == -1);
 }
@@ -661,7 +677,7 @@ int orc_moe_token_operand(const orc_moe_problem* pp, int which, uint8_t* codes, 
 /* Exact mode: the plain definition of the layer and its gradients in fp64.
  * Forward per routed slot (block b with expert e, token t, affinity a):
  *   g = x_t W_gu[e][:,0,:] + b1[e,0],  u = x_t W_gu[e][:,1,:] + b1[e,1]
- *   inter = silu(g) * u
+ *   inter = act(g) * u     (act = silu for SwiGLU, gelu for GeGLU)
  *   on H: y_t += a * (inter W_down[e] + b2[e])
  *   on I: y_t += (a * inter) W_down[e]                                        */
 int orc_moe_fwd_exact(const orc_moe_exact_problem* p, double* y, double* gu_ckpt) {
@@ -691,7 +707,7 @@ int orc_moe_fwd_exact(const orc_moe_exact_problem* p, double* y, double* gu_ckpt
       }
       for (int64_t h = 0; h < H; ++h) {
         double d = 0.0;
-        for (int64_t i = 0; i < I; ++i) d += silu(g[i]) * u[i] * p->wd[(e * I + i) * H + h];
+        for (int64_t i = 0; i < I; ++i) d += act(p->activation, g[i]) * u[i] * p->wd[(e * I + i) * H + h];
         if (p->affinity_on == 1) y[t * H + h] += a * d;
         else y[t * H + h] += a * (d + (p->b2 ? p->b2[e * H + h] : 0.0));
       }
@@ -703,7 +719,7 @@ int orc_moe_fwd_exact(const orc_moe_exact_problem* p, double* y, double* gu_ckpt
  * P3's db1_kernel and db2_and_ds_kernel):
  *   d(a)      = <dY_t, inter W_down[e] + b2[e]>
  *   dInter    = a * (dY_t W_down[e]^T)
- *   dG        = dInter * u * silu'(g),  dU = dInter * silu(g)
+ *   dG        = dInter * u * act'(g),  dU = dInter * act(g)
  *   dX_t     += [dG, dU] W_gu[e]^T
  *   dW_gu[e] += x_t^T [dG, dU],  dW_down[e] += inter^T (a dY_t)
  *   db1[e]   += [dG, dU],        db2[e]     += a dY_t                        */
@@ -732,7 +748,7 @@ int orc_moe_bwd_exact(const orc_moe_exact_problem* p, const double* dy, double* 
         }
         g[i] = sg;
         u[i] = su;
-        inter[i] = silu(sg) * su;
+        inter[i] = act(p->activation, sg) * su;
         double d = 0.0;
         for (int64_t h = 0; h < H; ++h) d += dy[t * H + h] * p->wd[(e * I + i) * H + h];
         dS[i] = d;
@@ -744,8 +760,8 @@ int orc_moe_bwd_exact(const orc_moe_exact_problem* p, const double* dy, double* 
       daff[t * E + e] += da;
       for (int64_t i = 0; i < I; ++i) {
         const double dinter = a * dS[i];
-        dG[i] = dinter * u[i] * dsilu(g[i]);
-        dU[i] = dinter * silu(g[i]);
+        dG[i] = dinter * u[i] * dact(p->activation, g[i]);
+        dU[i] = dinter * act(p->activation, g[i]);
       }
       for (int64_t h = 0; h < H; ++h) {
         double sx = 0.0;

@@ -99,6 +99,8 @@ typedef struct {
                           1 = every output element o becomes bf16(fp32(o + g)), the
                           buffer's value plus the exact gradient, rounded as an fp32
                           sum would be; 0 = bf16(fp32(g))                        */
+  int activation;      /* gated activation of the gate projection: 0 = SwiGLU
+                          (silu), 1 = GeGLU (gelu, the erf form g * Phi(g))       */
 } orc_moe_problem;
 
 /* All outputs bf16.  Full problem: dx [T][H], daff [T*E], dwgu [E][H][2][I],
@@ -143,6 +145,7 @@ typedef struct {
   const int32_t* tpid;
   const int32_t* b2e;
   int affinity_on;
+  int activation;     /* 0 = SwiGLU, 1 = GeGLU */
 } orc_moe_exact_problem;
 
 /* y [T][H]; gu_ckpt [N][2][I][B] pre-activations (NULL to skip). */

@@ -63,9 +63,9 @@ def pairs_to_rows(raw, rows: int, k: int) -> np.ndarray:
 # Frobenius bound of the whole tensor (2e-3).  Set from the measured error
 # distributions of every parity case with margin; the reasons are in the
 # design notes' parity section.
-EXPERT_TOL = 1e-2      # relative Frobenius error of one expert's slice
-ROW_TOL = 5e-2         # relative Frobenius error of one output row
-OUTLIER_C = 0.1        # element bound: |g - r| <= OUTLIER_C * rms(r) + 2^-7 |r|
+EXPERT_TOL = 4e-3      # relative Frobenius error of one expert's slice (measured worst 6.8e-4)
+ROW_TOL = 3e-2         # relative Frobenius error of one output row (measured worst 1.1e-2)
+OUTLIER_C = 0.1        # element bound: |g - r| <= OUTLIER_C * rms(r) + 2^-7 |r| (never exceeded)
 
 
 def parity_stats(g, r, rows=None, experts=None):
@@ -100,3 +100,10 @@ def assert_parity(name, st, tol=2e-3, row_tol=ROW_TOL, expert_tol=EXPERT_TOL):
     assert st["row_max"] <= row_tol, (name, "worst row", st)
     assert st["expert_max"] <= expert_tol, (name, "worst expert", st)
     assert st["outliers"] == 0, (name, "elements past the element bound", st)
+
+
+def rows_to_pairs(scales, rows: int, k: int) -> np.ndarray:
+    """Row-major scale bytes [rows][k/32] packed pair-major, [k/128][rows][4]
+    (the inverse of pairs_to_rows)."""
+    a = np.asarray(scales, dtype=np.uint8).reshape(rows, k // 128, 4)
+    return np.ascontiguousarray(a.transpose(1, 0, 2))

@@ -59,7 +59,8 @@ def test_validation_without_gpu():
 
 
 @pytest.mark.parametrize("cls,ctype", [("MoeBwdArgs", "moe_bwd_mxfp8_args"),
-                                       ("MoeWorkspaceLayout", "moe_bwd_mxfp8_workspace_layout")])
+                                       ("MoeWorkspaceLayout", "moe_bwd_mxfp8_workspace_layout"),
+                                       ("MatmulBwdArgs", "matmul_mxfp8_bwd_args")])
 def test_binding_structs_match_the_header(cls, ctype, tmp_path):
     """The ctypes mirrors of the header's structs: same size and every field at
     the offset the C compiler gives it."""
@@ -122,3 +123,44 @@ def test_moe_bwd_workspace_and_size_limits_without_gpu():
     ok = _fake_args(mx, L, T=262143, H=4096, I=256, E=8, B=1024)
     assert L.moe_bwd_mxfp8_workspace_size(C.byref(ok)) > 0
 
+
+def test_moe_bwd_rejects_an_unknown_activation_without_gpu():
+    import mxfp8_grouped_gemm_amd as mx
+    L = mx.lib()
+    a = _fake_args(mx, L)
+    a.activation = 2
+    assert L.moe_bwd_mxfp8(C.byref(a), C.c_void_p(0x10000), 1 << 40, None) == 1
+    assert "activation" in mx.last_error()
+
+
+def test_matmul_bwd_ex_validation_without_gpu():
+    """The pre-quantised dense entry point refuses, before any device call,
+    codes without scales, packed scales on an unswizzled operand or with a
+    contraction that is not a multiple of 128, a swizzle flag without the
+    operand it applies to, a flag outside {0,1}, and a missing bf16 input."""
+    import mxfp8_grouped_gemm_amd as mx
+    L = mx.lib()
+    f = 0x10000
+
+    def args(**kw):
+        a = mx.MatmulBwdArgs(256, 256, 128, f, f, f, mx.E5M2, mx.E4M3, mx.E4M3)
+        a.input_grad = a.weight_grad = f
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    run = lambda a: L.matmul_mxfp8_bwd_ex(C.byref(a), C.c_void_p(f), 1 << 40, None)
+    assert run(args(weight_codes=f)) == 1 and "together" in mx.last_error()
+    assert run(args(weight_codes=f, weight_scales=f, use_scale_packing=1)) == 1 and "swizzled" in mx.last_error()
+    assert run(args(M=96, output_grad_codes_m=f, output_grad_scales_m=f, output_grad_is_swizzled=1,
+                    use_scale_packing=1)) == 1 and "128" in mx.last_error()
+    assert run(args(weights_is_swizzled=1)) == 1 and "weights_is_swizzled" in mx.last_error()
+    assert run(args(input_is_swizzled=2)) == 1
+    assert run(args(use_scale_packing=1)) == 1
+    assert run(args(weights=None)) == 1 and "null" in mx.last_error()
+    assert run(args(weights=None, weight_codes=f, weight_scales=f, output_grad=None)) == 1
+    # every operand pre-quantised: no bf16 pointer is needed; only the workspace check remains
+    a = args(output_grad=None, weights=None, input_activation=None, output_grad_codes_n=f, output_grad_scales_n=f,
+             output_grad_codes_m=f, output_grad_scales_m=f, weight_codes=f, weight_scales=f, input_codes=f,
+             input_scales=f)
+    assert L.matmul_mxfp8_bwd_ex(C.byref(a), C.c_void_p(f), 16, None) == 3

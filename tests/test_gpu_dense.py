@@ -97,3 +97,54 @@ def test_dense_rejects_bad_shapes():
     t = _inputs(64, 64, 64, 1)
     with pytest.raises(mx.MxError):
         mx.matmul_mxfp8_bwd(t["dy"][:, :48].contiguous(), t["w"][:48].contiguous(), t["x"])
+
+
+def _prequantised(dy_b, w_b, x_b, swizzled, packed):
+    """[P2]'s pre-quantised operands, made by the oracle's quantiser, in the
+    layouts of matmul_mxfp8_bwd_ex: natural (as mxfp8_quantize writes them) or
+    swizzled (contraction contiguous), scales row-major or packed pair-major."""
+    from helpers import rows_to_pairs
+    T = lambda a: np.ascontiguousarray(a.T)
+    if not swizzled:
+        ops = {"output_grad_n": oracle.quantize(dy_b, 1, oracle.E5M2),
+               "output_grad_m": oracle.quantize(dy_b, 0, oracle.E5M2),
+               "weight_q": oracle.quantize(w_b, 0, oracle.E4M3), "input_q": oracle.quantize(x_b, 0, oracle.E4M3)}
+    else:
+        ops = {"output_grad_n": oracle.quantize(dy_b, 1, oracle.E5M2),
+               "output_grad_m": oracle.quantize(T(dy_b), 1, oracle.E5M2),
+               "weight_q": oracle.quantize(T(w_b), 1, oracle.E4M3), "input_q": oracle.quantize(T(x_b), 1, oracle.E4M3)}
+        if packed:
+            ops = {k: (c, rows_to_pairs(s, c.shape[0], c.shape[1])) for k, (c, s) in ops.items()}
+    return {k: (torch.from_numpy(np.ascontiguousarray(c)).cuda(), torch.from_numpy(np.ascontiguousarray(s)).cuda())
+            for k, (c, s) in ops.items()}
+
+
+@pytest.mark.parametrize("M,N,K,swizzled,packed", [(256, 320, 192, False, False), (512, 384, 640, False, False),
+                                                   (96, 160, 544, False, False), (256, 320, 192, True, False),
+                                                   (512, 384, 640, True, False), (512, 384, 640, True, True),
+                                                   (96, 160, 544, True, False)])
+def test_dense_prequantised_operands(M, N, K, swizzled, packed):
+    """P2's pre-computed scales (codes + E8M0 scales per operand, dY once per
+    contraction axis), unswizzled or in the GEMM's layout, row-major or packed
+    scales: the outputs equal the bf16-input call bit for bit (the GEMMs read
+    the same operand bytes) and keep parity with the oracle."""
+    mx = _mx()
+    t = _inputs(M, N, K, seed=M + 7 * N + K)
+    dy_b, w_b, x_b = (S.bf16_bits(t[k]) for k in ("dy", "w", "x"))
+    ref_dx, ref_dw = mx.matmul_mxfp8_bwd(t["dy"], t["w"], t["x"])
+    ops = _prequantised(dy_b, w_b, x_b, swizzled, packed)
+    flags = dict(output_grad_is_swizzled=swizzled, weights_is_swizzled=swizzled, input_is_swizzled=swizzled,
+                 use_scale_packing=packed)
+    # every operand pre-quantised: no bf16 input at all
+    dx, dw = mx.matmul_mxfp8_bwd_ex(M, N, K, "cuda", **ops, **flags)
+    # some pre-quantised, the rest quantised from bf16
+    dx2, dw2 = mx.matmul_mxfp8_bwd_ex(M, N, K, "cuda", output_grad=t["dy"], input_activation=t["x"],
+                                      output_grad_n=ops["output_grad_n"], weight_q=ops["weight_q"],
+                                      output_grad_is_swizzled=swizzled, weights_is_swizzled=swizzled,
+                                      use_scale_packing=packed)
+    torch.cuda.synchronize()
+    for a, b in ((dx, ref_dx), (dw, ref_dw), (dx2, ref_dx), (dw2, ref_dw)):
+        assert torch.equal(a, b)
+    rdx, rdw = oracle.dense_bwd(dy_b, w_b, x_b)
+    assert_parity("dX", parity_stats(bf(S.bf16_bits(dx)), bf(rdx), rows=M), tol=TOL)
+    assert_parity("dW", parity_stats(bf(S.bf16_bits(dw)), bf(rdw), rows=N), tol=TOL)

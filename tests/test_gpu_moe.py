@@ -474,3 +474,38 @@ def test_moe_accumulate(name):
     again = gp["op"].run()
     torch.cuda.synchronize()
     _check_outputs(cfg, again, base)
+
+
+# ----------------------------------------------------------------------------- GeGLU
+def _bound_op(gp, **kw):
+    """A MoeBwd over a problem's device tensors with extra arguments."""
+    import mxfp8_grouped_gemm_amd as mx
+    cfg, t = gp["cfg"], gp["t"]
+    gu_c, gu_s, d_c, d_s = gp["wq"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    return mx.MoeBwd(t["hidden"], torch.from_numpy(gp["aff"]).cuda(), gu_c.view(E, H, 2, I),
+                     gu_s.view(E, H, 2, I // 32), d_c.view(E, I, H), d_s.view(E, I, H // 32), gp["tpid"], gp["b2e"],
+                     t["dy"], cfg.B, t["ckpt"], down_proj_bias=t["b2"], affinity_on=cfg.affinity_on, **kw)
+
+
+@pytest.mark.parametrize("name", ["tiny", "medium_s", "fine_s", "large_s"])
+def test_moe_geglu(name):
+    """[P3]'s other gated activation, GeGLU (gelu in its erf form): every
+    gradient keeps parity with the oracle's GeGLU backward, the intermediate
+    operand's codes agree almost everywhere (erfc in fp32 against fp64), and
+    the result differs from the SwiGLU one."""
+    import dataclasses
+    cfg = SMALL[name]
+    gp = gpu_problem(cfg)
+    sw = {k: v.clone() for k, v in gp["op"].run().items() if v is not None}
+    op = _bound_op(gp, activation=1)
+    out = op.run()
+    torch.cuda.synchronize()
+    p, _ = oracle_problem(gp)
+    ref = oracle.moe_bwd(dataclasses.replace(p, activation=oracle.GEGLU))
+    _check_outputs(cfg, out, ref)
+    assert not torch.equal(sw["dx"], out["dx"])
+    P = gp["N"] * cfg.B
+    c, _ = oracle.moe_token_operand(dataclasses.replace(p, activation=oracle.GEGLU), oracle.TOK_INTER)
+    got = op.workspace.cpu().numpy()[op.layout["inter_tok_codes"]:op.layout["inter_tok_codes"] + cfg.I * P]
+    assert np.mean(got != c.ravel()) < 1e-3

@@ -29,19 +29,19 @@ def _routing(rng, T, K, E, B, N=None):
     return topk, tpid, b2e, aff.reshape(-1)
 
 
-def _exact_problem(rng, T=10, H=6, I=5, E=3, K=2, B=4, bias=True, on=0):
+def _exact_problem(rng, T=10, H=6, I=5, E=3, K=2, B=4, bias=True, on=0, act=0):
     topk, tpid, b2e, aff = _routing(rng, T, K, E, B)
     return oracle.MoeExact(
         x=rng.standard_normal((T, H)), aff=aff, wgu=rng.standard_normal((E, H, 2, I)) * 0.5,
         wd=rng.standard_normal((E, I, H)) * 0.5, tpid=tpid, b2e=b2e, B=B,
         b1=rng.standard_normal((E, 2, I)) * 0.3 if bias else None,
-        b2=rng.standard_normal((E, H)) * 0.3 if (bias and on == 0) else None, affinity_on=on)
+        b2=rng.standard_normal((E, H)) * 0.3 if (bias and on == 0) else None, affinity_on=on, activation=act)
 
 
-@pytest.mark.parametrize("on", [0, 1])
-def test_exact_mode_finite_differences(on):
-    rng = np.random.default_rng(20 + on)
-    p = _exact_problem(rng, on=on)
+@pytest.mark.parametrize("on,act", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_exact_mode_finite_differences(on, act):
+    rng = np.random.default_rng(20 + on + 10 * act)
+    p = _exact_problem(rng, on=on, act=act)
     T, H = p.x.shape
     dy = rng.standard_normal((T, H))
     g = oracle.moe_bwd_exact(p, dy)
@@ -65,11 +65,15 @@ def test_exact_mode_finite_differences(on):
         assert err < 1e-7, (pname, err)
 
 
-def test_exact_mode_matches_torch_autograd():
+@pytest.mark.parametrize("act", [0, 1])
+def test_exact_mode_matches_torch_autograd(act):
     """A forward written directly in torch (per token, over its chosen experts),
-    differentiated by autograd in float64 on the CPU."""
+    differentiated by autograd in float64 on the CPU.  GeGLU uses torch's GELU
+    in its erf form (approximate='none'); the tanh form differs by ~1e-3, far
+    past this test's tolerance, so the reading of GELU is pinned here."""
     rng = np.random.default_rng(23)
-    p = _exact_problem(rng, T=12, H=7, I=6, E=4, K=2, B=4)
+    p = _exact_problem(rng, T=12, H=7, I=6, E=4, K=2, B=4, act=act)
+    gate = torch.nn.functional.silu if act == 0 else (lambda v: torch.nn.functional.gelu(v, approximate="none"))
     T, H = p.x.shape
     E = p.wgu.shape[0]
     dy = rng.standard_normal((T, H))
@@ -80,7 +84,7 @@ def test_exact_mode_matches_torch_autograd():
     for t, e in routed:
         gu = tp["x"][t] @ tp["wgu"][e].reshape(H, -1)
         gu = gu.reshape(2, -1) + tp["b1"][e]
-        inter = torch.nn.functional.silu(gu[0]) * gu[1]
+        inter = gate(gu[0]) * gu[1]
         y = y.index_add(0, torch.tensor([t]), (tp["aff"][t * E + e] * (inter @ tp["wd"][e] + tp["b2"][e]))[None])
     (y * torch.from_numpy(dy)).sum().backward()
     g = oracle.moe_bwd_exact(p, dy)
@@ -89,7 +93,7 @@ def test_exact_mode_matches_torch_autograd():
 
 
 # ----------------------------------------------------------------------------- MX mode
-def _mx_and_exact(rng, T=24, H=64, I=64, E=3, K=2, B=32, on=0, bias=True, fmt_act=0, fmt_grad=1):
+def _mx_and_exact(rng, T=24, H=64, I=64, E=3, K=2, B=32, on=0, bias=True, fmt_act=0, fmt_grad=1, act=0):
     """An MX problem and the exact problem it approximates: same routing, bf16
     activations, dequantised weights, checkpoint = bf16 of the exact pre-activations."""
     topk, tpid, b2e, aff = _routing(rng, T, K, E, B)
@@ -104,24 +108,25 @@ def _mx_and_exact(rng, T=24, H=64, I=64, E=3, K=2, B=32, on=0, bias=True, fmt_ac
     ex = oracle.MoeExact(x=bf(x), aff=aff.astype(np.float64),
                          wgu=oracle.dequantize(gu_c.reshape(-1, I), gu_s.reshape(-1, I // 32), 1, 0).reshape(E, H, 2, I),
                          wd=oracle.dequantize(d_c.reshape(-1, H), d_s.reshape(-1, H // 32), 1, 0).reshape(E, I, H),
-                         tpid=tpid, b2e=b2e, B=B, b1=b1, b2=None if b2 is None else bf(b2), affinity_on=on)
+                         tpid=tpid, b2e=b2e, B=B, b1=b1, b2=None if b2 is None else bf(b2), affinity_on=on,
+                         activation=act)
     _, ck = oracle.moe_fwd_exact(ex, want_ckpt=True)
     mx = oracle.MoeProblem(T=T, H=H, I=I, E=E, N=b2e.size, B=B, hidden=x, aff=aff, wgu_codes=gu_c,
                            wgu_scales=gu_s, wd_codes=d_c, wd_scales=d_s, tpid=tpid, b2e=b2e, dy=dy,
                            ckpt=_bits(ck), b2=b2, affinity_on=on, has_bias=int(b2 is not None),
-                           fmt_act=fmt_act, fmt_grad=fmt_grad)
+                           fmt_act=fmt_act, fmt_grad=fmt_grad, activation=act)
     return mx, ex, bf(dy)
 
 
 KEYS = ("dx", "daff", "dwgu", "dwd", "db1", "db2")
 
 
-@pytest.mark.parametrize("on", [0, 1])
-def test_mx_mode_without_quantisation_matches_exact(on):
+@pytest.mark.parametrize("on,act", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_mx_mode_without_quantisation_matches_exact(on, act):
     """Activation and gradient quantisation switched off: only bf16 rounding points
     remain, so the quantised path's algebra must reproduce the exact gradients."""
     rng = np.random.default_rng(30 + on)
-    mx, ex, dy = _mx_and_exact(rng, on=on, fmt_act=oracle.NONE, fmt_grad=oracle.NONE)
+    mx, ex, dy = _mx_and_exact(rng, on=on, fmt_act=oracle.NONE, fmt_grad=oracle.NONE, act=act)
     got = oracle.moe_bwd(mx)
     ref = oracle.moe_bwd_exact(ex, dy)
     for k in KEYS:
@@ -130,10 +135,10 @@ def test_mx_mode_without_quantisation_matches_exact(on):
         assert rel_fro(bf(got[k]).reshape(ref[k].shape), ref[k]) < 1e-2, k
 
 
-@pytest.mark.parametrize("on", [0, 1])
-def test_mx_mode_within_quantisation_noise(on):
+@pytest.mark.parametrize("on,act", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_mx_mode_within_quantisation_noise(on, act):
     rng = np.random.default_rng(32 + on)
-    mx, ex, dy = _mx_and_exact(rng, on=on)
+    mx, ex, dy = _mx_and_exact(rng, on=on, act=act)
     got = oracle.moe_bwd(mx)
     ref = oracle.moe_bwd_exact(ex, dy)
     for k in ("dx", "daff", "dwgu", "dwd", "db1"):
@@ -350,3 +355,24 @@ def test_token_operands_of_the_epilogue_match_their_definition(on):
         oracle.moe_token_operand(p, oracle.TOK_INTER)[0],
         oracle.quantize(np.ascontiguousarray(np.concatenate([d["inter"] for d in det]).T * valid[None]
                                              .astype(np.uint16)), 1, oracle.E4M3)[0])
+
+
+def test_geglu_changes_only_what_the_gate_activation_reaches():
+    """Same problem under SwiGLU and GeGLU: every gradient that passes through
+    the gate activation changes, and the per-slot activation values are the
+    bf16 roundings of silu(g) and of g * Phi(g) (erf form) of the checkpoint."""
+    import math
+    rng = np.random.default_rng(54)
+    mx, _, _ = _mx_and_exact(rng, on=0, bias=True)
+    a = oracle.moe_bwd(mx)
+    mx.activation = oracle.GEGLU
+    b = oracle.moe_bwd(mx)
+    for k in ("dx", "daff", "dwgu", "dwd", "db1"):
+        assert not np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["db2"], b["db2"])           # a * dY does not see the activation
+    d = oracle.moe_block_detail(mx, 0)
+    g = bf(mx.ckpt[0, 0].T)                             # [B, I] gate pre-activations of block 0
+    valid = mx.tpid[:mx.B] >= 0
+    want = np.vectorize(lambda v: oracle.double_to_bf16(0.5 * v * math.erfc(-v / math.sqrt(2.0))),
+                        otypes=[np.uint16])(g)
+    assert np.array_equal(d["ga"][valid], want[valid])
