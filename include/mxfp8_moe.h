@@ -17,7 +17,9 @@
  *    bf16 tensors are passed as uint16_t bit patterns; all tensors are dense,
  *    row-major and must be 16-byte aligned.
  *  - The caller owns every buffer, including the workspace.  The library never
- *    allocates or frees device memory and keeps no state between calls.
+ *    allocates or frees device memory and keeps no state between calls, except
+ *    the allocation-free routing entry point's file-scope device scratch (one
+ *    1 MiB copy per GPU, part of the loaded library) and its address per device.
  *  - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t, NULL
  *    for the default stream) and the call returns without synchronising.  A
  *    device fault surfaces at the caller's next synchronisation.
@@ -193,6 +195,25 @@ int moe_build_blocks(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
                      int64_t block_size, int64_t N, int32_t* token_position_to_id,
                      int32_t* block_to_expert, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* moe_build_blocks_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moe_build_blocks without a workspace argument.  Its scratch
+ * (the counts and first slots per expert and token chunk) is a file-scope
+ * device array of 1 MiB inside the library, one copy per GPU, held until the
+ * process ends; its address is looked up once per device on the first call
+ * there.  Nothing is allocated and nothing is cleared: every scratch word the
+ * call reads it has written first.  Arguments, outputs and errors as for
+ * moe_build_blocks, except: E above MOE_BUILD_BLOCKS_NOALLOC_MAX_EXPERTS is
+ * UNSUPPORTED (use moe_build_blocks), and HIP if the scratch's address cannot
+ * be found.  The kernels run on `stream`'s device (the current device for
+ * NULL).  Every call on one GPU shares its scratch: calls that can overlap on
+ * one GPU (concurrent streams, several host threads) race and must be
+ * serialised by the caller; calls in order on one stream are safe. */
+#define MOE_BUILD_BLOCKS_NOALLOC_MAX_EXPERTS 4096
+int moe_build_blocks_noalloc(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
+                             int64_t block_size, int64_t N, int32_t* token_position_to_id,
+                             int32_t* block_to_expert, void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_bwd_mxfp8 -- P1's blockwise_mm_bwd_mxfp8: all gradients of a blockwise

@@ -88,6 +88,7 @@ def _declare(L):
                                        _p, C.c_size_t, _p]),
         ("moe_build_blocks_workspace_size", C.c_size_t, [_i64]),
         ("moe_build_blocks", C.c_int, [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, C.c_size_t, _p]),
+        ("moe_build_blocks_noalloc", C.c_int, [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p]),
         ("moe_bwd_mxfp8_workspace_query", C.c_int, [C.POINTER(MoeBwdArgs), C.POINTER(MoeWorkspaceLayout)]),
         ("moe_bwd_mxfp8_workspace_size", C.c_size_t, [C.POINTER(MoeBwdArgs)]),
         ("moe_bwd_mxfp8", C.c_int, [C.POINTER(MoeBwdArgs), _p, C.c_size_t, _p]),
@@ -264,6 +265,21 @@ def moe_build_blocks(topk_ids: torch.Tensor, E: int, block_size: int, N: Optiona
     _check(L.moe_build_blocks(_dev(topk_ids, torch.int32, "topk_ids"), T, K, E, block_size, N,
                               tpid.data_ptr(), b2e.data_ptr(), ws.data_ptr(), ws.numel(), _stream(topk_ids)),
            "moe_build_blocks")
+    return tpid, b2e
+
+
+def moe_build_blocks_noalloc(topk_ids: torch.Tensor, E: int, block_size: int, N: int, out):
+    """moe_build_blocks through the allocation-free entry point: the caller
+    passes the outputs (token_position_to_id [N*B], block_to_expert [N], int32),
+    and neither the library nor this wrapper allocates device memory."""
+    T, K = topk_ids.shape
+    tpid, b2e = out
+    for name, t, n in (("token_position_to_id", tpid, N * block_size), ("block_to_expert", b2e, N)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n or t.device != topk_ids.device:
+            raise ValueError(f"{name}: need a contiguous int32 tensor of {n} entries on {topk_ids.device}")
+    _check(lib().moe_build_blocks_noalloc(_dev(topk_ids, torch.int32, "topk_ids"), T, K, E, block_size, N,
+                                          tpid.data_ptr(), b2e.data_ptr(), _stream(topk_ids)),
+           "moe_build_blocks_noalloc")
     return tpid, b2e
 
 

@@ -276,6 +276,35 @@ int moe_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64
                     "moe_build_blocks");
 }
 
+int moe_build_blocks_noalloc(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
+                             int32_t* tpid, int32_t* b2e, void* stream) {
+  if (T <= 0 || K <= 0 || E <= 0 || B <= 0 || N <= 0)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks_noalloc: sizes must be positive");
+  if (E > MOE_BUILD_BLOCKS_NOALLOC_MAX_EXPERTS || E > mx::build_blocks_noalloc_max_experts())
+    return fail(MXFP8_ERR_UNSUPPORTED,
+                "moe_build_blocks_noalloc: E = %lld is above the %d experts its scratch holds "
+                "(use moe_build_blocks with a workspace)",
+                (long long)E, MOE_BUILD_BLOCKS_NOALLOC_MAX_EXPERTS);
+  const int64_t need = moe_num_blocks(T, K, E, B);
+  if (need < 0)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks_noalloc: T*K (%lld) < E (%lld)", (long long)(T * K),
+                (long long)E);
+  if (N < need)
+    return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks_noalloc: N = %lld is below the worst case %lld",
+                (long long)N, (long long)need);
+  if (!topk || !tpid || !b2e) return fail(MXFP8_ERR_INVALID_ARG, "moe_build_blocks_noalloc: null pointer");
+  if (T * K > INT32_MAX || N * B > INT32_MAX)
+    return fail(MXFP8_ERR_UNSUPPORTED, "moe_build_blocks_noalloc: sizes beyond int32 indexing");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return hip_status(e, "moe_build_blocks_noalloc: device of the stream");
+  int32_t* scratch = nullptr;
+  if ((e = mx::build_blocks_scratch(device, &scratch)) != hipSuccess)
+    return hip_status(e, "moe_build_blocks_noalloc: address of the scratch array");
+  return hip_status(mx::launch_build_blocks(topk, T, K, E, B, N, tpid, b2e, scratch, st), "moe_build_blocks_noalloc");
+}
+
 /* ---- MoE backward -------------------------------------------------------- */
 // An expert weight operand at least this large (8x one XCD's 4 MB L2) is shared
 // by all XCDs through the infinity cache: its GEMM hands tiles out round robin

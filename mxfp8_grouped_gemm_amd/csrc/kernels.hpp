@@ -83,6 +83,10 @@ hipError_t launch_fill_u16(void* p, int64_t n, uint16_t v, hipStream_t st);
 int64_t build_blocks_workspace_bytes(int64_t E);
 hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
                                int32_t* tpid, int32_t* b2e, int32_t* ws, hipStream_t st);
+// the allocation-free variant: the most experts its file-scope scratch holds,
+// and that scratch's device address on `device` (looked up once per device)
+int64_t build_blocks_noalloc_max_experts();
+hipError_t build_blocks_scratch(int device, int32_t** out);
 hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st);
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,

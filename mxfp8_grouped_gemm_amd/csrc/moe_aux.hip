@@ -8,6 +8,8 @@
 // Bias reductions: P3 (sonic-moe functional/backward.py) db2_and_ds_kernel
 // (db2 = sum of a*dY over an expert's slots; the <dY, b2> term of d(a)) and
 // db1_kernel (db1 = sum of the gate/up gradients).
+#include <mutex>
+
 #include "kernels.hpp"
 #include "mx_device.hpp"
 #include "swiglu.hpp"
@@ -134,6 +136,46 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
 }
 
 int64_t build_blocks_workspace_bytes(int64_t E) { return E > 0 ? 2 * E * kRouteChunks * 4 : 0; }
+
+// The allocation-free variant's scratch: the counts and first slots per
+// (expert, token chunk) for up to kNoAllocMaxExperts experts, 1 MiB per GPU,
+// held from the library's load until the process ends.  Every word the three
+// routing kernels read is written by an earlier one in the same call, so the
+// array needs no clearing; calls that overlap on one GPU share it and race.
+constexpr int64_t kNoAllocMaxExperts = 4096;
+static __device__ __align__(256) int32_t scratch[2 * kNoAllocMaxExperts * kRouteChunks];
+static_assert(sizeof(scratch) == 2 * kNoAllocMaxExperts * kRouteChunks * 4, "scratch size");
+
+int64_t build_blocks_noalloc_max_experts() { return kNoAllocMaxExperts; }
+
+// Device address of `scratch` on `device`, looked up once per device with that
+// device current (each GPU holds its own copy at its own address) and kept.
+// Host code never passes the array's name to a kernel: in host code it is a
+// host-side stand-in, not a device address.
+hipError_t build_blocks_scratch(int device, int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* ptrs[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[device] = static_cast<int32_t*>(p);
+  }
+  *out = ptrs[device];
+  return hipSuccess;
+}
 
 hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_t E, int64_t B, int64_t N,
                                int32_t* tpid, int32_t* b2e, int32_t* ws, hipStream_t st) {

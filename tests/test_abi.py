@@ -124,6 +124,21 @@ def test_moe_bwd_workspace_and_size_limits_without_gpu():
     assert L.moe_bwd_mxfp8_workspace_size(C.byref(ok)) > 0
 
 
+def test_noalloc_build_blocks_validation_without_gpu():
+    """The allocation-free routing entry point refuses, before any device call,
+    an expert count above its scratch (UNSUPPORTED), too few blocks, null
+    pointers and non-positive sizes (INVALID_ARG)."""
+    import mxfp8_grouped_gemm_amd as mx
+    L = mx.lib()
+    fake = C.c_void_p(0x10000)
+    f = L.moe_build_blocks_noalloc
+    assert f(fake, 8192, 1, 4097, 128, 4200, fake, fake, None) == 2 and "4096" in mx.last_error()
+    assert f(fake, 256, 2, 4, 128, 6, fake, fake, None) == 1 and "worst case" in mx.last_error()
+    assert f(None, 256, 2, 4, 128, 7, fake, fake, None) == 1
+    assert f(fake, 256, 2, 4, 128, 7, None, fake, None) == 1
+    assert f(fake, 0, 2, 4, 128, 7, fake, fake, None) == 1
+
+
 def test_moe_bwd_rejects_an_unknown_activation_without_gpu():
     import mxfp8_grouped_gemm_amd as mx
     L = mx.lib()
