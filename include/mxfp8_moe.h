@@ -326,8 +326,10 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *                                                     live slot tiles, and the total
  *   dx_slot [P,H] fp32 (each routed slot's dX row, summed per token at the end),
  *   slot_of [T,E] int32 (the slot of pair (t, e), -1 = none),
- *   daff_slot [P] fp32 (the <dY, b2> term), daff_part [I/32,P] fp32 (d(a) partials
- *   per 32 rows i), db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
+ *   daff_slot [P] fp32 (the <dY, b2> term when it is computed on its own, else 0),
+ *   daff_part [I/32 (+ H/128), P] fp32 (d(a) partials per 32 rows i; with a bias,
+ *   H % 128 == 0 and no down_proj_act_checkpoint, then the <dY, b2> shares per
+ *   128 columns h), db1_acc [E,2,I] fp32, db2_acc [E,H] fp32,
  *   expert_block_offsets [E+1] int32 and expert_block_list [N] int32: the blocks of
  *   expert e holding at least one routed slot are list[off[e] .. off[e+1]), ascending;
  *   slot_token [P] int32 (-1 = padding), slot_affinity [P] fp32, block_flag [N] int32
@@ -368,8 +370,10 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
  * is exactly one full call.  Stages:
  *   0 setup (zero accumulators, slot routing info, per-expert block lists)
  *   1 quantise dY along H (and lay out W_down's scales for Phase 1)
- *   2 gather-quantise X and a*dY (or dY) along slots
- *   3 bias reductions (has_bias only)
+ *   2 gather-quantise X and a*dY (or dY) along slots (and, with a bias, db2
+ *     and the <dY, b2> shares of d(a) from the same dY rows)
+ *   3 bias reductions (has_bias only; nothing when stage 2 does them: H a
+ *     multiple of 128 and no down_proj_act_checkpoint)
  *   4 Phase 1 (the product dS)
  *   5 Phase 1 epilogue (SwiGLU backward; dGU along I and along slots, the
  *     intermediate along slots, d(affinity) and db1 partial sums)

@@ -311,6 +311,13 @@ int moe_build_blocks_noalloc(const int32_t* topk, int64_t T, int64_t K, int64_t 
 // (moe_tiles.hpp).
 constexpr int64_t kRoundRobinWeightBytes = int64_t(32) << 20;
 
+// The bias reductions ride on the gather of dY rows (one read of each row)
+// when H is a multiple of 128 and those rows are gathered, i.e. no a*dY
+// checkpoint replaces them; otherwise they run as kernels of their own.
+static bool moe_fuse_bias(const moe_bwd_mxfp8_args* a) {
+  return a->has_bias && a->H % 128 == 0 && !a->down_proj_act_checkpoint;
+}
+
 static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layout* L) {
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, N = a->N, B = a->block_size, P = N * B;
   size_t o = 0;
@@ -341,7 +348,7 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->dx_slot, N * B * H * 4);
   put(L->slot_of, T * E * 4);
   put(L->daff_slot, P * 4);
-  put(L->daff_part, I / 32 * P * 4);
+  put(L->daff_part, (I / 32 + (moe_fuse_bias(a) ? H / 128 : 0)) * P * 4);
   put(L->db1_acc, E * 2 * I * 4);
   put(L->db2_acc, E * H * 4);
   put(L->expert_block_offsets, (E + 1) * 4);
@@ -491,12 +498,17 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
                               at(L.gy_tok_codes), at(L.gy_tok_scales), st, true, true),
          "quantize the a*dY checkpoint");
   } else {
+    // with a bias: db2 and the <dY, b2> shares of d(a) from the same row reads
+    // (rows I/32 .. I/32 + H/128 of daff_part)
+    const mx::TokBias tb{a->down_proj_bias, a->block_to_expert, B, db2_acc,
+                         reinterpret_cast<float*>(at(L.daff_part)) + (I / 32) * P};
     STEP(mx::launch_quant_tok(a->output_hidden_states_grad, T, H, slot_tok, a->affinity_on == 0 ? slot_aff : nullptr,
-                              P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st, true),
+                              P, a->fmt_grad, at(L.gy_tok_codes), at(L.gy_tok_scales), st, true, false,
+                              moe_fuse_bias(a) ? &tb : nullptr),
          "gather-quantize dY");
   }
   stage = 3;
-  if (a->has_bias)
+  if (a->has_bias && !moe_fuse_bias(a))
     STEP(mx::launch_bias(a->output_hidden_states_grad, a->down_proj_bias, slot_tok, slot_aff, a->block_to_expert,
                          flag, H, B, N, daff_slot, db2_acc, st),
          "bias reductions");
@@ -566,7 +578,8 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   // finalisation
   const bool acc = a->accumulate != 0;
   STEP(mx::launch_dx_reduce(dx_slot, slot_of, T, E, H, a->hidden_states_grad, st, acc), "dX per-token sums");
-  STEP(mx::launch_daff_scatter(daff_slot, reinterpret_cast<const float*>(at(L.daff_part)), I / 32, slot_tok,
+  STEP(mx::launch_daff_scatter(daff_slot, reinterpret_cast<const float*>(at(L.daff_part)),
+                               I / 32 + (moe_fuse_bias(a) ? H / 128 : 0), slot_tok,
                                a->block_to_expert, T, E, B, N, a->expert_affinities_masked_grad,
                                st, acc),
        "d(affinity) scatter");

@@ -84,14 +84,44 @@ struct TilePos {
   int g;
   int64_t m0, n0;
 };
+//
+// Several groups whose tile count P is not a multiple of 8 (e.g. 12 or 6 tiles
+// per expert): XCD x takes, of group g, the contiguous tiles
+// [floor(s P / 8), floor((s + 1) P / 8)) with s = (x - g) mod 8, so each XCD
+// still holds an eighth of every group, and which XCDs take the larger
+// shares rotates from group to group (over 8 groups every XCD takes exactly
+// P tiles).  The launcher then gives every XCD room for ceil(G / 8) * P
+// workgroups; those past its last tile exit (g = -1).  With contiguous
+// ranges instead, the XCDs holding the most loaded experts ran up to three
+// times longer than the others on skewed routing.
 template <int BM, int BN>
-__device__ __forceinline__ TilePos tile_pos(const GemmStoreArgs& p, int tile) {
+__device__ __forceinline__ TilePos tile_pos(const GemmStoreArgs& p, int tile, int groups) {
   const int per_group = p.tiles_m * p.tiles_n;
   int id;
   if (per_group % 8 == 0) {
     const int share = per_group / 8, j = tile / 8;   // j-th workgroup on XCD tile % 8
     const int gg = j / share;
     id = gg * per_group + (tile % 8) * share + (j - gg * share);
+  } else if (groups > 1) {
+    const int x = tile % 8, j = tile / 8;
+    const int q = j / per_group;
+    int r = j - q * per_group;
+    int g = -1, t = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int sl = (x - k + 64) & 7;
+      const int lo = sl * per_group / 8, c = (sl + 1) * per_group / 8 - lo;
+      if (g < 0) {
+        if (r < c) {
+          g = 8 * q + k;
+          t = lo + r;
+        } else {
+          r -= c;
+        }
+      }
+    }
+    if (g < 0 || g >= groups) return TilePos{-1, 0, 0};
+    id = g * per_group + t;
   } else {
     id = v2::xcd_remap(tile, p.total);
   }
@@ -107,7 +137,8 @@ template <int BM, int BN, int FA, int FB>
 __global__ void __launch_bounds__(v2::kThreads) gemm_store_generic(GemmStoreArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * v2::BK];
   constexpr int FM = BM / 64, FN = BN / 64;
-  const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x);
+  const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x, p.groups);
+  if (tp.g < 0) return;
   const int wave = threadIdx.x >> 6;
   v2::Operand<BM, FM> A;
   v2::Operand<BN, FN> B;
@@ -133,7 +164,8 @@ template <int BM, int BN, int FA, int FB, bool LIST, bool PAIR>
 __global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PAIR ? v4::smem_bytes(BM, BN) : v3::smem_bytes(BM, BN)];
   constexpr int FM = BM / 64, FN = BN / 64;
-  const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x);
+  const TilePos tp = tile_pos<BM, BN>(p, blockIdx.x, p.groups);
+  if (tp.g < 0) return;
   v3::ScaleDma<BM, BN> sd;
   v3::setup_scales(sd, p.a_scales, tp.m0, p.M, p.M * p.lda / 32, p.b_scales, tp.n0, p.N, p.N * p.ldb / 32);
   // K bytes of the tile's group: its blocks, the last one cut at its extent
@@ -207,14 +239,19 @@ hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStr
   const int BM = big ? 256 : 128, BN = big ? 256 : 128;
   p.tiles_m = int((p.M + BM - 1) / BM);
   p.tiles_n = int((p.N + BN - 1) / BN);
-  const int64_t total = int64_t(p.tiles_m) * p.tiles_n * groups;
+  const int64_t per_group = int64_t(p.tiles_m) * p.tiles_n;
+  const int64_t total = per_group * groups;
   if (total > INT32_MAX) return hipErrorInvalidValue;
   p.total = int(total);
+  p.groups = groups;
+  // rotating eighths (tile_pos): room for ceil(G / 8) * P workgroups per XCD
+  const int64_t launched = (per_group % 8 && groups > 1) ? 8 * ((groups + 7) / 8) * per_group : total;
+  if (launched > INT32_MAX) return hipErrorInvalidValue;
   if (generic) {
-    launch_generic<128, 128>(p, fa, fb, unsigned(total), st);
+    launch_generic<128, 128>(p, fa, fb, unsigned(launched), st);
     return hipGetLastError();
   }
-  const unsigned grid = unsigned(total);
+  const unsigned grid = unsigned(launched);
   if (big) {
     if (p.blk_list) {
       if (p.pair) launch_ring<256, 256, true, true>(p, fa, fb, grid, st);

@@ -17,9 +17,19 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int6
                                uint16_t* out, hipStream_t st);
 hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
                              uint8_t* scales, hipStream_t st);
+// The bias reductions fused into the gather of dY rows (see quant_tok_kernel):
+// db2_acc [E][cols] += a * dY sums; part [cols/128][rows] = <dY, b2> shares.
+struct TokBias {
+  const uint16_t* b2;      // [E][cols] bf16
+  const int32_t* b2e;      // [rows / B]
+  int64_t B;               // slots per block (a multiple of 128)
+  float* db2_acc;
+  float* part;             // null: no bias work
+};
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st, bool pairs = false, bool self_rows = false);
+                            uint8_t* scales_t, hipStream_t st, bool pairs = false, bool self_rows = false,
+                            const TokBias* bias = nullptr);
 // prequant.hip: an operand quantised along its rows (codes [R][C], scales
 // [R/32][C]) into the GEMM layout: codes [C][R]; scales pair-major
 // [R/128][C][4] (pairs) or row-major [C][R/32]
@@ -56,6 +66,7 @@ struct GemmStoreArgs {
                                   // four-slot ring (deeper look-ahead, for operands streamed from HBM)
   int tiles_m, tiles_n;
   int total;                      // tiles over all groups
+  int groups;                     // set by the launcher
 };
 hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStream_t st);
 

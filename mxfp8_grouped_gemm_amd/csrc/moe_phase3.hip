@@ -34,21 +34,21 @@ __device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int wg) {
   return P3Pos{bt.b, int64_t(tm) * BM, int64_t(tn) * BN};
 }
 
-// dX rows of one tile: routed slot s of block b stores its row.
+// dX rows of one tile.  Every slot of the tile stores its row: a padding
+// slot's dGU row is zeros, so its row is zeros too, and the finalisation
+// reads only routed slots' rows.  (Storing only routed rows made every store
+// wait for a load of the slot's token.)  Tiles lie inside one block (BM <= B).
 template <int BM, int BN>
 __device__ __forceinline__ void p3_store(const Phase3Args& p, const P3Pos& tp, const v16f (&acc)[BM / 64][BN / 64]) {
   const int64_t sbase = int64_t(tp.b) * p.B;
   v2::static_for<BM / 64>([&](auto FI) {
     v2::static_for<16>([&](auto Q) {
       const int64_t s = tp.m0 + v2::acc_row<BM, BN>(FI, Q);
-      const int64_t tok = s < p.B ? p.slot_tok[sbase + s] : -1;
-      if (tok >= 0) {
-        float* dst = p.dx_slot + (sbase + s) * p.H;
-        v2::static_for<BN / 64>([&](auto FJ) {
-          const int64_t hh = tp.n0 + v2::acc_col<BM, BN>(FJ);
-          if (hh < p.H) dst[hh] = acc[FI][FJ][int(Q)];
-        });
-      }
+      float* dst = p.dx_slot + (sbase + s) * p.H;
+      v2::static_for<BN / 64>([&](auto FJ) {
+        const int64_t hh = tp.n0 + v2::acc_col<BM, BN>(FJ);
+        if (hh < p.H) dst[hh] = acc[FI][FJ][int(Q)];
+      });
     });
   });
 }

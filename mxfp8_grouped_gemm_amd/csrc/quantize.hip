@@ -178,19 +178,42 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
 constexpr int kTokRows = 128;
 constexpr int kTokCols = 128;
 
-template <int FMT, bool GATHER, bool ROWSCALE, bool PAIRS, bool OFF32>
+// BIAS (the gathered dY rows of the MoE backward with a down-projection bias;
+// ROWSCALE and OFF32 hold, rows % 128 == 0, cols % 128 == 0, and a
+// workgroup's 128 rows are slots of one block of bias.B slots): from the raw
+// dY values already in registers, also
+//   db2[e][h]  += sum over the workgroup's slots of a * dY   (fp32; one atomic
+//                 per workgroup and column, the waves' sums added in order)
+//   part[c][s]  = sum over the 128 columns of column tile c of dY[s][h] * b2[e][h]
+//                 (each slot's share of <dY, b2>; the finalisation adds the
+//                 H/128 shares in order, so d(a) stays reproducible)
+// P3 (sonic-moe functional/backward.py, db2_and_ds_kernel): db2 and the bias
+// term of the affinity gradient.
+template <int FMT, bool GATHER, bool ROWSCALE, bool PAIRS, bool OFF32, bool BIAS>
 __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restrict__ x,
                                                          int64_t src_rows, int64_t cols,
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ rowscale,
                                                          int64_t rows, uint8_t* __restrict__ codes_t,
-                                                         uint8_t* __restrict__ scales_t, int self_rows) {
+                                                         uint8_t* __restrict__ scales_t, int self_rows,
+                                                         TokBias bias) {
   const int cp = threadIdx.x & 63;
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = int64_t(blockIdx.y) * kTokRows + grp * 32;
   const int64_t colA = int64_t(blockIdx.x) * kTokCols + 2 * cp;
-  if (row0 >= rows || colA >= cols) return;
+  if (!BIAS && (row0 >= rows || colA >= cols)) return;   // BIAS: every lane reaches the barrier
   uint32_t w[32];   // bf16 of columns colA (low half) and colA + 1 (high half), rows row0 ..
+  float dot[BIAS ? 32 : 1];        // BIAS: this lane's two columns' share of <dY, b2> per row
+  float db0 = 0.f, db1 = 0.f;      // BIAS: sums of a * dY over the wave's rows, columns colA, colA + 1
+  float b2lo = 0.f, b2hi = 0.f;
+#pragma unroll
+  for (int r = 0; r < (BIAS ? 32 : 1); ++r) dot[r] = 0.f;
+  if (BIAS) {
+    const int64_t e = bias.b2e[(int64_t(blockIdx.y) * kTokRows) / bias.B];
+    const uint32_t bw = *reinterpret_cast<const uint32_t*>(bias.b2 + e * cols + colA);
+    b2lo = __uint_as_float(bw << 16);
+    b2hi = __uint_as_float(bw & 0xffff0000u);
+  }
   if (src_rows > 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
     // OFF32 (source under 2 GiB): buffer loads at 32-bit offsets, a padding row
@@ -221,12 +244,48 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
       w[r] = v;
       if (ROWSCALE) {   // bf16(a * x), round to nearest even
         const float a = rowscale[row0 + r];
-        w[r] = bf16x2_pack(a * __uint_as_float(w[r] << 16), a * __uint_as_float(w[r] & 0xffff0000u));
+        const float x0 = __uint_as_float(w[r] << 16), x1 = __uint_as_float(w[r] & 0xffff0000u);
+        if (BIAS) {
+          dot[BIAS ? r : 0] = x0 * b2lo + x1 * b2hi;
+          db0 += a * x0;
+          db1 += a * x1;
+        }
+        w[r] = bf16x2_pack(a * x0, a * x1);
       }
     }
   } else {
 #pragma unroll
     for (int r = 0; r < 32; ++r) w[r] = 0u;
+  }
+  if constexpr (BIAS) {
+    // <dY, b2> shares: the 32 rows' values summed over the wave's 64 lanes by
+    // halving exchanges (stride 32 keeps rows 16..31 in the upper lanes, ...,
+    // stride 2 leaves row (lane >> 1) & 31), then lanes l and l ^ 1 add up.
+    const int lane = threadIdx.x & 63;
+    v2::static_for<5>([&](auto S) {
+      constexpr int n = 16 >> int(S);                // values kept after this stage
+      constexpr int stride = 32 >> int(S);
+      const bool up = (lane & stride) != 0;
+      v2::static_for<n>([&](auto I) {
+        const float send = up ? dot[I] : dot[I + n];
+        const float keep = up ? dot[I + n] : dot[I];
+        dot[I] = keep + __shfl_xor(send, stride, 64);
+      });
+    });
+    const float sum = dot[0] + __shfl_xor(dot[0], 1, 64);
+    const int64_t ct = int64_t(blockIdx.x);            // column tile of kTokCols columns
+    if ((lane & 1) == 0) bias.part[ct * rows + row0 + ((lane >> 1) & 31)] = sum;
+    // db2: the four waves' column sums added in wave order, one atomic per column
+    __shared__ float colsum[4][kTokCols];
+    colsum[grp][2 * cp] = db0;
+    colsum[grp][2 * cp + 1] = db1;
+    __syncthreads();
+    if (threadIdx.x < kTokCols) {
+      const float t = ((colsum[0][threadIdx.x] + colsum[1][threadIdx.x]) + colsum[2][threadIdx.x]) +
+                      colsum[3][threadIdx.x];
+      const int64_t e = bias.b2e[(int64_t(blockIdx.y) * kTokRows) / bias.B];
+      atomicAdd(bias.db2_acc + e * cols + int64_t(blockIdx.x) * kTokCols + threadIdx.x, t);
+    }
   }
   uint32_t m = 0;   // |bf16| maxima of both columns
 #pragma unroll
@@ -351,43 +410,55 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
 
 template <int FMT, bool PAIRS, bool OFF32>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
-                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows) {
-  if (idx && rs)
-    quant_tok_kernel<FMT, true, true, PAIRS, OFF32>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
+                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows,
+                         const TokBias& b) {
+  if (b.part && OFF32 && idx && rs)
+    quant_tok_kernel<FMT, true, true, PAIRS, OFF32, true>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+  else if (idx && rs)
+    quant_tok_kernel<FMT, true, true, PAIRS, OFF32, false>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
   else if (idx)
-    quant_tok_kernel<FMT, true, false, PAIRS, OFF32>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
+    quant_tok_kernel<FMT, true, false, PAIRS, OFF32, false>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
   else if (rs)
-    quant_tok_kernel<FMT, false, true, PAIRS, OFF32>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
+    quant_tok_kernel<FMT, false, true, PAIRS, OFF32, false>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
   else
-    quant_tok_kernel<FMT, false, false, PAIRS, OFF32>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
+    quant_tok_kernel<FMT, false, false, PAIRS, OFF32, false>
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
 }
 template <int FMT, bool PAIRS>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
-                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows) {
+                         const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows,
+                         const TokBias& b) {
   if (src_rows * cols * 2 < int64_t(v2::kOOB) && rows <= int64_t(INT32_MAX))
-    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
+    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
   else
-    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows);
+    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
 }
 
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st, bool pairs, bool self_rows) {
+                            uint8_t* scales_t, hipStream_t st, bool pairs, bool self_rows, const TokBias* bias) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (pairs && rows % 128) return hipErrorInvalidValue;
   if (self_rows && !idx) return hipErrorInvalidValue;
+  TokBias b{};
+  if (bias) {   // the fused bias reductions need whole tiles, row scales and 32-bit offsets
+    if (cols % kTokCols || rows % kTokRows || bias->B % kTokRows || !idx || !rowscale || self_rows ||
+        src_rows * cols * 2 >= int64_t(v2::kOOB) || rows > int64_t(INT32_MAX))
+      return hipErrorInvalidValue;
+    b = *bias;
+  }
   const int self = self_rows ? 1 : 0;
   dim3 grid(unsigned((cols + kTokCols - 1) / kTokCols), unsigned((rows + kTokRows - 1) / kTokRows));
   if (fmt == kE4M3) {
-    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
-    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
+    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
+    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
   } else {
-    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
-    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self);
+    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
+    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
   }
   return hipGetLastError();
 }

@@ -22,6 +22,8 @@ SMALL = {
     "large_s": S.scaled(S.LARGE, T=256, H=256, I=512, E=4, K=2, B=256),
     "fine_s": S.scaled(S.FINE, T=512, H=192, I=128, E=16, K=4, B=128),
     "medium_b512": S.scaled(S.MEDIUM, T=640, H=128, I=96, E=4, K=2, B=512),
+    # H a multiple of 128: the bias reductions ride on the dY gather
+    "fine_h256": S.scaled(S.FINE, T=512, H=256, I=128, E=16, K=4, B=128),
 }
 # experts of 32 MiB (W_down) and 64 MiB (W_gate_up): Phases 1 and 3 hand their
 # tiles to the XCDs round robin, which no other small case reaches
@@ -232,7 +234,7 @@ def test_moe_stages_in_order_equal_one_call():
     """The per-stage entry point: stages 0..NUM_STAGES-1 run in order on a fresh
     workspace produce what one full call produces (bitwise for every output with
     a fixed summation order; the bias sums use atomics)."""
-    for name in ("medium_s", "fine_s"):
+    for name in ("medium_s", "fine_s", "fine_h256"):
         cfg = SMALL[name]
         g1 = gpu_problem(cfg)
         o1 = {k: v.clone() for k, v in g1["op"].run().items() if v is not None}
