@@ -322,8 +322,9 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *                                                     (H % 128 == 0; else empty)
  *   phase1_ds                 [N,I,B] fp32            Phase 1's product dS per block
  *                                                     (slots past a block's extent unwritten)
- *   phase1_tiles/phase3_tiles [N+1] int32             first tile of each block over its
- *                                                     live slot tiles, and the total
+ *   phase1_tiles/phase3_tiles [N+1 + tiles] int32     first tile of each block over its
+ *                                                     live slot tiles, and the total; then
+ *                                                     each tile's block
  *   dx_slot [P,H] fp32 (each routed slot's dX row, summed per token at the end),
  *   slot_of [T,E] int32 (the slot of pair (t, e), -1 = none),
  *   daff_slot [P] fp32 (the <dY, b2> term when it is computed on its own, else 0),

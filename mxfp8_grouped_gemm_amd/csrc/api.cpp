@@ -343,8 +343,10 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->wgu_scales_pairs, E * H * 2 * I / 32);
   put(L->wd_scales_pairs, h_pairs ? E * I * H / 32 : 0);
   put(L->phase1_ds, N * I * B * 4);
-  put(L->phase1_tiles, (N + 1) * 4);
-  put(L->phase3_tiles, (N + 1) * 4);
+  // tile starts [N+1], then the tile -> block map over every tile a block can
+  // have at the smallest tile (128 x 128)
+  put(L->phase1_tiles, (N + 1 + N * ((I + 127) / 128) * ((B + 127) / 128)) * 4);
+  put(L->phase3_tiles, (N + 1 + N * ((B + 127) / 128) * ((H + 127) / 128)) * 4);
   put(L->dx_slot, N * B * H * 4);
   put(L->slot_of, T * E * 4);
   put(L->daff_slot, P * 4);

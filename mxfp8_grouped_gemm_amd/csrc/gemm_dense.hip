@@ -73,6 +73,42 @@ __device__ __forceinline__ void store_tile(const GemmStoreArgs& p, int g, int64_
   });
 }
 
+// The same store through LDS (the ring's, free once the main loop is done):
+// the tile's bf16 values are written to LDS as output rows padded by 16 bytes
+// (so a fragment's 32 rows fall on different banks), then every thread stores
+// 16-byte runs, and each store instruction writes whole row segments of the
+// output (two rows of 512 bytes for a 256-wide tile) instead of 16-byte
+// pieces of 32 rows.  Not for accumulation, which adds the old value to the
+// fp32 result before its one rounding.
+template <int BM, int BN, int SMEM>
+__device__ __forceinline__ void store_tile_staged(const GemmStoreArgs& p, int g, int64_t m0, int64_t n0,
+                                                  const v2::v16f (&acc)[BM / 64][BN / 64], uint8_t* smem) {
+  constexpr int RB = BM * 2 + 16;   // bytes per staged row
+  static_assert(BN * RB <= SMEM, "the staged tile fits in the ring's LDS");
+  __syncthreads();                  // every wave is done with the ring
+  v2::static_for<BM / 64>([&](auto I) {
+    v2::static_for<BN / 64>([&](auto J) {
+      const int r = v2::acc_col<BM, BN>(J);
+      v2::static_for<4>([&](auto K) {
+        const int c = v2::acc_row<BM, BN>(I, 4 * K);
+        *reinterpret_cast<uint2*>(smem + r * RB + c * 2) =
+            make_uint2(bf16x2_pack(acc[I][J][4 * K], acc[I][J][4 * K + 1]),
+                       bf16x2_pack(acc[I][J][4 * K + 2], acc[I][J][4 * K + 3]));
+      });
+    });
+  });
+  __syncthreads();
+  uint16_t* out = p.out + int64_t(g) * p.out_gstride;
+  constexpr int CPR = BM * 2 / 16;  // 16-byte runs per row
+#pragma unroll 4
+  for (int k = threadIdx.x; k < BN * CPR; k += v2::kThreads) {
+    const int r = k / CPR, ch = k % CPR;
+    const int64_t orow = n0 + r, ocol = m0 + ch * 8;
+    if (orow < p.N && ocol < p.M)
+      *reinterpret_cast<uint4*>(out + orow * p.ldo + ocol) = *reinterpret_cast<const uint4*>(smem + r * RB + ch * 16);
+  }
+}
+
 // Workgroup id -> (group, first row, first column).  Hardware hands out
 // workgroup ids round robin over the 8 XCDs, so ids are remapped to give each
 // XCD a contiguous range, walked GM tile-rows at a time (co-resident tiles
@@ -203,7 +239,8 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p)
       v3::mainloop<BM, BN, v3::kFp8, FA, FB>(A, B, &sd, nstages, v3::KMapPlain{}, smem, acc);
     }
   }
-  store_tile<BM, BN>(p, tp.g, tp.m0, tp.n0, acc);
+  if (p.accumulate) store_tile<BM, BN>(p, tp.g, tp.m0, tp.n0, acc);
+  else store_tile_staged<BM, BN, sizeof(smem)>(p, tp.g, tp.m0, tp.n0, acc, smem);
 }
 
 template <int BM, int BN>

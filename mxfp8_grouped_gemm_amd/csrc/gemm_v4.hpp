@@ -268,13 +268,17 @@ struct Ring {
     }
   }
 
-  // Pair step u in slot Q (see the top of the file).  The K byte of pair u+1
-  // comes first: a grouped K map reads it with a scalar load, which the wait in
-  // the second stage covers.
+  // Pair step u in slot Q (see the top of the file).  kc_next holds the K byte
+  // of pair u+1, loaded one step earlier; the K byte of pair u+2 is loaded
+  // here (a grouped K map reads it with a scalar load), so that load's latency
+  // passes behind this step's MFMAs: the wait before the mid-step barrier
+  // covers it, and no wait for it stands at the top of the next step.
+  uint32_t kc_next;
   template <int Q>
   __device__ __forceinline__ void pair_step(int u, v16f (&acc)[FM][FN]) {
     constexpr int QN = Q ^ 1;
-    const uint32_t kc = kc_of(u + 1);
+    const uint32_t kc = kc_next;
+    kc_next = kc_of(u + 2);
     v2::static_for<NR>([&](auto R) {
       constexpr int r = R;
       constexpr int j0 = r * NCI / NR, j1 = (r + 1) * NCI / NR;
@@ -314,6 +318,7 @@ struct Ring {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
     const int n = x.npairs;
+    kc_next = kc_of(1);
     {
       const uint32_t kc = kc_of(0);
       v2::static_for<NCI>([&](auto J) { issue_item<J, 0>(0, kc); });

@@ -283,7 +283,10 @@ __global__ void __launch_bounds__(256) expert_list_kernel(const int32_t* __restr
 }
 
 // Tile ranges of a slot-blocked GEMM (see moe_tiles.hpp): start[b] = sum over
-// blocks before b of ceil(extent / W) * other; start[N] = the total.  One workgroup.
+// blocks before b of ceil(extent / W) * other; start[N] = the total.  Then the
+// tile -> block map start[N + 1 + t] = b for every tile t of block b, so a
+// GEMM workgroup finds its block with one load instead of a binary search
+// (a dozen dependent loads before its first DMA).  One workgroup.
 __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restrict__ ext, int N, int W, int other,
                                                           int32_t* __restrict__ start) {
   __shared__ int red[4];
@@ -301,6 +304,12 @@ __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restr
     __syncthreads();
   }
   if (threadIdx.x == 0) start[N] = carry;
+  __syncthreads();   // the starts written above are visible to the whole workgroup
+  int32_t* map = start + N + 1;
+  for (int b = threadIdx.x; b < N; b += 256) {
+    const int t1 = start[b + 1];
+    for (int t = start[b]; t < t1; ++t) map[t] = b;
+  }
 }
 
 hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st) {

@@ -53,6 +53,45 @@ __device__ __forceinline__ void p3_store(const Phase3Args& p, const P3Pos& tp, c
   });
 }
 
+// The same rows through LDS (the ring's, free after the main loop), in passes
+// of R rows padded by 16 bytes: every thread then stores 16-byte runs, so each
+// store instruction writes whole row segments (BN * 4 bytes) instead of
+// 128-byte pieces of 2 rows.
+template <int BM, int BN, int SMEM>
+__device__ __forceinline__ void p3_store_staged(const Phase3Args& p, const P3Pos& tp,
+                                                const v16f (&acc)[BM / 64][BN / 64], uint8_t* smem) {
+  constexpr int RB = BN * 4 + 16;                       // bytes per staged row
+  constexpr int R = (SMEM / RB) >= BM ? BM : BM / 2;    // rows per pass
+  static_assert(R * RB <= SMEM && BM % R == 0 && (BM / 2) % 32 == 0, "staging passes");
+  const int64_t sbase = int64_t(tp.b) * p.B;
+  const int wave = threadIdx.x >> 6;
+  constexpr int CPR = BN * 4 / 16;                      // 16-byte runs per row
+  v2::static_for<BM / R>([&](auto PASS) {
+    __syncthreads();                                    // the ring, or the previous pass, is done
+    // pass PASS holds tile rows [PASS * R, PASS * R + R): R == BM, or the waves
+    // whose half of the rows (wave >> 1) is PASS
+    if (R == BM || (wave >> 1) == int(PASS)) {
+      v2::static_for<BM / 64>([&](auto FI) {
+        v2::static_for<16>([&](auto Q) {
+          const int r = v2::acc_row<BM, BN>(FI, Q) - int(PASS) * R;
+          v2::static_for<BN / 64>([&](auto FJ) {
+            *reinterpret_cast<float*>(smem + r * RB + v2::acc_col<BM, BN>(FJ) * 4) = acc[FI][FJ][int(Q)];
+          });
+        });
+      });
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = threadIdx.x; k < R * CPR; k += v2::kThreads) {
+      const int r = k / CPR, ch = k % CPR;
+      const int64_t s = tp.m0 + int(PASS) * R + r, hh = tp.n0 + ch * 4;
+      if (hh < p.H)
+        *reinterpret_cast<uint4*>(p.dx_slot + (sbase + s) * p.H + hh) =
+            *reinterpret_cast<const uint4*>(smem + r * RB + ch * 16);
+    }
+  });
+}
+
 // 2I not a multiple of 128 bytes: one tile per workgroup on the v2 loop.
 template <int BM, int BN, int FG, int FW>
 __global__ void __launch_bounds__(v2::kThreads) phase3_generic(Phase3Args p) {
@@ -96,7 +135,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
                    tp.n0, p.H, p.H * (twoI / 32));
   v16f acc[FM][FN];
   v3::mainloop<BM, BN, v3::kFp8, FG, FW>(A, B, &sd, int(twoI / v3::SK), v3::KMapPlain{}, smem, acc);
-  p3_store<BM, BN>(p, tp, acc);
+  p3_store_staged<BM, BN, sizeof(smem)>(p, tp, acc, smem);
 }
 
 template <int BM, int BN>

@@ -4,7 +4,8 @@
 // so the block contributes ceil(extent / W) slot tiles of W slots, each times
 // `other` tiles along the GEMM's other dimension.  start[b] (b = 0..N) is the
 // index of block b's first tile and start[N] the total, built on the device
-// before the GEMM (launch_tile_ranges).  The GEMM's grid covers every tile a
+// before the GEMM (launch_tile_ranges), followed by each tile's block
+// (start[N + 1 + t]).  The GEMM's grid covers every tile a
 // full block could have; workgroups past the total exit at once.  Being the
 // highest ids, those are spread over all XCDs, and the live ids are handed to
 // the XCDs evenly (in contiguous ranges or round robin, see block_tile):
@@ -38,15 +39,10 @@ __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, in
   if (wg >= t8) return false;
   const int id = rr ? wg : v2::xcd_remap(wg, t8);
   if (id >= total) return false;
-  int lo = 0, hi = N;   // start[lo] <= id < start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (start[mid] <= id) lo = mid;
-    else hi = mid;
-  }
-  t.b = lo;
-  t.local = id - start[lo];
-  t.slots = (start[lo + 1] - start[lo]) / other;
+  const int b = start[N + 1 + id];   // the tile -> block map after the starts
+  t.b = b;
+  t.local = id - start[b];
+  t.slots = (start[b + 1] - start[b]) / other;
   return true;
 }
 
