@@ -495,19 +495,21 @@ def oracle_dense_sample(nthreads, n_rows):
                       f"{flops / 1e9:.2f} GFLOP in {secs:.2f} s on {nthreads} thread(s)"}
 
 
-def kernel_only(cfg, stage_name, reps):
-    """Set the workload up, run the backward once, then launch one stage reps
-    times (the program rocprofv3 --pmc wraps for that stage's counters)."""
+def kernel_only(cfg, stage_names, reps):
+    """Set the workload up, run the backward once, then launch each of the
+    comma-separated stages reps times (the program rocprofv3 --pmc wraps for
+    those stages' counters)."""
     import torch
     import mxfp8_grouped_gemm_amd as mx
     op = build_problem(cfg)["op"]
     op.run()
     torch.cuda.synchronize()
-    s = op.STAGE_NAMES.index(stage_name)
-    for _ in range(reps):
-        op.stage(s)
-    torch.cuda.synchronize()
-    log(f"[bench] kernel-only: {stage_name} x{reps} on {cfg.name} (library {mx.version()})")
+    for name in stage_names.split(","):
+        s = op.STAGE_NAMES.index(name)
+        for _ in range(reps):
+            op.stage(s)
+        torch.cuda.synchronize()
+        log(f"[bench] kernel-only: {name} x{reps} on {cfg.name} (library {mx.version()})")
 
 
 def copy_calibration(nbytes):
@@ -537,7 +539,8 @@ def main():
                     help="oracle threads (0: every CPU this process may use, capped at the box's thread share)")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--cpu-cols", type=int, default=128)
-    ap.add_argument("--kernel-only", metavar="STAGE", help="set up, then launch one stage (for rocprofv3 --pmc)")
+    ap.add_argument("--kernel-only", metavar="STAGES",
+                    help="set up, then launch the comma-separated stages (for rocprofv3 --pmc)")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES", help="one copy of BYTES (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

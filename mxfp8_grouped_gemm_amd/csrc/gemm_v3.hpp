@@ -244,9 +244,11 @@ struct Tile {
   int nstages;
 };
 
-// The ring of one tile: stage t lives in code slot t % NBUF, with its pair's
-// scale words (one 4-byte word per row covering K elements [128p, 128p + 128),
-// loaded again for each stage of the pair) in scale slot t % NBUF.  Loads are
+// The ring of one tile: stage t lives in code slot t % NBUF; an even stage's
+// scale slot t % NBUF holds its pair's scale words (one 4-byte word per row
+// covering K elements [128p, 128p + 128)), which the odd stage reuses from
+// registers (loading them for both stages kept the texture addresser busier
+// on the address-bound Phases 3 and 4).  Loads are
 // issued NBUF stages ahead of use: after the prologue (positions 0 .. NBUF-1),
 // step t issues position t + NBUF into stage t's slot once every wave has read
 // that slot.  Positions past the last stage load through descriptors with no
@@ -266,7 +268,13 @@ struct Ring {
   static constexpr int CS = code_slot(BM, BN), SSB = scale_slot(BM, BN);
   static constexpr int NCI = (BM + BN) / 64;               // code DMA instructions per wave per stage
   static constexpr int NS = ScaleDma<BM, BN>::NS;          // scale DMA instructions per wave per stage
-  static constexpr int VM_STAGE = NCI + NS;
+  // DMA instructions per wave of a position: NCI code rows, plus NS scale
+  // chunks at even positions.  Wait counts: a position has landed once at
+  // most the loads of the positions issued after it remain, i.e. of the next
+  // two (one even, one odd) in a step, of the next three (one even) after the
+  // prologue.
+  static constexpr int VM_2AFTER = 2 * NCI + NS;
+  static constexpr int VM_3AFTER = 3 * NCI + NS;
   using T = Tile<BM, BN, KMap>;
 
   uint8_t* smem;
@@ -314,7 +322,9 @@ struct Ring {
       rb[2] = live ? rb[2] : 0;
       dma16(rb, cs + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc);
     }
-    if (J < NS) {
+    // a pair's scale words go with its first (even) stage only: the odd stage
+    // takes them from the registers its even stage read them into (read_item)
+    if (J < NS && (S >= 0 ? (S & 1) == 0 : (pos & 1) == 0)) {
       const uint32_t ss = lds_addr(smem) + NBUF * CS + slot * SSB;
       v4i rs = dS[J < NS ? J : 0];
       rs[2] = live ? rs[2] : 0;
@@ -353,14 +363,17 @@ struct Ring {
       const int row = (wave >> 1) * (BM / 2) + 32 * J + r;
       fa[P][J][0] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * (h ^ swz(row)));
       fa[P][J][1] = *reinterpret_cast<const uint4*>(cs + row * SK + 16 * ((2 + h) ^ swz(row)));
-      sa[P][J] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
+      // stage parity P: the odd stage's pair word is its even stage's, in set 0
+      if (P == 0) sa[P][J] = *reinterpret_cast<const uint32_t*>(ss + (row >> 6) * 256 + (row & 63) * 4);
+      else sa[P][J] = sa[0][J];
     } else {
       constexpr int j = J - FM;
       const int row = (wave & 1) * (BN / 2) + 32 * j + r;
       fb[P][j][0] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * (h ^ swz(row)));
       fb[P][j][1] = *reinterpret_cast<const uint4*>(cs + (BM + row) * SK + 16 * ((2 + h) ^ swz(row)));
       const int srow = BM + row;
-      sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (srow >> 6) * 256 + (srow & 63) * 4);
+      if (P == 0) sb[P][j] = *reinterpret_cast<const uint32_t*>(ss + (srow >> 6) * 256 + (srow & 63) * 4);
+      else sb[P][j] = sb[0][j];
     }
   }
 
@@ -418,7 +431,7 @@ struct Ring {
     constexpr int SN = S >= 0 ? (S + 1) % NBUF : -1;   // slot of stage t + 1
     if (READ) {
       const uint32_t kc = kc_of(t + NBUF);
-      __builtin_amdgcn_s_waitcnt(waitcnt(2 * VM_STAGE, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt(VM_2AFTER, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       v2::static_for<NR>([&](auto Q) {
@@ -455,7 +468,7 @@ struct Ring {
     issue<2>(2);
     issue<3>(3);
     // stage 0 has landed once at most the three later positions' loads remain
-    __builtin_amdgcn_s_waitcnt(waitcnt(3 * VM_STAGE, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt(VM_3AFTER, 0));
     __builtin_amdgcn_s_barrier();
     v2::static_for<NR>([&](auto J) { read_item<0, J, 0>(0); });
     int t = 0;
