@@ -135,6 +135,78 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
   }
 }
 
+// With E <= kRouteLdsExperts, one workgroup per chunk handles every expert:
+// it counts with an LDS histogram, then places its tokens 256 at a time, each
+// token finding its rank among the round's tokens of the same expert from a
+// per-expert bitmap of the round in LDS (tokens ascending, as above).  Every
+// chunk's ids are then read once per kernel instead of once per expert.
+constexpr int kRouteLdsExperts = 1024;
+
+// the token's expert at selection k, or -1: out of range, dropped, or a
+// repeat of an earlier selection of the same token (counted once, as above)
+__device__ __forceinline__ int route_sel(const int32_t* __restrict__ ids, int K, int k, int E) {
+  const int e = ids[k];
+  if (e < 0 || e >= E) return -1;
+  for (int j = 0; j < k; ++j)
+    if (ids[j] == e) return -1;
+  return e;
+}
+
+__global__ void __launch_bounds__(256) route_count_lds_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
+                                                              int64_t CH, int C, int E, int32_t* __restrict__ cnt) {
+  __shared__ int hist[kRouteLdsExperts];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256)
+    for (int k = 0; k < K; ++k) {
+      const int e = route_sel(topk + t * K, K, k, E);
+      if (e >= 0) atomicAdd(&hist[e], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e * C + c] = hist[e];
+}
+
+__global__ void __launch_bounds__(256) route_place_lds_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
+                                                              int64_t CH, int C, int E,
+                                                              const int32_t* __restrict__ off,
+                                                              int32_t* __restrict__ tpid) {
+  __shared__ uint32_t bits[kRouteLdsExperts][8];   // [expert][round token / 32]
+  __shared__ int run[kRouteLdsExperts];            // next slot of (expert, this chunk)
+  const int c = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) run[e] = off[e * C + c];
+  const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
+  for (int64_t tb = t0; tb < t1; tb += 256) {
+    for (int i = tid; i < E * 8; i += 256) bits[i >> 3][i & 7] = 0u;
+    __syncthreads();
+    const int64_t t = tb + tid;
+    const bool live = t < t1;
+    if (live)
+      for (int k = 0; k < K; ++k) {
+        const int e = route_sel(topk + t * K, K, k, E);
+        if (e >= 0) atomicOr(&bits[e][tid >> 5], 1u << (tid & 31));
+      }
+    __syncthreads();
+    if (live)
+      for (int k = 0; k < K; ++k) {
+        const int e = route_sel(topk + t * K, K, k, E);
+        if (e >= 0) {
+          int rank = __popc(bits[e][tid >> 5] & ((1u << (tid & 31)) - 1u));
+          for (int w = 0; w < (tid >> 5); ++w) rank += __popc(bits[e][w]);
+          tpid[run[e] + rank] = int32_t(t);
+        }
+      }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      int n = 0;
+      for (int w = 0; w < 8; ++w) n += __popc(bits[e][w]);
+      run[e] += n;
+    }
+    __syncthreads();
+  }
+}
+
 int64_t build_blocks_workspace_bytes(int64_t E) { return E > 0 ? 2 * E * kRouteChunks * 4 : 0; }
 
 // The allocation-free variant's scratch: the counts and first slots per
@@ -189,6 +261,12 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
   const int C = int((T + CH - 1) / CH);
   int32_t* cnt = ws;
   int32_t* off = ws + E * kRouteChunks;
+  if (E <= kRouteLdsExperts) {
+    route_count_lds_kernel<<<unsigned(C), 256, 0, st>>>(topk, T, int(K), CH, C, int(E), cnt);
+    route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), off, b2e);
+    route_place_lds_kernel<<<unsigned(C), 256, 0, st>>>(topk, T, int(K), CH, C, int(E), off, tpid);
+    return hipGetLastError();
+  }
   route_count_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, cnt);
   route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), off, b2e);
   route_place_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, off, tpid);

@@ -165,13 +165,11 @@ static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipS
 // Tile shape: 256 x 256 when the block and H allow, else 128 x 256; 2I not a
 // multiple of 128 bytes (unaligned scale rows / ragged last K stage): the v2
 // loop at 128 x 256.  A short contraction (2I < 1024: a few ring stages per
-// tile, so the tile's fp32 store is much of its time) takes 128 x 128 tiles,
-// whose smaller ring lets two workgroups share a CU and overlap one's stores
-// with the other's loads (measured 4% faster at 2I = 512).
+// tile) also takes 128 x 256 tiles: with the rows stored through LDS, they
+// measured 5% faster at 2I = 512 than 128 x 128 tiles at two per CU.
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st) {
   const bool g = (2 * p.I) % v2::BK != 0;
-  if (!g && 2 * p.I < 1024) return phase3_launch<128, 128>(p, fg, fw, false, st);
-  if (!g && p.B >= 256 && p.H >= 256) return phase3_launch<256, 256>(p, fg, fw, false, st);
+  if (!g && 2 * p.I >= 1024 && p.B >= 256 && p.H >= 256) return phase3_launch<256, 256>(p, fg, fw, false, st);
   return phase3_launch<128, 256>(p, fg, fw, g, st);
 }
 

@@ -114,7 +114,10 @@ def test_moe_small_full_parity(name):
 def test_moe_build_blocks_bit_exact_and_edge_cases():
     import mxfp8_grouped_gemm_amd as mx
     rng = np.random.default_rng(3)
-    for T, K, E, B in ((1000, 3, 7, 128), (64, 1, 64, 128), (4096, 8, 128, 128), (300, 2, 3, 1024)):
+    # (70000, 4, 1024, ...) places 9 rounds of 256 tokens per chunk with the most experts the
+    # per-chunk LDS kernels take; (20000, 8, 2048, ...) takes the per-(expert, chunk) kernels
+    for T, K, E, B in ((1000, 3, 7, 128), (64, 1, 64, 128), (4096, 8, 128, 128), (300, 2, 3, 1024),
+                       (70000, 4, 1024, 128), (20000, 8, 2048, 128)):
         topk = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
         if E == 7:
             topk[topk == 5] = 4 if K == 1 else topk[topk == 5]      # keep rows distinct
