@@ -224,7 +224,8 @@ int moe_build_blocks_noalloc(const int32_t* topk_ids, int64_t T, int64_t K, int6
  *   affinity on I (1): y_t += (a * inter) Wd[e]            (no bias)
  * Backward (P1 phases; P3's epilogue):
  *   Phase 1  dS = dY_t Wd[e]^T (quantised along H), then the SwiGLU-backward
- *            epilogue on the fp32 product (a kernel of its own):
+ *            epilogue on the fp32 product (a kernel of its own, or inside
+ *            Phase 1's kernel where that measured faster, see phase1_ds):
  *            d(a) = sum_i dS*inter + <dY_t, b2[e]>,  dInter = a*dS,
  *            dGate = dInter*up*silu'(g),  dUp = dInter*silu(g)
  *   Phase 3  dX_t += [dGate,dUp] Wgu[e]^T    (quantised along I)
@@ -321,7 +322,11 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *   wd_scales_pairs           P4 of down_scales per expert, [E][H/128][I][4]
  *                                                     (H % 128 == 0; else empty)
  *   phase1_ds                 [N,I,B] fp32            Phase 1's product dS per block
- *                                                     (slots past a block's extent unwritten)
+ *                                                     (slots past a block's extent unwritten;
+ *                                                     empty, like phase1_tiles, where Phase 1
+ *                                                     runs with its epilogue in one kernel:
+ *                                                     H % 128 == 0, H <= 2048, I <= 512 and
+ *                                                     no caller checkpoints)
  *   phase1_tiles/phase3_tiles [N+1 + tiles] int32     first tile of each block over its
  *                                                     live slot tiles, and the total; then
  *                                                     each tile's block
@@ -377,7 +382,9 @@ int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t worksp
  *     multiple of 128 and no down_proj_act_checkpoint)
  *   4 Phase 1 (the product dS)
  *   5 Phase 1 epilogue (SwiGLU backward; dGU along I and along slots, the
- *     intermediate along slots, d(affinity) and db1 partial sums)
+ *     intermediate along slots, d(affinity) and db1 partial sums); where the
+ *     layout has no phase1_ds (see there) stage 4 does this too and stage 5
+ *     nothing
  *   6 Phase 3 (dX rows per slot)  7 Phase 2 (dW_gate_up)       8 Phase 4 (dW_down)
  *   9 finalise (dX summed per token in expert order, the rest to bf16)
  * Errors as for moe_bwd_mxfp8, plus INVALID_ARG for a stage outside the range. */

@@ -318,6 +318,13 @@ static bool moe_fuse_bias(const moe_bwd_mxfp8_args* a) {
   return a->has_bias && a->H % 128 == 0 && !a->down_proj_act_checkpoint;
 }
 
+// Phase 1 with its epilogue in one kernel (the conditions of mx::phase1_fusable,
+// which its launcher checks again): no dS in HBM, and no tile ranges.
+static bool moe_phase1_fused(const moe_bwd_mxfp8_args* a) {
+  return a->H % 128 == 0 && a->H <= 2048 && a->I <= 512 && !a->gate_act_checkpoint_T &&
+         !a->intermediate_checkpoint_T && !a->scaled_intermediate_checkpoint_T;
+}
+
 static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layout* L) {
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, N = a->N, B = a->block_size, P = N * B;
   size_t o = 0;
@@ -342,10 +349,11 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->dgu_tok_scales, 2 * I * P / 32);
   put(L->wgu_scales_pairs, E * H * 2 * I / 32);
   put(L->wd_scales_pairs, h_pairs ? E * I * H / 32 : 0);
-  put(L->phase1_ds, N * I * B * 4);
+  const bool fused = moe_phase1_fused(a);
+  put(L->phase1_ds, fused ? 0 : N * I * B * 4);
   // tile starts [N+1], then the tile -> block map over every tile a block can
   // have at the smallest tile (128 x 128)
-  put(L->phase1_tiles, (N + 1 + N * ((I + 127) / 128) * ((B + 127) / 128)) * 4);
+  put(L->phase1_tiles, fused ? 0 : (N + 1 + N * ((I + 127) / 128) * ((B + 127) / 128)) * 4);
   put(L->phase3_tiles, (N + 1 + N * ((B + 127) / 128) * ((H + 127) / 128)) * 4);
   put(L->dx_slot, N * B * H * 4);
   put(L->slot_of, T * E * 4);
@@ -542,10 +550,16 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   // Tile order over the XCDs (measured: round robin 2.6% faster on Phase 1 with
   // 58 MB W_down experts; the contiguous ranges 6% faster with 0.4-3 MB ones)
   p1.rr_tiles = I * H >= kRoundRobinWeightBytes;
-  STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_weight, st), "phase 1");
+  // With the epilogue fused stage 4 does both and stage 5 nothing.
+  const bool fused = moe_phase1_fused(a);
+  if (fused) {
+    STEP(mx::launch_phase1_fused(p1, a->fmt_grad, a->fmt_weight, st), "phase 1 (with its epilogue)");
+  } else {
+    STEP(mx::launch_phase1(p1, a->fmt_grad, a->fmt_weight, st), "phase 1");
+  }
   stage = 5;
   // the SwiGLU backward on dS: dGU along both axes, the intermediate operand, d(a), db1
-  STEP(mx::launch_phase1_epi(p1, a->fmt_grad, st), "phase 1 epilogue");
+  if (!fused) STEP(mx::launch_phase1_epi(p1, a->fmt_grad, st), "phase 1 epilogue");
   stage = 6;
   // Phase 3: dX scatter-add
   mx::Phase3Args p3{};

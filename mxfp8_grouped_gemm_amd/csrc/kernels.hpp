@@ -155,6 +155,10 @@ struct Phase1Args {
 };
 hipError_t launch_phase1(const Phase1Args& p, int fmt_grad, int fmt_weight, hipStream_t st);
 hipError_t launch_phase1_epi(const Phase1Args& p, int fmt_grad, hipStream_t st);
+// Phase 1 and its epilogue in one kernel, where phase1_fusable: the same outputs
+// as launch_phase1 followed by launch_phase1_epi, without dS in HBM
+bool phase1_fusable(const Phase1Args& p);
+hipError_t launch_phase1_fused(const Phase1Args& p, int fmt_grad, int fmt_weight, hipStream_t st);
 
 struct Phase3Args {
   const uint8_t* dgu_row_codes;   // [P][2I]

@@ -1,0 +1,368 @@
+// moe_phase1_epi.hpp -- the SwiGLU (or GeGLU) backward after Phase 1's product (P1,
+// "Blockwise MM Backward MXFP8 Kernel API Reference": Phase 1's epilogue and
+// the checkpoint parameters; P3, sonic-moe functional/backward.py:
+// _down_projection_backward_act, the gated-activation backward).
+//
+// Per slot p of block b (token t, affinity a_p; padding slots contribute zeros)
+// and intermediate index i, from dS = Phase 1's product and the checkpoint g, u:
+//   ga = bf16(silu(g)) (GeGLU: bf16(gelu(g))), inter = bf16(ga * u)
+//   d(a)_p  = sum_i dS * inter                  (a partial per 32 rows i, summed
+//                                                at the end in order)
+//   dInter = a_p * dS
+//   dGate = bf16(dInter * u * silu'(g)) (GeGLU: gelu'(g)), dUp = bf16(dInter * ga)
+//   -> quantised along I        (Phase-3 A operand, dgu_row [P][2I])
+//   -> quantised along the slots (Phase-2 B operand, dgu_tok [2I][P])
+//   -> db1 partial sums along the slots (with a bias)
+//   the intermediate operand of Phase 4 (times a_p with the affinity on I),
+//   quantised along the slots (inter_tok [I][P]); blocks without tokens get zeros.
+//
+// The work is cut into chunks of TI rows i x TS slots of one block (TS =
+// min(B, 256), TI * TS = 8192), each done by one 256-thread workgroup in two
+// passes.  Pass 1, one thread per (slot, 32 rows): dS and the checkpoint, the
+// element-wise math, the I-axis groups in registers and their 32-byte code
+// runs, d(a) partials; dG|dU and the intermediate are staged in LDS.  Pass 2,
+// one thread per (row, 32-slot group): the slot-axis groups from LDS, stored
+// as 32-byte runs.  dS comes either from HBM (the stand-alone epilogue kernel)
+// or from LDS, where the fused Phase-1 kernel leaves each chunk of its tile's
+// product (DS_LDS); the arithmetic is the same either way, so the two give
+// identical bits.
+#pragma once
+#include "kernels.hpp"
+#include "gemm_v2.hpp"
+#include "mx_device.hpp"
+#include "swiglu.hpp"
+
+namespace mx {
+
+constexpr int kEpiThreads = 256;
+constexpr int kEpiElems = 8192;   // TI * TS
+
+// LDS of one chunk.  Staging: row r, slot s at r * GSW + (s / 32) * 33 + s % 32
+// (dG|dU words) and r * ISH + (s / 32) * 34 + s % 32 (intermediate values).
+// Pass 2's lanes read rows r..r+7, groups c = 0..7 at one offset: word
+// 8r + 33c (+ k) mod 64 is a different bank for each lane, and pass 1's lanes
+// write consecutive words.  With DS_LDS the chunk's dS sits at the start of the
+// same bytes, row r at r * DSW: fragment stores put rows 4 apart in the two
+// lane halves (4 * DSW = 32 mod 64 banks: no conflict), and pass 1 reads rows
+// of consecutive slots.  Pass 1 reads all of it before it writes the staging.
+template <int TS>
+struct EpiLds {
+  static constexpr int TI = kEpiElems / TS, NG = TS / 32;
+  static constexpr int GSW = 33 * NG, ISH = 34 * NG, DSW = TS + 8;
+  static constexpr int GU_BYTES = TI * GSW * 4, IN_BYTES = TI * ISH * 2;
+  static constexpr int BYTES = GU_BYTES + IN_BYTES;
+  static_assert(TI * DSW * 4 <= BYTES, "dS fits the staging bytes");
+};
+
+// The element-wise SwiGLU backward of one (slot, i): from dS = d, the
+// checkpoint's g and u and the affinity a, adds this element's share of d(a)
+// and returns bf16(dGate) | bf16(dUp) << 16 and the bf16 intermediate operand
+// (times a when on_i).  A supplied checkpoint value (has_*) replaces the
+// recomputed one; the values are rounded at the same points either way, so
+// consistent checkpoints give the same bits.
+// GEGLU: the gate activation is gelu (g * Phi(g)) instead of silu.
+template <bool GEGLU>
+__device__ __forceinline__ uint32_t swiglu_bwd(bool on_i, float d, float g, float u, float a, bool has_ga, float ga_in,
+                                               bool has_in, float in_in, bool has_sc, uint16_t sc_in, float& daff,
+                                               uint16_t& it) {
+  if constexpr (GEGLU) {
+    const float cdf = normal_cdf(g);
+    const float ga = has_ga ? ga_in : bf16_round(g * cdf);   // gelu(g)
+    const float in = has_in ? in_in : bf16_round(ga * u);    // intermediate
+    daff += d * in;
+    const float di = a * d;                                  // d(intermediate)
+    it = on_i ? (has_sc ? sc_in : bf16_rne(a * in)) : uint16_t(__float_as_uint(in) >> 16);
+    return bf16x2_rne(di * u * dgelu_from(g, cdf), di * ga);
+  } else {
+    const float sg = sigmoid_fast(g);
+    const float ga = has_ga ? ga_in : bf16_round(g * sg);   // silu(g)
+    const float in = has_in ? in_in : bf16_round(ga * u);   // intermediate
+    daff += d * in;
+    const float di = a * d;                                 // d(intermediate)
+    it = on_i ? (has_sc ? sc_in : bf16_rne(a * in)) : uint16_t(__float_as_uint(in) >> 16);
+    return bf16x2_rne(di * u * dsilu_from(g, sg), di * ga);
+  }
+}
+
+// A chunk of a block without tokens: its intermediate operand is all zeros
+// (codes 0, scale byte 0; scales pair-major [P/128][I][4]).
+template <int TS>
+__device__ __forceinline__ void epi_empty_chunk(const Phase1Args& p, int b, int64_t ti0, int64_t s0) {
+  constexpr int TI = kEpiElems / TS;
+  const int64_t P = p.N * p.B, sbase = int64_t(b) * p.B;
+  const int t = threadIdx.x;
+  for (int k = t; k < TI * (TS / 16); k += kEpiThreads) {
+    const int64_t i = ti0 + k / (TS / 16);
+    if (i < p.I)
+      *reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + sbase + s0 + (k % (TS / 16)) * 16) = uint4{0, 0, 0, 0};
+  }
+  for (int k = t; k < TI * (TS / 128); k += kEpiThreads) {
+    const int64_t i = ti0 + k / (TS / 128);
+    if (i < p.I)
+      *reinterpret_cast<uint32_t*>(p.inter_tok_scales + (((sbase + s0) / 128 + k % (TS / 128)) * p.I + i) * 4) = 0u;
+  }
+}
+
+// The checkpoint values (bf16 gate and up) one thread of pass 1 reads for a
+// chunk: slot (t % TS) of the chunk, the 32 rows of its group (t / TS).  The
+// fused kernel loads the next chunk's while it works on the current one.
+struct EpiGU {
+  uint32_t gu[32];   // bf16 gate | bf16 up << 16 (the d16 and d16_hi loads fill one register)
+};
+typedef unsigned short epi_us2 __attribute__((ext_vector_type(2)));
+template <int TS>
+__device__ __forceinline__ void epi_load_gu(const Phase1Args& p, int b, int64_t ti0, int64_t gstride, int64_t s0,
+                                            EpiGU& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int t = threadIdx.x, sl = t % TS;
+  const int64_t slot = int64_t(b) * p.B + s0 + sl, i0 = ti0 + (t / TS) * gstride;
+  if (i0 < p.I) {
+    const bool ok = p.slot_tok[slot] >= 0;
+    const uint32_t live = s0 < p.flag[b] ? 1u : 0u;
+    const auto rc = MX_RSRC(v2::make_rsrc(p.ckpt + int64_t(b) * 2 * p.I * p.B, live * uint32_t(p.I * p.B * 4)));
+    const uint32_t vc = ok ? uint32_t((s0 + sl) * 2) : v2::kOOB;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + k) * p.B));
+      const uint16_t g = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, row * 2, 0);
+      const uint16_t u = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, (row + uint32_t(p.I * p.B)) * 2, 0);
+      x.gu[k] = __builtin_bit_cast(uint32_t, epi_us2{g, u});
+    }
+  }
+#endif
+}
+
+// One chunk (TI rows of I in groups of 32, group k at rows ti0 + k * gstride ..
+// + 32; slots s0 .. s0 + TS of block b, which has tokens) by the whole
+// workgroup.  ONI: 0 / 1 the affinity on H / I known
+// at compile time, 2 read from p.  CK: the caller supplied at least one of the
+// [N][I][B] checkpoints (silu(gate), the intermediate, the scaled intermediate);
+// pass 1 then runs its 32 rows in two halves so that the extra loads fit in
+// registers.  lds: EpiLds<TS>::BYTES bytes (16-byte aligned), holding the
+// chunk's dS on entry when DS_LDS, which also takes the checkpoint values from
+// pre (loaded by epi_load_gu).  Ends with pass 2's stores issued; the caller
+// synchronises before it reuses the LDS.
+template <int FG, int ONI, int TS, bool CK, bool GEGLU, bool DS_LDS>
+__device__ __forceinline__ void epi_chunk(const Phase1Args& p, int b, int64_t ti0, int64_t gstride, int64_t s0,
+                                          uint8_t* lds, const EpiGU* pre = nullptr) {
+  static_assert(!(CK && DS_LDS), "supplied checkpoints take the stand-alone epilogue");
+  using L = EpiLds<TS>;
+  constexpr int NG = L::NG, GSW = L::GSW, ISH = L::ISH;
+  uint32_t* stg_gu = reinterpret_cast<uint32_t*>(lds);
+  uint16_t* stg_in = reinterpret_cast<uint16_t*>(lds + L::GU_BYTES);
+  const float* dsl = reinterpret_cast<const float*>(lds);
+  const bool on_i = ONI == 2 ? p.affinity_on_i != 0 : ONI == 1;
+  const int64_t P = p.N * p.B, twoI = 2 * p.I;
+  const int64_t sbase = int64_t(b) * p.B;
+  const int t = threadIdx.x;
+  const int64_t e = p.b2e[b];
+
+  // ---- pass 1: thread = slot s (of the chunk) x 32 rows r0 .. r0 + 31 --------------
+  {
+    const int sl = t % TS, r0 = 32 * (t / TS);
+    const int64_t slot = sbase + s0 + sl;
+    const int64_t i0 = ti0 + (t / TS) * gstride;
+    const bool ok = p.slot_tok[slot] >= 0;
+    const float a = ok ? p.slot_aff[slot] : 0.f;
+    const bool rows = i0 < p.I;   // I % 32 == 0: all 32 rows or none
+    // Buffer loads: row offsets are wave-uniform (scalar), the slot offset is
+    // this lane's; padding slots load through an offset past the buffer, which
+    // reads zeros, so no load is conditional (each would be a branch with its
+    // own wait, serialising the 96 loads a thread keeps in flight).
+    uint32_t gu[32];   // bf16(dGate) | bf16(dUp) << 16
+    uint32_t itp[16];  // bf16 intermediate operand, rows 2k | 2k + 1 << 16
+    float daff = 0.f, amg = 0.f, amu = 0.f;
+#if defined(__HIP_DEVICE_COMPILE__)
+    // a chunk past the block's extent is all padding (dS unwritten there): its
+    // descriptors have no records, so every load reads zero without memory traffic
+    const uint32_t live = s0 < p.flag[b] ? 1u : 0u;
+    const auto rd = MX_RSRC(v2::make_rsrc(p.ds + int64_t(b) * p.I * p.B, live * uint32_t(p.I * p.B * 4)));
+    const auto rc = MX_RSRC(v2::make_rsrc(p.ckpt + int64_t(b) * 2 * p.I * p.B, live * uint32_t(p.I * p.B * 4)));
+    // padding slots read dS and the checkpoint as zeros (their dS may be unwritten)
+    const uint32_t vd = ok ? uint32_t((s0 + sl) * 4) : v2::kOOB, vc = ok ? uint32_t((s0 + sl) * 2) : v2::kOOB;
+    // element k of the 32: its intermediate operand goes to half k & 1 of itp[k / 2]
+    auto put_it = [&](int k, uint16_t v) {
+      itp[k >> 1] = (k & 1) ? (itp[k >> 1] & 0xffffu) | (uint32_t(v) << 16) : uint32_t(v);
+    };
+    if constexpr (!CK && DS_LDS) {
+      // dS from LDS, read as it is used; all of it is read before the barrier,
+      // after which the staging overwrites it
+      if (rows) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const float x = dsl[(r0 + k) * L::DSW + sl];
+          uint16_t v;
+          gu[k] = swiglu_bwd<GEGLU>(on_i, ok ? x : 0.f, lo_bf16(pre->gu[k]), hi_bf16(pre->gu[k]), a, false,
+                                    0.f, false, 0.f, false, 0, daff, v);
+          put_it(k, v);
+          amg = fmaxf(amg, fabsf(lo_bf16(gu[k])));
+          amu = fmaxf(amu, fabsf(hi_bf16(gu[k])));
+        }
+      }
+      __syncthreads();
+    } else if constexpr (!CK) {
+      uint16_t gb[32], ub[32];
+      float dv[32];
+      if (rows) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + k) * p.B));
+          dv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, vd, row * 4, 0));
+          gb[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, row * 2, 0);
+          ub[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, (row + uint32_t(p.I * p.B)) * 2, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          uint16_t v;
+          gu[k] = swiglu_bwd<GEGLU>(on_i, dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, false, 0.f, false, 0.f,
+                                    false, 0, daff, v);
+          put_it(k, v);
+          amg = fmaxf(amg, fabsf(lo_bf16(gu[k])));
+          amu = fmaxf(amu, fabsf(hi_bf16(gu[k])));
+        }
+      }
+    } else if (rows) {
+      // a checkpoint that was not supplied is read through a descriptor with
+      // no records: zeros, no memory traffic, and the value is recomputed
+      const bool has_ga = p.ga_ckpt != nullptr, has_in = p.in_ckpt != nullptr, has_sc = p.sc_ckpt != nullptr;
+      const int64_t blk = int64_t(b) * p.I * p.B;
+      const uint32_t ck_bytes = live * uint32_t(p.I * p.B * 2);
+      const auto rga = MX_RSRC(v2::make_rsrc(has_ga ? p.ga_ckpt + blk : p.ckpt, has_ga ? ck_bytes : 0u));
+      const auto rin = MX_RSRC(v2::make_rsrc(has_in ? p.in_ckpt + blk : p.ckpt, has_in ? ck_bytes : 0u));
+      const auto rsc = MX_RSRC(v2::make_rsrc(has_sc ? p.sc_ckpt + blk : p.ckpt, has_sc ? ck_bytes : 0u));
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint16_t gb[16], ub[16], gab[16], inb[16], scb[16];
+        float dv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t row = __builtin_amdgcn_readfirstlane(uint32_t((i0 + 16 * hh + k) * p.B));
+          dv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, vd, row * 4, 0));
+          gb[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, row * 2, 0);
+          ub[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, (row + uint32_t(p.I * p.B)) * 2, 0);
+          gab[k] = __builtin_amdgcn_raw_buffer_load_b16(rga, vc, row * 2, 0);
+          inb[k] = __builtin_amdgcn_raw_buffer_load_b16(rin, vc, row * 2, 0);
+          scb[k] = __builtin_amdgcn_raw_buffer_load_b16(rsc, vc, row * 2, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int kk = 16 * hh + k;
+          uint16_t v;
+          gu[kk] = swiglu_bwd<GEGLU>(on_i, dv[k], bf16_to_f32(gb[k]), bf16_to_f32(ub[k]), a, has_ga,
+                                     bf16_to_f32(gab[k]), has_in, bf16_to_f32(inb[k]), has_sc, scb[k], daff, v);
+          put_it(kk, v);
+          amg = fmaxf(amg, fabsf(lo_bf16(gu[kk])));
+          amu = fmaxf(amu, fabsf(hi_bf16(gu[kk])));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#endif
+    if (rows) {
+      // I-axis groups: the thread's 32 rows are one group of dGate and one of dUp
+      const int Xg = scale_exp<FG>(__float_as_uint(amg)), Xu = scale_exp<FG>(__float_as_uint(amu));
+      const float ig = inv_scale(Xg), iu = inv_scale(Xu);
+      uint32_t wg[8], wu[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        wg[k] = encode4<FG>(lo_bf16(gu[4 * k]), lo_bf16(gu[4 * k + 1]), lo_bf16(gu[4 * k + 2]), lo_bf16(gu[4 * k + 3]),
+                            ig);
+        wu[k] = encode4<FG>(hi_bf16(gu[4 * k]), hi_bf16(gu[4 * k + 1]), hi_bf16(gu[4 * k + 2]), hi_bf16(gu[4 * k + 3]),
+                            iu);
+      }
+      uint4* rg = reinterpret_cast<uint4*>(p.dgu_row_codes + slot * twoI + i0);
+      uint4* ru = reinterpret_cast<uint4*>(p.dgu_row_codes + slot * twoI + p.I + i0);
+      rg[0] = uint4{wg[0], wg[1], wg[2], wg[3]};
+      rg[1] = uint4{wg[4], wg[5], wg[6], wg[7]};
+      ru[0] = uint4{wu[0], wu[1], wu[2], wu[3]};
+      ru[1] = uint4{wu[4], wu[5], wu[6], wu[7]};
+      const int64_t gg = i0 / 32, gu_ = (p.I + i0) / 32;
+      if (p.dgu_row_pairs) {   // pair-major [2I/128][P][4]
+        p.dgu_row_scales[((gg >> 2) * P + slot) * 4 + (gg & 3)] = uint8_t(Xg + 127);
+        p.dgu_row_scales[((gu_ >> 2) * P + slot) * 4 + (gu_ & 3)] = uint8_t(Xu + 127);
+      } else {                 // row-major [P][2I/32]
+        p.dgu_row_scales[slot * (twoI / 32) + gg] = uint8_t(Xg + 127);
+        p.dgu_row_scales[slot * (twoI / 32) + gu_] = uint8_t(Xu + 127);
+      }
+      p.daff_part[(i0 / 32) * P + slot] = daff;   // this 32-row group's share of d(a)
+      // staging for the slot-axis groups: consecutive threads, consecutive slots
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        stg_gu[(r0 + k) * GSW + (sl >> 5) * 33 + (sl & 31)] = gu[k];
+        stg_in[(r0 + k) * ISH + (sl >> 5) * 34 + (sl & 31)] = uint16_t(itp[k >> 1] >> (16 * (k & 1)));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- pass 2: thread = row r x 32-slot group c ---------------------------------------
+  {
+    const int r = t / NG, c = t % NG;
+    const int64_t i = ti0 + (r >> 5) * gstride + (r & 31);
+    if (i < p.I) {
+      const int64_t p0 = sbase + s0 + 32 * c;
+      const uint32_t* src = stg_gu + r * GSW + 33 * c;
+      uint32_t mg = 0, mu = 0;
+      float sg = 0.f, su = 0.f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const uint32_t x = src[k];
+        mg = max(mg, (x << 16) & 0x7fffffffu);
+        mu = max(mu, x & 0x7fff0000u);
+        if (p.has_bias) {
+          sg += __uint_as_float(x << 16);
+          su += __uint_as_float(x & 0xffff0000u);
+        }
+      }
+      const int Xg = scale_exp<FG>(mg), Xu = scale_exp<FG>(mu);
+      const float ig = inv_scale(Xg), iu = inv_scale(Xu);
+      uint32_t cg[8], cu[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t x0 = src[4 * k], x1 = src[4 * k + 1], x2 = src[4 * k + 2], x3 = src[4 * k + 3];
+        cg[k] = encode4<FG>(lo_bf16(x0), lo_bf16(x1), lo_bf16(x2), lo_bf16(x3), ig);
+        cu[k] = encode4<FG>(hi_bf16(x0), hi_bf16(x1), hi_bf16(x2), hi_bf16(x3), iu);
+      }
+      uint4* og = reinterpret_cast<uint4*>(p.dgu_tok_codes + i * P + p0);
+      uint4* ou = reinterpret_cast<uint4*>(p.dgu_tok_codes + (p.I + i) * P + p0);
+      og[0] = uint4{cg[0], cg[1], cg[2], cg[3]};
+      og[1] = uint4{cg[4], cg[5], cg[6], cg[7]};
+      ou[0] = uint4{cu[0], cu[1], cu[2], cu[3]};
+      ou[1] = uint4{cu[4], cu[5], cu[6], cu[7]};
+      const int64_t g32 = p0 / 32;   // pair-major [P/128][2I][4]
+      p.dgu_tok_scales[((g32 >> 2) * twoI + i) * 4 + (g32 & 3)] = uint8_t(Xg + 127);
+      p.dgu_tok_scales[((g32 >> 2) * twoI + p.I + i) * 4 + (g32 & 3)] = uint8_t(Xu + 127);
+      if (p.has_bias) {   // the row's NG groups sit in consecutive lanes: one atomic per row
+        for (int o = 1; o < NG; o <<= 1) {
+          sg += __shfl_xor(sg, o, 64);
+          su += __shfl_xor(su, o, 64);
+        }
+        if (c == 0) {
+          atomicAdd(p.db1_acc + (e * 2 + 0) * p.I + i, sg);
+          atomicAdd(p.db1_acc + (e * 2 + 1) * p.I + i, su);
+        }
+      }
+      // the intermediate operand (activation format)
+      const uint16_t* isrc = stg_in + r * ISH + 34 * c;
+      uint32_t mi = 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) mi = max(mi, (uint32_t(isrc[k]) << 16) & 0x7fffffffu);
+      const bool e5 = p.fmt_act == kE5M2;   // uniform
+      const int Xi = e5 ? scale_exp<kE5M2>(mi) : scale_exp<kE4M3>(mi);
+      const float ii = inv_scale(Xi);
+      uint32_t ci[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float v0 = bf16_to_f32(isrc[4 * k]), v1 = bf16_to_f32(isrc[4 * k + 1]);
+        const float v2 = bf16_to_f32(isrc[4 * k + 2]), v3 = bf16_to_f32(isrc[4 * k + 3]);
+        ci[k] = e5 ? encode4<kE5M2>(v0, v1, v2, v3, ii) : encode4<kE4M3>(v0, v1, v2, v3, ii);
+      }
+      uint4* oi = reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + p0);
+      oi[0] = uint4{ci[0], ci[1], ci[2], ci[3]};
+      oi[1] = uint4{ci[4], ci[5], ci[6], ci[7]};
+      p.inter_tok_scales[((g32 >> 2) * p.I + i) * 4 + (g32 & 3)] = uint8_t(Xi + 127);   // [P/128][I][4]
+    }
+  }
+}
+
+}  // namespace mx
