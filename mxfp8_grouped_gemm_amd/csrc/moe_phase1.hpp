@@ -62,7 +62,8 @@ __device__ __forceinline__ void phase1_ring_product(const Phase1Args& p, int64_t
 // ---------------------------------------------------------------------------
 // One 256-thread workgroup per tile; the tile's fp32 result goes straight to
 // dS: lane (r, h) of a fragment holds slot column r and 16 of its 32 rows, so
-// each store instruction writes two 128-byte row segments.
+// each store instruction writes two 128-byte row segments (with the
+// nontemporal hint: whole lines, read back once by the epilogue).
 template <int BM, int BN, int FG, int FW, bool GENERIC>
 __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   // GENERIC: H not a multiple of 128 (v2 loop on the bf16 values); otherwise a
@@ -105,7 +106,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
     if (i0 < p.I) {
       v2::static_for<16>([&](auto Q) {
         float* row = ds + (m0 + v2::acc_row<BM, BN>(FI, Q)) * p.B + n0;
-        v2::static_for<FN>([&](auto FJ) { row[v2::acc_col<BM, BN>(FJ)] = acc[FI][FJ][int(Q)]; });
+        v2::static_for<FN>([&](auto FJ) { store_nt(row + v2::acc_col<BM, BN>(FJ), acc[FI][FJ][int(Q)]); });
       });
     }
   });

@@ -17,6 +17,20 @@ namespace mx {
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;
 
+// Stores with the nontemporal hint (streaming: written lines are not kept in
+// the caches as if they would be read again soon), for results written once
+// and read, if at all, only after far more data than L2 and the infinity cache
+// hold has passed through them.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, static_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_nt(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, static_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(uint32_t(b) << 16);
 }
