@@ -23,6 +23,7 @@ constexpr int kE5M2 = 1;
 // hold has passed through them.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_nt(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, static_cast<u32x4_t*>(p));
 }

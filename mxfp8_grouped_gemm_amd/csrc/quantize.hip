@@ -162,6 +162,43 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
   }
 }
 
+// The 32 rows row0 .. row0 + 31 of columns colA, colA + 1 (w[r]: bf16 of colA
+// in the low half, colA + 1 in the high half) as one scale group each: codes
+// to codes_t [cols][rows], scale bytes to scales_t.
+template <int FMT, bool PAIRS>
+__device__ __forceinline__ void tok_encode_pair(const uint32_t (&w)[32], int64_t rows, int64_t cols, int64_t colA,
+                                                int64_t row0, uint8_t* __restrict__ codes_t,
+                                                uint8_t* __restrict__ scales_t) {
+  uint32_t m = 0;   // |bf16| maxima of both columns
+#pragma unroll
+  for (int r = 0; r < 32; ++r) m = absmax_bf16x2(m, w[r]);
+  const int X0 = scale_exp<FMT>(m << 16), X1 = scale_exp<FMT>(m & 0xffff0000u);
+  const uint32_t lim = bf16_limit<FMT>(X0) | (bf16_limit<FMT>(X1) << 16);
+  const float s0 = cvt_scale(X0), s1 = cvt_scale(X1);
+  uint32_t p0[8], p1[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t w0 = clamp_bf16x2(w[4 * q], lim), w1 = clamp_bf16x2(w[4 * q + 1], lim);
+    const uint32_t w2 = clamp_bf16x2(w[4 * q + 2], lim), w3 = clamp_bf16x2(w[4 * q + 3], lim);
+    p0[q] = encode_bf16x4<FMT>(lo_halves(w0, w1), lo_halves(w2, w3), s0);
+    p1[q] = encode_bf16x4<FMT>(hi_halves(w0, w1), hi_halves(w2, w3), s1);
+  }
+  uint4* dst0 = reinterpret_cast<uint4*>(codes_t + colA * rows + row0);
+  uint4* dst1 = reinterpret_cast<uint4*>(codes_t + (colA + 1) * rows + row0);
+  dst0[0] = make_uint4(p0[0], p0[1], p0[2], p0[3]);
+  dst0[1] = make_uint4(p0[4], p0[5], p0[6], p0[7]);
+  dst1[0] = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+  dst1[1] = make_uint4(p1[4], p1[5], p1[6], p1[7]);
+  if (PAIRS) {
+    const int64_t g = row0 / 32;
+    scales_t[((g >> 2) * cols + colA) * 4 + (g & 3)] = uint8_t(X0 + 127);
+    scales_t[((g >> 2) * cols + colA + 1) * 4 + (g & 3)] = uint8_t(X1 + 127);
+  } else {
+    scales_t[colA * (rows / 32) + row0 / 32] = uint8_t(X0 + 127);
+    scales_t[(colA + 1) * (rows / 32) + row0 / 32] = uint8_t(X1 + 127);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // quant_tok: a workgroup covers 128 logical rows x 128 columns; wave w takes
 // rows 32w .. 32w+31 (one scale group) and lane l the column pair 2l, 2l+1.
@@ -287,34 +324,7 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
       atomicAdd(bias.db2_acc + e * cols + int64_t(blockIdx.x) * kTokCols + threadIdx.x, t);
     }
   }
-  uint32_t m = 0;   // |bf16| maxima of both columns
-#pragma unroll
-  for (int r = 0; r < 32; ++r) m = absmax_bf16x2(m, w[r]);
-  const int X0 = scale_exp<FMT>(m << 16), X1 = scale_exp<FMT>(m & 0xffff0000u);
-  const uint32_t lim = bf16_limit<FMT>(X0) | (bf16_limit<FMT>(X1) << 16);
-  const float s0 = cvt_scale(X0), s1 = cvt_scale(X1);
-  uint32_t p0[8], p1[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint32_t w0 = clamp_bf16x2(w[4 * q], lim), w1 = clamp_bf16x2(w[4 * q + 1], lim);
-    const uint32_t w2 = clamp_bf16x2(w[4 * q + 2], lim), w3 = clamp_bf16x2(w[4 * q + 3], lim);
-    p0[q] = encode_bf16x4<FMT>(lo_halves(w0, w1), lo_halves(w2, w3), s0);
-    p1[q] = encode_bf16x4<FMT>(hi_halves(w0, w1), hi_halves(w2, w3), s1);
-  }
-  uint4* dst0 = reinterpret_cast<uint4*>(codes_t + colA * rows + row0);
-  uint4* dst1 = reinterpret_cast<uint4*>(codes_t + (colA + 1) * rows + row0);
-  dst0[0] = make_uint4(p0[0], p0[1], p0[2], p0[3]);
-  dst0[1] = make_uint4(p0[4], p0[5], p0[6], p0[7]);
-  dst1[0] = make_uint4(p1[0], p1[1], p1[2], p1[3]);
-  dst1[1] = make_uint4(p1[4], p1[5], p1[6], p1[7]);
-  if (PAIRS) {
-    const int64_t g = row0 / 32;
-    scales_t[((g >> 2) * cols + colA) * 4 + (g & 3)] = uint8_t(X0 + 127);
-    scales_t[((g >> 2) * cols + colA + 1) * 4 + (g & 3)] = uint8_t(X1 + 127);
-  } else {
-    scales_t[colA * (rows / 32) + row0 / 32] = uint8_t(X0 + 127);
-    scales_t[(colA + 1) * (rows / 32) + row0 / 32] = uint8_t(X1 + 127);
-  }
+  tok_encode_pair<FMT, PAIRS>(w, rows, cols, colA, row0, codes_t, scales_t);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,7 +442,8 @@ template <int FMT, bool PAIRS>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
                          const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows,
                          const TokBias& b) {
-  if (src_rows * cols * 2 < int64_t(v2::kOOB) && rows <= int64_t(INT32_MAX))
+  const bool off32 = src_rows * cols * 2 < int64_t(v2::kOOB) && rows <= int64_t(INT32_MAX);
+  if (off32)
     tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
   else
     tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
