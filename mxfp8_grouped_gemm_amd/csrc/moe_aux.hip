@@ -43,15 +43,25 @@ hipError_t launch_fill_u32(void* p, int64_t n, uint32_t v, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// moe_build_blocks: the tokens are cut into C chunks (C <= kRouteChunks).
-// Workgroup (e, c) counts the tokens of chunk c routed to expert e; one
-// workgroup turns the counts into each expert's first block and each (e, c)'s
-// first slot; workgroup (e, c) then places its chunk's tokens of expert e in
-// ascending order from there.  (One workgroup per expert scanning all tokens
-// took 80 us of the large workload's step.)  A token is routed to e when any
-// of its K ids is e; negative ids (dropped selections) and ids >= E match
-// nothing.
-constexpr int kRouteChunks = 32;
+// moe_build_blocks: the tokens are cut into C chunks of CH tokens (CH a
+// multiple of 256, C at most route_max_chunks(E)).  The count kernel writes
+// cnt[e * C + c], the tokens of chunk c routed to expert e; one workgroup turns
+// the totals into each expert's first slot first[e] (its first block times B)
+// and the block -> expert map; the place kernel then puts chunk c's tokens of
+// expert e, ascending, from first[e] + (e's tokens in chunks before c) on.
+// (One workgroup per expert scanning all tokens took 80 us of the large
+// workload's step.)  A token is routed to e when any of its K ids is e;
+// negative ids (dropped selections) and ids >= E match nothing.
+//
+// Chunks: one per 256 tokens up to kRouteChunkCap, with E * C at most
+// kRouteCells (the workspace: counts plus first slots, 2 * kRouteCells words
+// at most): more chunks, more workgroups in the count and place kernels.
+constexpr int64_t kRouteChunkCap = 256;
+constexpr int64_t kRouteCells = 4096 * 32;
+static int64_t route_max_chunks(int64_t E) {
+  const int64_t c = kRouteCells / E;
+  return c < 1 ? 1 : (c > kRouteChunkCap ? kRouteChunkCap : c);
+}
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[4]*/, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -92,39 +102,45 @@ __global__ void __launch_bounds__(256) route_count_kernel(const int32_t* __restr
   if (threadIdx.x == 0) cnt[e * C + c] = tot;
 }
 
-// One workgroup: expert e's blocks start after ceil(n_q / B) blocks of every q < e;
-// off[e*C + c] = its first slot + the tokens of e in chunks before c; b2e of used blocks.
+// One workgroup: expert e's blocks start after ceil(n_q / B) blocks of every
+// q < e, n_q the total over the chunks; first[e] = that block times B; b2e of
+// the used blocks.
 __global__ void __launch_bounds__(256) route_offsets_kernel(const int32_t* __restrict__ cnt, int E, int C, int B,
-                                                            int32_t* __restrict__ off, int32_t* __restrict__ b2e) {
+                                                            int32_t* __restrict__ first, int32_t* __restrict__ b2e) {
   __shared__ int red[4];
   int blk = 0;   // first block of the current expert chunk
   for (int e0 = 0; e0 < E; e0 += 256) {
     const int e = e0 + threadIdx.x;
     int n = 0;
-    if (e < E)
+    if (e < E) {
+#pragma unroll 8
       for (int c = 0; c < C; ++c) n += cnt[e * C + c];
+    }
     const int nb = (n + B - 1) / B;
     int tot;
-    const int first = blk + block_exclusive_scan(nb, red, &tot);
+    const int f = blk + block_exclusive_scan(nb, red, &tot);
     if (e < E) {
-      int run = first * B;
-      for (int c = 0; c < C; ++c) {
-        off[e * C + c] = run;
-        run += cnt[e * C + c];
-      }
-      for (int q = 0; q < nb; ++q) b2e[first + q] = e;
+      first[e] = f * B;
+      for (int q = 0; q < nb; ++q) b2e[f + q] = e;
     }
     blk += tot;
   }
 }
 
 __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
-                                                          int64_t CH, int C, const int32_t* __restrict__ off,
+                                                          int64_t CH, int C, const int32_t* __restrict__ cnt,
+                                                          const int32_t* __restrict__ first,
                                                           int32_t* __restrict__ tpid) {
   __shared__ int red[4];
   const int e = blockIdx.x, c = blockIdx.y;
   const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
-  int64_t base = off[e * C + c];
+  int before;   // e's tokens in the chunks before c, summed over the workgroup
+  {
+    int n = 0;
+    for (int q = threadIdx.x; q < c; q += 256) n += cnt[e * C + q];
+    block_exclusive_scan(n, red, &before);
+  }
+  int64_t base = first[e] + before;
   for (int64_t tb = t0; tb < t1; tb += 256) {
     const int64_t t = tb + threadIdx.x;
     const int hit = t < t1 ? routed_to(topk, t, K, e) : 0;
@@ -152,6 +168,16 @@ __device__ __forceinline__ int route_sel(const int32_t* __restrict__ ids, int K,
   return e;
 }
 
+// The same for a token whose K <= kRouteRegK ids sit in registers.
+constexpr int kRouteRegK = 16;
+__device__ __forceinline__ int route_sel_reg(const int (&ids)[kRouteRegK], int k, int E) {
+  const int e = ids[k];
+  if (e < 0 || e >= E) return -1;
+  for (int j = 0; j < k; ++j)
+    if (ids[j] == e) return -1;
+  return e;
+}
+
 __global__ void __launch_bounds__(256) route_count_lds_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
                                                               int64_t CH, int C, int E, int32_t* __restrict__ cnt) {
   __shared__ int hist[kRouteLdsExperts];
@@ -159,38 +185,70 @@ __global__ void __launch_bounds__(256) route_count_lds_kernel(const int32_t* __r
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256)
-    for (int k = 0; k < K; ++k) {
-      const int e = route_sel(topk + t * K, K, k, E);
-      if (e >= 0) atomicAdd(&hist[e], 1);
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) {
+    if (K <= kRouteRegK) {
+      int ids[kRouteRegK];
+      for (int k = 0; k < K; ++k) ids[k] = topk[t * K + k];
+      for (int k = 0; k < K; ++k) {
+        const int e = route_sel_reg(ids, k, E);
+        if (e >= 0) atomicAdd(&hist[e], 1);
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const int e = route_sel(topk + t * K, K, k, E);
+        if (e >= 0) atomicAdd(&hist[e], 1);
+      }
     }
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) cnt[e * C + c] = hist[e];
 }
 
 __global__ void __launch_bounds__(256) route_place_lds_kernel(const int32_t* __restrict__ topk, int64_t T, int K,
                                                               int64_t CH, int C, int E,
-                                                              const int32_t* __restrict__ off,
+                                                              const int32_t* __restrict__ cnt,
+                                                              const int32_t* __restrict__ first,
                                                               int32_t* __restrict__ tpid) {
   __shared__ uint32_t bits[kRouteLdsExperts][8];   // [expert][round token / 32]
   __shared__ int run[kRouteLdsExperts];            // next slot of (expert, this chunk)
   const int c = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) run[e] = off[e * C + c];
+  // first slots: first[e] plus the counts of the chunks before c.  With E <
+  // 256, tpe = 256 / E (a power of two) consecutive lanes share an expert,
+  // each summing every tpe-th of those counts, then adding up across the lanes.
+  {
+    int tpe = 1;
+    while (tpe * 2 * E <= 256 && tpe < 64) tpe *= 2;
+    for (int e0 = 0; e0 < E; e0 += 256 / tpe) {
+      const int e = e0 + tid / tpe, j = tid % tpe;
+      int n = 0;
+      if (e < E) {
+#pragma unroll 8
+        for (int q = j; q < c; q += tpe) n += cnt[e * C + q];
+      }
+      for (int o = 1; o < tpe; o <<= 1) n += __shfl_xor(n, o, 64);
+      if (e < E && j == 0) run[e] = first[e] + n;
+    }
+  }
+  __syncthreads();
   const int64_t t0 = int64_t(c) * CH, t1 = t0 + CH < T ? t0 + CH : T;
   for (int64_t tb = t0; tb < t1; tb += 256) {
     for (int i = tid; i < E * 8; i += 256) bits[i >> 3][i & 7] = 0u;
     __syncthreads();
     const int64_t t = tb + tid;
     const bool live = t < t1;
+    const bool reg = K <= kRouteRegK;
+    int ids[kRouteRegK];
+    if (live && reg)
+      for (int k = 0; k < K; ++k) ids[k] = topk[t * K + k];
     if (live)
       for (int k = 0; k < K; ++k) {
-        const int e = route_sel(topk + t * K, K, k, E);
+        const int e = reg ? route_sel_reg(ids, k, E) : route_sel(topk + t * K, K, k, E);
         if (e >= 0) atomicOr(&bits[e][tid >> 5], 1u << (tid & 31));
       }
     __syncthreads();
     if (live)
       for (int k = 0; k < K; ++k) {
-        const int e = route_sel(topk + t * K, K, k, E);
+        const int e = reg ? route_sel_reg(ids, k, E) : route_sel(topk + t * K, K, k, E);
         if (e >= 0) {
           int rank = __popc(bits[e][tid >> 5] & ((1u << (tid & 31)) - 1u));
           for (int w = 0; w < (tid >> 5); ++w) rank += __popc(bits[e][w]);
@@ -207,7 +265,7 @@ __global__ void __launch_bounds__(256) route_place_lds_kernel(const int32_t* __r
   }
 }
 
-int64_t build_blocks_workspace_bytes(int64_t E) { return E > 0 ? 2 * E * kRouteChunks * 4 : 0; }
+int64_t build_blocks_workspace_bytes(int64_t E) { return E > 0 ? 2 * E * route_max_chunks(E) * 4 : 0; }
 
 // The allocation-free variant's scratch: the counts and first slots per
 // (expert, token chunk) for up to kNoAllocMaxExperts experts, 1 MiB per GPU,
@@ -215,8 +273,9 @@ int64_t build_blocks_workspace_bytes(int64_t E) { return E > 0 ? 2 * E * kRouteC
 // routing kernels read is written by an earlier one in the same call, so the
 // array needs no clearing; calls that overlap on one GPU share it and race.
 constexpr int64_t kNoAllocMaxExperts = 4096;
-static __device__ __align__(256) int32_t scratch[2 * kNoAllocMaxExperts * kRouteChunks];
-static_assert(sizeof(scratch) == 2 * kNoAllocMaxExperts * kRouteChunks * 4, "scratch size");
+static __device__ __align__(256) int32_t scratch[2 * kRouteCells];
+static_assert(sizeof(scratch) == (1 << 20), "scratch size");
+static_assert(kNoAllocMaxExperts * 32 == kRouteCells, "the workspace of up to kNoAllocMaxExperts experts fits");
 
 int64_t build_blocks_noalloc_max_experts() { return kNoAllocMaxExperts; }
 
@@ -255,21 +314,22 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
   if ((err = launch_fill_u32(tpid, N * B, 0xffffffffu, st)) != hipSuccess) return err;
   if ((err = launch_fill_u32(b2e, N, uint32_t(E - 1), st)) != hipSuccess) return err;
   if (T <= 0) return hipSuccess;
-  // chunks of a multiple of 256 tokens, at most kRouteChunks of them
-  const int64_t per = (T + kRouteChunks - 1) / kRouteChunks;
+  // chunks of a multiple of 256 tokens, at most route_max_chunks(E) of them
+  const int64_t cmax = route_max_chunks(E);
+  const int64_t per = (T + cmax - 1) / cmax;
   const int64_t CH = (per + 255) / 256 * 256;
   const int C = int((T + CH - 1) / CH);
-  int32_t* cnt = ws;
-  int32_t* off = ws + E * kRouteChunks;
+  int32_t* cnt = ws;               // [E][C]
+  int32_t* first = ws + E * C;     // [E]; E * C + E <= 2 * E * cmax
   if (E <= kRouteLdsExperts) {
     route_count_lds_kernel<<<unsigned(C), 256, 0, st>>>(topk, T, int(K), CH, C, int(E), cnt);
-    route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), off, b2e);
-    route_place_lds_kernel<<<unsigned(C), 256, 0, st>>>(topk, T, int(K), CH, C, int(E), off, tpid);
+    route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), first, b2e);
+    route_place_lds_kernel<<<unsigned(C), 256, 0, st>>>(topk, T, int(K), CH, C, int(E), cnt, first, tpid);
     return hipGetLastError();
   }
   route_count_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, cnt);
-  route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), off, b2e);
-  route_place_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, off, tpid);
+  route_offsets_kernel<<<1, 256, 0, st>>>(cnt, int(E), C, int(B), first, b2e);
+  route_place_kernel<<<dim3(unsigned(E), unsigned(C)), 256, 0, st>>>(topk, T, int(K), CH, C, cnt, first, tpid);
   return hipGetLastError();
 }
 
