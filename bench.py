@@ -139,6 +139,11 @@ def stage_work(cfg, N):
     T, H, I, E, K, B = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.B
     TK, P = T * K, N * B
     q = 1 + 1 / 32                      # bytes per quantised element (code + its share of a scale)
+    # stages that another one does (their own launch is then empty): the bias
+    # reductions inside the dY gather (a bias, H % 128 == 0), the epilogue inside
+    # Phase 1's kernel (H % 128 == 0, H <= 2048, I <= 512; no optional checkpoints here)
+    bias_fused = cfg.has_bias and H % 128 == 0
+    epi_fused = H % 128 == 0 and H <= 2048 and I <= 512
     return {
         # slot routing info (token, affinity, the (token, expert) -> slot map, block
         # extents and lists) and the zeroed per-slot d(a) bias term
@@ -149,11 +154,11 @@ def stage_work(cfg, N):
         "quantize_dy": ("hbm", T * H * (2 + q) + E * H * 2 * I / 32 * 2
                         + (E * I * H / 32 * 2 if H % 128 == 0 else T * H * 2 + E * I * H * (q + 2))),
         "gather_quantize_x_dy": ("hbm", 2 * (TK * H * 2 + P * H * q)),
-        "bias": ("hbm", 2 * TK * H * 2 if cfg.has_bias else 0),
+        "bias": ("hbm", 2 * TK * H * 2 if cfg.has_bias and not bias_fused else 0),
         "phase1": ("mfma_bf16", 2 * TK * H * I),
         # per (pair, i): reads g, u and dS; writes dGU quantised along both axes and
         # the intermediate quantised
-        "phase1_epilogue": ("hbm", TK * I * (4 + 4 + 5 * q)),
+        "phase1_epilogue": ("hbm", 0 if epi_fused else TK * I * (4 + 4 + 5 * q)),
         "phase3": ("mfma", 4 * TK * H * I),
         "phase2": ("mfma", 4 * TK * H * I),
         "phase4": ("mfma", 2 * TK * H * I),
