@@ -159,8 +159,10 @@ typedef struct {
 int matmul_mxfp8_bwd_ex(const matmul_mxfp8_bwd_args* args, void* workspace, size_t workspace_bytes,
                         void* stream);
 /* Profiling aid: one stage of matmul_mxfp8_bwd on a workspace a full call has
- * filled: 0 quantise dY along N and W along N, 1 quantise dY and X along M,
- * 2 the dX GEMM, 3 the dW GEMM.  INVALID_ARG for another stage. */
+ * filled: 0 quantise dY along N and W along N (and dY along M as well when
+ * one pass does both: M % 32 == 0, N % 512 == 0), 1 quantise X (and dY, if
+ * stage 0 did not) along M, 2 the dX GEMM, 3 the dW GEMM.  INVALID_ARG for
+ * another stage. */
 int matmul_mxfp8_bwd_stage(const uint16_t* output_grad, const uint16_t* weights,
                            const uint16_t* input_activation, int64_t M, int64_t N, int64_t K,
                            int fmt_output_grad, int fmt_weights, int fmt_input,

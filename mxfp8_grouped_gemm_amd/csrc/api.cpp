@@ -175,10 +175,14 @@ static int dense_run(const matmul_mxfp8_bwd_args* a, void* ws, size_t ws_bytes, 
   }
   const uint16_t* dy = a->output_grad;
   const int fdy = a->fmt_output_grad, fw = a->fmt_weights, fx = a->fmt_input;
+  // dY along both axes from one read where the shapes allow (stage 0 then makes stream 2 too)
+  const bool dual = !pc[0] && !pc[2] && mx::quant_dual_fits(M, N);
   auto prep = [&](int i) -> hipError_t {
     const bool pairs = kdim[i] % 128 == 0;
     uint8_t* wc = base + off[2 * i];
     uint8_t* wsc = base + off[2 * i + 1];
+    if (dual && i == 0) return mx::launch_quant_dual(dy, M, N, fdy, wc, wsc, base + off[4], base + off[5], st);
+    if (dual && i == 2) return hipSuccess;
     if (!pc[i]) {   // quantise from bf16 along the contraction
       switch (i) {
         case 0: return mx::launch_quant_rows(dy, M, N, fdy, wc, wsc, st, nullptr, pairs);

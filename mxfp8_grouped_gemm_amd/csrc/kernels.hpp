@@ -26,6 +26,11 @@ struct TokBias {
   float* db2_acc;
   float* part;             // null: no bias work
 };
+// x [rows][cols] along both axes in one pass, the same bytes as launch_quant_rows
+// (pairs) and launch_quant_tok (no index) each give: rows % 32 == 0, cols % 512 == 0
+bool quant_dual_fits(int64_t rows, int64_t cols);
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
+                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st);
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
                             uint8_t* scales_t, hipStream_t st, bool pairs = false, bool self_rows = false,

@@ -328,6 +328,69 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// quant_dual: one matrix [rows][cols] quantised along both axes from one read,
+// as quant_rows (groups of 32 along a row: codes [rows][cols], scales
+// pair-major [cols/128][rows][4]) and quant_tok without an index (groups of
+// 32 along a column: codes_t [cols][rows], scales_t pair-major
+// [rows/128][cols][4], or [cols][rows/32] when rows % 128 != 0), bit for bit.
+// Wave w of a workgroup takes rows 32w .. 32w+31 of its 128, lane l columns
+// 8l .. 8l+7 of its 512: 32 loads of 16 bytes, then the row groups (4 lanes
+// each) and the column groups (a lane's 8 columns over the wave's 32 rows)
+// from the same registers.  rows % 32 == 0, cols % 512 == 0.
+constexpr int kDualCols = 512;
+
+template <int FMT, bool PAIRS_T>
+__global__ void __launch_bounds__(256) quant_dual_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                          uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                          uint8_t* __restrict__ codes_t,
+                                                          uint8_t* __restrict__ scales_t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = int64_t(blockIdx.y) * 128 + (threadIdx.x >> 6) * 32;
+  if (row0 >= rows) return;   // a partial last workgroup of rows (no barrier below)
+  const int64_t col0 = int64_t(blockIdx.x) * kDualCols + 8 * lane;
+  uint32_t w[32][4];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (row0 + r) * cols + col0);
+    w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+  }
+  // groups along the rows: this lane's 8 values and its 3 neighbours' (quant_rows)
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      amax = max(amax, abs_bits_bf16(uint16_t(w[r][k] & 0xffffu)));
+      amax = max(amax, abs_bits_bf16(uint16_t(w[r][k] >> 16)));
+    }
+    amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
+    amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
+    const int X = scale_exp<FMT>(amax);
+    const float inv = inv_scale(X);
+    uint32_t out[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      out[k] = encode4<FMT>(__uint_as_float(w[r][2 * k] << 16), __uint_as_float(w[r][2 * k] & 0xffff0000u),
+                            __uint_as_float(w[r][2 * k + 1] << 16), __uint_as_float(w[r][2 * k + 1] & 0xffff0000u),
+                            inv);
+    const int64_t row = row0 + r;
+    codes[(row * cols + col0) / 8] = make_uint2(out[0], out[1]);
+    if ((lane & 3) == 0) {   // group g of the row -> word (g / 4, row), byte g % 4
+      const int64_t g = col0 / 32;
+      scales[((g >> 2) * rows + row) * 4 + (g & 3)] = uint8_t(X + 127);
+    }
+  }
+  // groups along the columns: the lane's four column pairs (quant_tok)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t wq[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) wq[r] = w[r][q];
+    tok_encode_pair<FMT, PAIRS_T>(wq, rows, cols, col0 + 2 * q, row0, codes_t, scales_t);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row-major scales of `groups` matrices [rows][k/32] -> pair-major
 // [groups][k/128][rows][4]; k % 128 == 0.  A transpose of 4-byte words
 // ([rows][kp] -> [kp][rows] per group) through LDS: a workgroup moves 64 rows x
@@ -470,6 +533,26 @@ hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, c
   } else {
     if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
     else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
+  }
+  return hipGetLastError();
+}
+
+bool quant_dual_fits(int64_t rows, int64_t cols) {
+  return rows > 0 && cols > 0 && rows % 32 == 0 && cols % kDualCols == 0 && (rows + 127) / 128 <= 65535;
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
+                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st) {
+  if (!quant_dual_fits(rows, cols)) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(cols / kDualCols), unsigned((rows + 127) / 128));
+  uint2* cs = reinterpret_cast<uint2*>(codes);
+  const bool pt = rows % 128 == 0;
+  if (fmt == kE4M3) {
+    if (pt) quant_dual_kernel<kE4M3, true><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
+    else quant_dual_kernel<kE4M3, false><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
+  } else {
+    if (pt) quant_dual_kernel<kE5M2, true><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
+    else quant_dual_kernel<kE5M2, false><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
   }
   return hipGetLastError();
 }

@@ -25,8 +25,11 @@ def _inputs(M, N, K, seed):
     return S.dense_tensors(cfg, "cuda")
 
 
+# N % 512 == 0 with M % 32 == 0 takes the one-pass dual-axis dY quantiser: M a
+# multiple of 128 (pair-major dY^T scales) or not, and a partial last row tile
 @pytest.mark.parametrize("M,N,K", [(64, 96, 128), (256, 320, 192), (96, 160, 544), (512, 384, 640),
-                                   (32, 32, 32), (288, 544, 96)])
+                                   (32, 32, 32), (288, 544, 96), (256, 1024, 96), (96, 512, 160),
+                                   (160, 512, 64)])
 def test_dense_small_full_parity(M, N, K):
     mx = _mx()
     t = _inputs(M, N, K, seed=M + N + K)
@@ -61,7 +64,7 @@ def test_dense_small_full_parity(M, N, K):
 @pytest.mark.parametrize("fdy,fw,fx", [(0, 0, 0), (1, 1, 1), (0, 1, 1), (1, 0, 1)])
 def test_dense_format_combinations(fdy, fw, fx):
     mx = _mx()
-    M, N, K = 192, 256, 320
+    M, N, K = 192, 512, 320
     t = _inputs(M, N, K, seed=3)
     dx, dw = mx.matmul_mxfp8_bwd(t["dy"], t["w"], t["x"], fdy, fw, fx)
     rdx, rdw = oracle.dense_bwd(*(S.bf16_bits(t[k]) for k in ("dy", "w", "x")), fmt_dy=fdy, fmt_w=fw, fmt_x=fx)
