@@ -346,7 +346,8 @@ def run_dense(reps):
            "dW_gemm": roofline_of("mfma", gemm_flops, st[3]) | {"ms": round(st[3], 4)},
            "quantize_N_ms": round(st[0], 4), "quantize_M_ms": round(st[1], 4)}
     x = S.normal_bf16((4096, 4096), 1.0, 0, 99, "cuda")
-    qms = _events_ms(lambda: mx.mxfp8_quantize(x, 1, mx.E4M3), reps)
+    qout = mx.mxfp8_quantize(x, 1, mx.E4M3)   # outputs allocated once, outside the timed calls
+    qms = _events_ms(lambda: mx.mxfp8_quantize(x, 1, mx.E4M3, out=qout), reps)
     qbytes = 4096 * 4096 * (2 + 1 + 1 / 32)
     res_q = {"shape": [4096, 4096], "axis": 1, "ms": round(qms, 5), **roofline_of("hbm", qbytes, qms)}
     return res, res_q

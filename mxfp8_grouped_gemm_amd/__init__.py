@@ -133,15 +133,23 @@ def _dev(t: Optional[torch.Tensor], dtype, name):
 
 
 # ----------------------------------------------------------------------------- quantiser
-def mxfp8_quantize(x: torch.Tensor, axis: int = 1, fmt: int = E4M3):
+def mxfp8_quantize(x: torch.Tensor, axis: int = 1, fmt: int = E4M3, out=None):
     """x [rows, cols] bf16 -> (codes uint8 [rows, cols], scales uint8 E8M0).
 
     axis 1: groups of 32 along cols, scales [rows, cols/32];
-    axis 0: groups of 32 along rows, scales [rows/32, cols]."""
+    axis 0: groups of 32 along rows, scales [rows/32, cols].
+    out: optional (codes, scales) of those shapes to write into."""
     rows, cols = x.shape
-    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     sshape = (rows, cols // 32) if axis == 1 else (rows // 32, cols)
-    scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    if out is not None:
+        codes, scales = out
+        if tuple(codes.shape) != (rows, cols) or tuple(scales.shape) != sshape or \
+                codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or \
+                not codes.is_contiguous() or not scales.is_contiguous():
+            raise ValueError("mxfp8_quantize: out must be contiguous uint8 tensors of the codes' and scales' shapes")
+    else:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
     _check(lib().mxfp8_quantize(_dev(x, torch.bfloat16, "x"), rows, cols, axis, fmt, codes.data_ptr(),
                                 scales.data_ptr(), _stream(x)), "mxfp8_quantize")
     return codes, scales
