@@ -179,3 +179,15 @@ def test_matmul_bwd_ex_validation_without_gpu():
              output_grad_codes_m=f, output_grad_scales_m=f, weight_codes=f, weight_scales=f, input_codes=f,
              input_scales=f)
     assert L.matmul_mxfp8_bwd_ex(C.byref(a), C.c_void_p(f), 16, None) == 3
+
+
+def test_quantize_out_must_match_the_outputs():
+    """mxfp8_quantize(out=...) checks the given buffers before any library call."""
+    import torch
+    import mxfp8_grouped_gemm_amd as mx
+    x = torch.zeros((64, 128), dtype=torch.bfloat16)
+    good = (torch.empty((64, 128), dtype=torch.uint8), torch.empty((64, 4), dtype=torch.uint8))
+    for bad in ((good[0][:, :64], good[1]), (good[0], torch.empty((64, 4), dtype=torch.int32)),
+                (good[0], torch.empty((2, 128), dtype=torch.uint8)), (good[0].t(), good[1])):
+        with pytest.raises(ValueError):
+            mx.mxfp8_quantize(x, 1, mx.E4M3, out=bad)
