@@ -360,7 +360,14 @@ int moe_bwd_mxfp8_workspace_query(const moe_bwd_mxfp8_args* args,
 /* Host.  Workspace size in bytes (0 on invalid shapes). */
 size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
 
-/* Enqueues the whole backward.  Errors: INVALID_ARG (shapes, null required
+/* Enqueues the whole backward on `stream`.  When Phase 3 has between one and
+ * eight rounds of tiles over the device's CUs, part of the work (the
+ * token-axis gathers and Phases 2 and 4) runs on a second stream that the
+ * library creates once per device (default priority) and keeps; `stream`
+ * waits for it before the call returns, so work enqueued on `stream` later is
+ * ordered after the whole backward, as with one stream.  Host threads that
+ * call this on one device at the same time are serialised while they enqueue.
+ * Errors: INVALID_ARG (shapes, null required
  * pointers, alignment, formats, accumulate or activation outside {0,1}), UNSUPPORTED
  * (block_size outside the set, affinity on I together with a bias, or sizes
  * beyond 32-bit indexing: N * block_size or T * E above 2^31 - 1, a [T,H] bf16

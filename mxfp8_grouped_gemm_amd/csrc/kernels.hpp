@@ -180,5 +180,7 @@ struct Phase3Args {
   int tiles_m, tiles_n;
 };
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st);
+// Phase 3 tiles when every slot tile of every block is live (an upper bound)
+int64_t phase3_max_tiles(const Phase3Args& p);
 
 }  // namespace mx

@@ -169,10 +169,17 @@ static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipS
 // loop at 128 x 256.  A short contraction (2I < 1024: a few ring stages per
 // tile) also takes 128 x 256 tiles: with the rows stored through LDS, they
 // measured 5% faster at 2I = 512 than 128 x 128 tiles at two per CU.
+static bool phase3_wide(const Phase3Args& p) {
+  return (2 * p.I) % v2::BK == 0 && 2 * p.I >= 1024 && p.B >= 256 && p.H >= 256;
+}
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st) {
-  const bool g = (2 * p.I) % v2::BK != 0;
-  if (!g && 2 * p.I >= 1024 && p.B >= 256 && p.H >= 256) return phase3_launch<256, 256>(p, fg, fw, false, st);
-  return phase3_launch<128, 256>(p, fg, fw, g, st);
+  if (phase3_wide(p)) return phase3_launch<256, 256>(p, fg, fw, false, st);
+  return phase3_launch<128, 256>(p, fg, fw, (2 * p.I) % v2::BK != 0, st);
+}
+
+int64_t phase3_max_tiles(const Phase3Args& p) {
+  const int64_t bm = phase3_wide(p) ? 256 : 128, bn = 256;
+  return p.N * ((p.B + bm - 1) / bm) * ((p.H + bn - 1) / bn);
 }
 
 }  // namespace mx

@@ -236,9 +236,13 @@ def test_moe_full_size_sampled(name):
 def test_moe_stages_in_order_equal_one_call():
     """The per-stage entry point: stages 0..NUM_STAGES-1 run in order on a fresh
     workspace produce what one full call produces (bitwise for every output with
-    a fixed summation order; the bias sums use atomics)."""
-    for name in ("medium_s", "fine_s", "fine_h256"):
-        cfg = SMALL[name]
+    a fixed summation order; the bias sums use atomics).  The last two cases have
+    enough Phase-3 tiles (one to eight rounds over the CUs) for a full call to run
+    the gathers and Phases 2 and 4 on the library's second stream."""
+    cases = {**{n: SMALL[n] for n in ("medium_s", "fine_s", "fine_h256")},
+             "medium_2s": S.scaled(S.MEDIUM, T=4096, H=1024, I=704, E=8, K=4, B=256),
+             "fine_2s": S.scaled(S.FINE, T=4096, H=512, I=256, E=32, K=4, B=128)}
+    for name, cfg in cases.items():
         g1 = gpu_problem(cfg)
         o1 = {k: v.clone() for k, v in g1["op"].run().items() if v is not None}
         g2 = gpu_problem(cfg)
