@@ -313,12 +313,12 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *                                                     (H % 128 != 0; else empty)
  *   wd_deq                    [E,I,H] bf16            exact values of the W_down codes
  *                                                     (H % 128 != 0; else empty)
- *   x_tok_codes/scales        [H,P] / P4[P,H]         X along slots (Phase 2), P = N*B
- *   gy_tok_codes/scales       [H,P] / P4[P,H]         a*dY (on H) or dY (on I), Phase 4
- *   inter_tok_codes/scales    [I,P] / P4[P,I]         inter (on H) or a*inter (on I)
- *   dgu_row_codes/scales      [P,2I] / P4[2I,P]       [dGate|dUp] along I (Phase 3);
- *                                                     scales [P,2I/32] when 2I % 128 != 0
- *   dgu_tok_codes/scales      [2I,P] / P4[P,2I]       [dGate;dUp] along slots (Phase 2)
+ *   x_tok_codes/scales        S64[P,H] / P4[P,H]      X along slots (Phase 2), P = N*B
+ *   gy_tok_codes/scales       S64[P,H] / P4[P,H]      a*dY (on H) or dY (on I), Phase 4
+ *   inter_tok_codes/scales    S64[P,I] / P4[P,I]      inter (on H) or a*inter (on I)
+ *   dgu_row_codes/scales      S64[2I,P] / P4[2I,P]    [dGate|dUp] along I (Phase 3);
+ *                                                     [P,2I] / [P,2I/32] when 2I % 128 != 0
+ *   dgu_tok_codes/scales      S64[P,2I] / P4[P,2I]    [dGate;dUp] along slots (Phase 2)
  *   wgu_scales_pairs          P4 of gate_up_scales per expert, [E][2I/128][H][4]
  *                                                     (written when 2I % 128 == 0)
  *   wd_scales_pairs           P4 of down_scales per expert, [E][H/128][I][4]
@@ -345,7 +345,12 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  * P4[K,R] is the pair-major scale layout of an operand with R rows contracted
  * over K elements: [K/128][R][4] bytes, word (p, r) holding row r's E8M0 bytes
  * for elements [128p, 128p+128) (so one stage pair's words for consecutive rows
- * are contiguous).  Pad slots hold code 0.  Rows of a region are contiguous. */
+ * are contiguous).  S64[K,R] is the stage-major code layout of such an
+ * operand: the rows in panels of 256 (the last one holds R % 256 when that is
+ * not 0), panel rows r0 .. r0+n-1 at bytes [r0*K, (r0+n)*K) as [K/64][n][64], so
+ * that code (r, k) sits at r0*K + ((k/64)*n + r - r0)*64 + k%64 (64 elements of
+ * every row of a panel in one contiguous run: whole cache lines per load).
+ * Pad slots hold code 0.  Otherwise, rows of a region are contiguous. */
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
@@ -372,8 +377,9 @@ size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
  * (block_size outside the set, affinity on I together with a bias, or sizes
  * beyond 32-bit indexing: N * block_size or T * E above 2^31 - 1, a [T,H] bf16
  * tensor of 2 GiB or more, i.e. T * H * 2 > 2^31 - 1, which the gathers
- * address through one buffer descriptor, or I * block_size * 4 beyond 2 GiB),
- * WORKSPACE (too small).  Device-side
+ * address through one buffer descriptor, I * block_size * 4 beyond 2 GiB, or a
+ * 256-row panel of a stage-major operand, 256 * N * block_size or 256 * 2I
+ * bytes, beyond 2^32 - 1), WORKSPACE (too small).  Device-side
  * preconditions (not checked): block_to_expert entries in [0,E) (blocks with
  * other values are skipped); each (t,e) pair appears in at most one slot. */
 int moe_bwd_mxfp8(const moe_bwd_mxfp8_args* args, void* workspace, size_t workspace_bytes,

@@ -233,8 +233,13 @@ __global__ void __launch_bounds__(v2::kThreads) gemm_store_ring(GemmStoreArgs p)
   } else {
     v3::Op<BM> A;
     v3::Op<BN> B;
-    v3::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
-    v3::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
+    if (p.stage_major) {
+      v3::setup_rows_sm(A, p.a_codes, tp.m0, p.M, p.M, p.lda);
+      v3::setup_rows_sm(B, p.b_codes, tp.n0, p.N, p.N, p.ldb);
+    } else {
+      v3::setup_rows(A, p.a_codes, tp.m0, p.M, p.lda);
+      v3::setup_rows(B, p.b_codes, tp.n0, p.N, p.ldb);
+    }
     const int nstages = int(kbytes / v3::SK);
     if constexpr (LIST) {
       const v3::KMapList km{p.blk_list, b0, p.blk, 31 - __builtin_clz(unsigned(p.blk / v3::SK))};
@@ -274,6 +279,8 @@ hipError_t launch_gemm_store(GemmStoreArgs p, int groups, int fa, int fb, hipStr
   // every stage full and scale rows 4-byte aligned -> the ring; otherwise the v2 loop
   const bool generic = (p.lda % v2::BK) || (p.ldb % v2::BK) || (!p.blk_list && (p.K % v2::BK)) ||
                        (p.blk_list && (p.blk % v2::BK));
+  // stage-major operands: only the four-slot ring reads them
+  if (p.stage_major && (generic || p.pair)) return hipErrorInvalidValue;
   // larger tiles once there are enough of them to fill the chip
   const bool big = !generic && p.M >= 256 && p.N >= 256 &&
                    ((p.M + 255) / 256) * ((p.N + 255) / 256) * int64_t(groups) >= 200;

@@ -40,6 +40,7 @@
 // compiler keeps this order.
 #pragma once
 #include "gemm_v2.hpp"
+#include "mx_device.hpp"
 
 namespace mx {
 namespace v3 {
@@ -104,10 +105,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // One operand's code rows: buffer and this lane's DMA offsets.  Instruction j
 // of wave w fills rows w*ROWS/4 + 16j .. +16 of a slot; lane l fills row
 // +(l >> 2), physical chunk l & 3, fetching the logical chunk stored there.
+// Two code layouts of an operand with R rows contracted over K bytes:
+//   row-major    [R][K] (kmul == 1): the lane offsets point at K byte 0 of
+//                their rows and a position's K byte kc is the scalar offset;
+//   stage-major  panels of 256 rows, each [K/64][rows][64] (see
+//                stage_major_off; kmul == the tile's panel's rows): the lane
+//                offsets are row * 64 within the panel's first stage, and the
+//                scalar offset kc * kmul moves them to stage kc / 64.
+// Why stage-major: one DMA instruction then reads 1 KB of consecutive bytes,
+// 8 whole 128-byte lines, where 16 rows x 64 bytes of a row-major operand are
+// 16 half lines; the texture path's throughput goes by lines, not bytes
+// (measured on gfx950 with L2-resident data: ~34 B/clk per CU with 64-byte
+// pieces of rows, ~66 B/clk with whole lines).
 template <int ROWS>
 struct Op {
   Buf codes;
   uint32_t off[ROWS / 64];
+  uint32_t kmul;   // scalar offset of K byte kc: kc * kmul
 };
 
 template <int ROWS>
@@ -129,6 +143,7 @@ __device__ __forceinline__ void setup_rows(Op<ROWS>& op, const uint8_t* codes, i
                                            int64_t ld) {
   const int64_t have = nrows - row0 < ROWS ? nrows - row0 : ROWS;
   op.codes = v2::make_rsrc(codes + row0 * ld, uint32_t(have * ld));
+  op.kmul = 1;
 #pragma unroll
   for (int j = 0; j < ROWS / 64; ++j) {
     const int r = dma_row<ROWS>(j);
@@ -137,11 +152,34 @@ __device__ __forceinline__ void setup_rows(Op<ROWS>& op, const uint8_t* codes, i
   }
 }
 
+// Stage-major codes (see Op) of an operand with R rows and K bytes: the
+// tile's rows row0 .. (a multiple of ROWS, so they lie in one panel) of the
+// rows below `limit` (<= R; rows from there on load zeros).  The descriptor
+// covers the panel from the tile's first row on.
+template <int ROWS>
+__device__ __forceinline__ void setup_rows_sm(Op<ROWS>& op, const uint8_t* codes, int64_t row0, int64_t limit,
+                                              int64_t R, int64_t K) {
+  static_assert(kPanelRows % ROWS == 0, "a tile lies in one panel");
+  const int64_t have = limit - row0 < ROWS ? limit - row0 : ROWS;
+  const int64_t p0 = row0 & ~int64_t(kPanelRows - 1);
+  const int64_t rp = R - p0 < kPanelRows ? R - p0 : kPanelRows;
+  const int64_t skip = (row0 - p0) * SK;
+  op.codes = v2::make_rsrc(codes + p0 * K + skip, uint32_t(rp * K - skip));
+  op.kmul = uint32_t(rp);
+#pragma unroll
+  for (int j = 0; j < ROWS / 64; ++j) {
+    const int r = dma_row<ROWS>(j);
+    const int lc = (threadIdx.x & 3) ^ swz(r);
+    op.off[j] = r < have ? uint32_t(r * SK + 16 * lc) : kOOB;
+  }
+}
+
 // Gathered rows: tile row r reads source row rowid(r) (negative: zeros).
 template <int ROWS, class RowId>
 __device__ __forceinline__ void setup_gather(Op<ROWS>& op, const uint8_t* codes, int64_t src_rows, int64_t ld,
                                              const RowId& rowid) {
   op.codes = v2::make_rsrc(codes, uint32_t(src_rows * ld));
+  op.kmul = 1;
 #pragma unroll
   for (int j = 0; j < ROWS / 64; ++j) {
     const int r = dma_row<ROWS>(j);
@@ -316,11 +354,11 @@ struct Ring {
     if (J < FM) {
       v4i ra = dA;
       ra[2] = live ? ra[2] : 0;
-      dma16(ra, cs + uint32_t(wave * (BM / 4) + 16 * J) * SK, x.A.off[J], kc);
+      dma16(ra, cs + uint32_t(wave * (BM / 4) + 16 * J) * SK, x.A.off[J], kc * x.A.kmul);
     } else {
       v4i rb = dB;
       rb[2] = live ? rb[2] : 0;
-      dma16(rb, cs + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc);
+      dma16(rb, cs + uint32_t(BM + wave * (BN / 4) + 16 * (J - FM)) * SK, x.B.off[J - FM], kc * x.B.kmul);
     }
     // a pair's scale words go with its first (even) stage only: the odd stage
     // takes them from the registers its even stage read them into (read_item)

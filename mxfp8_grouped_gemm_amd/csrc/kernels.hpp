@@ -31,10 +31,11 @@ struct TokBias {
 bool quant_dual_fits(int64_t rows, int64_t cols);
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
                              uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st);
+// stage_major: codes_t stage-major, cols rows over rows elements (rows % 128 == 0)
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
                             uint8_t* scales_t, hipStream_t st, bool pairs = false, bool self_rows = false,
-                            const TokBias* bias = nullptr);
+                            const TokBias* bias = nullptr, bool stage_major = false);
 // prequant.hip: an operand quantised along its rows (codes [R][C], scales
 // [R/32][C]) into the GEMM layout: codes [C][R]; scales pair-major
 // [R/128][C][4] (pairs) or row-major [C][R/32]
@@ -69,6 +70,9 @@ struct GemmStoreArgs {
   int accumulate;                 // 1: out = bf16(out + C) instead of bf16(C)
   int pair;                       // 1: 256 x 256 tiles run the pair-slot ring (128-byte rows), 0: the
                                   // four-slot ring (deeper look-ahead, for operands streamed from HBM)
+  int stage_major;                // 1: both operands' codes are stage-major (stage_major_off; lda and
+                                  // ldb are then their K); needs the four-slot ring: pair == 0, every
+                                  // ld a multiple of 128 and, with a block list, blk too
   int tiles_m, tiles_n;
   int total;                      // tiles over all groups
   int groups;                     // set by the launcher
@@ -142,11 +146,13 @@ struct Phase1Args {
   const uint16_t* in_ckpt;
   const uint16_t* sc_ckpt;
   int64_t T, H, I, E, N, B;
-  uint8_t* dgu_row_codes;       // [P][2I]
+  // stage-major codes: the four-slot ring's layout (mx_device.hpp, stage_major_off)
+  uint8_t* dgu_row_codes;       // stage-major, P rows over 2I (dgu_row_pairs), or row-major [P][2I]
   uint8_t* dgu_row_scales;      // pair-major [2I/128][P][4] (dgu_row_pairs) or row-major [P][2I/32]
-  uint8_t* dgu_tok_codes;       // [2I][P]
+  uint8_t* dgu_tok_codes;       // stage-major, 2I rows over P
   uint8_t* dgu_tok_scales;      // pair-major [P/128][2I][4]
-  uint8_t* inter_tok_codes;     // [I][P]: the intermediate (times a with the affinity on I), slot groups
+  uint8_t* inter_tok_codes;     // stage-major, I rows over P: the intermediate (times a with the
+                                // affinity on I), slot groups
   uint8_t* inter_tok_scales;    // pair-major [P/128][I][4]
   float* daff_part;             // [I/32][P]: d(a) partial sums per 32 rows i
   float* db1_acc;               // [E][2][I]
@@ -154,7 +160,8 @@ struct Phase1Args {
   int has_bias;                 // 1: accumulate db1
   int fmt_act;                  // format of the intermediate operand (activation format)
   int geglu;                    // gated activation: 0 SwiGLU (silu), 1 GeGLU (gelu, erf form)
-  int dgu_row_pairs;            // 1: dGU along I feeds the ring loop (2I % 128 == 0): pair-major scales
+  int dgu_row_pairs;            // 1: dGU along I feeds the ring loop (2I % 128 == 0): stage-major
+                                // codes, pair-major scales
   int rr_tiles;                 // tile order over the XCDs (moe_tiles.hpp)
   int tiles_m, tiles_n;
 };
@@ -166,7 +173,7 @@ bool phase1_fusable(const Phase1Args& p);
 hipError_t launch_phase1_fused(const Phase1Args& p, int fmt_grad, int fmt_weight, hipStream_t st);
 
 struct Phase3Args {
-  const uint8_t* dgu_row_codes;   // [P][2I]
+  const uint8_t* dgu_row_codes;   // 2I % 128 == 0: stage-major, P rows over 2I; else row-major [P][2I]
   const uint8_t* dgu_row_scales;  // 2I % 128 == 0: pair-major [2I/128][P][4]; else row-major [P][2I/32]
   const uint8_t* wgu_codes;       // [E][H][2I]
   const uint8_t* wgu_scales;      // 2I % 128 == 0: pair-major [E][2I/128][H][4]; else row-major [E][H][2I/32]

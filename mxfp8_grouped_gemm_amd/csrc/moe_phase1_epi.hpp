@@ -10,11 +10,13 @@
 //                                                at the end in order)
 //   dInter = a_p * dS
 //   dGate = bf16(dInter * u * silu'(g)) (GeGLU: gelu'(g)), dUp = bf16(dInter * ga)
-//   -> quantised along I        (Phase-3 A operand, dgu_row [P][2I])
-//   -> quantised along the slots (Phase-2 B operand, dgu_tok [2I][P])
+//   -> quantised along I        (Phase-3 A operand, dgu_row: stage-major, P rows
+//                                 over 2I, when 2I % 128 == 0, else [P][2I])
+//   -> quantised along the slots (Phase-2 B operand, dgu_tok: stage-major, 2I rows over P)
 //   -> db1 partial sums along the slots (with a bias)
 //   the intermediate operand of Phase 4 (times a_p with the affinity on I),
-//   quantised along the slots (inter_tok [I][P]); blocks without tokens get zeros.
+//   quantised along the slots (inter_tok: stage-major, I rows over P); blocks
+//   without tokens get zeros.
 //
 // The work is cut into chunks of TI rows i x TS slots of one block (TS =
 // min(B, 256), TI * TS = 8192), each done by one 256-thread workgroup in two
@@ -97,7 +99,8 @@ __device__ __forceinline__ void epi_empty_chunk(const Phase1Args& p, int b, int6
   for (int k = t; k < TI * (TS / 16); k += kEpiThreads) {
     const int64_t i = ti0 + k / (TS / 16);
     if (i < p.I)
-      *reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + sbase + s0 + (k % (TS / 16)) * 16) = uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4*>(p.inter_tok_codes + stage_major_off(i, sbase + s0 + (k % (TS / 16)) * 16, p.I, P)) =
+          uint4{0, 0, 0, 0};
   }
   for (int k = t; k < TI * (TS / 128); k += kEpiThreads) {
     const int64_t i = ti0 + k / (TS / 128);
@@ -273,8 +276,11 @@ __device__ __forceinline__ void epi_chunk(const Phase1Args& p, int b, int64_t ti
         wu[k] = encode4<FG>(hi_bf16(gu[4 * k]), hi_bf16(gu[4 * k + 1]), hi_bf16(gu[4 * k + 2]), hi_bf16(gu[4 * k + 3]),
                             iu);
       }
-      uint4* rg = reinterpret_cast<uint4*>(p.dgu_row_codes + slot * twoI + i0);
-      uint4* ru = reinterpret_cast<uint4*>(p.dgu_row_codes + slot * twoI + p.I + i0);
+      // stage-major (P rows over 2I) for the ring loop, else row-major [P][2I]
+      uint4* rg = reinterpret_cast<uint4*>(
+          p.dgu_row_codes + (p.dgu_row_pairs ? stage_major_off(slot, i0, P, twoI) : slot * twoI + i0));
+      uint4* ru = reinterpret_cast<uint4*>(
+          p.dgu_row_codes + (p.dgu_row_pairs ? stage_major_off(slot, p.I + i0, P, twoI) : slot * twoI + p.I + i0));
       rg[0] = uint4{wg[0], wg[1], wg[2], wg[3]};
       rg[1] = uint4{wg[4], wg[5], wg[6], wg[7]};
       ru[0] = uint4{wu[0], wu[1], wu[2], wu[3]};
@@ -326,8 +332,8 @@ __device__ __forceinline__ void epi_chunk(const Phase1Args& p, int b, int64_t ti
         cg[k] = encode4<FG>(lo_bf16(x0), lo_bf16(x1), lo_bf16(x2), lo_bf16(x3), ig);
         cu[k] = encode4<FG>(hi_bf16(x0), hi_bf16(x1), hi_bf16(x2), hi_bf16(x3), iu);
       }
-      uint4* og = reinterpret_cast<uint4*>(p.dgu_tok_codes + i * P + p0);
-      uint4* ou = reinterpret_cast<uint4*>(p.dgu_tok_codes + (p.I + i) * P + p0);
+      uint4* og = reinterpret_cast<uint4*>(p.dgu_tok_codes + stage_major_off(i, p0, twoI, P));   // 2I rows over P
+      uint4* ou = reinterpret_cast<uint4*>(p.dgu_tok_codes + stage_major_off(p.I + i, p0, twoI, P));
       og[0] = uint4{cg[0], cg[1], cg[2], cg[3]};
       og[1] = uint4{cg[4], cg[5], cg[6], cg[7]};
       ou[0] = uint4{cu[0], cu[1], cu[2], cu[3]};
@@ -360,7 +366,7 @@ __device__ __forceinline__ void epi_chunk(const Phase1Args& p, int b, int64_t ti
         const float v2 = bf16_to_f32(isrc[4 * k + 2]), v3 = bf16_to_f32(isrc[4 * k + 3]);
         ci[k] = e5 ? encode4<kE5M2>(v0, v1, v2, v3, ii) : encode4<kE4M3>(v0, v1, v2, v3, ii);
       }
-      uint4* oi = reinterpret_cast<uint4*>(p.inter_tok_codes + i * P + p0);
+      uint4* oi = reinterpret_cast<uint4*>(p.inter_tok_codes + stage_major_off(i, p0, p.I, P));   // I rows over P
       oi[0] = uint4{ci[0], ci[1], ci[2], ci[3]};
       oi[1] = uint4{ci[4], ci[5], ci[6], ci[7]};
       p.inter_tok_scales[((g32 >> 2) * p.I + i) * 4 + (g32 & 3)] = uint8_t(Xi + 127);   // [P/128][I][4]

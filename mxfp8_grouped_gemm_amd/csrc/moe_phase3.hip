@@ -129,10 +129,12 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
   v3::Op<BM> A;
   v3::Op<BN> B;
   v3::ScaleDma<BM, BN> sd;
-  v3::setup_rows(A, p.dgu_row_codes + sbase * twoI, tp.m0, p.B, twoI);
+  const int64_t P = p.N * p.B;
+  // dGU stage-major over all P slots (the tile's rows stop at its block's end);
+  // W_gate_up row-major, as the caller holds it
+  v3::setup_rows_sm(A, p.dgu_row_codes, sbase + tp.m0, sbase + p.B, P, twoI);
   v3::setup_rows(B, p.wgu_codes + e * p.H * twoI, tp.n0, p.H, twoI);
   // pair-major scales: dGU along I over all P slots; W_gate_up re-laid per expert
-  const int64_t P = p.N * p.B;
   v3::setup_scales(sd, p.dgu_row_scales, sbase + tp.m0, P, P * (twoI / 32), p.wgu_scales + e * p.H * (twoI / 32),
                    tp.n0, p.H, p.H * (twoI / 32));
   v16f acc[FM][FN];

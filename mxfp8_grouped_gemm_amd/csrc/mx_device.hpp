@@ -17,6 +17,18 @@ namespace mx {
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;
 
+// The stage-major code layout of an operand with R rows contracted over K
+// elements (K % 64 == 0), what the four-slot GEMM ring reads in whole cache
+// lines: the rows in panels of kPanelRows (the last one may hold fewer), each
+// panel [K/64][panel rows][64], so that the 64 elements of one ring stage of
+// all the panel's rows form one contiguous run.  Byte (r, k):
+constexpr int kPanelRows = 256;
+__host__ __device__ __forceinline__ int64_t stage_major_off(int64_t r, int64_t k, int64_t R, int64_t K) {
+  const int64_t p0 = r & ~int64_t(kPanelRows - 1);              // the panel's first row
+  const int64_t rp = R - p0 < kPanelRows ? R - p0 : kPanelRows;  // its rows
+  return p0 * K + ((k >> 6) * rp + (r - p0)) * 64 + (k & 63);
+}
+
 // Stores with the nontemporal hint (streaming: written lines are not kept in
 // the caches as if they would be read again soon), for results written once
 // and read, if at all, only after far more data than L2 and the infinity cache

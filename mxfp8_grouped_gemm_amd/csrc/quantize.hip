@@ -164,11 +164,12 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(const uint16_t* __restr
 
 // The 32 rows row0 .. row0 + 31 of columns colA, colA + 1 (w[r]: bf16 of colA
 // in the low half, colA + 1 in the high half) as one scale group each: codes
-// to codes_t [cols][rows], scale bytes to scales_t.
+// to codes_t [cols][rows] (or stage-major, see stage_major_off, with cols rows
+// contracted over rows elements), scale bytes to scales_t.
 template <int FMT, bool PAIRS>
 __device__ __forceinline__ void tok_encode_pair(const uint32_t (&w)[32], int64_t rows, int64_t cols, int64_t colA,
                                                 int64_t row0, uint8_t* __restrict__ codes_t,
-                                                uint8_t* __restrict__ scales_t) {
+                                                uint8_t* __restrict__ scales_t, bool stage_major) {
   uint32_t m = 0;   // |bf16| maxima of both columns
 #pragma unroll
   for (int r = 0; r < 32; ++r) m = absmax_bf16x2(m, w[r]);
@@ -183,8 +184,10 @@ __device__ __forceinline__ void tok_encode_pair(const uint32_t (&w)[32], int64_t
     p0[q] = encode_bf16x4<FMT>(lo_halves(w0, w1), lo_halves(w2, w3), s0);
     p1[q] = encode_bf16x4<FMT>(hi_halves(w0, w1), hi_halves(w2, w3), s1);
   }
-  uint4* dst0 = reinterpret_cast<uint4*>(codes_t + colA * rows + row0);
-  uint4* dst1 = reinterpret_cast<uint4*>(codes_t + (colA + 1) * rows + row0);
+  const int64_t o0 = stage_major ? stage_major_off(colA, row0, cols, rows) : colA * rows + row0;
+  const int64_t o1 = stage_major ? stage_major_off(colA + 1, row0, cols, rows) : o0 + rows;
+  uint4* dst0 = reinterpret_cast<uint4*>(codes_t + o0);
+  uint4* dst1 = reinterpret_cast<uint4*>(codes_t + o1);
   dst0[0] = make_uint4(p0[0], p0[1], p0[2], p0[3]);
   dst0[1] = make_uint4(p0[4], p0[5], p0[6], p0[7]);
   dst1[0] = make_uint4(p1[0], p1[1], p1[2], p1[3]);
@@ -233,7 +236,7 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
                                                          const float* __restrict__ rowscale,
                                                          int64_t rows, uint8_t* __restrict__ codes_t,
                                                          uint8_t* __restrict__ scales_t, int self_rows,
-                                                         TokBias bias) {
+                                                         TokBias bias, int stage_major) {
   const int cp = threadIdx.x & 63;
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = int64_t(blockIdx.y) * kTokRows + grp * 32;
@@ -324,7 +327,7 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
       atomicAdd(bias.db2_acc + e * cols + int64_t(blockIdx.x) * kTokCols + threadIdx.x, t);
     }
   }
-  tok_encode_pair<FMT, PAIRS>(w, rows, cols, colA, row0, codes_t, scales_t);
+  tok_encode_pair<FMT, PAIRS>(w, rows, cols, colA, row0, codes_t, scales_t, stage_major != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -386,7 +389,7 @@ __global__ void __launch_bounds__(256) quant_dual_kernel(const uint16_t* __restr
     uint32_t wq[32];
 #pragma unroll
     for (int r = 0; r < 32; ++r) wq[r] = w[r][q];
-    tok_encode_pair<FMT, PAIRS_T>(wq, rows, cols, col0 + 2 * q, row0, codes_t, scales_t);
+    tok_encode_pair<FMT, PAIRS_T>(wq, rows, cols, col0 + 2 * q, row0, codes_t, scales_t, false);
   }
 }
 
@@ -484,39 +487,40 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int 
 template <int FMT, bool PAIRS, bool OFF32>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
                          const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows,
-                         const TokBias& b) {
+                         const TokBias& b, int sm) {
   if (b.part && OFF32 && idx && rs)
     quant_tok_kernel<FMT, true, true, PAIRS, OFF32, true>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
   else if (idx && rs)
     quant_tok_kernel<FMT, true, true, PAIRS, OFF32, false>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
   else if (idx)
     quant_tok_kernel<FMT, true, false, PAIRS, OFF32, false>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
   else if (rs)
     quant_tok_kernel<FMT, false, true, PAIRS, OFF32, false>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
   else
     quant_tok_kernel<FMT, false, false, PAIRS, OFF32, false>
-        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+        <<<grid, 256, 0, st>>>(x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
 }
 template <int FMT, bool PAIRS>
 static void tok_dispatch(dim3 grid, hipStream_t st, const uint16_t* x, int64_t src_rows, int64_t cols,
                          const int32_t* idx, const float* rs, int64_t rows, uint8_t* ct, uint8_t* sct, int self_rows,
-                         const TokBias& b) {
+                         const TokBias& b, int sm) {
   const bool off32 = src_rows * cols * 2 < int64_t(v2::kOOB) && rows <= int64_t(INT32_MAX);
   if (off32)
-    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+    tok_dispatch<FMT, PAIRS, true>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
   else
-    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b);
+    tok_dispatch<FMT, PAIRS, false>(grid, st, x, src_rows, cols, idx, rs, rows, ct, sct, self_rows, b, sm);
 }
 
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st, bool pairs, bool self_rows, const TokBias* bias) {
+                            uint8_t* scales_t, hipStream_t st, bool pairs, bool self_rows, const TokBias* bias,
+                            bool stage_major) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  if (pairs && rows % 128) return hipErrorInvalidValue;
+  if ((pairs || stage_major) && rows % 128) return hipErrorInvalidValue;
   if (self_rows && !idx) return hipErrorInvalidValue;
   TokBias b{};
   if (bias) {   // the fused bias reductions need whole tiles, row scales and 32-bit offsets
@@ -525,14 +529,14 @@ hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, c
       return hipErrorInvalidValue;
     b = *bias;
   }
-  const int self = self_rows ? 1 : 0;
+  const int self = self_rows ? 1 : 0, sm = stage_major ? 1 : 0;
   dim3 grid(unsigned((cols + kTokCols - 1) / kTokCols), unsigned((rows + kTokRows - 1) / kTokRows));
   if (fmt == kE4M3) {
-    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
-    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
+    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
+    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
   } else {
-    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
-    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b);
+    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
+    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
   }
   return hipGetLastError();
 }

@@ -59,6 +59,20 @@ def pairs_to_rows(raw, rows: int, k: int) -> np.ndarray:
     return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(rows, k // 32))
 
 
+def stage_major_to_rows(raw, rows: int, k: int) -> np.ndarray:
+    """Codes of `rows` rows over k elements stored stage-major (the four-slot
+    ring's layout: the rows in panels of 256, the last one possibly shorter,
+    each panel [k/64][panel rows][64]) as row-major [rows][k]."""
+    a = np.asarray(raw, dtype=np.uint8).reshape(-1)
+    assert a.size == rows * k and k % 64 == 0
+    out = np.empty((rows, k), dtype=np.uint8)
+    for p0 in range(0, rows, 256):
+        rp = min(256, rows - p0)
+        panel = a[p0 * k:(p0 + rp) * k].reshape(k // 64, rp, 64)
+        out[p0:p0 + rp] = panel.transpose(1, 0, 2).reshape(rp, k)
+    return out
+
+
 # Localised-defect bounds of the GPU parity checks, next to the relative
 # Frobenius bound of the whole tensor (2e-3).  Set from the measured error
 # distributions of every parity case with margin; the reasons are in the

@@ -122,6 +122,11 @@ def test_moe_bwd_workspace_and_size_limits_without_gpu():
     assert L.moe_bwd_mxfp8_workspace_size(C.byref(big)) == 0
     ok = _fake_args(mx, L, T=262143, H=4096, I=256, E=8, B=1024)
     assert L.moe_bwd_mxfp8_workspace_size(C.byref(ok)) > 0
+    # more than 2^24 slots: a 256-row panel of a stage-major operand over the slots
+    # would pass 2^32 bytes
+    many = _fake_args(mx, L, T=8_500_000, H=32, I=256, E=8, B=1024)
+    assert L.moe_bwd_mxfp8(C.byref(many), C.c_void_p(0x10000), 1 << 62, None) == 2
+    assert "2^24" in mx.last_error()
 
 
 def test_noalloc_build_blocks_validation_without_gpu():

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import assert_parity, bf, pairs_to_rows, parity_stats, rel_fro
+from helpers import assert_parity, bf, pairs_to_rows, parity_stats, rel_fro, stage_major_to_rows
 from moe_gpu_common import gpu_problem, host, oracle_problem
 
 pytestmark = pytest.mark.gpu
@@ -89,7 +89,8 @@ def test_moe_small_full_parity(name):
     for which, name_c, name_s in ((oracle.TOK_X, "x_tok_codes", "x_tok_scales"),
                                   (oracle.TOK_GY, "gy_tok_codes", "gy_tok_scales")):
         c, s = oracle.moe_token_operand(p, which)
-        assert np.array_equal(ws[L[name_c]:L[name_c] + H * P], c.ravel()), name_c
+        # token-axis codes are stage-major (H rows over P slots)
+        assert np.array_equal(stage_major_to_rows(ws[L[name_c]:L[name_c] + H * P], H, P), c.reshape(H, P)), name_c
         # token-axis scales are pair-major ([P/128][H][4])
         got = pairs_to_rows(ws[L[name_s]:L[name_s] + H * P // 32], H, P)
         assert np.array_equal(got, s.reshape(H, P // 32)), name_s
@@ -107,8 +108,16 @@ def test_moe_small_full_parity(name):
     # the intermediate operand: silu is evaluated in fp32 on the GPU and in fp64 by the
     # oracle, so a rare bf16 rounding may differ; codes must agree almost everywhere
     c, s = oracle.moe_token_operand(p, oracle.TOK_INTER)
-    got = ws[L["inter_tok_codes"]:L["inter_tok_codes"] + cfg.I * P]
-    assert np.mean(got != c.ravel()) < 1e-3
+    got = stage_major_to_rows(ws[L["inter_tok_codes"]:L["inter_tok_codes"] + cfg.I * P], cfg.I, P)
+    assert np.mean(got != c.reshape(cfg.I, P)) < 1e-3
+    # dGate|dUp along the slots (Phase 2's operand), with the same caveat, at the
+    # routed slots (blocks without any are never written: no GEMM reads them)
+    c, s = oracle.moe_token_operand(p, oracle.TOK_DGU)
+    got = stage_major_to_rows(ws[L["dgu_tok_codes"]:L["dgu_tok_codes"] + 2 * cfg.I * P], 2 * cfg.I, P)
+    tp = host(gp["tpid"]).reshape(-1)
+    routed = (tp >= 0) & (tp < T)
+    assert routed.any()
+    assert np.mean(got[:, routed] != c.reshape(2 * cfg.I, P)[:, routed]) < 1e-3
 
 
 def test_moe_build_blocks_bit_exact_and_edge_cases():
@@ -330,11 +339,13 @@ def test_moe_supplied_checkpoints(name):
     L = op.layout
     P = gp["N"] * cfg.B
     c, s = oracle.moe_token_operand(p, oracle.TOK_INTER)
-    assert np.array_equal(ws[L["inter_tok_codes"]:L["inter_tok_codes"] + I * P], c.ravel())
+    assert np.array_equal(stage_major_to_rows(ws[L["inter_tok_codes"]:L["inter_tok_codes"] + I * P], I, P),
+                          c.reshape(I, P))
     assert np.array_equal(pairs_to_rows(ws[L["inter_tok_scales"]:L["inter_tok_scales"] + I * P // 32], I, P),
                           s.reshape(I, P // 32))
     c, s = oracle.moe_token_operand(p, oracle.TOK_GY)
-    assert np.array_equal(ws[L["gy_tok_codes"]:L["gy_tok_codes"] + H * P], c.ravel())
+    assert np.array_equal(stage_major_to_rows(ws[L["gy_tok_codes"]:L["gy_tok_codes"] + H * P], H, P),
+                          c.reshape(H, P))
 
 
 def test_moe_checkpoints_rejected_with_the_wrong_affinity_placement():
@@ -517,4 +528,4 @@ def test_moe_geglu(name):
     P = gp["N"] * cfg.B
     c, _ = oracle.moe_token_operand(dataclasses.replace(p, activation=oracle.GEGLU), oracle.TOK_INTER)
     got = op.workspace.cpu().numpy()[op.layout["inter_tok_codes"]:op.layout["inter_tok_codes"] + cfg.I * P]
-    assert np.mean(got != c.ravel()) < 1e-3
+    assert np.mean(stage_major_to_rows(got, cfg.I, P) != c.reshape(cfg.I, P)) < 1e-3
