@@ -100,8 +100,13 @@ int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis, int 
  *     [3]  X^T codes along M [K,M]  + scales [K,M/32]
  *   Scales of [0],[1] are pair-major ([N/128][rows][4]: word (p, r) = row r's
  *   bytes for elements [128p, 128p+128)) when N % 128 == 0, and those of
- *   [2],[3] ([M/128][rows][4]) when M % 128 == 0; the region sizes are the same.
- *   each region starting on a 256-byte boundary, in this order, codes first.
+ *   [2],[3] ([M/128][rows][4]) when M % 128 == 0.  The codes of a product's
+ *   two operands are stage-major (S64, as defined with
+ *   moe_bwd_mxfp8_workspace_layout: 256-row panels, each [C/64][rows][64],
+ *   C the contraction) when both are quantised here from bf16 and C is a
+ *   multiple of 128 below 2^24 (N for [0],[1], M for [2],[3]); otherwise
+ *   row-major as shown.  The region sizes are the same either way, each
+ *   region starting on a 256-byte boundary, in this order, codes first.
  * ------------------------------------------------------------------------- */
 size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
 
@@ -121,7 +126,8 @@ size_t matmul_mxfp8_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
  *     weights (along N)    codes [N,K], scales [N/32, K]   (axis 0)
  *     input (along M)      codes [M,K], scales [M/32, K]   (axis 0)
  *   swizzled (*_is_swizzled = 1; the GEMM's operand layout, contraction
- *   contiguous, as workspace regions [0]-[3] of matmul_mxfp8_bwd hold it):
+ *   contiguous, as workspace regions [0]-[3] of matmul_mxfp8_bwd hold it
+ *   when they are not stage-major):
  *     output_grad along N  codes [M,N], scales [M, N/32]
  *     output_grad along M  codes [N,M], scales [N, M/32]
  *     weights              codes [K,N], scales [K, N/32]

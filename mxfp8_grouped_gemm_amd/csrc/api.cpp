@@ -176,20 +176,33 @@ static int dense_run(const matmul_mxfp8_bwd_args* a, void* ws, size_t ws_bytes, 
   }
   const uint16_t* dy = a->output_grad;
   const int fdy = a->fmt_output_grad, fw = a->fmt_weights, fx = a->fmt_input;
+  // A GEMM whose two operands are both quantised here from bf16, on the ring
+  // loop (contraction a multiple of 128), gets them stage-major and runs the
+  // four-slot ring: whole cache lines per DMA instruction (mx_device.hpp,
+  // stage_major_off).  Operands the caller hands in keep their row-major layout.
+  const bool sm_dx = !pc[0] && !pc[1] && N % 128 == 0 && N < (int64_t(1) << 24) && M * (N / 32) <= int64_t(UINT32_MAX);
+  const bool sm_dw = !pc[2] && !pc[3] && M % 128 == 0 && M < (int64_t(1) << 24);
+  const bool sm[4] = {sm_dx, sm_dx, sm_dw, sm_dw};
   // dY along both axes from one read where the shapes allow (stage 0 then makes stream 2 too)
   const bool dual = !pc[0] && !pc[2] && mx::quant_dual_fits(M, N);
   auto prep = [&](int i) -> hipError_t {
     const bool pairs = kdim[i] % 128 == 0;
     uint8_t* wc = base + off[2 * i];
     uint8_t* wsc = base + off[2 * i + 1];
-    if (dual && i == 0) return mx::launch_quant_dual(dy, M, N, fdy, wc, wsc, base + off[4], base + off[5], st);
+    if (dual && i == 0)
+      return mx::launch_quant_dual(dy, M, N, fdy, wc, wsc, base + off[4], base + off[5], st, sm[0], sm[2]);
     if (dual && i == 2) return hipSuccess;
     if (!pc[i]) {   // quantise from bf16 along the contraction
       switch (i) {
-        case 0: return mx::launch_quant_rows(dy, M, N, fdy, wc, wsc, st, nullptr, pairs);
-        case 1: return mx::launch_quant_tok(a->weights, N, K, nullptr, nullptr, N, fw, wc, wsc, st, pairs);
-        case 2: return mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fdy, wc, wsc, st, pairs);
-        default: return mx::launch_quant_tok(a->input_activation, M, K, nullptr, nullptr, M, fx, wc, wsc, st, pairs);
+        case 0: return mx::launch_quant_rows(dy, M, N, fdy, wc, wsc, st, nullptr, pairs, sm[0]);
+        case 1:
+          return mx::launch_quant_tok(a->weights, N, K, nullptr, nullptr, N, fw, wc, wsc, st, pairs, false, nullptr,
+                                      sm[1]);
+        case 2:
+          return mx::launch_quant_tok(dy, M, N, nullptr, nullptr, M, fdy, wc, wsc, st, pairs, false, nullptr, sm[2]);
+        default:
+          return mx::launch_quant_tok(a->input_activation, M, K, nullptr, nullptr, M, fx, wc, wsc, st, pairs, false,
+                                      nullptr, sm[3]);
       }
     }
     if (i == 0 || swz[i]) {   // GEMM layout: at most the row-major scales become pair-major
@@ -209,13 +222,18 @@ static int dense_run(const matmul_mxfp8_bwd_args* a, void* ws, size_t ws_bytes, 
   g.a_codes = op[0].codes; g.a_scales = op[0].scales; g.lda = N;
   g.b_codes = op[1].codes; g.b_scales = op[1].scales; g.ldb = N;
   g.M = M; g.N = K; g.K = N; g.out = a->input_grad; g.ldo = K;
-  g.pair = 1;   // measured 6% faster than the four-slot ring on 8192^3, 5% on 4096^3
+  // row-major operands: the pair-slot ring, measured 6% faster than the
+  // four-slot ring on 8192^3, 5% on 4096^3
+  g.stage_major = sm_dx;
+  g.pair = sm_dx ? 0 : 1;
   // stage 2 -- dX GEMM
   if (lo <= 2 && 2 <= hi && (e = mx::launch_gemm_store(g, 1, fdy, fw, st)) != hipSuccess)
     return hip_status(e, "dX GEMM");
   g.a_codes = op[2].codes; g.a_scales = op[2].scales; g.lda = M;
   g.b_codes = op[3].codes; g.b_scales = op[3].scales; g.ldb = M;
   g.M = N; g.N = K; g.K = M; g.out = a->weight_grad; g.ldo = K;
+  g.stage_major = sm_dw;
+  g.pair = sm_dw ? 0 : 1;
   // stage 3 -- dW GEMM
   if (lo <= 3 && 3 <= hi && (e = mx::launch_gemm_store(g, 1, fdy, fx, st)) != hipSuccess)
     return hip_status(e, "dW GEMM");

@@ -10,8 +10,10 @@ namespace mx {
 // quantize.hip
 // Scale layouts: row-major [rows][K/32], or pair-major [K/128][rows][4] (pairs
 // = true) for operands of the ring GEMM loop; see gemm_v3.hpp.
+// stage_major (with pairs): codes stage-major (mx_device.hpp, stage_major_off), rows rows over cols
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, hipStream_t st, uint16_t* deq = nullptr, bool pairs = false);
+                             uint8_t* scales, hipStream_t st, uint16_t* deq = nullptr, bool pairs = false,
+                             bool stage_major = false);
 // codes [rows][cols] + scales [rows][cols/32] (groups along cols) -> exact bf16 values
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, int fmt,
                                uint16_t* out, hipStream_t st);
@@ -29,8 +31,10 @@ struct TokBias {
 // x [rows][cols] along both axes in one pass, the same bytes as launch_quant_rows
 // (pairs) and launch_quant_tok (no index) each give: rows % 32 == 0, cols % 512 == 0
 bool quant_dual_fits(int64_t rows, int64_t cols);
+// stage_major / stage_major_t: codes / codes_t stage-major (codes_t needs rows % 128 == 0)
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st);
+                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st,
+                             bool stage_major = false, bool stage_major_t = false);
 // stage_major: codes_t stage-major, cols rows over rows elements (rows % 128 == 0)
 hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, const int32_t* idx,
                             const float* rowscale, int64_t rows, int fmt, uint8_t* codes_t,

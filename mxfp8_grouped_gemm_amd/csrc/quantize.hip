@@ -35,12 +35,14 @@ __device__ __forceinline__ uint32_t deq_pk(uint32_t codes, float scale) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// stage_major (with PAIRS): codes stage-major (stage_major_off, rows rows over
+// 32 * gpr columns) instead of row-major; rows * gpr < 2^32.
 template <int FMT, bool DEQ, bool PAIRS>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict__ x,
                                                           uint2* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
                                                           int64_t nchunks, uint4* __restrict__ deq,
-                                                          int64_t rows, int64_t gpr) {
+                                                          int64_t rows, int64_t gpr, int stage_major) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
     const uint4 v = x[c];
@@ -60,7 +62,13 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict
     for (int k = 0; k < 2; ++k)
       out[k] = encode4<FMT>(__uint_as_float(w[2 * k] << 16), __uint_as_float(w[2 * k] & 0xffff0000u),
                             __uint_as_float(w[2 * k + 1] << 16), __uint_as_float(w[2 * k + 1] & 0xffff0000u), inv);
-    codes[c] = make_uint2(out[0], out[1]);
+    if (PAIRS && stage_major) {   // chunk c = 8 codes of row c / (4 gpr)
+      const uint32_t row = uint32_t(c >> 2) / uint32_t(gpr);
+      const int64_t col = (c - int64_t(row) * gpr * 4) * 8;
+      codes[stage_major_off(row, col, rows, gpr * 32) >> 3] = make_uint2(out[0], out[1]);
+    } else {
+      codes[c] = make_uint2(out[0], out[1]);
+    }
     if ((c & 3) == 0) {
       if (PAIRS) {   // group G = row * gpr + g  ->  word (g / 4, row), byte g % 4
         const int64_t G = c >> 2, row = G / gpr, g = G - row * gpr;
@@ -342,11 +350,12 @@ __global__ void __launch_bounds__(256) quant_tok_kernel(const uint16_t* __restri
 // from the same registers.  rows % 32 == 0, cols % 512 == 0.
 constexpr int kDualCols = 512;
 
+// sm / sm_t: codes / codes_t stage-major (stage_major_off) instead of row-major.
 template <int FMT, bool PAIRS_T>
 __global__ void __launch_bounds__(256) quant_dual_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                           uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                                                           uint8_t* __restrict__ codes_t,
-                                                          uint8_t* __restrict__ scales_t) {
+                                                          uint8_t* __restrict__ scales_t, int sm, int sm_t) {
   const int lane = threadIdx.x & 63;
   const int64_t row0 = int64_t(blockIdx.y) * 128 + (threadIdx.x >> 6) * 32;
   if (row0 >= rows) return;   // a partial last workgroup of rows (no barrier below)
@@ -377,7 +386,7 @@ __global__ void __launch_bounds__(256) quant_dual_kernel(const uint16_t* __restr
                             __uint_as_float(w[r][2 * k + 1] << 16), __uint_as_float(w[r][2 * k + 1] & 0xffff0000u),
                             inv);
     const int64_t row = row0 + r;
-    codes[(row * cols + col0) / 8] = make_uint2(out[0], out[1]);
+    codes[(sm ? stage_major_off(row, col0, rows, cols) : row * cols + col0) / 8] = make_uint2(out[0], out[1]);
     if ((lane & 3) == 0) {   // group g of the row -> word (g / 4, row), byte g % 4
       const int64_t g = col0 / 32;
       scales[((g >> 2) * rows + row) * 4 + (g & 3)] = uint8_t(X + 127);
@@ -389,7 +398,7 @@ __global__ void __launch_bounds__(256) quant_dual_kernel(const uint16_t* __restr
     uint32_t wq[32];
 #pragma unroll
     for (int r = 0; r < 32; ++r) wq[r] = w[r][q];
-    tok_encode_pair<FMT, PAIRS_T>(wq, rows, cols, col0 + 2 * q, row0, codes_t, scales_t, false);
+    tok_encode_pair<FMT, PAIRS_T>(wq, rows, cols, col0 + 2 * q, row0, codes_t, scales_t, sm_t != 0);
   }
 }
 
@@ -421,24 +430,27 @@ __global__ void __launch_bounds__(256) scales_to_pairs_kernel(const uint32_t* __
 // host launchers
 template <int FMT>
 static void rows_dispatch(int blocks, hipStream_t st, const uint4* xs, uint2* cs, uint8_t* scales, int64_t nchunks,
-                          uint4* ds, int64_t rows, int64_t gpr, bool pairs) {
-  if (ds) quant_rows_kernel<FMT, true, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr);
-  else if (pairs) quant_rows_kernel<FMT, false, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr);
-  else quant_rows_kernel<FMT, false, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr);
+                          uint4* ds, int64_t rows, int64_t gpr, bool pairs, int sm) {
+  if (ds) quant_rows_kernel<FMT, true, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, 0);
+  else if (pairs)
+    quant_rows_kernel<FMT, false, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, sm);
+  else quant_rows_kernel<FMT, false, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, 0);
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, hipStream_t st, uint16_t* deq, bool pairs) {
+                             uint8_t* scales, hipStream_t st, uint16_t* deq, bool pairs, bool stage_major) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
   if (deq && pairs) return hipErrorInvalidValue;   // no caller needs both
+  if (stage_major && (!pairs || rows * (cols / 32) > int64_t(UINT32_MAX))) return hipErrorInvalidValue;
   const int64_t want = (nchunks + 255) / 256;
   const int blocks = int(want < 65536 ? want : 65536);
   const uint4* xs = reinterpret_cast<const uint4*>(x);
   uint2* cs = reinterpret_cast<uint2*>(codes);
   uint4* ds = reinterpret_cast<uint4*>(deq);
-  if (fmt == kE4M3) rows_dispatch<kE4M3>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs);
-  else rows_dispatch<kE5M2>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs);
+  const int sm = stage_major ? 1 : 0;
+  if (fmt == kE4M3) rows_dispatch<kE4M3>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs, sm);
+  else rows_dispatch<kE5M2>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs, sm);
   return hipGetLastError();
 }
 
@@ -546,17 +558,20 @@ bool quant_dual_fits(int64_t rows, int64_t cols) {
 }
 
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
-                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st) {
+                             uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, hipStream_t st, bool stage_major,
+                             bool stage_major_t) {
   if (!quant_dual_fits(rows, cols)) return hipErrorInvalidValue;
+  const bool pt = rows % 128 == 0;
+  if (stage_major_t && !pt) return hipErrorInvalidValue;
   const dim3 grid(unsigned(cols / kDualCols), unsigned((rows + 127) / 128));
   uint2* cs = reinterpret_cast<uint2*>(codes);
-  const bool pt = rows % 128 == 0;
+  const int sm = stage_major ? 1 : 0, smt = stage_major_t ? 1 : 0;
   if (fmt == kE4M3) {
-    if (pt) quant_dual_kernel<kE4M3, true><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
-    else quant_dual_kernel<kE4M3, false><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
+    if (pt) quant_dual_kernel<kE4M3, true><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t, sm, smt);
+    else quant_dual_kernel<kE4M3, false><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t, sm, smt);
   } else {
-    if (pt) quant_dual_kernel<kE5M2, true><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
-    else quant_dual_kernel<kE5M2, false><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t);
+    if (pt) quant_dual_kernel<kE5M2, true><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t, sm, smt);
+    else quant_dual_kernel<kE5M2, false><<<grid, 256, 0, st>>>(x, rows, cols, cs, scales, codes_t, scales_t, sm, smt);
   }
   return hipGetLastError();
 }

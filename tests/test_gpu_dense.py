@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synthetic as S
-from helpers import assert_parity, bf, pairs_to_rows, parity_stats, rel_fro
+from helpers import assert_parity, bf, pairs_to_rows, parity_stats, rel_fro, stage_major_to_rows
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -29,7 +29,7 @@ def _inputs(M, N, K, seed):
 # multiple of 128 (pair-major dY^T scales) or not, and a partial last row tile
 @pytest.mark.parametrize("M,N,K", [(64, 96, 128), (256, 320, 192), (96, 160, 544), (512, 384, 640),
                                    (32, 32, 32), (288, 544, 96), (256, 1024, 96), (96, 512, 160),
-                                   (160, 512, 64)])
+                                   (160, 512, 64), (640, 512, 416)])
 def test_dense_small_full_parity(M, N, K):
     mx = _mx()
     t = _inputs(M, N, K, seed=M + N + K)
@@ -51,10 +51,14 @@ def test_dense_small_full_parity(M, N, K):
             oracle.quantize(np.ascontiguousarray(dy_b.T), 1, oracle.E5M2),
             oracle.quantize(np.ascontiguousarray(x_b.T), 1, oracle.E4M3)]
     # scales of a GEMM whose contraction (N for [0],[1], M for [2],[3]) is a
-    # multiple of 128 are stored pair-major
+    # multiple of 128 are stored pair-major, and its codes (both operands
+    # quantised here from bf16) stage-major
     kdim = [N, N, M, M]
     for (co, so), (c, s), kk in zip(regs, want, kdim):
-        assert np.array_equal(wsh[co:co + c.size], c.ravel())
+        got = wsh[co:co + c.size]
+        if kk % 128 == 0:
+            got = stage_major_to_rows(got, c.shape[0], kk)
+        assert np.array_equal(got.ravel(), c.ravel())
         got = wsh[so:so + s.size]
         if kk % 128 == 0:
             got = pairs_to_rows(got, s.shape[0], kk)
