@@ -9,10 +9,13 @@
 //             reduced on the bf16 MFMA, whose accumulation is exact enough
 //             that results requantised afterwards round as an exact sum would.
 //
-// Why a ring: a CU streams L2 -> LDS at ~55 B/clk with buffer_load ... lds,
-// but a stage can only start when the slowest of its ~500 cache lines has
-// landed, and a few percent of them miss L2.  With one stage in flight the
-// loop runs at that miss latency; with three it runs at the stream rate.
+// Why a ring: a stage can only start when the slowest of its ~500 cache lines
+// has landed, and a few percent of them miss L2.  With one stage in flight the
+// loop runs at that miss latency; with three it runs near the stream rate (a
+// fifth slot measured no faster).  The stream rate goes by cache lines: a CU
+// moves about 66 B/clk of L2-resident whole lines with buffer_load ... lds but
+// about 34 B/clk when every row gives half a line, hence the stage-major
+// operand layout (see Op).
 //
 // Stage = 64 bytes of K (one 64-element fp8 MFMA step, two 16-element bf16
 // steps).  LDS: NBUF code slots of (BM + BN) rows x 64 B (16-byte chunks

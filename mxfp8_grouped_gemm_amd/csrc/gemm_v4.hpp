@@ -19,10 +19,15 @@
 // cache lines, where the four-slot ring of 64-byte stages (gemm_v3.hpp) moves
 // 16 rows x 64 bytes, two requests per line.  The price is look-ahead: that
 // ring issues each stage three stages before its use, this one a pair one pair
-// (two stages) before.  Measured: 6% faster on the dense 8192^3 GEMM and 3%
-// on Phase 1 and Phase 2, whose operand tiles are reused from L2; 4% slower
-// on Phase 3 and 2% on Phase 4, which stream more of their operands from HBM
-// and need the deeper look-ahead.  Each kernel uses the faster of the two.
+// (two stages) before.  Measured with row-major operands: 6% faster on the
+// dense 8192^3 GEMM and 3% on Phase 1 and Phase 2, whose operand tiles are
+// reused from L2; 4% slower on Phase 3 and 2% on Phase 4, which stream more
+// of their operands from HBM and need the deeper look-ahead.  Operands the
+// library writes itself are stage-major (gemm_v3.hpp, Op), which gives the
+// four-slot ring whole lines too; with them it beats this ring by 5-9% (dense
+// from bf16, Phase 2).  This ring keeps the products of row-major operands
+// the caller holds: Phase 1 (W_down and the dY rows it gathers) and the dense
+// GEMMs on pre-quantised operands.
 //
 // Loads are issued with inline asm (s_mov_b32 m0 + buffer_load_dword{,x4} ...
 // lds) because the compiler's wait-count pass treats every LDS read after an
