@@ -353,6 +353,14 @@ def run_dense(reps):
     qms = _events_ms(lambda: mx.mxfp8_quantize(x, 1, mx.E4M3, out=qout), reps)
     qbytes = 4096 * 4096 * (2 + 1 + 1 / 32)
     res_q = {"shape": [4096, 4096], "axis": 1, "ms": round(qms, 5), **roofline_of("hbm", qbytes, qms)}
+    # the same on an input larger than the 256 MB infinity cache (512 MiB), so
+    # back-to-back calls read it from HBM; start and drain are a small part of it
+    xl = S.normal_bf16((16384, 16384), 1.0, 0, 98, "cuda")
+    qlout = mx.mxfp8_quantize(xl, 1, mx.E4M3)
+    qlms = _events_ms(lambda: mx.mxfp8_quantize(xl, 1, mx.E4M3, out=qlout), reps)
+    res_q["larger"] = {"shape": [16384, 16384], "axis": 1, "ms": round(qlms, 5),
+                       **roofline_of("hbm", 16384 * 16384 * (2 + 1 + 1 / 32), qlms)}
+    del xl, qlout
     return res, res_q
 
 
@@ -592,7 +600,8 @@ def main():
         dense, quant = run_dense(args.profile_reps + 5)
         out["dense"] = dense
         out["quantize"] = quant
-        log(f"[bench] dense: {dense['TFLOP/s']} TFLOP/s; quantize {quant['achieved']} GB/s")
+        log(f"[bench] dense: {dense['TFLOP/s']} TFLOP/s; quantize {quant['achieved']} GB/s "
+            f"([16384, 16384]: {quant['larger']['achieved']} GB/s)")
         out["router_bwd"] = run_router(args.profile_reps + 5)
         log("[bench] router backward: " + ", ".join(f"{k} {v['ms']} ms" for k, v in out["router_bwd"].items()
                                                      if isinstance(v, dict)))
