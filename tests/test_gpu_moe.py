@@ -24,6 +24,9 @@ SMALL = {
     "medium_b512": S.scaled(S.MEDIUM, T=640, H=128, I=96, E=4, K=2, B=512),
     # H a multiple of 128: the bias reductions ride on the dY gather
     "fine_h256": S.scaled(S.FINE, T=512, H=256, I=128, E=16, K=4, B=128),
+    # stage-major operands whose rows end in a short 256-row panel: X and dY over
+    # H = 384 (256 + 128), dGU over 2I = 384, the intermediate over I = 192
+    "ragged_panels": S.scaled(S.MEDIUM, T=384, H=384, I=192, E=4, K=2, B=128),
 }
 # experts of 32 MiB (W_down) and 64 MiB (W_gate_up): Phases 1 and 3 hand their
 # tiles to the XCDs round robin, which no other small case reaches
