@@ -35,52 +35,74 @@ __device__ __forceinline__ uint32_t deq_pk(uint32_t codes, float scale) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// One chunk c (8 values of a row) from its loaded 16 bytes v.  The four lanes of
+// a group (c = 4g .. 4g + 3, consecutive lanes) exchange their maxima.
 // stage_major (with PAIRS): codes stage-major (stage_major_off, rows rows over
 // 32 * gpr columns) instead of row-major; rows * gpr < 2^32.
 template <int FMT, bool DEQ, bool PAIRS>
+__device__ __forceinline__ void quant_rows_chunk(const uint4 v, int64_t c, uint2* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, uint4* __restrict__ deq,
+                                                 int64_t rows, int64_t gpr, int stage_major) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    amax = max(amax, abs_bits_bf16(uint16_t(w[k] & 0xffffu)));
+    amax = max(amax, abs_bits_bf16(uint16_t(w[k] >> 16)));
+  }
+  amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
+  amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
+  const int X = scale_exp<FMT>(amax);
+  const float inv = inv_scale(X);
+  uint32_t out[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    out[k] = encode4<FMT>(__uint_as_float(w[2 * k] << 16), __uint_as_float(w[2 * k] & 0xffff0000u),
+                          __uint_as_float(w[2 * k + 1] << 16), __uint_as_float(w[2 * k + 1] & 0xffff0000u), inv);
+  if (PAIRS && stage_major) {   // chunk c = 8 codes of row c / (4 gpr)
+    const uint32_t row = uint32_t(c >> 2) / uint32_t(gpr);
+    const int64_t col = (c - int64_t(row) * gpr * 4) * 8;
+    codes[stage_major_off(row, col, rows, gpr * 32) >> 3] = make_uint2(out[0], out[1]);
+  } else {
+    codes[c] = make_uint2(out[0], out[1]);
+  }
+  if ((c & 3) == 0) {
+    if (PAIRS) {   // group G = row * gpr + g  ->  word (g / 4, row), byte g % 4
+      const int64_t G = c >> 2, row = G / gpr, g = G - row * gpr;
+      scales[((g >> 2) * rows + row) * 4 + (g & 3)] = uint8_t(X + 127);
+    } else {
+      scales[c >> 2] = uint8_t(X + 127);
+    }
+  }
+  if (DEQ) {
+    const float sc = pow2_f32(X);
+    deq[c] = make_uint4(deq_pk<FMT, false>(out[0], sc), deq_pk<FMT, true>(out[0], sc),
+                        deq_pk<FMT, false>(out[1], sc), deq_pk<FMT, true>(out[1], sc));
+  }
+}
+
+// U chunks per thread and pass, their loads issued together (U = 4 for small
+// inputs, where a thread per chunk leaves the kernel mostly workgroup start-up:
+// measured on [4096, 4096]).  nchunks is a multiple of 4, so a group's lanes
+// are all in range or all out.
+template <int FMT, bool DEQ, bool PAIRS, int U>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint4* __restrict__ x,
                                                           uint2* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
                                                           int64_t nchunks, uint4* __restrict__ deq,
                                                           int64_t rows, int64_t gpr, int stage_major) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
-    const uint4 v = x[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t amax = 0;
+  for (int64_t c0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c0 < nchunks; c0 += U * stride) {
+    uint4 v[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      amax = max(amax, abs_bits_bf16(uint16_t(w[k] & 0xffffu)));
-      amax = max(amax, abs_bits_bf16(uint16_t(w[k] >> 16)));
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * stride;
+      v[u] = c < nchunks ? x[c] : make_uint4(0u, 0u, 0u, 0u);
     }
-    amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
-    amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
-    const int X = scale_exp<FMT>(amax);
-    const float inv = inv_scale(X);
-    uint32_t out[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      out[k] = encode4<FMT>(__uint_as_float(w[2 * k] << 16), __uint_as_float(w[2 * k] & 0xffff0000u),
-                            __uint_as_float(w[2 * k + 1] << 16), __uint_as_float(w[2 * k + 1] & 0xffff0000u), inv);
-    if (PAIRS && stage_major) {   // chunk c = 8 codes of row c / (4 gpr)
-      const uint32_t row = uint32_t(c >> 2) / uint32_t(gpr);
-      const int64_t col = (c - int64_t(row) * gpr * 4) * 8;
-      codes[stage_major_off(row, col, rows, gpr * 32) >> 3] = make_uint2(out[0], out[1]);
-    } else {
-      codes[c] = make_uint2(out[0], out[1]);
-    }
-    if ((c & 3) == 0) {
-      if (PAIRS) {   // group G = row * gpr + g  ->  word (g / 4, row), byte g % 4
-        const int64_t G = c >> 2, row = G / gpr, g = G - row * gpr;
-        scales[((g >> 2) * rows + row) * 4 + (g & 3)] = uint8_t(X + 127);
-      } else {
-        scales[c >> 2] = uint8_t(X + 127);
-      }
-    }
-    if (DEQ) {
-      const float sc = pow2_f32(X);
-      deq[c] = make_uint4(deq_pk<FMT, false>(out[0], sc), deq_pk<FMT, true>(out[0], sc),
-                          deq_pk<FMT, false>(out[1], sc), deq_pk<FMT, true>(out[1], sc));
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * stride;
+      if (c < nchunks) quant_rows_chunk<FMT, DEQ, PAIRS>(v[u], c, codes, scales, deq, rows, gpr, stage_major);
     }
   }
 }
@@ -428,13 +450,22 @@ __global__ void __launch_bounds__(256) scales_to_pairs_kernel(const uint32_t* __
 
 // ---------------------------------------------------------------------------
 // host launchers
-template <int FMT>
+template <int FMT, int U>
 static void rows_dispatch(int blocks, hipStream_t st, const uint4* xs, uint2* cs, uint8_t* scales, int64_t nchunks,
                           uint4* ds, int64_t rows, int64_t gpr, bool pairs, int sm) {
-  if (ds) quant_rows_kernel<FMT, true, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, 0);
+  if (ds) quant_rows_kernel<FMT, true, false, U><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, 0);
   else if (pairs)
-    quant_rows_kernel<FMT, false, true><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, sm);
-  else quant_rows_kernel<FMT, false, false><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, 0);
+    quant_rows_kernel<FMT, false, true, U><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, sm);
+  else quant_rows_kernel<FMT, false, false, U><<<blocks, 256, 0, st>>>(xs, cs, scales, nchunks, ds, rows, gpr, 0);
+}
+template <int FMT>
+static void rows_dispatch(int64_t nchunks, hipStream_t st, const uint4* xs, uint2* cs, uint8_t* scales, uint4* ds,
+                          int64_t rows, int64_t gpr, bool pairs, int sm) {
+  const bool small = nchunks <= (int64_t(1) << 22);
+  const int64_t want = small ? (nchunks + 1023) / 1024 : (nchunks + 255) / 256;
+  const int blocks = int(want < 65536 ? want : 65536);
+  if (small) rows_dispatch<FMT, 4>(blocks, st, xs, cs, scales, nchunks, ds, rows, gpr, pairs, sm);
+  else rows_dispatch<FMT, 1>(blocks, st, xs, cs, scales, nchunks, ds, rows, gpr, pairs, sm);
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
@@ -443,14 +474,12 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int 
   if (nchunks == 0) return hipSuccess;
   if (deq && pairs) return hipErrorInvalidValue;   // no caller needs both
   if (stage_major && (!pairs || rows * (cols / 32) > int64_t(UINT32_MAX))) return hipErrorInvalidValue;
-  const int64_t want = (nchunks + 255) / 256;
-  const int blocks = int(want < 65536 ? want : 65536);
   const uint4* xs = reinterpret_cast<const uint4*>(x);
   uint2* cs = reinterpret_cast<uint2*>(codes);
   uint4* ds = reinterpret_cast<uint4*>(deq);
   const int sm = stage_major ? 1 : 0;
-  if (fmt == kE4M3) rows_dispatch<kE4M3>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs, sm);
-  else rows_dispatch<kE5M2>(blocks, st, xs, cs, scales, nchunks, ds, rows, cols / 32, pairs, sm);
+  if (fmt == kE4M3) rows_dispatch<kE4M3>(nchunks, st, xs, cs, scales, ds, rows, cols / 32, pairs, sm);
+  else rows_dispatch<kE5M2>(nchunks, st, xs, cs, scales, ds, rows, cols / 32, pairs, sm);
   return hipGetLastError();
 }
 
