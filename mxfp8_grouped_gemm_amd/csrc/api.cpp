@@ -180,7 +180,8 @@ static int dense_run(const matmul_mxfp8_bwd_args* a, void* ws, size_t ws_bytes, 
   // loop (contraction a multiple of 128), gets them stage-major and runs the
   // four-slot ring: whole cache lines per DMA instruction (mx_device.hpp,
   // stage_major_off).  Operands the caller hands in keep their row-major layout.
-  const bool sm_dx = !pc[0] && !pc[1] && N % 128 == 0 && N < (int64_t(1) << 24) && M * (N / 32) <= int64_t(UINT32_MAX);
+  const bool sm_dx = !pc[0] && !pc[1] && N % 128 == 0 && N < (int64_t(1) << 24) &&
+                     M * (N / 32) <= int64_t(UINT32_MAX);
   const bool sm_dw = !pc[2] && !pc[3] && M % 128 == 0 && M < (int64_t(1) << 24);
   const bool sm[4] = {sm_dx, sm_dx, sm_dw, sm_dw};
   // dY along both axes from one read where the shapes allow (stage 0 then makes stream 2 too)

@@ -14,6 +14,8 @@
 // Scale layouts: row-major [rows][K/32] (one byte per group), or -- for
 // operands of the ring GEMM loop -- pair-major [K/128][rows][4], where word
 // (p, r) holds row r's four groups of K elements [128p, 128p + 128).
+#include <type_traits>
+
 #include "gemm_v2.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
@@ -572,12 +574,18 @@ hipError_t launch_quant_tok(const uint16_t* x, int64_t src_rows, int64_t cols, c
   }
   const int self = self_rows ? 1 : 0, sm = stage_major ? 1 : 0;
   dim3 grid(unsigned((cols + kTokCols - 1) / kTokCols), unsigned((rows + kTokRows - 1) / kTokRows));
+  auto go = [&](auto F, auto PAIRS) {
+    tok_dispatch<decltype(F)::value, decltype(PAIRS)::value>(grid, st, x, src_rows, cols, idx, rowscale, rows,
+                                                             codes_t, scales_t, self, b, sm);
+  };
+  using E4 = std::integral_constant<int, kE4M3>;
+  using E5 = std::integral_constant<int, kE5M2>;
   if (fmt == kE4M3) {
-    if (pairs) tok_dispatch<kE4M3, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
-    else tok_dispatch<kE4M3, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
+    if (pairs) go(E4{}, std::true_type{});
+    else go(E4{}, std::false_type{});
   } else {
-    if (pairs) tok_dispatch<kE5M2, true>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
-    else tok_dispatch<kE5M2, false>(grid, st, x, src_rows, cols, idx, rowscale, rows, codes_t, scales_t, self, b, sm);
+    if (pairs) go(E5{}, std::true_type{});
+    else go(E5{}, std::false_type{});
   }
   return hipGetLastError();
 }
