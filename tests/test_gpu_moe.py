@@ -200,8 +200,8 @@ FULL = {"medium": S.MEDIUM, "large": S.LARGE, "fine": S.FINE}
 @pytest.mark.parametrize("name", list(FULL))
 def test_moe_full_size_sampled(name):
     """The benchmark's sizes and launch configuration.  The oracle computes
-    sampled outputs: whole dX rows and d(a) entries of a few tokens, and whole
-    dW columns / rows of a few intermediate indices of two experts."""
+    sampled outputs: whole dX rows and d(a) entries of 24 tokens, and whole dW
+    columns / rows of 8 intermediate indices of three experts."""
     cfg = FULL[name]
     gp = gpu_problem(cfg)
     out = gp["op"].run()
@@ -211,7 +211,7 @@ def test_moe_full_size_sampled(name):
     assert np.array_equal(host(gp["tpid"]), ex["tpid"]) and np.array_equal(host(gp["b2e"]), ex["b2e"])
     rng = np.random.default_rng(1)
     cnt = np.bincount(gp["topk"].ravel(), minlength=cfg.E)
-    tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 6)])).astype(np.int32)
+    tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 22)])).astype(np.int32)
     dx_r, da_r = oracle.moe_token_rows(p, tokens)
     gdx = bf(host(out["dx"]))[tokens]
     gda = bf(host(out["daff"])).reshape(cfg.T, cfg.E)[tokens]
@@ -219,8 +219,11 @@ def test_moe_full_size_sampled(name):
     assert np.all(gda[bf(da_r) == 0] == 0)
     local = {"dx": parity_stats(gdx, bf(dx_r), rows=len(tokens)),
              "daff": parity_stats(gda, bf(da_r), rows=len(tokens))}
-    experts = [int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30)))]
-    icols = np.unique(np.concatenate([[0, cfg.I - 1], rng.integers(0, cfg.I, 2)])).astype(np.int32)
+    # the busiest, the least busy and a median expert (among those with tokens)
+    live = np.nonzero(cnt > 0)[0]
+    experts = sorted({int(np.argmax(cnt)), int(live[np.argmin(cnt[live])]),
+                      int(live[np.argsort(cnt[live])[len(live) // 2]])})
+    icols = np.unique(np.concatenate([[0, cfg.I - 1], rng.integers(0, cfg.I, 6)])).astype(np.int32)
     errs = {"dx": e_dx, "daff": e_da}
     for e in experts:
         r = oracle.moe_expert_cols(p, e, icols)
