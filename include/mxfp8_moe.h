@@ -381,9 +381,10 @@ size_t moe_bwd_mxfp8_workspace_size(const moe_bwd_mxfp8_args* args);
  * Errors: INVALID_ARG (shapes, null required
  * pointers, alignment, formats, accumulate or activation outside {0,1}), UNSUPPORTED
  * (block_size outside the set, affinity on I together with a bias, or sizes
- * beyond 32-bit indexing: N * block_size or T * E above 2^31 - 1, a [T,H] bf16
- * tensor of 2 GiB or more, i.e. T * H * 2 > 2^31 - 1, which the gathers
- * address through one buffer descriptor, I * block_size * 4 beyond 2 GiB, or a
+ * beyond 32-bit indexing: N * block_size, T * E or T * H above 2^31 - 1 (dY's
+ * [T,H] codes are gathered through one buffer descriptor), a [T,H] bf16 tensor
+ * of 2 GiB or more (T * H * 2 > 2^31 - 1) when H is not a multiple of 128
+ * (Phase 1 then gathers dY's bf16 values that way), I * block_size * 4 beyond 2 GiB, or a
  * 256-row panel of a stage-major operand, 256 * N * block_size or 256 * 2I
  * bytes, beyond 2^32 - 1), WORKSPACE (too small).  Device-side
  * preconditions (not checked): block_to_expert entries in [0,E) (blocks with

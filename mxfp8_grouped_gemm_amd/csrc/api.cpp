@@ -381,8 +381,10 @@ constexpr int64_t kRoundRobinWeightBytes = int64_t(32) << 20;
 // The bias reductions ride on the gather of dY rows (one read of each row)
 // when H is a multiple of 128 and those rows are gathered, i.e. no a*dY
 // checkpoint replaces them; otherwise they run as kernels of their own.
+// The bias reductions inside dY's gather, which then reads dY at 32-bit offsets
+// (under 2 GiB); otherwise their own kernels.
 static bool moe_fuse_bias(const moe_bwd_mxfp8_args* a) {
-  return a->has_bias && a->H % 128 == 0 && !a->down_proj_act_checkpoint;
+  return a->has_bias && a->H % 128 == 0 && !a->down_proj_act_checkpoint && a->T * a->H * 2 <= INT32_MAX;
 }
 
 // Phase 1 with its epilogue in one kernel (the conditions of mx::phase1_fusable,
@@ -447,8 +449,14 @@ static int moe_check_shapes(const moe_bwd_mxfp8_args* a) {
   const int64_t B = a->block_size;
   if (B != 128 && B != 256 && B != 512 && B != 1024)
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: block_size %lld not in {128,256,512,1024}", (long long)B);
-  if (a->N * B > INT32_MAX || a->T * a->E > INT32_MAX || a->T * a->H * 2 > INT32_MAX)
+  if (a->N * B > INT32_MAX || a->T * a->E > INT32_MAX || a->T * a->H > INT32_MAX)
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: sizes beyond 32-bit indexing");
+  // Phase 1 gathers dY's code rows ([T, H] bytes) through one buffer at 32-bit
+  // offsets: T * H < 2^31.  Where H is not a multiple of 128 it gathers dY's
+  // bf16 values (twice the bytes) that way instead.
+  if (a->T * a->H * 2 > INT32_MAX && a->H % 128)
+    return fail(MXFP8_ERR_UNSUPPORTED,
+                "moe_bwd_mxfp8: a [T,H] bf16 tensor of 2 GiB or more needs H %% 128 == 0 (32-bit indexing)");
   // the stage-major operands' panels (256 rows over P slots or 2I) are read through one buffer
   if (a->N * B * 256 > int64_t(UINT32_MAX) || 2 * a->I * 256 > int64_t(UINT32_MAX))
     return fail(MXFP8_ERR_UNSUPPORTED, "moe_bwd_mxfp8: N * block_size = %lld slots beyond 2^24 or I = %lld beyond 2^23",

@@ -96,17 +96,22 @@ def test_moe_bwd_rejects_a_bad_accumulate_flag_without_gpu():
     assert "accumulate" in mx.last_error()
 
 
-def _fake_args(mx, L, T=256, H=128, I=256, E=4, B=128, accumulate=0):
+def _fake_args(mx, L, T=256, H=128, I=256, E=4, B=128, accumulate=0, bias=False):
     fake = 0x10000
     N = L.moe_num_blocks(T, 2, E, B)
-    return mx.MoeBwdArgs(T, H, I, E, N, B, *([fake] * 10), None, 0, 0, mx.E4M3, mx.E4M3, mx.E5M2,
-                         fake, fake, fake, fake, None, None, None, None, None, None, None, accumulate)
+    a = mx.MoeBwdArgs(T, H, I, E, N, B, *([fake] * 10), None, 0, 0, mx.E4M3, mx.E4M3, mx.E5M2,
+                      fake, fake, fake, fake, None, None, None, None, None, None, None, accumulate)
+    if bias:
+        a.has_bias = 1
+        a.down_proj_bias = a.gate_and_up_proj_bias_grad = a.down_proj_bias_grad = fake
+    return a
 
 
 def test_moe_bwd_workspace_and_size_limits_without_gpu():
-    """A workspace below the size query is MXFP8_ERR_WORKSPACE (3), and a [T,H]
-    bf16 tensor of 2 GiB or more is MXFP8_ERR_UNSUPPORTED (2): both found in
-    validation, before any device access (the pointers are never dereferenced)."""
+    """A workspace below the size query is MXFP8_ERR_WORKSPACE (3); T * H of
+    2^31 or more, or a [T,H] bf16 tensor of 2 GiB or more with H not a multiple
+    of 128, is MXFP8_ERR_UNSUPPORTED (2): all found in validation, before any
+    device access (the pointers are never dereferenced)."""
     import mxfp8_grouped_gemm_amd as mx
     L = mx.lib()
     a = _fake_args(mx, L)
@@ -115,13 +120,21 @@ def test_moe_bwd_workspace_and_size_limits_without_gpu():
     assert L.moe_bwd_mxfp8(C.byref(a), C.c_void_p(0x10000), need - 1, None) == 3
     assert "workspace" in mx.last_error()
     assert L.moe_bwd_mxfp8(C.byref(a), C.c_void_p(0x10000), 1024, None) == 3
-    # T * H * 2 = 2^31 bytes: one past the limit; one token fewer is accepted by validation
-    big = _fake_args(mx, L, T=262144, H=4096, I=256, E=8, B=1024)
+    # T * H = 2^31: one past the limit; one token fewer is accepted by validation,
+    # with or without a bias (4 GiB bf16 tensors)
+    big = _fake_args(mx, L, T=524288, H=4096, I=256, E=8, B=1024)
     assert L.moe_bwd_mxfp8(C.byref(big), C.c_void_p(0x10000), 1 << 62, None) == 2
     assert "32-bit" in mx.last_error()
     assert L.moe_bwd_mxfp8_workspace_size(C.byref(big)) == 0
-    ok = _fake_args(mx, L, T=262143, H=4096, I=256, E=8, B=1024)
-    assert L.moe_bwd_mxfp8_workspace_size(C.byref(ok)) > 0
+    for bias in (False, True):
+        ok = _fake_args(mx, L, T=524287, H=4096, I=256, E=8, B=1024, bias=bias)
+        assert L.moe_bwd_mxfp8_workspace_size(C.byref(ok)) > 0
+    # H not a multiple of 128: the bf16 [T,H] tensors stay under 2 GiB
+    odd = _fake_args(mx, L, T=262144, H=4096 + 32, I=256, E=8, B=1024)
+    assert L.moe_bwd_mxfp8(C.byref(odd), C.c_void_p(0x10000), 1 << 62, None) == 2
+    assert "128" in mx.last_error()
+    odd_ok = _fake_args(mx, L, T=262143 * 4096 // (4096 + 32), H=4096 + 32, I=256, E=8, B=1024)
+    assert L.moe_bwd_mxfp8_workspace_size(C.byref(odd_ok)) > 0
     # more than 2^24 slots: a 256-row panel of a stage-major operand over the slots
     # would pass 2^32 bytes
     many = _fake_args(mx, L, T=8_500_000, H=32, I=256, E=8, B=1024)

@@ -202,7 +202,20 @@ def test_moe_full_size_sampled(name):
     """The benchmark's sizes and launch configuration.  The oracle computes
     sampled outputs: whole dX rows and d(a) entries of 24 tokens, and whole dW
     columns / rows of 8 intermediate indices of three experts."""
-    cfg = FULL[name]
+    _check_sampled(FULL[name], name)
+
+
+def test_moe_bf16_inputs_over_2gib_sampled():
+    """X and dY of 2.1 GB each (T * H * 2 above 2^31): the gathers along the
+    slots read them at 64-bit addresses and the bias reductions run in their
+    own kernels.  Sampled as at the full sizes."""
+    cfg = S.scaled(S.FINE, T=262400, H=4096, I=256, E=8, K=1, B=512)
+    assert cfg.T * cfg.H * 2 > 2**31 - 1 and cfg.has_bias
+    _check_sampled(cfg, "over_2gib")
+
+
+def _check_sampled(cfg, name):
+    print(f"{name}: {cfg.name}", flush=True)
     gp = gpu_problem(cfg)
     out = gp["op"].run()
     torch.cuda.synchronize()
