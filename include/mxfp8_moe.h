@@ -339,6 +339,10 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *                                                     live slot tiles, and the total; then
  *                                                     each tile's block
  *   dx_slot [P,H] fp32 (each routed slot's dX row, summed per token at the end),
+ *   phase3_parts: Phase 3's last, partly filled round of tiles cut along K: each
+ *   XCD's cut (256 bytes), then fp32 tiles (up to 256 of 256 x 256 or 128 x 256)
+ *   holding the later K parts of the cut tiles, which are added into dx_slot
+ *   before the stage ends (empty when 2I % 128 != 0 or 2I < 1024),
  *   slot_of [T,E] int32 (the slot of pair (t, e), -1 = none),
  *   daff_slot [P] fp32 (the <dY, b2> term when it is computed on its own, else 0),
  *   daff_part [I/32 (+ H/128), P] fp32 (d(a) partials per 32 rows i; with a bias,
@@ -360,7 +364,8 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
 typedef struct {
   size_t dy_codes, dy_scales, dy_deq, wd_deq, x_tok_codes, x_tok_scales, gy_tok_codes, gy_tok_scales,
       inter_tok_codes, inter_tok_scales, dgu_row_codes, dgu_row_scales, dgu_tok_codes,
-      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_slot, slot_of, daff_slot, daff_part, db1_acc, db2_acc, expert_block_offsets,
+      dgu_tok_scales, wgu_scales_pairs, wd_scales_pairs, phase1_ds, phase1_tiles, phase3_tiles, dx_slot,
+      phase3_parts, slot_of, daff_slot, daff_part, db1_acc, db2_acc, expert_block_offsets,
       expert_block_list, slot_token, slot_affinity, block_flag, total;
 } moe_bwd_mxfp8_workspace_layout;
 

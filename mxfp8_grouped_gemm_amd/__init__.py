@@ -66,7 +66,8 @@ class MoeBwdArgs(C.Structure):
 
 LAYOUT_FIELDS = ("dy_codes", "dy_scales", "dy_deq", "wd_deq", "x_tok_codes", "x_tok_scales", "gy_tok_codes", "gy_tok_scales",
                  "inter_tok_codes", "inter_tok_scales", "dgu_row_codes", "dgu_row_scales", "dgu_tok_codes",
-                 "dgu_tok_scales", "wgu_scales_pairs", "wd_scales_pairs", "phase1_ds", "phase1_tiles", "phase3_tiles", "dx_slot", "slot_of", "daff_slot", "daff_part", "db1_acc", "db2_acc", "expert_block_offsets",
+                 "dgu_tok_scales", "wgu_scales_pairs", "wd_scales_pairs", "phase1_ds", "phase1_tiles", "phase3_tiles", "dx_slot",
+                 "phase3_parts", "slot_of", "daff_slot", "daff_part", "db1_acc", "db2_acc", "expert_block_offsets",
                  "expert_block_list", "slot_token", "slot_affinity", "block_flag", "total")
 
 

@@ -2,6 +2,7 @@
 // carving and the launch sequence on the caller's stream.  No device memory is
 // allocated here and nothing is synchronised.
 #include <climits>
+#include <atomic>
 #include <mutex>
 #include <cstdarg>
 #include <cstdio>
@@ -373,6 +374,21 @@ static SideStream* side_stream(int device) {
   }
   return x.ok ? &x : nullptr;
 }
+// CUs of the device that `st` runs on (0 if unknown), looked up once per device.
+static int device_cus(hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int device = -1;
+  if ((st ? hipStreamGetDevice(st, &device) : hipGetDevice(&device)) != hipSuccess || device < 0 ||
+      device >= kMaxDevices)
+    return 0;
+  int c = cache[device].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || c <= 0) return 0;
+    cache[device].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
 // An expert weight operand at least this large (8x one XCD's 4 MB L2) is shared
 // by all XCDs through the infinity cache: its GEMM hands tiles out round robin
 // (moe_tiles.hpp).
@@ -425,6 +441,11 @@ static int moe_layout(const moe_bwd_mxfp8_args* a, moe_bwd_mxfp8_workspace_layou
   put(L->phase1_tiles, fused ? 0 : (N + 1 + N * ((I + 127) / 128) * ((B + 127) / 128)) * 4);
   put(L->phase3_tiles, (N + 1 + N * ((B + 127) / 128) * ((H + 127) / 128)) * 4);
   put(L->dx_slot, N * B * H * 4);
+  {
+    mx::Phase3Args q{};
+    q.H = H; q.I = I; q.N = N; q.B = B;
+    put(L->phase3_parts, mx::phase3_parts_bytes(q));
+  }
   put(L->slot_of, T * E * 4);
   put(L->daff_slot, P * 4);
   put(L->daff_part, (I / 32 + (moe_fuse_bias(a) ? H / 128 : 0)) * P * 4);
@@ -673,6 +694,9 @@ static int moe_run(const moe_bwd_mxfp8_args* a, void* ws, size_t ws_bytes, void*
   p3.slot_tok = slot_tok; p3.b2e = a->block_to_expert; p3.flag = flag;
   p3.tile_start = reinterpret_cast<int32_t*>(at(L.phase3_tiles));
   p3.H = H; p3.I = I; p3.N = N; p3.B = B; p3.dx_slot = dx_slot;
+  // the last round of tiles cut along K over the device's CUs
+  p3.conc = device_cus(st);
+  p3.parts = mx::phase3_parts_bytes(p3) > 0 ? at(L.phase3_parts) : nullptr;
   // measured: round robin 4.8% faster with 117 MB W_gate_up experts, the
   // contiguous ranges 6-14% faster with 0.8-6 MB ones
   p3.rr_tiles = H * 2 * I >= kRoundRobinWeightBytes;

@@ -111,7 +111,9 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
 // and that scratch's device address on `device` (looked up once per device)
 int64_t build_blocks_noalloc_max_experts();
 hipError_t build_blocks_scratch(int device, int32_t** out);
-hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st);
+struct TailCut;
+hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st,
+                              TailCut* cut = nullptr, int conc = 0, int npairs = 0, int rr = 0);
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,
                              int32_t* slot_of, int32_t* flag, int32_t* off, int32_t* list, hipStream_t st);
@@ -188,10 +190,18 @@ struct Phase3Args {
   int64_t H, I, N, B;
   float* dx_slot;                 // [P][H] fp32: each routed slot's row of dX
   int rr_tiles;                   // tile order over the XCDs (moe_tiles.hpp)
-  int tiles_m, tiles_n;
+  // The last round of tiles cut along K (moe_tiles.hpp, TailCut): conc =
+  // workgroups resident at once (0: no cut); parts = phase3_parts_bytes(...)
+  // bytes: the cut of each XCD (8 TailCut, 256 bytes), then the later parts'
+  // fp32 tiles
+  int conc;
+  uint8_t* parts;
+  int tiles_m, tiles_n, grid_main, npairs;   // set by the launcher
 };
 hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st);
 // Phase 3 tiles when every slot tile of every block is live (an upper bound)
 int64_t phase3_max_tiles(const Phase3Args& p);
+// bytes of the parts buffer (H, I, N, B set)
+int64_t phase3_parts_bytes(const Phase3Args& p);
 
 }  // namespace mx

@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "kernels.hpp"
+#include "moe_tiles.hpp"
 #include "mx_device.hpp"
 #include "swiglu.hpp"
 
@@ -426,7 +427,8 @@ __global__ void __launch_bounds__(256) expert_list_kernel(const int32_t* __restr
 // GEMM workgroup finds its block with one load instead of a binary search
 // (a dozen dependent loads before its first DMA).  One workgroup.
 __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restrict__ ext, int N, int W, int other,
-                                                          int32_t* __restrict__ start) {
+                                                          int32_t* __restrict__ start, TailCut* __restrict__ cut,
+                                                          int conc, int npairs, int rr) {
   __shared__ int red[4];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
@@ -441,7 +443,18 @@ __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restr
     if (threadIdx.x == 0) carry += tot;
     __syncthreads();
   }
-  if (threadIdx.x == 0) start[N] = carry;
+  if (threadIdx.x == 0) {
+    start[N] = carry;
+    if (cut) {   // the tail cut of each XCD
+      int base = 0;
+      for (int x = 0; x < 8; ++x) {
+        TailCut c = tail_cut_one(carry, x, rr, conc, npairs);
+        c.base = base;
+        base += c.tail * (c.S - 1);
+        cut[x] = c;
+      }
+    }
+  }
   __syncthreads();   // the starts written above are visible to the whole workgroup
   int32_t* map = start + N + 1;
   for (int b = threadIdx.x; b < N; b += 256) {
@@ -450,8 +463,9 @@ __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restr
   }
 }
 
-hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st) {
-  tile_ranges_kernel<<<1, 256, 0, st>>>(ext, int(N), W, other, start);
+hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st,
+                              TailCut* cut, int conc, int npairs, int rr) {
+  tile_ranges_kernel<<<1, 256, 0, st>>>(ext, int(N), W, other, start, cut, conc, npairs, rr);
   return hipGetLastError();
 }
 

@@ -34,6 +34,121 @@ __device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int wg) {
   return P3Pos{bt.b, int64_t(tm) * BM, int64_t(tn) * BN};
 }
 
+// ---------------------------------------------------------------------------
+// The last round of tiles, cut along K (moe_tiles.hpp, TailCut; the cut of each
+// XCD is computed with the tile ranges).  A cut tile's own workgroup runs its
+// first part and stores its rows to dx_slot as usual; extra workgroups after
+// the main grid (ids x mod 8 again: the same XCD, after its last round has
+// started) run the other parts and store their fp32 tiles to the parts
+// buffer; p3_fixup_kernel then adds those into dx_slot in part order, so the
+// result stays the same from run to run.
+constexpr int kP3MaxExtra = 256;   // extra workgroups (and part tiles) at most
+
+__device__ __forceinline__ const TailCut* p3_cuts(const Phase3Args& p) {
+  return reinterpret_cast<const TailCut*>(p.parts);
+}
+__device__ __forceinline__ float* p3_part_tiles(const Phase3Args& p) {
+  return reinterpret_cast<float*>(p.parts + 256);
+}
+
+// What workgroup wg runs: a whole tile, the first part of a cut tile (its own
+// id), or another part (ids from grid_main on), and where that part goes.
+struct P3Work {
+  P3Pos tp;        // tp.b < 0: nothing
+  int pair0, npairs;
+  int part_slot;   // >= 0: the fp32 tile goes to part tile part_slot
+};
+template <int BM, int BN>
+__device__ __forceinline__ P3Work p3_work(const Phase3Args& p, int wg) {
+  P3Work w{P3Pos{-1, 0, 0}, 0, p.npairs, -1};
+  const bool extra = wg >= p.grid_main;
+  if (p.conc <= 0) {
+    if (!extra) w.tp = p3_pos<BM, BN>(p, wg);
+    return w;
+  }
+  const int e = extra ? wg - p.grid_main : wg;
+  const int x = e % 8, q = e / 8;
+  const TailCut c = p3_cuts(p)[x];
+  int main_wg = wg, part = 0;
+  bool cut;
+  if (extra) {
+    if (q >= c.tail * (c.S - 1)) return w;   // also every extra id when nothing is cut
+    const int i = q / (c.S - 1);
+    part = 1 + q % (c.S - 1);
+    main_wg = 8 * (c.nx - c.tail + i) + x;
+    w.part_slot = c.base + q;
+    cut = true;
+  } else {
+    cut = q >= c.nx - c.tail && q < c.nx;   // tail == 0: never
+  }
+  w.tp = p3_pos<BM, BN>(p, main_wg);
+  if (cut) {
+    w.pair0 = part * p.npairs / c.S;
+    w.npairs = (part + 1) * p.npairs / c.S - w.pair0;
+  }
+  return w;
+}
+
+// stage s of a part that starts at stage s0
+struct P3KMap {
+  int s0;
+  __device__ __forceinline__ uint32_t operator()(int s) const { return uint32_t(s + s0) * v3::SK; }
+};
+
+// A part's fp32 tile, row-major BM x BN (lanes of a fragment row write 128
+// consecutive bytes).
+template <int BM, int BN>
+__device__ __forceinline__ void p3_store_part(float* dst, const v16f (&acc)[BM / 64][BN / 64]) {
+  v2::static_for<BM / 64>([&](auto FI) {
+    v2::static_for<16>([&](auto Q) {
+      float* row = dst + v2::acc_row<BM, BN>(FI, Q) * BN;
+      v2::static_for<BN / 64>([&](auto FJ) { row[v2::acc_col<BM, BN>(FJ)] = acc[FI][FJ][int(Q)]; });
+    });
+  });
+}
+
+// dx_slot += the other parts of each cut tile, in part order.  One workgroup
+// per 16 rows of a cut tile: ids x + 8 (i * BM / 16 + slab) for tile i of XCD
+// x; a thread takes one 4-column group of 4 rows, all of its loads issued
+// before the sums.
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) p3_fixup_kernel(Phase3Args p) {
+  constexpr int NSL = BM / 16, CG = BN / 4;   // slabs per tile, 4-column groups per row
+  static_assert(CG * 4 == 256, "a thread per 4-column group and row of 4");
+  const int x = blockIdx.x % 8, rest = blockIdx.x / 8, i = rest / NSL, slab = rest % NSL;
+  const TailCut c = p3_cuts(p)[x];
+  if (i >= c.tail) return;
+  const P3Pos tp = p3_pos<BM, BN>(p, 8 * (c.nx - c.tail + i) + x);
+  if (tp.b < 0) return;
+  const int col = (threadIdx.x % CG) * 4, r0 = slab * 16 + threadIdx.x / CG;
+  if (tp.n0 + col >= p.H) return;   // H % 32 == 0: a group is all inside or all outside
+  const float* part = p3_part_tiles(p) + int64_t(c.base + i * (c.S - 1)) * (BM * BN);
+  float* out = p.dx_slot + (int64_t(tp.b) * p.B + tp.m0) * p.H + tp.n0 + col;
+  float4 v[4], q[kCutMaxParts - 1][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = r0 + 4 * j;
+    v[j] = *reinterpret_cast<const float4*>(out + int64_t(r) * p.H);
+#pragma unroll
+    for (int k = 0; k < kCutMaxParts - 1; ++k)
+      q[k][j] = k < c.S - 1 ? *reinterpret_cast<const float4*>(part + int64_t(k) * (BM * BN) + r * BN + col)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < kCutMaxParts - 1; ++k) {
+      if (k < c.S - 1) {
+        v[j].x += q[k][j].x;
+        v[j].y += q[k][j].y;
+        v[j].z += q[k][j].z;
+        v[j].w += q[k][j].w;
+      }
+    }
+    *reinterpret_cast<float4*>(out + int64_t(r0 + 4 * j) * p.H) = v[j];
+  }
+}
+
 // dX rows of one tile.  Every slot of the tile stores its row: a padding
 // slot's dGU row is zeros, so its row is zeros too, and the finalisation
 // reads only routed slots' rows.  (Storing only routed rows made every store
@@ -122,7 +237,8 @@ template <int BM, int BN, int FG, int FW>
 __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[v3::smem_bytes(BM, BN)];
   constexpr int FM = BM / 64, FN = BN / 64;
-  const P3Pos tp = p3_pos<BM, BN>(p, blockIdx.x);
+  const P3Work w = p3_work<BM, BN>(p, blockIdx.x);
+  const P3Pos& tp = w.tp;
   if (tp.b < 0) return;
   const int64_t e = p.b2e[tp.b];
   const int64_t sbase = int64_t(tp.b) * p.B, twoI = 2 * p.I;
@@ -138,17 +254,33 @@ __global__ void __launch_bounds__(v2::kThreads) phase3_ring(Phase3Args p) {
   v3::setup_scales(sd, p.dgu_row_scales, sbase + tp.m0, P, P * (twoI / 32), p.wgu_scales + e * p.H * (twoI / 32),
                    tp.n0, p.H, p.H * (twoI / 32));
   v16f acc[FM][FN];
-  v3::mainloop<BM, BN, v3::kFp8, FG, FW>(A, B, &sd, int(twoI / v3::SK), v3::KMapPlain{}, smem, acc);
-  p3_store_staged<BM, BN, sizeof(smem)>(p, tp, acc, smem);
+  v3::mainloop<BM, BN, v3::kFp8, FG, FW>(A, B, &sd, 2 * w.npairs, P3KMap{2 * w.pair0}, smem, acc);
+  if (w.part_slot >= 0)
+    p3_store_part<BM, BN>(p3_part_tiles(p) + int64_t(w.part_slot) * (BM * BN), acc);
+  else
+    p3_store_staged<BM, BN, sizeof(smem)>(p, tp, acc, smem);
 }
 
 template <int BM, int BN>
 static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipStream_t st) {
+  // the ring's LDS keeps these tiles at one workgroup per CU, so the CU count
+  // is the number resident at once (TailCut)
+  static_assert(2 * v3::smem_bytes(BM, BN) > 160 * 1024, "one workgroup per CU");
   p.tiles_m = int((p.B + BM - 1) / BM);
   p.tiles_n = int((p.H + BN - 1) / BN);
   const int64_t total = (int64_t(p.tiles_m) * p.tiles_n * p.N + 7) & ~int64_t(7);   // every tile, rounded to 8
-  if (total > INT32_MAX) return hipErrorInvalidValue;
-  hipError_t e = launch_tile_ranges(p.flag, p.N, BM, p.tiles_n, p.tile_start, st);
+  if (total + kP3MaxExtra > INT32_MAX) return hipErrorInvalidValue;
+  p.grid_main = int(total);
+  p.npairs = int(2 * p.I / 128);
+  // the cut needs the ring, the parts buffer, whole XCDs of CUs (at most
+  // kP3MaxExtra: the extra workgroups and part tiles) and at least two parts'
+  // worth of stage pairs
+  const bool cut = !generic && p.parts && phase3_parts_bytes(p) > 0 && p.conc >= 8 && p.conc % 8 == 0 &&
+                   p.conc <= kP3MaxExtra && p.npairs >= 2 * kCutMinPairs;
+  if (!cut) p.conc = 0;
+  hipError_t e = launch_tile_ranges(p.flag, p.N, BM, p.tiles_n, p.tile_start, st,
+                                    cut ? reinterpret_cast<TailCut*>(p.parts) : nullptr, p.conc, p.npairs,
+                                    p.rr_tiles);
   if (e != hipSuccess) return e;
   if (generic) {
     const unsigned grid = unsigned(total);
@@ -157,11 +289,12 @@ static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipS
     else if (fw == 0) phase3_generic<BM, BN, 1, 0><<<grid, v2::kThreads, 0, st>>>(p);
     else phase3_generic<BM, BN, 1, 1><<<grid, v2::kThreads, 0, st>>>(p);
   } else {
-    const unsigned grid = unsigned(total);
+    const unsigned grid = unsigned(total + p.conc);   // p.conc extra workgroups for the cut parts
     if (fg == 0 && fw == 0) phase3_ring<BM, BN, 0, 0><<<grid, v2::kThreads, 0, st>>>(p);
     else if (fg == 0) phase3_ring<BM, BN, 0, 1><<<grid, v2::kThreads, 0, st>>>(p);
     else if (fw == 0) phase3_ring<BM, BN, 1, 0><<<grid, v2::kThreads, 0, st>>>(p);
     else phase3_ring<BM, BN, 1, 1><<<grid, v2::kThreads, 0, st>>>(p);
+    if (p.conc) p3_fixup_kernel<BM, BN><<<unsigned(p.conc * (BM / 16)), 256, 0, st>>>(p);
   }
   return hipGetLastError();
 }
@@ -182,6 +315,17 @@ hipError_t launch_phase3(const Phase3Args& p, int fg, int fw, hipStream_t st) {
 int64_t phase3_max_tiles(const Phase3Args& p) {
   const int64_t bm = phase3_wide(p) ? 256 : 128, bn = 256;
   return p.N * ((p.B + bm - 1) / bm) * ((p.H + bn - 1) / bn);
+}
+
+// The parts buffer: the 8 XCDs' cuts (256 bytes), then the later parts' tiles:
+// fewer than the extra workgroups, and at most kCutMaxParts - 1 per tile.
+// Empty where nothing can be cut (the v2 loop, or too few stage pairs).
+int64_t phase3_parts_bytes(const Phase3Args& p) {
+  if ((2 * p.I) % v2::BK != 0 || 2 * p.I / 128 < 2 * kCutMinPairs) return 0;
+  const int64_t bm = phase3_wide(p) ? 256 : 128, bn = 256;
+  int64_t tiles = (kCutMaxParts - 1) * phase3_max_tiles(p);
+  tiles = tiles < kP3MaxExtra ? tiles : kP3MaxExtra;
+  return 256 + tiles * bm * bn * 4;
 }
 
 }  // namespace mx

@@ -46,4 +46,46 @@ __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, in
   return true;
 }
 
+// The last round of a GEMM's tiles cut along K (Phase 3, moe_phase3.hip).
+// The tiles take equal times and run in rounds of `conc` workgroups (those
+// resident at once), conc / 8 per XCD; XCD x runs the workgroup ids equal to
+// x mod 8 in order and holds nx of the live tiles, and its last
+// nx mod (conc / 8) tiles would run while most of its CUs idle.  Each of
+// those is cut into S parts of whole stage pairs, S <= kCutMaxParts, at least
+// kCutMinPairs pairs a part, S * tail <= conc / 8; the parts after the first
+// are numbered XCD by XCD (base), tile by tile, part by part.  A part pays a
+// tile's fixed costs (the ring's fill, its store) and the parts are added up
+// afterwards, so the cut pays only on long contractions: measured on Phase 3,
+// 6% faster with 448 stages a tile (2I = 28672), slower with 44 (2I = 2816).
+constexpr int kCutMaxParts = 4;
+constexpr int kCutMinPairs = 16;
+struct TailCut {
+  int nx;     // live tiles of the XCD
+  int tail;   // its last `tail` tiles are cut (0: none)
+  int S;      // parts of a cut tile
+  int base;   // number of the XCD's first later part
+};
+__host__ __device__ inline TailCut tail_cut_one(int total, int x, int rr, int conc, int npairs) {
+  int nx;
+  if (rr) {   // ids as dispatched
+    nx = total > x ? (total - x + 7) / 8 : 0;
+  } else {    // block_tile's contiguous ranges of t8 / 8 ids
+    const int per = ((total + 7) & ~7) / 8;
+    nx = total - x * per < per ? total - x * per : per;
+    nx = nx > 0 ? nx : 0;
+  }
+  TailCut c{nx, 0, 1, 0};
+  const int cx = conc / 8;
+  const int r = cx > 0 ? nx % cx : 0;
+  if (r == 0) return c;
+  int S = cx / r;
+  S = S < kCutMaxParts ? S : kCutMaxParts;
+  S = S < npairs / kCutMinPairs ? S : npairs / kCutMinPairs;
+  if (S > 1) {
+    c.tail = r;
+    c.S = S;
+  }
+  return c;
+}
+
 }  // namespace mx

@@ -29,7 +29,9 @@ SMALL = {
     "ragged_panels": S.scaled(S.MEDIUM, T=384, H=384, I=192, E=4, K=2, B=128),
 }
 # experts of 32 MiB (W_down) and 64 MiB (W_gate_up): Phases 1 and 3 hand their
-# tiles to the XCDs round robin, which no other small case reaches
+# tiles to the XCDs round robin, which no other small case reaches; with 2I =
+# 16384 and fewer tiles than CUs, Phase 3 also cuts every tile along K into
+# parts summed afterwards
 ROUND_ROBIN = {"large_rr": S.scaled(S.LARGE, T=256, H=4096, I=8192, E=2, K=1, B=128)}
 
 
@@ -200,7 +202,7 @@ FULL = {"medium": S.MEDIUM, "large": S.LARGE, "fine": S.FINE}
 @pytest.mark.parametrize("name", list(FULL))
 def test_moe_full_size_sampled(name):
     """The benchmark's sizes and launch configuration.  The oracle computes
-    sampled outputs: whole dX rows and d(a) entries of 24 tokens, and whole dW
+    sampled outputs: whole dX rows and d(a) entries of 26 tokens, and whole dW
     columns / rows of 8 intermediate indices of three experts."""
     _check_sampled(FULL[name], name)
 
@@ -224,7 +226,12 @@ def _check_sampled(cfg, name):
     assert np.array_equal(host(gp["tpid"]), ex["tpid"]) and np.array_equal(host(gp["b2e"]), ex["b2e"])
     rng = np.random.default_rng(1)
     cnt = np.bincount(gp["topk"].ravel(), minlength=cfg.E)
-    tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 22)])).astype(np.int32)
+    # plus the tokens of the last two routed slots: the last live block's last
+    # slot tile, in Phase 3's last round of tiles (cut along K at long 2I)
+    tp = host(gp["tpid"]).reshape(-1)
+    routed = np.nonzero((tp >= 0) & (tp < cfg.T))[0]
+    tokens = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 22),
+                                       tp[routed[-2:]]])).astype(np.int32)
     dx_r, da_r = oracle.moe_token_rows(p, tokens)
     gdx = bf(host(out["dx"]))[tokens]
     gda = bf(host(out["daff"])).reshape(cfg.T, cfg.E)[tokens]
