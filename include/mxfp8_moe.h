@@ -342,7 +342,7 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *   phase3_parts: Phase 3's last, partly filled round of tiles cut along K: each
  *   XCD's cut (256 bytes), then fp32 tiles (up to 256 of 256 x 256 or 128 x 256)
  *   holding the later K parts of the cut tiles, which are added into dx_slot
- *   before the stage ends (empty when 2I % 128 != 0 or 2I < 1024),
+ *   before the stage ends (empty when 2I % 128 != 0 or 2I < 4096),
  *   slot_of [T,E] int32 (the slot of pair (t, e), -1 = none),
  *   daff_slot [P] fp32 (the <dY, b2> term when it is computed on its own, else 0),
  *   daff_part [I/32 (+ H/128), P] fp32 (d(a) partials per 32 rows i; with a bias,
