@@ -148,24 +148,26 @@ def test_moe_build_blocks_bit_exact_and_edge_cases():
         mx.moe_build_blocks(torch.zeros((4, 2), dtype=torch.int32, device="cuda"), 4, 128, 1)
 
 
-def test_moe_deterministic_weight_grads_and_dy_scaling():
-    """Phases 2/4, the per-token dX sums and the d(a) partials have a fixed
-    summation order: repeated runs give identical dW, dX and d(a), and scaling dY
-    by 2^3 scales them by exactly 8 (the E8M0 scales absorb it).  The bias sums
-    use atomics."""
-    cfg = SMALL["fine_s"]
+@pytest.mark.parametrize("name", ["fine_s", "cut_contiguous"])
+def test_moe_deterministic_weight_grads_and_dy_scaling(name):
+    """Phases 2/4, the per-token dX sums, Phase 3's cut tiles (cut_contiguous)
+    and the d(a) partials have a fixed summation order: repeated runs give
+    identical dW, dX and d(a), and scaling dY by 2^3 scales them by exactly 8
+    (the E8M0 scales absorb it).  The bias sums use atomics."""
+    cfg = SMALL[name]
     gp = gpu_problem(cfg)
     a = {k: v.clone() for k, v in gp["op"].run().items() if v is not None}
     b = gp["op"].run()
     for k in ("dwgu", "dwd", "dx", "daff"):
         assert torch.equal(a[k], b[k]), k
-    for k in ("db1", "db2"):
+    bias = ("db1", "db2") if cfg.has_bias else ()
+    for k in bias:
         assert rel_fro(bf(host(b[k])), bf(host(a[k]))) < 1e-5, k
     gp["t"]["dy"].mul_(8.0)
     c = gp["op"].run()
     for k in ("dwgu", "dwd", "dx", "daff"):
         assert torch.equal(c[k].float(), 8.0 * a[k].float()), k
-    for k in ("db1", "db2"):
+    for k in bias:
         assert rel_fro(bf(host(c[k])), 8.0 * bf(host(a[k]))) < 1e-5, k
 
 
