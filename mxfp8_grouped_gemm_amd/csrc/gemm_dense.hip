@@ -102,14 +102,26 @@ __device__ __forceinline__ void store_tile_staged(const GemmStoreArgs& p, int g,
     });
   });
   __syncthreads();
-  uint16_t* out = p.out + int64_t(g) * p.out_gstride;
-  constexpr int CPR = BM * 2 / 16;  // 16-byte runs per row
+  // a thread keeps one 16-byte column run and walks the rows RPP apart, so its
+  // addresses advance by constants; whole tiles skip the row test
+  constexpr int CPR = BM * 2 / 16;           // 16-byte runs per row
+  constexpr int RPP = v2::kThreads / CPR;    // rows per pass
+  static_assert(v2::kThreads % CPR == 0 && BN % RPP == 0, "passes of whole rows");
+  const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+  const int64_t ocol = m0 + ch * 8;
+  if (ocol >= p.M) return;
+  uint16_t* dst = p.out + int64_t(g) * p.out_gstride + (n0 + r0) * p.ldo + ocol;
+  const uint8_t* src = smem + r0 * RB + ch * 16;
+  const int64_t step = int64_t(RPP) * p.ldo;
+  if (n0 + BN <= p.N) {
+#pragma unroll
+    for (int q = 0; q < BN / RPP; ++q)
+      store_nt(dst + q * step, *reinterpret_cast<const uint4*>(src + q * (RPP * RB)));
+  } else {
+    const int64_t nr = p.N - n0;   // rows of the tile inside the output
 #pragma unroll 4
-  for (int k = threadIdx.x; k < BN * CPR; k += v2::kThreads) {
-    const int r = k / CPR, ch = k % CPR;
-    const int64_t orow = n0 + r, ocol = m0 + ch * 8;
-    if (orow < p.N && ocol < p.M)
-      store_nt(out + orow * p.ldo + ocol, *reinterpret_cast<const uint4*>(smem + r * RB + ch * 16));
+    for (int q = 0; q < BN / RPP; ++q)
+      if (r0 + q * RPP < nr) store_nt(dst + q * step, *reinterpret_cast<const uint4*>(src + q * (RPP * RB)));
   }
 }
 

@@ -199,12 +199,17 @@ __device__ __forceinline__ void p3_store_staged(const Phase3Args& p, const P3Pos
       });
     }
     __syncthreads();
-#pragma unroll 4
-    for (int k = threadIdx.x; k < R * CPR; k += v2::kThreads) {
-      const int r = k / CPR, ch = k % CPR;
-      const int64_t s = tp.m0 + int(PASS) * R + r, hh = tp.n0 + ch * 4;
-      if (hh < p.H)
-        store_nt(p.dx_slot + (sbase + s) * p.H + hh, *reinterpret_cast<const uint4*>(smem + r * RB + ch * 16));
+    // a thread keeps one 16-byte column run and walks the rows RPP apart
+    constexpr int RPP = v2::kThreads / CPR;   // rows per pass
+    static_assert(v2::kThreads % CPR == 0 && R % RPP == 0, "passes of whole rows");
+    const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+    const int64_t hh = tp.n0 + ch * 4;
+    if (hh < p.H) {
+      float* dst = p.dx_slot + (sbase + tp.m0 + int(PASS) * R + r0) * p.H + hh;
+      const uint8_t* src = smem + r0 * RB + ch * 16;
+#pragma unroll 8
+      for (int q = 0; q < R / RPP; ++q)
+        store_nt(dst + int64_t(q) * RPP * p.H, *reinterpret_cast<const uint4*>(src + q * (RPP * RB)));
     }
   });
 }
