@@ -336,7 +336,9 @@ typedef enum { MXFP8_ACT_SWIGLU = 0, MXFP8_ACT_GEGLU = 1 } mxfp8_activation;
  *                                                     H % 128 == 0, H <= 2048, I <= 512 and
  *                                                     no caller checkpoints)
  *   phase1_tiles/phase3_tiles [N+1 + tiles] int32     first tile of each block over its
- *                                                     live slot tiles, and the total; then
+ *                                                     live slot tiles (with round-robin tile
+ *                                                     order the blocks whose slot tiles are
+ *                                                     all live first), and the total; then
  *                                                     each tile's block
  *   dx_slot [P,H] fp32 (each routed slot's dX row, summed per token at the end),
  *   phase3_parts: Phase 3's last, partly filled round of tiles cut along K: each

@@ -112,8 +112,10 @@ hipError_t launch_build_blocks(const int32_t* topk, int64_t T, int64_t K, int64_
 int64_t build_blocks_noalloc_max_experts();
 hipError_t build_blocks_scratch(int device, int32_t** out);
 struct TailCut;
+// rr: the tiles handed out round robin over the XCDs (the blocks whose slot
+// tiles are all live first, blk = the block size); cut: Phase 3's tail cut
 hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st,
-                              TailCut* cut = nullptr, int conc = 0, int npairs = 0, int rr = 0);
+                              TailCut* cut, int conc, int npairs, int rr, int blk);
 hipError_t launch_slot_setup(const int32_t* tpid, const int32_t* b2e, const float* aff, int64_t T, int64_t E,
                              int64_t N, int64_t B, const int32_t* nvalid, int32_t* slot_tok, float* slot_aff,
                              int32_t* slot_of, int32_t* flag, int32_t* off, int32_t* list, hipStream_t st);

@@ -428,44 +428,59 @@ __global__ void __launch_bounds__(256) expert_list_kernel(const int32_t* __restr
 // (a dozen dependent loads before its first DMA).  One workgroup.
 __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restrict__ ext, int N, int W, int other,
                                                           int32_t* __restrict__ start, TailCut* __restrict__ cut,
-                                                          int conc, int npairs, int rr) {
+                                                          int conc, int npairs, int rr, int cmax) {
+  // With rr, the blocks whose slot tiles are all live (cmax tiles) come first,
+  // in block order, and the partly filled ones after them: every round of
+  // tiles then covers whole blocks of one expert (moe_tiles.hpp).
   __shared__ int red[4];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
+  __shared__ int carry_full, carry_part;
+  if (threadIdx.x == 0) carry_full = carry_part = 0;
   __syncthreads();
   for (int b0 = 0; b0 < N; b0 += 256) {
     const int b = b0 + threadIdx.x;
     const int c = b < N ? (ext[b] + W - 1) / W * other : 0;
-    int tot;
-    const int pos = block_exclusive_scan(c, red, &tot) + carry;
-    if (b < N) start[b] = pos;
+    const bool full = rr && c == cmax;
+    int tot_full, tot_part;
+    const int pos_full = block_exclusive_scan(full ? c : 0, red, &tot_full) + carry_full;
+    const int pos_part = block_exclusive_scan(full ? 0 : c, red, &tot_part) + carry_part;
+    if (b < N) start[b] = full ? pos_full : pos_part;   // partly filled blocks: relative for now
     __syncthreads();
-    if (threadIdx.x == 0) carry += tot;
+    if (threadIdx.x == 0) {
+      carry_full += tot_full;
+      carry_part += tot_part;
+    }
     __syncthreads();
   }
+  const int total = carry_full + carry_part;
+  // partly filled blocks after the full ones
+  for (int b = threadIdx.x; b < N; b += 256) {
+    const int c = (ext[b] + W - 1) / W * other;
+    if (!(rr && c == cmax)) start[b] += carry_full;
+  }
   if (threadIdx.x == 0) {
-    start[N] = carry;
+    start[N] = total;
     if (cut) {   // the tail cut of each XCD
       int base = 0;
       for (int x = 0; x < 8; ++x) {
-        TailCut c = tail_cut_one(carry, x, rr, conc, npairs);
-        c.base = base;
-        base += c.tail * (c.S - 1);
-        cut[x] = c;
+        TailCut tc = tail_cut_one(total, x, rr, conc, npairs);
+        tc.base = base;
+        base += tc.tail * (tc.S - 1);
+        cut[x] = tc;
       }
     }
   }
   __syncthreads();   // the starts written above are visible to the whole workgroup
   int32_t* map = start + N + 1;
   for (int b = threadIdx.x; b < N; b += 256) {
-    const int t1 = start[b + 1];
-    for (int t = start[b]; t < t1; ++t) map[t] = b;
+    const int t0 = start[b], c = (ext[b] + W - 1) / W * other;
+    for (int t = t0; t < t0 + c; ++t) map[t] = b;
   }
 }
 
 hipError_t launch_tile_ranges(const int32_t* ext, int64_t N, int W, int other, int32_t* start, hipStream_t st,
-                              TailCut* cut, int conc, int npairs, int rr) {
-  tile_ranges_kernel<<<1, 256, 0, st>>>(ext, int(N), W, other, start, cut, conc, npairs, rr);
+                              TailCut* cut, int conc, int npairs, int rr, int blk) {
+  const int cmax = (blk + W - 1) / W * other;   // tiles of a block whose slot tiles are all live
+  tile_ranges_kernel<<<1, 256, 0, st>>>(ext, int(N), W, other, start, cut, conc, npairs, rr, cmax);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(v2::kThreads) phase1_kernel(Phase1Args p) {
   constexpr int FM = BM / 64, FN = BN / 64;
   // live tiles only: block b's slot tiles up to its extent, times the I tiles
   BlockTiles bt;
-  if (!block_tile(p.tile_start, int(p.N), p.tiles_m, blockIdx.x, p.rr_tiles, bt)) return;
+  if (!block_tile(p.tile_start, p.flag, BN, int(p.N), blockIdx.x, p.rr_tiles, bt)) return;
   const int b = bt.b;
   int tm, tn;
   v2::grouped_tile<8>(bt.local, p.tiles_m, bt.slots, tm, tn);
@@ -125,7 +125,8 @@ hipError_t phase1_launch(Phase1Args p, int fg, int fw, hipStream_t st) {
   const int64_t blocks = (int64_t(p.tiles_m) * p.tiles_n * p.N + 7) & ~int64_t(7);   // every tile, rounded to 8
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const unsigned grid = unsigned(blocks);
-  hipError_t e = launch_tile_ranges(p.flag, p.N, BN, p.tiles_m, p.tile_start, st);
+  hipError_t e = launch_tile_ranges(p.flag, p.N, BN, p.tiles_m, p.tile_start, st, nullptr, 0, 0, p.rr_tiles,
+                                    int(p.B));
   if (e != hipSuccess) return e;
   if (G) {   // the bf16 values carry no format
     phase1_go<BM, BN, G, kE4M3, kE4M3>(p, grid, st);

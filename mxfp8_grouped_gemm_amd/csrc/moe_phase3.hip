@@ -28,7 +28,7 @@ struct P3Pos {
 template <int BM, int BN>
 __device__ __forceinline__ P3Pos p3_pos(const Phase3Args& p, int wg) {
   BlockTiles bt;
-  if (!block_tile(p.tile_start, int(p.N), p.tiles_n, wg, p.rr_tiles, bt)) return P3Pos{-1, 0, 0};
+  if (!block_tile(p.tile_start, p.flag, BM, int(p.N), wg, p.rr_tiles, bt)) return P3Pos{-1, 0, 0};
   int tm, tn;
   v2::grouped_tile<8>(bt.local, bt.slots, p.tiles_n, tm, tn);
   return P3Pos{bt.b, int64_t(tm) * BM, int64_t(tn) * BN};
@@ -285,7 +285,7 @@ static hipError_t phase3_launch(Phase3Args p, int fg, int fw, bool generic, hipS
   if (!cut) p.conc = 0;
   hipError_t e = launch_tile_ranges(p.flag, p.N, BM, p.tiles_n, p.tile_start, st,
                                     cut ? reinterpret_cast<TailCut*>(p.parts) : nullptr, p.conc, p.npairs,
-                                    p.rr_tiles);
+                                    p.rr_tiles, int(p.B));
   if (e != hipSuccess) return e;
   if (generic) {
     const unsigned grid = unsigned(total);

@@ -2,7 +2,7 @@
 //
 // Block b's slots past its extent (one past its last routed slot) are padding,
 // so the block contributes ceil(extent / W) slot tiles of W slots, each times
-// `other` tiles along the GEMM's other dimension.  start[b] (b = 0..N) is the
+// `other` tiles along the GEMM's other dimension.  start[b] (b = 0..N-1) is the
 // index of block b's first tile and start[N] the total, built on the device
 // before the GEMM (launch_tile_ranges), followed by each tile's block
 // (start[N + 1 + t]).  The GEMM's grid covers every tile a
@@ -31,9 +31,12 @@ struct BlockTiles {
 //     weights together through the infinity cache -- the better order for
 //     weights many times the L2, which no single XCD can keep.  With a
 //     block's tile count a multiple of 8, each XCD still holds a compact
-//     group of tiles.
-__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, int N, int other, int wg, int rr,
-                                           BlockTiles& t) {
+//     group of tiles.  The blocks whose slot tiles are all live come first
+//     (launch_tile_ranges), so that a round's tiles are whole blocks of one
+//     expert, not the tail of one block and the head of the next.
+// ext: the blocks' extents; W: slots per slot tile.
+__device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, const int32_t* __restrict__ ext, int W,
+                                           int N, int wg, int rr, BlockTiles& t) {
   const int total = start[N];
   const int t8 = (total + 7) & ~7;   // the XCD remap needs a multiple of 8 ids
   if (wg >= t8) return false;
@@ -42,7 +45,7 @@ __device__ __forceinline__ bool block_tile(const int32_t* __restrict__ start, in
   const int b = start[N + 1 + id];   // the tile -> block map after the starts
   t.b = b;
   t.local = id - start[b];
-  t.slots = (start[b + 1] - start[b]) / other;
+  t.slots = (ext[b] + W - 1) / W;
   return true;
 }
 
