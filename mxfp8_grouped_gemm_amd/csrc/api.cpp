@@ -396,9 +396,8 @@ constexpr int64_t kRoundRobinWeightBytes = int64_t(32) << 20;
 
 // The bias reductions ride on the gather of dY rows (one read of each row)
 // when H is a multiple of 128 and those rows are gathered, i.e. no a*dY
-// checkpoint replaces them; otherwise they run as kernels of their own.
-// The bias reductions inside dY's gather, which then reads dY at 32-bit offsets
-// (under 2 GiB); otherwise their own kernels.
+// checkpoint replaces them, and dY is under 2 GiB (that gather then reads it
+// at 32-bit offsets); otherwise they run as kernels of their own.
 static bool moe_fuse_bias(const moe_bwd_mxfp8_args* a) {
   return a->has_bias && a->H % 128 == 0 && !a->down_proj_act_checkpoint && a->T * a->H * 2 <= INT32_MAX;
 }
