@@ -440,8 +440,8 @@ __global__ void __launch_bounds__(256) tile_ranges_kernel(const int32_t* __restr
     const int b = b0 + threadIdx.x;
     const int c = b < N ? (ext[b] + W - 1) / W * other : 0;
     const bool full = rr && c == cmax;
-    int tot_full, tot_part;
-    const int pos_full = block_exclusive_scan(full ? c : 0, red, &tot_full) + carry_full;
+    int tot_full = 0, tot_part;
+    const int pos_full = rr ? block_exclusive_scan(full ? c : 0, red, &tot_full) + carry_full : 0;   // rr: uniform
     const int pos_part = block_exclusive_scan(full ? 0 : c, red, &tot_part) + carry_part;
     if (b < N) start[b] = full ? pos_full : pos_part;   // partly filled blocks: relative for now
     __syncthreads();
